@@ -1,0 +1,698 @@
+"""Pins of the oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something the pages print, a closed
+form, a textbook or library routine, brute force, or an invariant of the
+method -- never against a retyping of the oracle's own formula.  The
+sections cited are those of "The inference core" page.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from workloads import blob as B
+from workloads.configs import Shape
+from conftest import read_table, golden_constants
+
+M64 = (1 << 64) - 1
+
+
+def s64(v: int) -> int:
+    v &= M64
+    return v - (1 << 64) if v >> 63 else v
+
+
+# --------------------------------------------------------------------------
+# "The resumable state": the four run-account sizes the page prints
+
+def test_pages_state_sizes_match_printed_values():
+    rows = read_table("state_sizes.txt")
+    assert len(rows) == 4
+    for r in rows:
+        cfg = tuple(int(v) for v in r[1:8])
+        pb, mx, cp, size = (int(v) for v in r[8:12])
+        assert O.pages_state_size(cfg, pb, mx) == size, r
+        # the cache-positions rule: prompt bytes + max + 1, up to the context
+        assert min(pb + mx + 1, cfg[6]) == cp
+
+
+def test_ids_state_shares_the_pages_buffer_table():
+    # The ids-in state differs from the page's account only in its first
+    # buffers; from the activations on the two are the same table.
+    cfg = (288, 768, 6, 6, 6, 32000, 256)
+    L = O.state_layout(cfg, 10, 16)
+    cp = 10 + 16 - 1
+    assert L["cache_positions"] == cp
+    assert L["ids"] == 128 and L["out"] == 128 + 40
+    assert L["w1"] - L["x"] == 8 * 288 and L["up"] - L["gate"] == 8 * 768
+    assert L["scores"] - L["logits"] == 8 * 32000
+    assert L["keys"] - L["scores"] == 8 * cp
+    assert L["values"] - L["keys"] == 4 * 6 * cp * 288
+    assert L["total"] - L["values"] == 4 * 6 * cp * 288
+    pages = O.pages_state_size(cfg, 0, cp - 1)  # cache positions = 0 + (cp-1) + 1
+    tail_pages = pages - 256 - (128 + 0 + 8 + 4 * (cp - 1) + 128 * (cp - 1))
+    assert L["total"] - L["x"] == tail_pages
+
+
+# --------------------------------------------------------------------------
+# "RMS normalization"
+
+def test_isqrt_matches_math_isqrt():
+    rng = np.random.default_rng(5)
+    cases = list(range(0, 5000)) + [2**64 - 1, 2**63, 2**62, 2**32, 2**32 - 1]
+    for k in [1, 2, 3, 255, 65535, 65536, 2**31 - 1, 2**31, 2**32 - 1]:
+        cases += [k * k - 1, k * k, k * k + 1, k * k + 2 * k]
+    cases += [int(v) for v in rng.integers(0, 2**63, 2000, dtype=np.uint64)]
+    cases += [int(v) << 1 for v in rng.integers(0, 2**63, 500, dtype=np.uint64)]
+    for n in cases:
+        n &= M64
+        assert O.isqrt(n) == math.isqrt(n), n
+
+
+def test_rmsnorm_of_constant_vector_is_one():
+    # mean(x^2) = x^2 for a constant vector, so x / rms(x) = sign(x): with
+    # unit weights the output is exactly +-1.0 (2^16) for c >= 1.
+    for d in (1, 7, 64, 4096):
+        for c in (1, 2, 3, 100):
+            for sign in (1, -1):
+                x = np.full(d, sign * c * 65536, dtype=np.int64)
+                w = np.full(d, 1 << 24, dtype=np.int32)
+                assert np.all(O.rmsnorm(x, w) == sign * 65536), (d, c, sign)
+
+
+def test_rmsnorm_epsilon_against_textbook():
+    # y = x * w / sqrt(mean(x^2) + 1e-5) with the page's epsilon; at tiny
+    # inputs the epsilon dominates, so a wrong epsilon fails.
+    K = golden_constants()
+    assert K["rms_epsilon_q32"] == round(1e-5 * 2**32)
+    rng = np.random.default_rng(7)
+    for scale in (1e-4, 1e-3, 3e-3, 1e-2, 0.5, 3.0):
+        xr = rng.standard_normal(256) * scale
+        x = np.rint(xr * 65536).astype(np.int64)
+        gr = 1.0 + 0.05 * rng.standard_normal(256)
+        w = np.rint(gr * 2**24).astype(np.int32)
+        xq, wq = x / 65536.0, w / 2.0**24
+        ref = xq * wq / np.sqrt(np.mean(xq * xq) + 1e-5)
+        got = O.rmsnorm(x, w) / 65536.0
+        # integer square root and two truncations: a few parts in rms, plus 2 ulp
+        rms = math.sqrt(np.mean(xq * xq) + 1e-5) * 65536
+        tol = np.abs(ref) * 2.0 / rms + 2.0 / 65536
+        assert np.all(np.abs(got - ref) <= tol), scale
+
+
+def test_rmsnorm_division_truncates_then_floors():
+    # One element, weight 1.0: y = (x * 2^24 / rms) >> 8.  For x = -1 (Q16)
+    # the quotient truncates to a small negative number and the shift
+    # floors it to -1: a floor division would give the same here, so use a
+    # case where truncation and floor differ before the shift.
+    x = np.array([-3], dtype=np.int64)
+    w = np.array([1 << 24], dtype=np.int32)
+    rms = math.isqrt(9 // 1 + 42950)
+    q = -((3 * (1 << 24)) // rms)          # truncation toward zero
+    assert O.rmsnorm(x, w)[0] == q >> 8     # Python >> floors
+
+
+# --------------------------------------------------------------------------
+# "A matrix row"
+
+def signed_dot(w, x):
+    return sum((int(b) - 128) * int(v) for b, v in zip(w, x))
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 64, 172, 1000])
+def test_row_equals_signed_dot_under_wrap(n):
+    # The page: unsigned bytes times 64-bit words, corrected once by
+    # 128 * sum, equal the signed dot product modulo 2^64.  Scale 2^24 shows
+    # the low 40 bits of that dot and scale 1 its high 40 bits.
+    rng = np.random.default_rng(n)
+    for trial in range(4):
+        w = rng.integers(0, 256, n, dtype=np.uint8)
+        if trial == 0:
+            x = rng.integers(-2**20, 2**20, n, dtype=np.int64)
+        else:
+            x = W.adversarial_row_inputs(1, n, 100 * n + trial)[0]
+        dot = signed_dot(w, x)
+        assert O.row(w, 1 << 24, x) == s64(dot << 24) >> 24
+        assert O.row(w, 1, x) == s64(dot) >> 24
+        if trial == 0:
+            assert O.row(w, 1 << 24, x) == dot
+
+
+def test_row_scale_zero_and_powers_of_two():
+    rng = np.random.default_rng(1)
+    w = rng.integers(0, 256, 300, dtype=np.uint8)
+    x = rng.integers(-2**30, 2**30, 300, dtype=np.int64)
+    dot = signed_dot(w, x)
+    assert O.row(w, 0, x) == 0
+    for k in range(0, 32):
+        # y = floor(dot * 2^k / 2^24) while the product stays in range, and
+        # the wrapped product beyond it
+        want = (dot << k) >> 24 if abs(dot << k) < 2**63 else s64(dot << k) >> 24
+        assert O.row(w, 1 << k, x) == want, k
+
+
+def test_row_matches_scaled_dot_with_floor():
+    rng = np.random.default_rng(2)
+    for n in (16, 4096):
+        w = rng.integers(0, 256, n, dtype=np.uint8)
+        x = np.rint(rng.standard_normal(n) * 2 * 65536).astype(np.int64)
+        for s in rng.integers(1 << 14, 1 << 18, 5):
+            s = int(s)
+            assert O.row(w, s, x) == (signed_dot(w, x) * s) // (1 << 24)
+
+
+def test_rows_batch_is_rows_of_single_vectors():
+    Wm, s, x = W.row_operands(37, 53, 5, 9)
+    y = O.rows(Wm, s, x)
+    for b in range(5):
+        for r in (0, 1, 36):
+            assert y[b, r] == O.row(Wm[r], int(s[r]), x[b])
+
+
+def test_rows_threads_do_not_change_results():
+    Wm, s, x = W.row_operands(257, 300, 3, 11)
+    O.set_threads(1)
+    y1 = O.rows(Wm, s, x)
+    O.set_threads(4)
+    y4 = O.rows(Wm, s, x)
+    O.set_threads(1)
+    assert np.array_equal(y1, y4)
+
+
+# --------------------------------------------------------------------------
+# Phase 8, rotary
+
+def test_rotation_special_angles():
+    rng = np.random.default_rng(3)
+    one = 1 << 24
+    for _ in range(200):
+        a, b = (int(v) for v in rng.integers(-2**38, 2**38, 2))
+        assert O.rotate(a, b, one, 0) == (a, b)          # 0 degrees
+        assert O.rotate(a, b, 0, one) == (-b, a)         # 90 degrees
+        assert O.rotate(a, b, -one, 0) == (-a, -b)       # 180 degrees
+        assert O.rotate(a, b, 0, -one) == (b, -a)        # 270 degrees
+
+
+def test_rotation_matches_real_rotation():
+    rng = np.random.default_rng(4)
+    for _ in range(500):
+        th = rng.uniform(-math.pi, math.pi)
+        c, s = round(math.cos(th) * 2**24), round(math.sin(th) * 2**24)
+        a, b = (int(v) for v in rng.integers(-2**24, 2**24, 2))
+        ra = (a * c - b * s) / 2**24
+        rb = (a * s + b * c) / 2**24
+        ga, gb = O.rotate(a, b, c, s)
+        assert abs(ga - ra) < 1.0 and abs(gb - rb) < 1.0
+
+
+# --------------------------------------------------------------------------
+# "Lookup tables"
+
+def test_exp_index_rules():
+    K = golden_constants()
+    cap = K["exp_index_cap"]
+    assert O.exp_index(0) == 0 and O.exp_index(255) == 0 and O.exp_index(256) == 1
+    assert O.exp_index(cap * 256 - 1) == cap - 1
+    assert O.exp_index(cap * 256) == cap
+    assert O.exp_index(2**40) == cap and O.exp_index(2**64 - 1) == cap
+    # a step of 1/256 in a Q16 difference: index = floor(d_real * 256)
+    rng = np.random.default_rng(6)
+    for d in rng.integers(0, 16 * 65536, 2000):
+        assert O.exp_index(int(d)) == math.floor(Fraction(int(d), 65536) * 256)
+
+
+def test_silu_index_and_edges_with_identity_table():
+    # With TAB[i] = i the table lookup shows its index: for -16 < x < 16 it
+    # is floor((x + 16) * 128), a step of 1/128 from -16.
+    tab = np.arange(4097, dtype=np.int32)
+    lim = golden_constants()["silu_limit_q16"]
+    assert lim == 16 * 65536
+    assert O.silu(lim, tab) == lim and O.silu(lim + 12345, tab) == lim + 12345
+    assert O.silu(2**62, tab) == 2**62
+    assert O.silu(-lim, tab) == 0 and O.silu(-2**62, tab) == 0
+    assert O.silu(-lim + 1, tab) == 0 and O.silu(lim - 1, tab) == 4095
+    rng = np.random.default_rng(8)
+    for x in rng.integers(-lim + 1, lim, 3000):
+        x = int(x)
+        assert O.silu(x, tab) == math.floor((Fraction(x, 65536) + 16) * 128)
+
+
+def test_silu_with_real_table_approximates_silu():
+    tab = B.silu_table()
+    rng = np.random.default_rng(9)
+    for xr in rng.uniform(-20, 20, 2000):
+        x = int(round(xr * 65536))
+        got = O.silu(x, tab) / 65536.0
+        xq = x / 65536.0
+        want = xq / (1 + math.exp(-xq)) if abs(xq) < 16 else (xq if xq >= 16 else 0.0)
+        # the table steps by 1/128 and SiLU's slope is below 1.1
+        assert abs(got - want) <= 1.1 / 128 + 2 / 65536, xr
+
+
+# --------------------------------------------------------------------------
+# "Attention, stage by stage"
+
+def test_attention_single_position_returns_value():
+    exp_tab = B.exp_table()
+    assert exp_tab[0] == 1 << 30
+    rng = np.random.default_rng(10)
+    for head in (2, 16, 128):
+        q = rng.integers(-2**20, 2**20, head).astype(np.int64)
+        K = rng.integers(-2**20, 2**20, (1, head)).astype(np.int32)
+        V = rng.integers(-2**31, 2**31, (1, head), dtype=np.int64).astype(np.int32)
+        out, p, m, ssum = O.attention_head(q, K, V, 2**24 // 4, exp_tab)
+        assert p[0] == 1 << 24 and ssum == 1 << 30
+        assert np.array_equal(out, V[0].astype(np.int64))
+
+
+def test_attention_equal_scores_give_uniform_weights():
+    exp_tab = B.exp_table()
+    rng = np.random.default_rng(11)
+    for n in (2, 3, 7, 100, 1000):
+        q = rng.integers(-2**18, 2**18, 16).astype(np.int64)
+        K = np.tile(rng.integers(-2**18, 2**18, 16).astype(np.int32), (n, 1))
+        c = rng.integers(-2**20, 2**20, 16)
+        V = np.tile(c.astype(np.int32), (n, 1))
+        out, p, m, ssum = O.attention_head(q, K, V, 4194304, exp_tab)
+        assert ssum == n << 30
+        assert np.all(p == (1 << 24) // n)
+        assert np.array_equal(out, (n * ((1 << 24) // n) * c.astype(object)) // (1 << 24))
+
+
+def test_attention_score_scaling_and_max():
+    # Scores: (((q . k) >> 16) * inv) >> 24; with inv = 2^24 / sqrt(head)
+    # that is the textbook q . k / sqrt(head) in Q16, floored twice.
+    exp_tab = B.exp_table()
+    rng = np.random.default_rng(12)
+    head = 64
+    inv = round(2**24 / math.sqrt(head))
+    assert inv == 2097152
+    q = rng.integers(-2**17, 2**17, head).astype(np.int64)
+    K = rng.integers(-2**17, 2**17, (40, head)).astype(np.int32)
+    V = rng.integers(-2**17, 2**17, (40, head)).astype(np.int32)
+    _, _, m, _ = O.attention_head(q, K, V, inv, exp_tab)
+    dots = [int(np.dot(q.astype(object), K[j].astype(object))) for j in range(40)]
+    scores = [((d >> 16) * inv) >> 24 for d in dots]
+    assert m == max(scores)
+    # and it is within two ulp of the real scaled dot
+    real = max(d / 65536.0 / math.sqrt(head) for d in dots)
+    assert abs(m - real) <= 2
+
+
+def test_attention_matches_softmax_attention():
+    exp_tab = B.exp_table()
+    rng = np.random.default_rng(13)
+    for head, n in ((16, 5), (64, 33), (128, 200)):
+        inv = round(2**24 / math.sqrt(head))
+        qr = rng.standard_normal(head)
+        Kr = rng.standard_normal((n, head))
+        Vr = rng.standard_normal((n, head))
+        q = np.rint(qr * 65536).astype(np.int64)
+        K = np.rint(Kr * 65536).astype(np.int32)
+        V = np.rint(Vr * 65536).astype(np.int32)
+        out, p, m, ssum = O.attention_head(q, K, V, inv, exp_tab)
+        sc = (K / 65536.0) @ (q / 65536.0) / math.sqrt(head)
+        pr = np.exp(sc - sc.max())
+        pr /= pr.sum()
+        ref = pr @ (V / 65536.0)
+        # probabilities: the table steps by 1/256 in the score difference
+        assert np.all(np.abs(p / 2**24 - pr) <= pr * (1 / 256.0 + 1e-3) + 2**-23)
+        assert np.all(np.abs(out / 65536.0 - ref) <= 0.01 * np.abs(V / 65536.0).max() + 1e-4)
+
+
+def test_attention_saturated_differences_use_last_entry():
+    # Differences of 16 or more all read entry 4,096.
+    exp_tab = np.arange(4097, dtype=np.uint32) + 1  # strictly positive, shows the index
+    head = 2
+    q = np.array([65536, 0], dtype=np.int64)
+    inv = 1 << 24
+    K = np.array([[0, 0], [-17 * 65536, 0], [-16 * 65536, 0], [-255, 0]], dtype=np.int32)
+    V = np.zeros((4, 2), dtype=np.int32)
+    _, p, m, ssum = O.attention_head(q, K, V, inv, exp_tab)
+    # scores (Q16): 0, -17.0, -16.0, -255/65536 -> floor -> -1 (one ulp)
+    e = [exp_tab[0], exp_tab[4096], exp_tab[4096], exp_tab[0]]
+    assert ssum == sum(int(v) for v in e)
+    assert m == 0
+
+
+# --------------------------------------------------------------------------
+# "Sampling"
+
+def test_xorshift_multiplier_is_the_printed_constant():
+    M = golden_constants()["xorshift_multiplier"]
+    rng = np.random.default_rng(14)
+    for st in rng.integers(1, 2**63, 50, dtype=np.uint64):
+        new, out = O.xorshift64s(int(st))
+        if new % 2 == 1:
+            # the multiplier is out / new modulo 2^64 (new is invertible)
+            assert (out * pow(new, -1, 1 << 64)) % (1 << 64) == M
+
+
+def _gf2_matmul(A, Bm):
+    # rows as 64-bit masks: (A*B) row i = xor of B rows j where A[i] has bit j
+    out = []
+    for a in A:
+        acc = 0
+        j = 0
+        while a:
+            if a & 1:
+                acc ^= Bm[j]
+            a >>= 1
+            j += 1
+        out.append(acc)
+    return out
+
+
+def _gf2_pow(A, e):
+    R = [1 << i for i in range(64)]
+    while e:
+        if e & 1:
+            R = _gf2_matmul(R, A)
+        A = _gf2_matmul(A, A)
+        e >>= 1
+    return R
+
+
+def test_xorshift_state_map_has_full_period():
+    # Marsaglia's xorshift generators are the GF(2)-linear maps T of maximal
+    # period 2^64 - 1: T^(2^64-1) = I and T^((2^64-1)/p) != I for each prime
+    # p dividing 2^64 - 1.  The map is read off the oracle one bit at a time.
+    cols = [O.xorshift64s(1 << i)[0] for i in range(64)]
+    # T as row masks: bit j of row i = bit i of T(e_j)
+    T = [sum(((cols[j] >> i) & 1) << j for j in range(64)) for i in range(64)]
+    I = [1 << i for i in range(64)]
+    order = (1 << 64) - 1
+    assert _gf2_pow(T, order) == I
+    for p in (3, 5, 17, 257, 641, 65537, 6700417):
+        assert _gf2_pow(T, order // p) != I, p
+
+
+def test_seed_zero_starts_at_golden_ratio_constant():
+    # 0x9E3779B97F4A7C15 is floor(2^64 / phi) = floor(2^63 (sqrt 5 - 1)).
+    K = golden_constants()
+    phi_frac = (math.isqrt(5 << 128) - (1 << 64)) // 2
+    assert phi_frac == K["seed_zero_state"]
+    cfg = (64, 172, 1, 4, 4, 512, 32)
+    e, st = O.init_state(cfg, [5, 6], 4, 0, 0)
+    assert e == 0 and O.state_info(st)[1]["generator"] == K["seed_zero_state"]
+    e, st = O.init_state(cfg, [5, 6], 4, 0, 77)
+    assert O.state_info(st)[1]["generator"] == 77
+
+
+def test_greedy_is_first_argmax():
+    rng = np.random.default_rng(15)
+    exp_tab = B.exp_table()
+    for _ in range(50):
+        lg = rng.integers(-5, 5, 300).astype(np.int64)  # many ties
+        tok, g = O.sample(lg, 0, exp_tab, 123)
+        assert tok == int(np.argmax(lg)) and g == 123
+
+
+def test_draw_walk_is_inverse_cdf():
+    # At temperature 1.0 (2^16) the sum pass reads the same entries as
+    # attention; the walk then picks the entry whose prefix-sum interval holds
+    # the draw: searchsorted over the cumulative sum.
+    rng = np.random.default_rng(16)
+    exp_tab = B.exp_table()
+    M = golden_constants()["xorshift_multiplier"]
+    for trial in range(40):
+        V = int(rng.integers(2, 500))
+        lg = rng.integers(-20 * 65536, 20 * 65536, V).astype(np.int64)
+        seed = int(rng.integers(1, 2**63))
+        tok, g = O.sample(lg, 65536, exp_tab, seed)
+        new, _ = O.xorshift64s(seed)
+        assert g == new
+        m = int(lg.max())
+        e = np.array([exp_tab[O.exp_index(m - int(v))] for v in lg], dtype=np.uint64)
+        cs = np.cumsum(e)
+        r = ((new * M) % (1 << 64)) % int(cs[-1])
+        assert tok == int(np.searchsorted(cs, r, side="right"))
+
+
+def test_temperature_sampling_frequencies():
+    # Over many seeds the draw follows the weights e_i / sum.
+    exp_tab = B.exp_table()
+    lg = np.array([0, -65536, -2 * 65536, -30 * 65536], dtype=np.int64)
+    counts = np.zeros(4)
+    n = 20000
+    for s in range(1, n + 1):
+        tok, _ = O.sample(lg, 65536, exp_tab, s * 0x9E3779B97F4A7C15 % (1 << 64))
+        counts[tok] += 1
+    want = np.exp(-np.arange(4.0) * np.array([1, 1, 1, 1]))
+    want[3] = math.exp(-16)
+    want /= want.sum()
+    assert np.all(np.abs(counts / n - want) < 0.015)
+
+
+# --------------------------------------------------------------------------
+# The artifact, the state and "Core errors"
+
+def tiny_setup(shape=None, seed=1000):
+    shape = shape or W.TINY.shape
+    bl = B.build_blob(shape, seed)
+    return shape, bl
+
+
+def test_blob_check_accepts_and_rejects():
+    shape, bl = tiny_setup()
+    assert O.blob_check(bl) == (0, shape.as_tuple())
+    bad = bl.copy(); bad[0] = ord("X")
+    assert O.blob_check(bad)[0] == 2
+    bad = bl.copy(); bad[8:12] = np.frombuffer(np.uint32(63).tobytes(), np.uint8)  # dim % heads
+    assert O.blob_check(bad)[0] == 1
+    lay = B.plan(shape)
+    bad = bl.copy(); bad[lay.offsets["exp"]:lay.offsets["exp"] + 4] = 0    # EXP[0] = 0
+    assert O.blob_check(bad)[0] == 2
+    assert O.blob_check(bl[: lay.sections[-1][0] + 10].copy())[0] == 5      # truncated
+    bad = bl.copy(); bad[40] += 1                                            # matrix count
+    assert O.blob_check(bad)[0] == 2
+    bad = bl.copy(); d0 = lay.offsets["desc"]; bad[d0 + 8] += 1              # rows
+    assert O.blob_check(bad)[0] == 2
+    bad = bl.copy(); bad[d0 + 32 * 2] = bad[d0 + 32]                         # duplicate kind
+    bad[d0 + 32 * 2 + 4] = bad[d0 + 32 + 4]
+    assert O.blob_check(bad)[0] == 2
+    # a section length shorter than its matrix
+    bad = bl.copy()
+    o = B.SECTION_TABLE + 16 * 3 + 8
+    bad[o:o + 8] = np.frombuffer(np.uint64(100).tobytes(), np.uint8)
+    assert O.blob_check(bad)[0] == 5
+
+
+def test_init_state_errors():
+    cfg = W.TINY.shape.as_tuple()
+    ctx = cfg[6]
+    assert O.init_state(cfg, [5] * 4, 0)[0] == 6                     # max 0
+    assert O.init_state(cfg, [5] * 4, ctx + 1)[0] == 6               # max > context
+    assert O.init_state(cfg, [], 4)[0] == 6                          # no ids
+    assert O.init_state(cfg, [512], 4)[0] == 6                       # id >= vocab
+    assert O.init_state(cfg, [5], 4, 16 * 65536 + 1)[0] == 6         # temperature > 16
+    assert O.init_state(cfg, [5], 4, 16 * 65536)[0] == 0
+    assert O.init_state(cfg, [5] * 16, 17)[0] == 0                   # 16 + 17 - 1 = 32
+    assert O.init_state(cfg, [5] * 16, 18)[0] == 7                   # 33 > 32
+    assert O.init_state((0,) + cfg[1:], [5], 4)[0] == 1
+    n = O.state_size(cfg, 3, 4)
+    assert O.state_size(cfg, 3, 0) == 2**64 - 1
+    assert O.init_state(cfg, [5] * 3, 4, state=O.aligned_zeros(n + 8))[0] == 4
+    buf = O.aligned_zeros(n + 8)[1:n + 1]
+    assert O.init_state(cfg, [5] * 3, 4, state=buf)[0] == 3           # misaligned
+
+
+def test_turn_state_errors():
+    shape, bl = tiny_setup()
+    cfg = shape.as_tuple()
+    e, st = O.init_state(cfg, [5, 6, 7], 2)
+    bad = st.copy(); bad[0] = 0
+    assert O.turn(bl, bad, 1) == 3
+    assert O.turn(bl, st, 10) == 0
+    assert O.state_info(st)[1]["complete"] == 1
+    assert O.turn(bl, st, 1) == 3                                   # complete
+    bad = bl.copy(); bad[0] = 0
+    e, st = O.init_state(cfg, [5, 6, 7], 2)
+    assert O.turn(bad, st, 1) == 2
+
+
+def fit_failure_blob(shape, kind, seed=1000):
+    """An artifact whose key or value rows overflow 32 bits at position 0."""
+    bl = B.build_blob(shape, seed)
+    w, s = B.matrix_view(bl, shape, kind, 0)
+    w[:] = 255
+    s[:] = 2**32 - 1
+    return bl
+
+
+@pytest.mark.parametrize("kind,phase", [(B.KIND_K, 6), (B.KIND_V, 7)])
+def test_cache_fit_check_fails_with_arithmetic(kind, phase):
+    shape = W.TINY.shape
+    bl = fit_failure_blob(shape, kind)
+    e, st = O.init_state(shape.as_tuple(), [5, 6, 7], 4)
+    assert O.turn(bl, st, 4) == 8
+    info = O.state_info(st)[1]
+    assert (info["error"], info["phase"], info["layer"], info["position"]) == (8, phase, 0, 0)
+    assert O.turn(bl, st, 1) == 3
+
+
+def test_rotary_fit_check_fails_at_phase_8():
+    # Keys that fit 32 bits before the rotation but not after it: key rows of
+    # +-(2^31 - 1) turned by 45 degrees.
+    shape = Shape(8, 16, 1, 1, 1, 16, 4)
+    cos, sin = B.rope_tables(shape)
+    c45 = round(2**24 * math.sqrt(0.5))
+    cos[0, :] = c45
+    sin[0, :] = c45
+    bl = B.build_blob(shape, 5, tables={"cos": cos, "sin": sin, "norm": np.full(3 * 8, 1 << 24, np.int32)})
+    w, s = B.matrix_view(bl, shape, B.KIND_K, 0)
+    Wq, sq = B.matrix_view(bl, shape, B.KIND_EMBED, 0)
+    # embedding: every element +1.0 exactly, so the normalized vector is all 1.0
+    Wq[:] = 129
+    sq[:] = 1 << 32 - 8  # (1 * 2^24) >> 8 = 2^16
+    # key row 2j: +x, row 2j+1: -x with x just below 2^31
+    w[0::2, :] = 255
+    w[1::2, :] = 1
+    s[:] = int((2**31 - 2**20) / (127 * 8) * 2**24 / 65536)
+    e, st = O.init_state(shape.as_tuple(), [3], 2)
+    assert O.turn(bl, st, 1) == 8
+    info = O.state_info(st)[1]
+    assert (info["phase"], info["layer"]) == (8, 0)
+
+
+# --------------------------------------------------------------------------
+# Whole-pass pins
+
+def run_logits(shape, bl, ids, max_tokens, temp=0, seed=0):
+    """Turn one position at a time; collect the logits at each generating
+    position and the final state."""
+    cfg = shape.as_tuple()
+    e, st = O.init_state(cfg, ids, max_tokens, temp, seed)
+    assert e == 0
+    L = O.state_layout(cfg, len(ids), max_tokens)
+    out = []
+    while True:
+        assert O.turn(bl, st, 1) == 0
+        info = O.state_info(st)[1]
+        if info["position"] >= len(ids):
+            out.append(st[L["logits"]: L["logits"] + 8 * shape.vocab].view(np.int64).copy())
+        if info["complete"]:
+            break
+    toks = st[L["out"]: L["out"] + 4 * max_tokens].view(np.uint32)[: info["generated"]].copy()
+    return out, toks, st, L
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa", "ragged"])
+def test_whole_pass_tracks_float_forward(name):
+    from float_model import FloatModel
+    shape = W.SMALL_SHAPES[name]
+    bl = B.build_blob(shape, 77)
+    ids = W.prompt_ids(shape.vocab, 6, 5, 0)
+    logits, toks, st, L = run_logits(shape, bl, ids, 8)
+    fm = FloatModel(bl, shape)
+    seq = list(ids) + list(toks)
+    k = 0
+    for t, tok in enumerate(seq[: len(ids) + len(toks) - 1]):
+        lf, xf = fm.step(int(tok))
+        if t >= len(ids) - 1:
+            got = logits[k] / 65536.0
+            k += 1
+            assert np.abs(got - lf).max() < 0.05, (t, np.abs(got - lf).max())
+            assert np.corrcoef(got, lf)[0, 1] > 0.999
+    x = st[L["x"]: L["x"] + 8 * shape.dim].view(np.int64) / 65536.0
+    assert np.abs(x - xf).max() < 0.05
+
+
+def test_activations_stay_below_eight():
+    shape = W.TINY.shape
+    bl = B.build_blob(shape, 1000)
+    ids = W.prompt_ids(shape.vocab, 16, 2000, 0)
+    logits, toks, st, L = run_logits(shape, bl, ids, 16)
+    assert len(toks) == 16
+    x = st[L["x"]: L["x"] + 8 * shape.dim].view(np.int64)
+    assert np.abs(x).max() < 8 * 65536
+
+
+def test_incremental_equals_recompute():
+    # Prefix runs (ids + the tokens generated so far, one token each) give the
+    # same tokens as the one run that keeps its cache: the cache holds what a
+    # recomputation would.
+    shape = W.SMALL_SHAPES["gqa"]
+    bl = B.build_blob(shape, 3)
+    ids = W.prompt_ids(shape.vocab, 5, 9, 0)
+    _, toks, _, _ = run_logits(shape, bl, ids, 6)
+    seq = list(ids)
+    for t in toks:
+        _, tk, _, _ = run_logits(shape, bl, seq, 1)
+        assert tk[0] == t
+        seq.append(int(t))
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    # Head h reads key/value head h / (heads / kv_heads): a grouped model is
+    # the same as the full-head model whose key and value rows repeat each
+    # group's head.
+    g = Shape(64, 96, 2, 8, 2, 100, 20)
+    m = Shape(64, 96, 2, 8, 8, 100, 20)
+    bg = B.build_blob(g, 21)
+    bm = B.build_blob(m, 22)
+    for l in range(2):
+        for kind in B.LAYER_KINDS:
+            wg, sg = B.matrix_view(bg, g, kind, l)
+            wm, sm = B.matrix_view(bm, m, kind, l)
+            if kind in (B.KIND_K, B.KIND_V):
+                hs = g.head_size
+                for h in range(8):
+                    src = h // 4
+                    wm[h * hs:(h + 1) * hs] = wg[src * hs:(src + 1) * hs]
+                    sm[h * hs:(h + 1) * hs] = sg[src * hs:(src + 1) * hs]
+            else:
+                wm[:] = wg
+                sm[:] = sg
+    for kind in (B.KIND_EMBED, B.KIND_CLS):
+        wm, sm = B.matrix_view(bm, m, kind)
+        wg, sg = B.matrix_view(bg, g, kind)
+        wm[:] = wg; sm[:] = sg
+    lg, lm = B.plan(g), B.plan(m)
+    for name in ("norm",):
+        n = 4 * (2 * 2 + 1) * 64
+        bm[lm.offsets[name]: lm.offsets[name] + n] = bg[lg.offsets[name]: lg.offsets[name] + n]
+    ids = [7, 8, 9, 10]
+    la, ta, _, _ = run_logits(g, bg, ids, 5)
+    lb, tb, _, _ = run_logits(m, bm, ids, 5)
+    assert np.array_equal(ta, tb)
+    for a, b in zip(la, lb):
+        assert np.array_equal(a, b)
+
+
+def test_turn_cuts_do_not_change_results():
+    shape = W.SMALL_SHAPES["ragged"]
+    bl = B.build_blob(shape, 31)
+    ids = W.prompt_ids(shape.vocab, 7, 3, 0)
+    cfg = shape.as_tuple()
+    e, a = O.init_state(cfg, ids, 9, 3 * 65536 // 2, 99)
+    assert O.run_to_end(bl, a) == 0
+    e, b = O.init_state(cfg, ids, 9, 3 * 65536 // 2, 99)
+    for k in (1, 3, 2, 1, 4, 100):
+        assert O.turn(bl, b, k) == 0
+        if O.state_info(b)[1]["complete"]:
+            break
+    # only the turn counter differs
+    ia, ib = O.state_info(a)[1], O.state_info(b)[1]
+    assert ia["turns"] == 1 and ib["turns"] > 1
+    a[80:88] = 0
+    b[80:88] = 0
+    assert np.array_equal(a, b)
+
+
+def test_stop_token_completes_the_run():
+    # A classifier that always prefers token 2 (the closing token): the first
+    # sampled token completes the run.
+    shape = W.TINY.shape
+    bl = B.build_blob(shape, 1000)
+    w, s = B.matrix_view(bl, shape, B.KIND_CLS)
+    s[:] = 0
+    s[2] = 1
+    w[2, :] = 255
+    e, st = O.init_state(shape.as_tuple(), [10, 11], 5)
+    assert O.run_to_end(bl, st) == 0
+    info = O.state_info(st)[1]
+    assert info["complete"] and info["generated"] == 1
