@@ -1,0 +1,189 @@
+"""Python binding of libfpi8 (include/fpi8.h): the same names, argument
+marshalling only.  Every step of the forward pass runs in the library's HIP
+kernels; this module converts numpy arrays, torch tensors and integers to
+pointers and back.
+
+Loading fails loudly when libfpi8.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfpi8.so")
+
+# Core error numbers ("Core errors") and the library's own.
+OK, INVALID_CONFIG, INVALID_FORMAT, INVALID_STATE, BUFFER_TOO_SMALL = 0, 1, 2, 3, 4
+MISSING_WEIGHTS, INVALID_PROMPT, CONTEXT_EXCEEDED, ARITHMETIC = 5, 6, 7, 8
+ERR_HIP, ERR_UNSUPPORTED, ERR_ARGUMENT = 100, 101, 102
+
+# Kernel classes of fpi8_engine_set_timing.
+T_ROWS, T_ATTN, T_NORM, T_SAMPLE, T_EMBED = range(5)
+
+UINT64_MAX = (1 << 64) - 1
+
+# Symbols include/fpi8.h declares.
+EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_init_state",
+           "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
+           "fpi8_engine_destroy", "fpi8_turn", "fpi8_engine_set_timing", "fpi8_engine_timing",
+           "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows")
+
+
+class fpi8_info(C.Structure):
+    _fields_ = [(n, C.c_uint32) for n in
+                ("phase", "layer", "position", "token", "n_ids", "max_tokens",
+                 "temperature_q16", "generated", "cache_positions", "error", "complete",
+                 "reserved")] + [("generator", C.c_uint64), ("turns", C.c_uint64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+_P = C.c_void_p
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        sig = {
+            "fpi8_blob_check": (C.c_int32, [_P, C.c_uint64, _P]),
+            "fpi8_state_size": (C.c_uint64, [_P, C.c_uint32, C.c_uint32]),
+            "fpi8_state_offsets": (C.c_int32, [_P, C.c_uint32, C.c_uint32, _P]),
+            "fpi8_init_state": (C.c_int32, [_P, _P, C.c_uint64, _P, C.c_uint32, C.c_uint32,
+                                            C.c_uint32, C.c_uint64]),
+            "fpi8_state_info": (C.c_int32, [_P, C.c_uint64, C.POINTER(fpi8_info)]),
+            "fpi8_output_tokens": (_P, [_P, C.c_uint64, C.POINTER(C.c_uint32)]),
+            "fpi8_engine_create": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint32,
+                                               C.POINTER(_P)]),
+            "fpi8_engine_destroy": (None, [_P]),
+            "fpi8_turn": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
+            "fpi8_engine_set_timing": (C.c_int32, [_P, C.c_int32, C.c_int32]),
+            "fpi8_engine_timing": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_double),
+                                               C.POINTER(C.c_uint64)]),
+            "fpi8_matrix_rows_workspace_size": (C.c_uint64, [C.c_uint32, C.c_uint32, C.c_uint32]),
+            "fpi8_matrix_rows": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32, _P,
+                                             _P, C.c_uint64, _P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(_P)
+
+
+def _cfg(cfg) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(cfg, dtype=np.uint32).reshape(7))
+
+
+def _dev_ptr(t) -> int:
+    """Device address of a torch tensor or a plain integer address."""
+    return t if isinstance(t, int) else int(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# ---- host functions ------------------------------------------------------------
+
+def fpi8_blob_check(blob: np.ndarray):
+    cfg = np.zeros(7, dtype=np.uint32)
+    e = lib().fpi8_blob_check(_np_ptr(blob), blob.size, _np_ptr(cfg))
+    return e, tuple(int(v) for v in cfg)
+
+
+def fpi8_state_size(cfg, n_ids: int, max_tokens: int) -> int:
+    return lib().fpi8_state_size(_np_ptr(_cfg(cfg)), n_ids, max_tokens)
+
+
+OFFSET_NAMES = ("ids", "out", "x", "w1", "w2", "w3", "gate", "up", "logits", "scores", "keys",
+                "values", "total")
+
+
+def fpi8_state_offsets(cfg, n_ids: int, max_tokens: int) -> dict:
+    out = np.zeros(13, dtype=np.uint64)
+    e = lib().fpi8_state_offsets(_np_ptr(_cfg(cfg)), n_ids, max_tokens, _np_ptr(out))
+    if e:
+        raise ValueError(f"fpi8_state_offsets: error {e}")
+    return dict(zip(OFFSET_NAMES, (int(v) for v in out)))
+
+
+def fpi8_init_state(cfg, state: np.ndarray, ids, max_tokens: int, temperature_q16: int = 0,
+                    seed: int = 0) -> int:
+    ids = np.ascontiguousarray(ids, dtype=np.uint32)
+    return lib().fpi8_init_state(_np_ptr(_cfg(cfg)), _np_ptr(state), state.size, _np_ptr(ids),
+                                 ids.size, max_tokens, temperature_q16, C.c_uint64(seed))
+
+
+def fpi8_state_info(state: np.ndarray):
+    info = fpi8_info()
+    e = lib().fpi8_state_info(_np_ptr(state), state.size, C.byref(info))
+    return e, info.as_dict()
+
+
+def fpi8_output_tokens(state: np.ndarray) -> np.ndarray:
+    n = C.c_uint32(0)
+    p = lib().fpi8_output_tokens(_np_ptr(state), state.size, C.byref(n))
+    if not p:
+        raise ValueError("fpi8_output_tokens: invalid state")
+    off = p - state.ctypes.data
+    return state[off: off + 4 * n.value].view(np.uint32).copy()
+
+
+# ---- the GPU engine ---------------------------------------------------------------
+
+def fpi8_engine_create(section0: np.ndarray, d_blob, blob_len: int, max_runs: int):
+    h = _P()
+    e = lib().fpi8_engine_create(_np_ptr(section0), section0.size, _dev_ptr(d_blob), blob_len,
+                                 max_runs, C.byref(h))
+    return e, h
+
+
+def fpi8_engine_destroy(engine) -> None:
+    lib().fpi8_engine_destroy(engine)
+
+
+def fpi8_turn(engine, d_states, state_stride: int, n_runs: int, max_positions: int,
+              stream=None):
+    errs = np.zeros(n_runs, dtype=np.int32)
+    e = lib().fpi8_turn(engine, _dev_ptr(d_states), state_stride, n_runs, max_positions,
+                        _stream_ptr(stream), _np_ptr(errs))
+    return e, errs
+
+
+def fpi8_engine_set_timing(engine, kernel: int, enable: bool) -> int:
+    return lib().fpi8_engine_set_timing(engine, kernel, 1 if enable else 0)
+
+
+def fpi8_engine_timing(engine, kernel: int):
+    ms = C.c_double(0)
+    n = C.c_uint64(0)
+    e = lib().fpi8_engine_timing(engine, kernel, C.byref(ms), C.byref(n))
+    return e, ms.value, n.value
+
+
+def fpi8_matrix_rows_workspace_size(rows: int, cols: int, batch: int) -> int:
+    return lib().fpi8_matrix_rows_workspace_size(rows, cols, batch)
+
+
+def fpi8_matrix_rows(d_W, d_scale, rows: int, cols: int, d_x, batch: int, d_y, d_work,
+                     work_len: int, stream=None) -> int:
+    return lib().fpi8_matrix_rows(_dev_ptr(d_W), _dev_ptr(d_scale), rows, cols, _dev_ptr(d_x),
+                                  batch, _dev_ptr(d_y), _dev_ptr(d_work), work_len,
+                                  _stream_ptr(stream))

@@ -1,0 +1,422 @@
+// fpi8_engine.cpp - the GPU engine of libfpi8: binds an artifact in device
+// memory, owns the workspace, and runs turns by launching the kernels of
+// fpi8_kernels.hip one position at a time for a whole batch of runs.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/fpi8.h"
+#include "fpi8_internal.h"
+
+using namespace fpi8;
+
+namespace {
+
+constexpr int kTimingClasses = 5;
+enum { T_ROWS = 0, T_ATTN = 1, T_NORM = 2, T_SAMPLE = 3, T_EMBED = 4 };
+
+struct Mat {
+  const uint8_t *W = nullptr;
+  const uint32_t *S = nullptr;
+  uint32_t rows = 0, cols = 0;
+  bool vec = false;
+};
+
+struct Timer {
+  bool on = false;
+  std::vector<hipEvent_t> starts, stops;
+  size_t used = 0;
+};
+
+inline uint32_t round_up(uint32_t v, uint32_t m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+struct fpi8_engine {
+  Model model;
+  Cfg c;
+  const uint8_t *d_blob = nullptr;
+  uint64_t blob_len = 0;
+  uint32_t max_runs = 0, bp = 0, kp = 0, max_npos = 0;
+  const uint32_t *exp_tab = nullptr;
+  const int32_t *silu = nullptr, *cos_t = nullptr, *sin_t = nullptr, *norm = nullptr;
+  std::vector<Mat> mats;  // [0] embedding, [1 + 7l + kind - 1], [1 + 7L] classifier
+  // device workspace
+  RunDesc *d_runs = nullptr;
+  int8_t *d_planes0 = nullptr, *d_planes1 = nullptr;
+  uint32_t *d_oflags = nullptr;
+  uint32_t n_oflags = 0;
+  int32_t *d_run_err = nullptr;
+  // pinned host buffers
+  RunDesc *h_runs = nullptr;
+  uint8_t *h_headers = nullptr;
+  int32_t *h_err = nullptr;
+  Timer timers[kTimingClasses];
+
+  const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
+};
+
+namespace {
+
+int hip_ok(hipError_t e) { return e == hipSuccess ? 0 : FPI8_ERR_HIP; }
+
+// Brackets a launch with events when its class is being timed.
+struct TimedLaunch {
+  fpi8_engine *e;
+  int cls;
+  hipStream_t s;
+  bool on;
+  TimedLaunch(fpi8_engine *eng, int c, hipStream_t st) : e(eng), cls(c), s(st) {
+    Timer &t = e->timers[cls];
+    on = t.on;
+    if (!on) return;
+    if (t.used == t.starts.size()) {
+      hipEvent_t a, b;
+      (void)hipEventCreate(&a);
+      (void)hipEventCreate(&b);
+      t.starts.push_back(a);
+      t.stops.push_back(b);
+    }
+    (void)hipEventRecord(t.starts[t.used], s);
+  }
+  ~TimedLaunch() {
+    if (!on) return;
+    Timer &t = e->timers[cls];
+    (void)hipEventRecord(t.stops[t.used], s);
+    t.used++;
+  }
+};
+
+uint32_t batch_tiles(uint32_t n_runs) { return n_runs <= 16 ? 1 : n_runs <= 32 ? 2 : 4; }
+
+RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t cols,
+                   const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer) {
+  RowsArgs a;
+  memset(&a, 0, sizeof a);
+  a.cols = cols;
+  a.kblocks = (cols + 63) / 64;
+  a.planes = planes;
+  a.kp = e->kp;
+  a.bp = e->bp;
+  a.n_runs = n_runs;
+  a.in_sel = in_sel;
+  a.oflag = oflag;
+  a.states = states;
+  a.runs = e->d_runs;
+  a.layer = layer;
+  a.rope_cos = e->cos_t;
+  a.rope_sin = e->sin_t;
+  a.silu = e->silu;
+  a.head = e->c.head;
+  a.half = e->c.head / 2;
+  a.kv_heads = e->c.kv_heads;
+  a.hidden = e->c.hidden;
+  return a;
+}
+
+void add_seg(RowsArgs &a, const Mat &m, uint32_t role, uint32_t rows_per_tile) {
+  Seg &s = a.seg[a.nseg++];
+  s.W = m.W;
+  s.S = m.S;
+  s.rows = m.rows;
+  s.tile0 = a.ntiles;
+  s.role = role;
+  s.pad = m.vec ? 1u : 0u;
+  a.ntiles += (m.rows + rows_per_tile - 1) / rows_per_tile;
+}
+
+int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t s) {
+  const uint32_t bt = batch_tiles(n_runs);
+  const uint32_t chunks = (n_runs + 16 * bt - 1) / (16 * bt);
+  TimedLaunch t(e, T_ROWS, s);
+  return launch_rows(epi, epi == EPI_GATEUP ? 2 : 1, (int)bt, a, chunks, s);
+}
+
+// One position of every active run.
+int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
+  const Cfg &c = e->c;
+  int r;
+  {
+    BeginArgs a{states, e->d_runs, n_runs, e->d_oflags, e->n_oflags};
+    if ((r = launch_begin(a, s))) return r;
+  }
+  {
+    EmbedArgs a{states, e->d_runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S};
+    TimedLaunch t(e, T_EMBED, s);
+    if ((r = launch_embed(a, s))) return r;
+  }
+  for (uint32_t l = 0; l < c.layers; l++) {
+    uint32_t *fl = e->d_oflags + 4 * l;
+    NormArgs na{states, e->d_runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
+                e->d_planes0, e->kp, e->bp, fl + 0, 0};
+    {
+      TimedLaunch t(e, T_NORM, s);
+      if ((r = launch_norm(na, s))) return r;
+    }
+    {
+      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 0, IN_W1, l);
+      add_seg(a, e->layer_mat(l, M_Q), ROLE_Q, 16);
+      add_seg(a, e->layer_mat(l, M_K), ROLE_K, 16);
+      add_seg(a, e->layer_mat(l, M_V), ROLE_V, 16);
+      if ((r = run_rows(e, EPI_QKV, a, n_runs, s))) return r;
+    }
+    {
+      AttnArgs a{states, e->d_runs, n_runs, l, c.heads, c.kv_heads, c.head,
+                 c.heads / c.kv_heads, e->model.inv, e->exp_tab, e->d_planes0, e->kp, e->bp,
+                 fl + 1, e->max_npos};
+      TimedLaunch t(e, T_ATTN, s);
+      if ((r = launch_attention(a, s))) return r;
+    }
+    {
+      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 1, IN_W3, l);
+      add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN, 16);
+      if ((r = run_rows(e, EPI_RESID, a, n_runs, s))) return r;
+    }
+    na.w = e->norm + (uint64_t)(2 * l + 1) * c.dim;
+    na.oflag = fl + 2;
+    {
+      TimedLaunch t(e, T_NORM, s);
+      if ((r = launch_norm(na, s))) return r;
+    }
+    {
+      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 2, IN_W1, l);
+      add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN, 16);
+      a.ntiles = 0;  // gate and up share the tile index
+      add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN, 16);
+      a.planes_out = e->d_planes1;
+      a.kp_out = e->kp;
+      a.oflag_out = fl + 3;
+      if ((r = run_rows(e, EPI_GATEUP, a, n_runs, s))) return r;
+    }
+    {
+      RowsArgs a = rows_base(e, states, n_runs, c.hidden, e->d_planes1, fl + 3, IN_GATE, l);
+      add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN, 16);
+      if ((r = run_rows(e, EPI_DOWN, a, n_runs, s))) return r;
+    }
+  }
+  uint32_t *ff = e->d_oflags + 4 * c.layers;
+  {
+    NormArgs na{states, e->d_runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
+                e->d_planes0, e->kp, e->bp, ff, 1};
+    TimedLaunch t(e, T_NORM, s);
+    if ((r = launch_norm(na, s))) return r;
+  }
+  {
+    RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, ff, IN_W1, 0);
+    add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN, 16);
+    if ((r = run_rows(e, EPI_CLS, a, n_runs, s))) return r;
+  }
+  {
+    SampleArgs a{states, e->d_runs, n_runs, c.vocab, e->exp_tab, e->d_run_err};
+    TimedLaunch t(e, T_SAMPLE, s);
+    if ((r = launch_sample(a, s))) return r;
+  }
+  return 0;
+}
+
+void release(fpi8_engine *e) {
+  if (!e) return;
+  (void)hipFree(e->d_runs);
+  (void)hipFree(e->d_planes0);
+  (void)hipFree(e->d_planes1);
+  (void)hipFree(e->d_oflags);
+  (void)hipFree(e->d_run_err);
+  (void)hipHostFree(e->h_runs);
+  (void)hipHostFree(e->h_headers);
+  (void)hipHostFree(e->h_err);
+  for (Timer &t : e->timers) {
+    for (hipEvent_t ev : t.starts) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : t.stops) (void)hipEventDestroy(ev);
+  }
+  delete e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *d_blob,
+                           uint64_t blob_len, uint32_t max_runs, fpi8_engine **out) {
+  if (!out || !h_section0 || !d_blob || max_runs == 0 || max_runs > 65536) return FPI8_ERR_ARGUMENT;
+  *out = nullptr;
+  fpi8_engine *e = new fpi8_engine();
+  int r = parse_section0(h_section0, section0_len, blob_len, &e->model);
+  if (r) { delete e; return r; }
+  e->c = e->model.cfg;
+  const Cfg &c = e->c;
+  if (c.head > 256) { delete e; return FPI8_ERR_UNSUPPORTED; }
+  e->d_blob = d_blob;
+  e->blob_len = blob_len;
+  e->max_runs = max_runs;
+  e->max_npos = c.context;
+  if (attention_lds_bytes(e->max_npos, c.head) > 160 * 1024) { delete e; return FPI8_ERR_UNSUPPORTED; }
+  e->exp_tab = reinterpret_cast<const uint32_t *>(d_blob + e->model.off_exp);
+  e->silu = reinterpret_cast<const int32_t *>(d_blob + e->model.off_silu);
+  e->cos_t = reinterpret_cast<const int32_t *>(d_blob + e->model.off_cos);
+  e->sin_t = reinterpret_cast<const int32_t *>(d_blob + e->model.off_sin);
+  e->norm = reinterpret_cast<const int32_t *>(d_blob + e->model.off_norm);
+  e->mats.resize(e->model.mats.size());
+  for (size_t i = 0; i < e->mats.size(); i++) {
+    const MatLoc &ml = e->model.mats[i];
+    Mat &m = e->mats[i];
+    m.W = d_blob + ml.w;
+    m.S = reinterpret_cast<const uint32_t *>(d_blob + ml.s);
+    m.rows = ml.rows;
+    m.cols = ml.cols;
+    m.vec = (ml.cols % 16 == 0) && ((reinterpret_cast<uintptr_t>(m.W) & 15) == 0);
+  }
+  // Workspace: digit planes [3][bp][kp] twice, run descriptors, flags.
+  e->bp = round_up(max_runs, 64);
+  e->kp = round_up(std::max(c.dim, c.hidden), 64);
+  e->n_oflags = 4 * c.layers + 1;
+  const size_t planes = 3ull * e->bp * e->kp;
+  if ((r = hip_ok(hipMalloc(&e->d_runs, sizeof(RunDesc) * max_runs))) ||
+      (r = hip_ok(hipMalloc(&e->d_planes0, planes))) ||
+      (r = hip_ok(hipMalloc(&e->d_planes1, planes))) ||
+      (r = hip_ok(hipMalloc(&e->d_oflags, 4ull * e->n_oflags))) ||
+      (r = hip_ok(hipMalloc(&e->d_run_err, 4ull * max_runs))) ||
+      (r = hip_ok(hipHostMalloc(&e->h_runs, sizeof(RunDesc) * max_runs))) ||
+      (r = hip_ok(hipHostMalloc(&e->h_headers, 128ull * max_runs))) ||
+      (r = hip_ok(hipHostMalloc(&e->h_err, 4ull * max_runs))) ||
+      (r = hip_ok(hipMemset(e->d_planes0, 0, planes))) ||
+      (r = hip_ok(hipMemset(e->d_planes1, 0, planes))) ||
+      (r = hip_ok(hipMemset(e->d_oflags, 0, 4ull * e->n_oflags))) ||
+      (r = kernels_init(e->max_npos, c.head))) {
+    release(e);
+    return r;
+  }
+  *out = e;
+  return 0;
+}
+
+void fpi8_engine_destroy(fpi8_engine *e) { release(e); }
+
+int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
+                  uint32_t max_positions, void *stream, int32_t *h_run_errors) {
+  if (!e || !d_states || n_runs == 0 || n_runs > e->max_runs) return FPI8_ERR_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  if ((reinterpret_cast<uintptr_t>(d_states) & 7) != 0 || (stride & 7) != 0 || stride < 128) {
+    if (h_run_errors)
+      for (uint32_t b = 0; b < n_runs; b++) h_run_errors[b] = FPI8_INVALID_STATE;
+    return FPI8_INVALID_STATE;
+  }
+  int r;
+  // Read every header, check it, fill the static run descriptors.
+  if ((r = hip_ok(hipMemcpy2DAsync(e->h_headers, 128, d_states, stride, 128, n_runs,
+                                   hipMemcpyDeviceToHost, s))) ||
+      (r = hip_ok(hipStreamSynchronize(s))))
+    return r;
+  uint32_t steps = 0;
+  for (uint32_t b = 0; b < n_runs; b++) {
+    RunDesc &rd = e->h_runs[b];
+    memset(&rd, 0, sizeof rd);
+    const uint8_t *h = e->h_headers + 128ull * b;
+    StateLayout L;
+    const int chk = check_header(e->c, h, stride, &L);
+    e->h_err[b] = chk > 0 ? chk : 0;
+    if (chk != 0) continue;
+    uint32_t v;
+    memcpy(&v, h + ST_NIDS, 4); rd.n_ids = v;
+    memcpy(&v, h + ST_MAX, 4); rd.max_tokens = v;
+    memcpy(&v, h + ST_TEMP, 4); rd.temp = v;
+    rd.cachepos = L.cachepos;
+    rd.valid = 1;
+    rd.base = stride * b;
+    rd.off_x = L.x; rd.off_w1 = L.w1; rd.off_w2 = L.w2; rd.off_w3 = L.w3;
+    rd.off_gate = L.gate; rd.off_up = L.up; rd.off_logits = L.logits; rd.off_scores = L.scores;
+    rd.off_keys = L.keys; rd.off_values = L.values; rd.off_ids = L.ids; rd.off_out = L.out;
+    memcpy(&v, h + ST_POSITION, 4);
+    steps = std::max(steps, L.cachepos - v);
+  }
+  steps = std::min(steps, max_positions);
+  if ((r = hip_ok(hipMemcpyAsync(e->d_runs, e->h_runs, sizeof(RunDesc) * n_runs,
+                                 hipMemcpyHostToDevice, s))) ||
+      (r = hip_ok(hipMemcpyAsync(e->d_run_err, e->h_err, 4ull * n_runs, hipMemcpyHostToDevice, s))))
+    return r;
+  if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
+  for (uint32_t k = 0; k < steps; k++)
+    if ((r = step(e, d_states, n_runs, s))) return r;
+  if ((r = hip_ok(hipMemcpyAsync(e->h_err, e->d_run_err, 4ull * n_runs, hipMemcpyDeviceToHost, s))) ||
+      (r = hip_ok(hipStreamSynchronize(s))))
+    return r;
+  int32_t first = 0;
+  for (uint32_t b = 0; b < n_runs; b++) {
+    if (h_run_errors) h_run_errors[b] = e->h_err[b];
+    if (!first && e->h_err[b]) first = e->h_err[b];
+  }
+  return first;
+}
+
+int32_t fpi8_engine_set_timing(fpi8_engine *e, int32_t kernel, int32_t enable) {
+  if (!e || kernel < 0 || kernel >= kTimingClasses) return FPI8_ERR_ARGUMENT;
+  Timer &t = e->timers[kernel];
+  t.on = enable != 0;
+  t.used = 0;
+  return 0;
+}
+
+int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uint64_t *launches) {
+  if (!e || kernel < 0 || kernel >= kTimingClasses) return FPI8_ERR_ARGUMENT;
+  Timer &t = e->timers[kernel];
+  double sum = 0;
+  for (size_t i = 0; i < t.used; i++) {
+    if (hipEventSynchronize(t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, t.starts[i], t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = t.used;
+  return 0;
+}
+
+uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
+  (void)rows;
+  const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
+  return 256 + 3 * bp * kp;
+}
+
+int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
+                         uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
+                         void *d_work, uint64_t work_len, void *stream) {
+  if (!d_W || !d_scale || !d_x || !d_y || !d_work || rows == 0 || cols == 0 || batch == 0 ||
+      cols > 65536 || batch > 65536)
+    return FPI8_ERR_ARGUMENT;
+  if (work_len < fpi8_matrix_rows_workspace_size(rows, cols, batch) ||
+      (reinterpret_cast<uintptr_t>(d_work) & 255) != 0)
+    return FPI8_ERR_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t kp = round_up(cols, 64), bp = round_up(batch, 64);
+  uint32_t *flag = reinterpret_cast<uint32_t *>(d_work);
+  int8_t *planes = reinterpret_cast<int8_t *>(d_work) + 256;
+  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
+  if (r) return r;
+  RowsArgs a;
+  memset(&a, 0, sizeof a);
+  a.cols = cols;
+  a.kblocks = (cols + 63) / 64;
+  a.planes = planes;
+  a.kp = kp;
+  a.bp = bp;
+  a.n_runs = batch;
+  a.in_sel = IN_RAW;
+  a.oflag = flag;
+  a.x_raw = d_x;
+  a.y_raw = d_y;
+  Seg &sg = a.seg[0];
+  sg.W = d_W;
+  sg.S = d_scale;
+  sg.rows = rows;
+  sg.tile0 = 0;
+  sg.role = ROLE_PLAIN;
+  sg.pad = (cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0) ? 1u : 0u;
+  a.nseg = 1;
+  a.ntiles = (rows + 15) / 16;
+  const uint32_t bt = batch_tiles(batch);
+  const uint32_t chunks = (batch + 16 * bt - 1) / (16 * bt);
+  return launch_rows(EPI_RAW, 1, (int)bt, a, chunks, s);
+}
+
+}  // extern "C"

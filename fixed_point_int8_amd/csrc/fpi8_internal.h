@@ -1,0 +1,179 @@
+// fpi8_internal.h - types shared by the host side and the HIP kernels of
+// libfpi8 (the MI355X fixed-point inference core).  Not part of the C ABI.
+#pragma once
+#include <stdint.h>
+
+#include <vector>
+
+namespace fpi8 {
+
+// Configuration: dim, hidden, layers, heads, kv_heads, vocab, context.
+struct Cfg {
+  uint32_t dim, hidden, layers, heads, kv_heads, vocab, context;
+  uint32_t head, kvd;
+};
+
+bool cfg_from_words(const uint32_t w[7], Cfg *c);
+
+// Where a matrix lies inside the artifact (byte offsets from its start).
+struct MatLoc {
+  uint64_t w = 0, s = 0;
+  uint32_t rows = 0, cols = 0;
+};
+
+// Section zero, parsed: table offsets and the matrix table, [0] embedding,
+// [1 + 7 * layer + kind - 1] layer matrices, [1 + 7 * layers] classifier.
+struct Model {
+  Cfg cfg;
+  uint32_t inv;
+  uint64_t off_exp, off_silu, off_cos, off_sin, off_norm;
+  std::vector<MatLoc> mats;
+};
+
+int parse_section0(const uint8_t *s0, uint64_t s0_len, uint64_t blob_len, Model *m);
+
+// Byte offsets of a run's buffers inside its state.
+struct StateLayout {
+  uint64_t ids, out, x, w1, w2, w3, gate, up, logits, scores, keys, values, total;
+  uint32_t cachepos;
+};
+bool state_layout(const Cfg &c, uint32_t n_ids, uint32_t max_tokens, StateLayout *L);
+int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L);
+
+// State header field offsets.
+enum : uint32_t {
+  ST_PHASE = 8, ST_LAYER = 12, ST_ROW = 16, ST_POSITION = 20, ST_TOKEN = 24, ST_ERROR = 28,
+  ST_NIDS = 32, ST_MAX = 36, ST_TEMP = 40, ST_GENERATED = 44, ST_CACHEPOS = 48,
+  ST_GENERATOR = 72, ST_TURNS = 80, ST_HEADER = 128
+};
+
+// Matrix kinds of the artifact.
+enum : uint32_t { M_EMBED, M_Q, M_K, M_V, M_O, M_GATE, M_UP, M_DOWN, M_CLS, M_KINDS };
+
+// What one launch needs to know about a run.  The static part is filled on
+// the host at the start of a turn, the dynamic part by the first kernel of
+// every position.
+struct RunDesc {
+  // dynamic
+  uint32_t flags;     // RUN_ACTIVE, RUN_GEN
+  uint32_t pos;       // position computed in this step
+  uint32_t token;     // token embedded in this step
+  uint32_t errkey;    // first failing (layer, phase) of this step, ~0 if none
+  // static
+  uint32_t n_ids, max_tokens, temp, cachepos;
+  uint32_t valid;     // passed the host checks at the start of the turn
+  uint32_t pad;
+  uint64_t base;      // byte offset of the run's state in the arena
+  uint64_t off_x, off_w1, off_w2, off_w3, off_gate, off_up, off_logits, off_scores;
+  uint64_t off_keys, off_values, off_ids, off_out;
+};
+
+enum : uint32_t { RUN_ACTIVE = 1u, RUN_GEN = 2u };
+
+// Rows of one matrix inside a row-kernel launch.
+struct Seg {
+  const uint8_t *W;      // rows x cols weight bytes (weight + 128), row-major
+  const uint32_t *S;     // rows Q24 scales
+  uint32_t rows;
+  uint32_t tile0;        // first row tile of this matrix in the launch
+  uint32_t role;         // epilogue role of the rows (ROLE_*)
+  uint32_t pad;
+};
+
+enum : uint32_t { ROLE_Q, ROLE_K, ROLE_V, ROLE_PLAIN };
+
+// Epilogues of the row kernel.
+enum : int { EPI_RAW, EPI_QKV, EPI_RESID, EPI_GATEUP, EPI_DOWN, EPI_CLS };
+
+// Which i64 input the exact (non-limb) path reads.
+enum : uint32_t { IN_W1, IN_W3, IN_GATE, IN_RAW };
+
+struct RowsArgs {
+  Seg seg[3];
+  uint32_t nseg;
+  uint32_t ntiles;          // row tiles (16 * MT rows each) over all segments
+  uint32_t cols;            // contraction length
+  uint32_t kblocks;         // ceil(cols / 64)
+  const int8_t *planes;     // [3][bp][kp] signed digits of the input
+  uint32_t kp;              // plane pitch in bytes (multiple of 64, >= kblocks * 64)
+  uint32_t bp;              // planes per limb (multiple of 16)
+  uint32_t n_runs;
+  uint32_t in_sel;          // IN_* for the exact path
+  const uint32_t *oflag;    // nonzero: some input needs more than three limbs
+  // context
+  uint8_t *states;          // state arena (turn) or nullptr (standalone)
+  RunDesc *runs;
+  uint32_t layer;
+  const int32_t *rope_cos, *rope_sin;   // [context][head/2]
+  const int32_t *silu;                  // [4097]
+  uint32_t head, half, kv_heads, hidden;
+  // gate/up epilogue: digits of the hidden vector for the down matrix
+  int8_t *planes_out;
+  uint32_t kp_out;
+  uint32_t *oflag_out;
+  // standalone matrix rows
+  const int64_t *x_raw;     // [n_runs][cols]
+  int64_t *y_raw;           // [n_runs][rows]
+};
+
+struct NormArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs, dim;
+  const int32_t *w;         // norm weights
+  int8_t *planes;
+  uint32_t kp, bp;
+  uint32_t *oflag;
+  uint32_t final_norm;      // 1: only generating runs (phase 17)
+};
+
+struct EmbedArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs, dim, vocab;
+  const uint8_t *E;
+  const uint32_t *S;
+};
+
+struct AttnArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs, layer, heads, kv_heads, head, group;
+  uint32_t inv;
+  const uint32_t *exp_tab;
+  int8_t *planes;
+  uint32_t kp, bp;
+  uint32_t *oflag;
+  uint32_t max_npos;        // LDS sized for this many positions
+};
+
+struct SampleArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs, vocab;
+  const uint32_t *exp_tab;
+  int32_t *run_err;
+};
+
+struct BeginArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs;
+  uint32_t *oflags;
+  uint32_t n_oflags;
+};
+
+// Launchers (defined in the .hip file).
+int launch_begin(const BeginArgs &a, void *stream);
+int launch_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs, void *stream);
+int launch_embed(const EmbedArgs &a, void *stream);
+int launch_norm(const NormArgs &a, void *stream);
+int launch_rows(int epi, int mt, int bt, const RowsArgs &a, uint32_t batch_chunks, void *stream);
+int launch_attention(const AttnArgs &a, void *stream);
+int launch_sample(const SampleArgs &a, void *stream);
+int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
+                      uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream);
+size_t attention_lds_bytes(uint32_t max_npos, uint32_t head);
+int kernels_init(uint32_t max_npos, uint32_t head);
+
+}  // namespace fpi8

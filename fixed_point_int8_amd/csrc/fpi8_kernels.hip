@@ -1,0 +1,836 @@
+// fpi8_kernels.hip - HIP kernels (gfx950) of the fixed-point forward pass of
+// the curta-core inference core ("The inference core" page).
+//
+// Every value is an integer with a fixed count of fractional bits ("Fixed-
+// point arithmetic"); 64-bit products and sums wrap, ">>" on signed values
+// floors, "/" truncates.  The kernels advance a batch of independent runs by
+// one position per launch sequence:
+//
+//   begin -> embedding -> per layer [norm -> Q/K/V rows (+ rotary, cache
+//   store, fit checks) -> attention -> output rows (+ residual) -> norm ->
+//   gate/up rows (+ SiLU) -> down rows (+ residual)] -> final norm ->
+//   classifier rows -> sampling
+//
+// The matrix row ("A matrix row") runs on the int8 matrix cores.  Each i64
+// input x is split into three signed base-256 digits, x = d0 + 256 d1 +
+// 65536 d2 with every d in [-128, 127], which covers |x| up to about 2^23
+// (128.0 at Q16).  The weight byte b becomes the signed weight b - 128 by
+// flipping its top bit, and one 16x16x64 int8 MFMA per digit gives exact
+// i32 partial sums (|sum| <= 2^14 * cols < 2^31).  Recombined they are the
+// signed dot sum_c (b_c - 128) x_c exactly, which equals the page's
+// acc - 128 * sum modulo 2^64.  A launch whose inputs hold any value outside
+// the three-digit range takes an exact 64-bit path instead, so the result is
+// the page's for every input.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fpi8.h"
+#include "fpi8_internal.h"
+
+namespace fpi8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t wmul(int64_t a, int64_t b) {
+  return (int64_t)((uint64_t)a * (uint64_t)b);
+}
+__device__ __forceinline__ int64_t wadd(int64_t a, int64_t b) {
+  return (int64_t)((uint64_t)a + (uint64_t)b);
+}
+__device__ __forceinline__ int64_t wsub(int64_t a, int64_t b) {
+  return (int64_t)((uint64_t)a - (uint64_t)b);
+}
+
+// Signed base-256 digits of x (three of them); false when x needs more.
+__device__ __forceinline__ bool digits3(int64_t x, int8_t &d0, int8_t &d1, int8_t &d2) {
+  const bool fits = x >= -8421504LL && x <= 8355711LL;  // -128*65793 .. 127*65793
+  d0 = (int8_t)(uint8_t)(x & 0xFF);
+  const int64_t t1 = wsub(x, d0) >> 8;
+  d1 = (int8_t)(uint8_t)(t1 & 0xFF);
+  const int64_t t2 = wsub(t1, d1) >> 8;
+  d2 = (int8_t)(uint8_t)(t2 & 0xFF);
+  return fits;
+}
+
+__device__ __forceinline__ void put_digits(int8_t *planes, uint64_t limb_pitch, uint64_t at,
+                                           int64_t x, uint32_t *oflag) {
+  int8_t d0, d1, d2;
+  if (!digits3(x, d0, d1, d2)) atomicOr(oflag, 1u);
+  planes[at] = d0;
+  planes[limb_pitch + at] = d1;
+  planes[2 * limb_pitch + at] = d2;
+}
+
+__device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
+  uint64_t r = (uint64_t)sqrt((double)n);
+  if (r > 0xFFFFFFFFull) r = 0xFFFFFFFFull;
+  while (r * r > n) --r;
+  while (r < 0xFFFFFFFFull && (r + 1) * (r + 1) <= n) ++r;
+  return r;
+}
+
+__device__ __forceinline__ uint8_t *run_base(uint8_t *states, const RunDesc &rd) {
+  return states + rd.base;
+}
+
+// Block-wide sums and maxima (256 threads).
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *scratch) {
+  for (int o = 32; o > 0; o >>= 1) v += (uint64_t)__shfl_xor((long long)v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  uint64_t s = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); i++) s += scratch[i];
+  return s;
+}
+
+__device__ __forceinline__ int64_t block_max_i64(int64_t v, int64_t *scratch) {
+  for (int o = 32; o > 0; o >>= 1) {
+    int64_t u = (int64_t)__shfl_xor((long long)v, o, 64);
+    v = u > v ? u : v;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  int64_t m = scratch[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); i++) m = scratch[i] > m ? scratch[i] : m;
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Turn and position bookkeeping
+
+__global__ void k_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs) {
+  const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_runs || !runs[b].valid) return;
+  uint64_t *turns = reinterpret_cast<uint64_t *>(run_base(states, runs[b]) + ST_TURNS);
+  *turns += 1;
+}
+
+// First kernel of a position: which runs compute it, which generate.
+__global__ void k_begin(BeginArgs a) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.n_oflags) a.oflags[i] = 0;
+  if (i >= a.n_runs) return;
+  RunDesc &rd = a.runs[i];
+  uint32_t flags = 0;
+  if (rd.valid) {
+    const uint8_t *st = run_base(a.states, rd);
+    const uint32_t phase = *reinterpret_cast<const uint32_t *>(st + ST_PHASE);
+    const uint32_t err = *reinterpret_cast<const uint32_t *>(st + ST_ERROR);
+    if (phase == 3 && err == 0) {
+      const uint32_t pos = *reinterpret_cast<const uint32_t *>(st + ST_POSITION);
+      rd.pos = pos;
+      rd.token = *reinterpret_cast<const uint32_t *>(st + ST_TOKEN);
+      flags = RUN_ACTIVE | (pos + 1 >= rd.n_ids ? RUN_GEN : 0u);
+    }
+  }
+  rd.flags = flags;
+  rd.errkey = 0xFFFFFFFFu;
+}
+
+// Phase 3: ((byte - 128) * scale) >> 8 with the token row's scale.
+__global__ void k_embed(EmbedArgs a) {
+  const uint32_t b = blockIdx.y;
+  const RunDesc &rd = a.runs[b];
+  if (!(rd.flags & RUN_ACTIVE)) return;
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.dim) return;
+  const uint32_t tok = rd.token;
+  if (tok >= a.vocab) return;  // an id the state should not hold; never read past the table
+  const int64_t s = (int64_t)(uint64_t)a.S[tok];
+  const int64_t w = (int64_t)a.E[(uint64_t)tok * a.dim + i] - 128;
+  int64_t *x = reinterpret_cast<int64_t *>(run_base(a.states, rd) + rd.off_x);
+  x[i] = wmul(w, s) >> 8;
+}
+
+// Phases 4, 11 (normalization part) and 17: RMS normalization of x into w1,
+// rms = isqrt(sum(x*x) / dim + 42,950) at least 1, y = ((x * w) / rms) >> 8;
+// also writes the digits of w1 for the next matrix.
+__global__ __launch_bounds__(256) void k_norm(NormArgs a) {
+  __shared__ uint64_t scratch[8];
+  const uint32_t b = blockIdx.x;
+  const RunDesc &rd = a.runs[b];
+  const uint32_t need = a.final_norm ? RUN_GEN : RUN_ACTIVE;
+  if (!(rd.flags & need)) return;
+  uint8_t *st = run_base(a.states, rd);
+  const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
+  int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
+  uint64_t ss = 0;
+  for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) ss += (uint64_t)wmul(x[i], x[i]);
+  ss = block_sum_u64(ss, scratch);
+  uint64_t r = isqrt64(ss / a.dim + 42950u);
+  if (r < 1) r = 1;
+  const int64_t rms = (int64_t)r;
+  const uint64_t pitch = (uint64_t)a.bp * a.kp;
+  for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) {
+    const int64_t v = (wmul(x[i], (int64_t)a.w[i]) / rms) >> 8;
+    y[i] = v;
+    put_digits(a.planes, pitch, (uint64_t)b * a.kp + i, v, a.oflag);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The matrix row on the int8 matrix cores.
+//
+// A workgroup of four waves owns 16*MT rows and BT*16 runs; the waves split
+// the 64-column blocks of the contraction round-robin and add their i32
+// partial sums through LDS.  MFMA 16x16x64 lanes: lane (i = lane % 16,
+// g = lane / 16) supplies row i of the weight tile and run i of the digit
+// tile, columns [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of
+// run i.
+
+__device__ __forceinline__ v4i load_weights(const uint8_t *W, uint32_t row, uint32_t rows,
+                                            uint32_t cols, uint32_t k0, bool vec) {
+  v4i r = {0, 0, 0, 0};
+  if (row >= rows) return r;
+  const uint8_t *p = W + (uint64_t)row * cols + k0;
+  if (vec && k0 + 16 <= cols) {
+    r = *reinterpret_cast<const v4i *>(p);
+    const int flip = (int)0x80808080u;
+    r.x ^= flip; r.y ^= flip; r.z ^= flip; r.w ^= flip;
+    return r;
+  }
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int t = 0; t < 16; t++) {
+    const uint32_t k = k0 + t;
+    const uint32_t v = k < cols ? (uint32_t)(p[t] ^ 0x80u) : 0u;
+    w[t >> 2] |= v << (8 * (t & 3));
+  }
+  r.x = (int)w[0]; r.y = (int)w[1]; r.z = (int)w[2]; r.w = (int)w[3];
+  return r;
+}
+
+template <int EPI>
+__device__ __forceinline__ bool row_run_ok(const RowsArgs &a, uint32_t b) {
+  if (b >= a.n_runs) return false;
+  if (EPI == EPI_RAW) return true;
+  const uint32_t f = a.runs[b].flags;
+  return EPI == EPI_CLS ? (f & RUN_GEN) != 0 : (f & RUN_ACTIVE) != 0;
+}
+
+template <int EPI>
+__device__ __forceinline__ const int64_t *row_input(const RowsArgs &a, uint32_t b) {
+  if (EPI == EPI_RAW) return a.x_raw + (uint64_t)b * a.cols;
+  const RunDesc &rd = a.runs[b];
+  const uint8_t *st = a.states + rd.base;
+  const uint64_t off = a.in_sel == IN_W1 ? rd.off_w1 : a.in_sel == IN_W3 ? rd.off_w3 : rd.off_gate;
+  return reinterpret_cast<const int64_t *>(st + off);
+}
+
+__device__ __forceinline__ bool fits32(int64_t v) { return v >= INT32_MIN && v <= INT32_MAX; }
+
+__device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase) {
+  atomicMin(&rd.errkey, (layer << 8) | phase);
+}
+
+template <int EPI, int MT, int BT>
+__global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
+  constexpr int NACC = MT * 3 * BT;
+  __shared__ v4i red[3][NACC][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const uint32_t tile = blockIdx.x;
+  const uint32_t b0 = blockIdx.y * BT * 16;
+
+  uint32_t si = 0;
+  if (EPI != EPI_GATEUP)
+    while (si + 1 < a.nseg && tile >= a.seg[si + 1].tile0) ++si;
+  const uint8_t *Wp[MT];
+  const uint32_t *Sp[MT];
+  uint32_t rbase[MT], rcount[MT];
+  bool vec[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt] : a.seg[si];
+    Wp[mt] = sg.W;
+    Sp[mt] = sg.S;
+    rcount[mt] = sg.rows;
+    vec[mt] = sg.pad != 0;
+    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 : (tile - sg.tile0) * 16 * MT + 16 * mt;
+  }
+  const bool exact = a.oflag != nullptr && *a.oflag != 0;
+
+  int64_t v[MT][BT][4];
+  if (!exact) {
+    v4i acc[MT][3][BT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int l = 0; l < 3; l++)
+#pragma unroll
+        for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
+    const uint64_t limb = (uint64_t)a.bp * a.kp;
+    for (uint32_t kb = wave; kb < a.kblocks; kb += 4) {
+      const uint32_t k0 = kb * 64 + lg * 16;
+      v4i A[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+        A[mt] = load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, k0, vec[mt]);
+#pragma unroll
+      for (int l = 0; l < 3; l++)
+#pragma unroll
+        for (int bt = 0; bt < BT; bt++) {
+          const v4i Bv = *reinterpret_cast<const v4i *>(
+              a.planes + l * limb + (uint64_t)(b0 + bt * 16 + li) * a.kp + k0);
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+            acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mt], Bv, acc[mt][l][bt], 0, 0, 0);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int l = 0; l < 3; l++)
+#pragma unroll
+          for (int bt = 0; bt < BT; bt++) red[wave - 1][(mt * 3 + l) * BT + bt][lane] = acc[mt][l][bt];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; w++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int l = 0; l < 3; l++)
+#pragma unroll
+          for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] += red[w][(mt * 3 + l) * BT + bt][lane];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
+                         ((int64_t)acc[mt][2][bt][j] << 16);
+  } else {
+    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products.
+    if (wave != 0) return;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++) {
+        const uint32_t b = b0 + bt * 16 + li;
+        const bool ok = row_run_ok<EPI>(a, b);
+        const int64_t *x = ok ? row_input<EPI>(a, b) : nullptr;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t row = rbase[mt] + 4 * lg + j;
+          int64_t s = 0;
+          if (ok && row < rcount[mt]) {
+            const uint8_t *w = Wp[mt] + (uint64_t)row * a.cols;
+            for (uint32_t k = 0; k < a.cols; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+          }
+          v[mt][bt][j] = s;
+        }
+      }
+  }
+
+  // Epilogue (wave 0): y = (v * scale) >> 24, then the phase's own work.
+#pragma unroll
+  for (int bt = 0; bt < BT; bt++) {
+    const uint32_t b = b0 + bt * 16 + li;
+    if (!row_run_ok<EPI>(a, b)) continue;
+    int64_t y[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t row = rbase[mt] + 4 * lg + j;
+        y[mt][j] = row < rcount[mt] ? wmul(v[mt][bt][j], (int64_t)(uint64_t)Sp[mt][row]) >> 24 : 0;
+      }
+    const uint32_t r0 = rbase[0] + 4 * lg;
+    if (EPI == EPI_RAW) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t row = rbase[mt] + 4 * lg + j;
+          if (row < rcount[mt]) a.y_raw[(uint64_t)b * rcount[mt] + row] = y[mt][j];
+        }
+      continue;
+    }
+    RunDesc &rd = a.runs[b];
+    uint8_t *st = a.states + rd.base;
+    if (EPI == EPI_CLS) {
+      int64_t *lg_out = reinterpret_cast<int64_t *>(st + rd.off_logits);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (r0 + j < rcount[0]) lg_out[r0 + j] = y[0][j];
+    } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
+      int64_t *x = reinterpret_cast<int64_t *>(st + rd.off_x);
+      int64_t *w1 = reinterpret_cast<int64_t *>(st + rd.off_w1);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (r0 + j < rcount[0]) {
+          if (EPI == EPI_DOWN) w1[r0 + j] = y[0][j];
+          x[r0 + j] = wadd(x[r0 + j], y[0][j]);
+        }
+    } else if (EPI == EPI_GATEUP) {
+      // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
+      int64_t *gate = reinterpret_cast<int64_t *>(st + rd.off_gate);
+      int64_t *up = reinterpret_cast<int64_t *>(st + rd.off_up);
+      const uint64_t pitch = (uint64_t)a.bp * a.kp_out;
+      const int64_t lim = (int64_t)16 << 16;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t row = r0 + j;
+        if (row >= a.hidden) continue;
+        const int64_t g = y[0][j], u = y[1][j];
+        const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)a.silu[(g + lim) >> 9];
+        const int64_t h = wmul(sg, u) >> 16;
+        gate[row] = h;
+        up[row] = u;
+        put_digits(a.planes_out, pitch, (uint64_t)b * a.kp_out + row, h, a.oflag_out);
+      }
+    } else if (EPI == EPI_QKV) {
+      const uint32_t role = a.seg[si].role;
+      const uint32_t pos = rd.pos;
+      if (role == ROLE_V) {
+        // Phase 7: the value rows into the cache, each checked to fit 32 bits.
+        int32_t *V = reinterpret_cast<int32_t *>(st + rd.off_values);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t row = r0 + j;
+          if (row >= rcount[0]) continue;
+          if (!fits32(y[0][j])) { fail(rd, a.layer, 7); continue; }
+          const uint32_t kvh = row / a.head, e = row % a.head;
+          V[(((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e] = (int32_t)y[0][j];
+        }
+      } else {
+        // Phase 8 on the query (kept in w2) and on the key after its
+        // phase-6 store check: pairs (2p, 2p+1) of each head turned by
+        // position pos's cosine and sine p.
+        const int32_t *cs = a.rope_cos + (uint64_t)pos * a.half;
+        const int32_t *sn = a.rope_sin + (uint64_t)pos * a.half;
+        int64_t *q = reinterpret_cast<int64_t *>(st + rd.off_w2);
+        int32_t *K = reinterpret_cast<int32_t *>(st + rd.off_keys);
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const uint32_t row = r0 + j;
+          if (row >= rcount[0]) continue;
+          int64_t A0 = y[0][j], B0 = y[0][j + 1];
+          if (role == ROLE_K) {
+            bool ok = true;
+            if (!fits32(A0)) { fail(rd, a.layer, 6); ok = false; }
+            if (!fits32(B0)) { fail(rd, a.layer, 6); ok = false; }
+            if (!ok) continue;
+          }
+          const uint32_t p = (row % a.head) >> 1;
+          const int64_t c = cs[p], s = sn[p];
+          const int64_t ra = wsub(wmul(A0, c), wmul(B0, s)) >> 24;
+          const int64_t rb = wadd(wmul(A0, s), wmul(B0, c)) >> 24;
+          if (role == ROLE_Q) {
+            q[row] = ra;
+            q[row + 1] = rb;
+          } else {
+            if (!fits32(ra) || !fits32(rb)) { fail(rd, a.layer, 8); continue; }
+            const uint32_t kvh = row / a.head, e = row % a.head;
+            int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e;
+            dst[0] = (int32_t)ra;
+            dst[1] = (int32_t)rb;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
+__global__ void k_zero_flag(uint32_t *flag) { *flag = 0; }
+
+__global__ void k_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
+                             uint32_t kp, uint32_t bp, uint32_t *oflag) {
+  const uint32_t b = blockIdx.y;
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_runs || i >= cols) return;
+  put_digits(planes, (uint64_t)bp * kp, (uint64_t)b * kp + i, x[(uint64_t)b * cols + i], oflag);
+}
+
+// ---------------------------------------------------------------------------
+// Phase 9, one workgroup per (run, head) ("Attention, stage by stage").
+// Scores, exponentials and probabilities of the head's positions stay in
+// LDS with the exponential table.
+
+template <int HS>
+__global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
+  __shared__ uint64_t scratch[8];
+  __shared__ int64_t qs[256];
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint32_t *exps = reinterpret_cast<uint32_t *>(lds);
+  int64_t *sc = reinterpret_cast<int64_t *>(lds + 16400);
+  int64_t *red = sc + a.max_npos;
+
+  const uint32_t h = blockIdx.x, b = blockIdx.y;
+  const RunDesc &rd = a.runs[b];
+  if (!(rd.flags & RUN_ACTIVE)) return;
+  const uint32_t hs = HS ? HS : a.head;
+  const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+  const uint32_t npos = rd.pos + 1, cachepos = rd.cachepos;
+  uint8_t *st = a.states + rd.base;
+  const int64_t *q = reinterpret_cast<const int64_t *>(st + rd.off_w2) + (uint64_t)h * hs;
+  const uint32_t kvh = h / a.group;
+  const uint64_t head_base = ((uint64_t)a.layer * a.kv_heads + kvh) * cachepos * hs;
+  const int32_t *K = reinterpret_cast<const int32_t *>(st + rd.off_keys) + head_base;
+  const int32_t *V = reinterpret_cast<const int32_t *>(st + rd.off_values) + head_base;
+
+  for (uint32_t i = tid; i < 4097; i += blockDim.x) exps[i] = a.exp_tab[i];
+  for (uint32_t i = tid; i < hs; i += blockDim.x) qs[i] = q[i];
+  __syncthreads();
+
+  // Stage 0, scores: s_j = (((q . K_j) >> 16) * inv) >> 24; 16 lanes per
+  // position, 16 positions at a time.
+  int64_t lmax = INT64_MIN;
+  const int64_t inv = (int64_t)(uint64_t)a.inv;
+  if constexpr (HS != 0 && HS % 4 == 0) {
+    constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
+    constexpr int CPL = (NCH + 15) / 16;
+    int64_t qr[CPL][4];
+#pragma unroll
+    for (int t = 0; t < CPL; t++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int c = l16 + 16 * t;
+        qr[t][u] = c < NCH ? qs[4 * c + u] : 0;
+      }
+    for (uint32_t j = grp; j < npos; j += 16) {
+      const int32_t *kr = K + (uint64_t)j * HS;
+      int64_t dot = 0;
+#pragma unroll
+      for (int t = 0; t < CPL; t++) {
+        const int c = l16 + 16 * t;
+        if (c < NCH) {
+          const int4 kv = *reinterpret_cast<const int4 *>(kr + 4 * c);
+          dot = wadd(dot, wmul(qr[t][0], kv.x));
+          dot = wadd(dot, wmul(qr[t][1], kv.y));
+          dot = wadd(dot, wmul(qr[t][2], kv.z));
+          dot = wadd(dot, wmul(qr[t][3], kv.w));
+        }
+      }
+      for (int o = 8; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, 16));
+      if (l16 == 0) {
+        const int64_t s = wmul(dot >> 16, inv) >> 24;
+        sc[j] = s;
+        lmax = s > lmax ? s : lmax;
+      }
+    }
+  } else {
+    for (uint32_t j = grp; j < npos; j += 16) {
+      const int32_t *kr = K + (uint64_t)j * hs;
+      int64_t dot = 0;
+      for (uint32_t e = l16; e < hs; e += 16) dot = wadd(dot, wmul(qs[e], kr[e]));
+      for (int o = 8; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, 16));
+      if (l16 == 0) {
+        const int64_t s = wmul(dot >> 16, inv) >> 24;
+        sc[j] = s;
+        lmax = s > lmax ? s : lmax;
+      }
+    }
+  }
+  const int64_t m = block_max_i64(lmax, reinterpret_cast<int64_t *>(scratch));
+
+  // Stage 1, exponentials: EXP[min((m - s) >> 8, 4096)], and their sum.
+  uint64_t lsum = 0;
+  for (uint32_t j = tid; j < npos; j += blockDim.x) {
+    const uint64_t d = (uint64_t)m - (uint64_t)sc[j];
+    const uint64_t idx = d >> 8;
+    const uint32_t e = exps[idx > 4096 ? 4096 : idx];
+    sc[j] = e;
+    lsum += e;
+  }
+  const uint64_t S = block_sum_u64(lsum, scratch);
+
+  // Stage 2, normalization: (e << 24) / S, at most 2^24.
+  int64_t *scores_out = (h + 1 == a.heads) ? reinterpret_cast<int64_t *>(st + rd.off_scores) : nullptr;
+  for (uint32_t j = tid; j < npos; j += blockDim.x) {
+    const int64_t p = (int64_t)(((uint64_t)sc[j] << 24) / S);
+    sc[j] = p;
+    if (scores_out) scores_out[j] = p;
+  }
+  __syncthreads();
+
+  // Stage 3, weighted values: o_i = (sum_j p_j * V_j,i) >> 24.
+  int64_t *w3 = reinterpret_cast<int64_t *>(st + rd.off_w3) + (uint64_t)h * hs;
+  const uint64_t pitch = (uint64_t)a.bp * a.kp;
+  if constexpr (HS != 0 && HS % 4 == 0) {
+    constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
+    constexpr int CPL = (NCH + 15) / 16;
+    int64_t acc[CPL][4];
+#pragma unroll
+    for (int t = 0; t < CPL; t++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) acc[t][u] = 0;
+    for (uint32_t j = grp; j < npos; j += 16) {
+      const int32_t *vr = V + (uint64_t)j * HS;
+      const int32_t p = (int32_t)sc[j];
+#pragma unroll
+      for (int t = 0; t < CPL; t++) {
+        const int c = l16 + 16 * t;
+        if (c < NCH) {
+          const int4 vv = *reinterpret_cast<const int4 *>(vr + 4 * c);
+          acc[t][0] = wadd(acc[t][0], (int64_t)p * vv.x);
+          acc[t][1] = wadd(acc[t][1], (int64_t)p * vv.y);
+          acc[t][2] = wadd(acc[t][2], (int64_t)p * vv.z);
+          acc[t][3] = wadd(acc[t][3], (int64_t)p * vv.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < CPL; t++) {
+      const int c = l16 + 16 * t;
+      if (c < NCH)
+#pragma unroll
+        for (int u = 0; u < 4; u++) red[grp * HS + 4 * c + u] = acc[t][u];
+    }
+    __syncthreads();
+    for (uint32_t e = tid; e < HS; e += blockDim.x) {
+      int64_t o = 0;
+      for (int g = 0; g < 16; g++) o = wadd(o, red[g * HS + e]);
+      o >>= 24;
+      w3[e] = o;
+      put_digits(a.planes, pitch, (uint64_t)b * a.kp + (uint64_t)h * HS + e, o, a.oflag);
+    }
+  } else {
+    const uint32_t groups = blockDim.x / hs;  // hs <= 256
+    const uint32_t g = tid / hs, e = tid % hs;
+    int64_t acc = 0;
+    if (g < groups)
+      for (uint32_t j = g; j < npos; j += groups) acc = wadd(acc, (int64_t)(int32_t)sc[j] * V[(uint64_t)j * hs + e]);
+    if (g < groups) red[g * hs + e] = acc;
+    __syncthreads();
+    if (tid < (int)hs) {
+      int64_t o = 0;
+      for (uint32_t gg = 0; gg < groups; gg++) o = wadd(o, red[gg * hs + tid]);
+      o >>= 24;
+      w3[tid] = o;
+      put_digits(a.planes, pitch, (uint64_t)b * a.kp + (uint64_t)h * hs + tid, o, a.oflag);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 19 and the end of a position ("Sampling").
+
+__device__ __forceinline__ uint32_t temp_index(uint64_t d, uint32_t t) {
+  // floor(d * 2^16 / t) >> 8, capped at 4,096: at or above the cap exactly
+  // when d >= 16 t; below it d < 2^24 and the quotient fits 64 bits.
+  if (d >= 16ull * t) return 4096u;
+  const uint64_t i = ((d << 16) / t) >> 8;
+  return i > 4096 ? 4096u : (uint32_t)i;
+}
+
+__global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
+  __shared__ int64_t best_v[256];
+  __shared__ uint32_t best_i[256];
+  __shared__ uint64_t part[256];
+  __shared__ uint64_t bcast[4];
+  const uint32_t b = blockIdx.x;
+  RunDesc &rd = a.runs[b];
+  if (!(rd.flags & RUN_ACTIVE)) return;
+  uint8_t *st = a.states + rd.base;
+  const int tid = threadIdx.x;
+  if (rd.errkey != 0xFFFFFFFFu) {
+    // The run froze in this position: error 8 at the failing phase and layer.
+    if (tid == 0) {
+      *reinterpret_cast<uint32_t *>(st + ST_ERROR) = FPI8_ARITHMETIC;
+      *reinterpret_cast<uint32_t *>(st + ST_PHASE) = rd.errkey & 0xFFu;
+      *reinterpret_cast<uint32_t *>(st + ST_LAYER) = rd.errkey >> 8;
+      a.run_err[b] = FPI8_ARITHMETIC;
+    }
+    return;
+  }
+  const uint32_t pos = rd.pos;
+  uint32_t token = 0;
+  bool complete = false;
+  if (rd.flags & RUN_GEN) {
+    const int64_t *lgt = reinterpret_cast<const int64_t *>(st + rd.off_logits);
+    const uint32_t V = a.vocab;
+    const uint32_t chunk = (V + blockDim.x - 1) / blockDim.x;
+    const uint32_t c0 = tid * chunk, c1 = min(V, c0 + chunk);
+    // Maximum pass: the largest logit, the lowest index on a tie.
+    int64_t bv = INT64_MIN;
+    uint32_t bi = 0xFFFFFFFFu;
+    for (uint32_t i = c0; i < c1; i++)
+      if (bi == 0xFFFFFFFFu || lgt[i] > bv) { bv = lgt[i]; bi = i; }
+    best_v[tid] = bv;
+    best_i[tid] = bi;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) {
+        const int64_t ov = best_v[tid + s];
+        const uint32_t oi = best_i[tid + s];
+        if (oi != 0xFFFFFFFFu &&
+            (best_i[tid] == 0xFFFFFFFFu || ov > best_v[tid] || (ov == best_v[tid] && oi < best_i[tid]))) {
+          best_v[tid] = ov;
+          best_i[tid] = oi;
+        }
+      }
+      __syncthreads();
+    }
+    const int64_t m = best_v[0];
+    token = best_i[0];
+    const uint32_t T = rd.temp;
+    if (T != 0) {
+      // Sum pass over each thread's slice, then the draw and the walk.
+      uint64_t s = 0;
+      for (uint32_t i = c0; i < c1; i++) s += a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
+      part[tid] = s;
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t total = 0;
+        for (int i = 0; i < 256; i++) total += part[i];
+        uint64_t *gen = reinterpret_cast<uint64_t *>(st + ST_GENERATOR);
+        uint64_t x = *gen;
+        x ^= x >> 12;
+        x ^= x << 25;
+        x ^= x >> 27;
+        *gen = x;
+        uint64_t r = (x * 0x2545F4914F6CDD1Dull) % total;
+        uint32_t c = 0;
+        while (c < 255 && r >= part[c]) { r -= part[c]; c++; }
+        bcast[0] = c;
+        bcast[1] = r;
+      }
+      __syncthreads();
+      if ((uint64_t)tid == bcast[0]) {
+        uint64_t r = bcast[1];
+        for (uint32_t i = c0; i < c1; i++) {
+          const uint64_t e = a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
+          if (r < e) { bcast[2] = i; break; }
+          r -= e;
+        }
+      }
+      __syncthreads();
+      token = (uint32_t)bcast[2];
+    }
+    if (tid == 0) {
+      uint32_t *gen_count = reinterpret_cast<uint32_t *>(st + ST_GENERATED);
+      uint32_t *out = reinterpret_cast<uint32_t *>(st + rd.off_out);
+      const uint32_t g = *gen_count;
+      out[g] = token;
+      *gen_count = g + 1;
+      complete = token == 1 || token == 2 || g + 1 == rd.max_tokens;
+    }
+  } else if (tid == 0) {
+    token = reinterpret_cast<const uint32_t *>(st + rd.off_ids)[pos + 1];
+  }
+  if (tid == 0) {
+    *reinterpret_cast<uint32_t *>(st + ST_TOKEN) = token;
+    *reinterpret_cast<uint32_t *>(st + ST_POSITION) = pos + 1;
+    *reinterpret_cast<uint32_t *>(st + ST_PHASE) = complete ? 20u : 3u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+
+static inline int ok(hipError_t e) { return e == hipSuccess ? 0 : FPI8_ERR_HIP; }
+
+int launch_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs, void *stream) {
+  if (!n_runs) return 0;
+  hipLaunchKernelGGL(k_turn_start, dim3((n_runs + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                     states, runs, n_runs);
+  return ok(hipGetLastError());
+}
+
+int launch_begin(const BeginArgs &a, void *stream) {
+  const uint32_t n = a.n_runs > a.n_oflags ? a.n_runs : a.n_oflags;
+  hipLaunchKernelGGL(k_begin, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, a);
+  return ok(hipGetLastError());
+}
+
+int launch_embed(const EmbedArgs &a, void *stream) {
+  hipLaunchKernelGGL(k_embed, dim3((a.dim + 255) / 256, a.n_runs), dim3(256), 0,
+                     (hipStream_t)stream, a);
+  return ok(hipGetLastError());
+}
+
+int launch_norm(const NormArgs &a, void *stream) {
+  hipLaunchKernelGGL(k_norm, dim3(a.n_runs), dim3(256), 0, (hipStream_t)stream, a);
+  return ok(hipGetLastError());
+}
+
+template <int EPI, int MT>
+static int rows_bt(int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
+  const dim3 grid(a.ntiles, chunks), block(256);
+  switch (bt) {
+    case 1: hipLaunchKernelGGL((k_rows<EPI, MT, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rows<EPI, MT, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rows<EPI, MT, 4>), grid, block, 0, s, a); break;
+    default: return FPI8_ERR_ARGUMENT;
+  }
+  return ok(hipGetLastError());
+}
+
+int launch_rows(int epi, int mt, int bt, const RowsArgs &a, uint32_t chunks, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.ntiles == 0 || chunks == 0) return 0;
+  switch (epi) {
+    case EPI_RAW: return mt == 1 ? rows_bt<EPI_RAW, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_QKV: return mt == 1 ? rows_bt<EPI_QKV, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_RESID: return mt == 1 ? rows_bt<EPI_RESID, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_DOWN: return mt == 1 ? rows_bt<EPI_DOWN, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_CLS: return mt == 1 ? rows_bt<EPI_CLS, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_GATEUP: return mt == 2 ? rows_bt<EPI_GATEUP, 2>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+  }
+  return FPI8_ERR_ARGUMENT;
+}
+
+size_t attention_lds_bytes(uint32_t max_npos, uint32_t head) {
+  const size_t red = (head % 4 == 0 && (head & (head - 1)) == 0) ? 16ull * head : 256ull;
+  return 16400 + 8ull * max_npos + 8ull * red;
+}
+
+static bool pow2_head(uint32_t h) { return h >= 4 && h <= 256 && (h & (h - 1)) == 0; }
+
+int kernels_init(uint32_t max_npos, uint32_t head) {
+  const int bytes = (int)attention_lds_bytes(max_npos, head);
+  hipError_t e = hipSuccess;
+  switch (pow2_head(head) ? head : 0) {
+    case 4: e = hipFuncSetAttribute((const void *)k_attention<4>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 8: e = hipFuncSetAttribute((const void *)k_attention<8>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 16: e = hipFuncSetAttribute((const void *)k_attention<16>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 32: e = hipFuncSetAttribute((const void *)k_attention<32>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 64: e = hipFuncSetAttribute((const void *)k_attention<64>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 128: e = hipFuncSetAttribute((const void *)k_attention<128>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    case 256: e = hipFuncSetAttribute((const void *)k_attention<256>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+    default: e = hipFuncSetAttribute((const void *)k_attention<0>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
+  }
+  return ok(e);
+}
+
+int launch_attention(const AttnArgs &a, void *stream) {
+  const dim3 grid(a.heads, a.n_runs), block(256);
+  const size_t lds = attention_lds_bytes(a.max_npos, a.head);
+  hipStream_t s = (hipStream_t)stream;
+  switch (pow2_head(a.head) ? a.head : 0) {
+    case 4: hipLaunchKernelGGL(k_attention<4>, grid, block, lds, s, a); break;
+    case 8: hipLaunchKernelGGL(k_attention<8>, grid, block, lds, s, a); break;
+    case 16: hipLaunchKernelGGL(k_attention<16>, grid, block, lds, s, a); break;
+    case 32: hipLaunchKernelGGL(k_attention<32>, grid, block, lds, s, a); break;
+    case 64: hipLaunchKernelGGL(k_attention<64>, grid, block, lds, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attention<128>, grid, block, lds, s, a); break;
+    case 256: hipLaunchKernelGGL(k_attention<256>, grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL(k_attention<0>, grid, block, lds, s, a); break;
+  }
+  return ok(hipGetLastError());
+}
+
+int launch_sample(const SampleArgs &a, void *stream) {
+  hipLaunchKernelGGL(k_sample, dim3(a.n_runs), dim3(256), 0, (hipStream_t)stream, a);
+  return ok(hipGetLastError());
+}
+
+int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
+                      uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, s, oflag);
+  hipLaunchKernelGGL(k_digits_raw, dim3((cols + 255) / 256, n_runs), dim3(256), 0, s, x, n_runs,
+                     cols, planes, kp, bp, oflag);
+  return ok(hipGetLastError());
+}
+
+}  // namespace fpi8

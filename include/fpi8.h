@@ -1,0 +1,171 @@
+/*
+ * fpi8.h - C ABI of libfpi8, the MI355X (gfx950) implementation of the
+ * fixed-point transformer forward pass of the curta-core inference core
+ * ("The inference core" page: sections "Fixed-point arithmetic", "A matrix
+ * row", "RMS normalization", "The attention cache", "Lookup tables", "The
+ * forward pass, in order", "Attention, stage by stage", "The resumable
+ * state", "Sampling", "The Rust API", "WebAssembly exports", "Core errors").
+ *
+ * Conventions (after the page's WebAssembly exports): plain C functions,
+ * pointers and 64-bit lengths, the configuration as seven u32 values in the
+ * order dim, hidden, layers, heads, kv_heads, vocab, context.  Every
+ * function returns 0 on success or one of the page's core error numbers
+ * (1-8); numbers from 100 up are failures of the GPU runtime.  Pointers named
+ * d_* are device memory, h_* and the rest host memory; the caller owns all
+ * of it, and the library only borrows a pointer for the length of a call
+ * (an engine keeps d_blob until it is destroyed).  A stream argument is a
+ * hipStream_t passed as void* (NULL: the default stream).
+ *
+ * Token ids are fed in: the tokenizer phases 0-2 stay with the caller.
+ */
+#ifndef FPI8_H
+#define FPI8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* "Core errors". */
+enum {
+  FPI8_OK = 0,
+  FPI8_INVALID_CONFIG = 1,    /* a configuration value out of range */
+  FPI8_INVALID_FORMAT = 2,    /* artifact tag, counts, offsets or descriptors */
+  FPI8_INVALID_STATE = 3,     /* state tag, size, alignment, cursor, frozen */
+  FPI8_BUFFER_TOO_SMALL = 4,  /* init_state given a length other than state_size */
+  FPI8_MISSING_WEIGHTS = 5,   /* a matrix section absent or shorter than its matrix */
+  FPI8_INVALID_PROMPT = 6,    /* no ids, an id >= vocab, max tokens 0 or > context,
+                                 temperature above 16 (1,048,576 at Q16) */
+  FPI8_CONTEXT_EXCEEDED = 7,  /* ids + max tokens - 1 above the context */
+  FPI8_ARITHMETIC = 8,        /* a key or value that does not fit 32 bits */
+  FPI8_ERR_HIP = 100,         /* a HIP runtime call failed */
+  FPI8_ERR_UNSUPPORTED = 101, /* a shape the kernels cannot run (see engine_create) */
+  FPI8_ERR_ARGUMENT = 102     /* a null pointer or a count beyond the engine's limits */
+};
+
+/* The cursor of a state ("The Rust API", StateInfo::read). */
+typedef struct {
+  uint32_t phase;           /* 3 at the start of a position, 20 when complete; on an
+                               Arithmetic failure the phase that failed (6, 7 or 8) */
+  uint32_t layer;           /* 0, or the failing layer */
+  uint32_t position;        /* positions computed so far */
+  uint32_t token;           /* the token the next position embeds */
+  uint32_t n_ids, max_tokens, temperature_q16, generated;
+  uint32_t cache_positions; /* n_ids + max_tokens - 1 */
+  uint32_t error;           /* 0, or 8 once the run froze */
+  uint32_t complete;        /* phase == 20 */
+  uint32_t reserved;
+  uint64_t generator;       /* xorshift64* state */
+  uint64_t turns;           /* turns run on this state */
+} fpi8_info;
+
+/* ---- The artifact ----------------------------------------------------------
+ * Little-endian, offsets from the artifact's start.  Section zero begins at
+ * offset 0 and holds: tag "CURTAW01" (8 bytes); the configuration u32[7] at
+ * 8; u32 section count at 36; u32 matrix count (2 + 7*layers) at 40; u32 one
+ * over the square root of the head size (Q24) at 44; u64 offsets of the
+ * exponential table u32[4097] Q30 (48), the SiLU table i32[4097] Q16 (56),
+ * rotary cosines i32[context][head/2] Q24 (64), sines (72), normalization
+ * weights i32 Q24 [layers][2][dim] then [dim] (80), the tokenizer block (88)
+ * and its length (96), and the matrix descriptors (104); the section table
+ * at 128, {u64 offset, u64 length} per section, entry 0 being {0, length of
+ * section zero}.  A descriptor is 32 bytes: u32 kind, layer, rows, cols,
+ * section, 0, then u64 offset inside the section of rows*cols weight bytes
+ * (weight + 128, row-major), followed 8-aligned by rows u32 Q24 scales.
+ * Kinds: 0 embedding [vocab][dim], 1 query, 2 key [kv_dim][dim], 3 value,
+ * 4 attention output [dim][dim], 5 gate [hidden][dim], 6 up, 7 down
+ * [dim][hidden], 8 classifier [vocab][dim].                                */
+
+/* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
+ * (may be NULL) receives the configuration. */
+int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);
+
+/* ---- The state ("The resumable state") -----------------------------------
+ * A 128-byte header tagged "FPI8ST01" (u32 phase 8, layer 12, row 16,
+ * position 20, token 24, error 28, n_ids 32, max tokens 36, temperature 40,
+ * generated 44, cache positions 48; u64 generator 72, turns 80; the other
+ * words are zero at position boundaries), then 8-aligned buffers: ids
+ * u32[n_ids], output tokens u32[max], activations and three working vectors
+ * i64[dim], gate and up i64[hidden], logits i64[vocab], scores
+ * i64[cache positions], keys and values i32[layers][kv_heads][cache
+ * positions][head].                                                         */
+
+/* Size of a state; UINT64_MAX for parameters out of range. */
+uint64_t fpi8_state_size(const uint32_t cfg[7], uint32_t n_ids, uint32_t max_tokens);
+
+/* Byte offsets of the buffers: ids, out, x, w1, w2, w3, gate, up, logits,
+ * scores, keys, values, total size.  0, 1 or 6. */
+int32_t fpi8_state_offsets(const uint32_t cfg[7], uint32_t n_ids, uint32_t max_tokens,
+                           uint64_t out[13]);
+
+/* Writes a fresh state into a host buffer of exactly fpi8_state_size bytes,
+ * 8-byte aligned ("The Rust API", init_state).  A zero seed starts the
+ * generator at 0x9E3779B97F4A7C15.  Errors 1, 6, 7, 4, 3 in that order. */
+int32_t fpi8_init_state(const uint32_t cfg[7], uint8_t *state, uint64_t state_len,
+                        const uint32_t *ids, uint32_t n_ids, uint32_t max_tokens,
+                        uint32_t temperature_q16, uint64_t seed);
+
+/* Reads the cursor of a host copy of a state: 0 or 3. */
+int32_t fpi8_state_info(const uint8_t *state, uint64_t len, fpi8_info *out);
+
+/* The generated ids of a host copy of a state (count receives how many);
+ * NULL for an invalid state. */
+const uint32_t *fpi8_output_tokens(const uint8_t *state, uint64_t len, uint32_t *count);
+
+/* ---- The GPU engine ---------------------------------------------------- */
+
+typedef struct fpi8_engine fpi8_engine;
+
+/* Binds an artifact already in device memory.  h_section0 is a host copy of
+ * its section zero (at least the length the section table names), d_blob
+ * the whole artifact on the device, blob_len its length; max_runs bounds the
+ * runs of one turn.  Errors 1, 2, 5; 101 when the context is too long for
+ * the attention kernel's on-chip score buffer; 100 on a HIP failure. The
+ * engine allocates its own workspace here, once. */
+int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len,
+                           const uint8_t *d_blob, uint64_t blob_len, uint32_t max_runs,
+                           fpi8_engine **out);
+
+void fpi8_engine_destroy(fpi8_engine *engine);
+
+/* Advances every run of a batch by up to max_positions whole positions
+ * (phases 3-16 per layer, then 17-19 where a token is generated; "The forward
+ * pass, in order").  d_states holds n_runs states at a fixed byte stride
+ * (multiple of 8; each state no larger than the stride), written by
+ * fpi8_init_state and copied to the device.  Runs are independent: a run
+ * that completes stops, others go on.  A run that is already complete is left
+ * as it is (error 0); an invalid or frozen state gets error 3; a key or
+ * value that does not fit 32 bits freezes the run with error 8, its cursor at
+ * the failing phase and layer.  h_run_errors (may be NULL) receives one code
+ * per run; the return value is the first nonzero of them, or a 100+ code.
+ * Synchronizes the stream before returning. */
+int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
+                  uint32_t n_runs, uint32_t max_positions, void *stream,
+                  int32_t *h_run_errors);
+
+/* Kernel timing for measurement: while enabled, every launch of the kernel
+ * class `kernel` is bracketed by HIP events on its stream.  Classes: 0 row
+ * kernel (all matrices), 1 attention, 2 normalization, 3 sampling, 4 embedding.
+ * fpi8_engine_timing returns the summed milliseconds and the launch count
+ * since the last enable (it synchronizes on the recorded events). */
+int32_t fpi8_engine_set_timing(fpi8_engine *engine, int32_t kernel, int32_t enable);
+int32_t fpi8_engine_timing(fpi8_engine *engine, int32_t kernel, double *total_ms,
+                           uint64_t *launches);
+
+/* ---- The standalone matrix row ("A matrix row") ------------------------
+ * y[b][r] = ((sum_c W[r][c] * x[b][c] - 128 * sum_c x[b][c]) * scale[r]) >> 24
+ * in wrapping 64-bit arithmetic, for W rows x cols bytes (weight + 128,
+ * row-major), scale u32 Q24, x [batch][cols] i64 Q16, y [batch][rows] i64.
+ * The workspace (device, at least fpi8_matrix_rows_workspace_size bytes)
+ * holds the byte digits of x.  Errors 102 (sizes, null pointers, small
+ * workspace), 100. */
+uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch);
+int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
+                         uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
+                         void *d_work, uint64_t work_len, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

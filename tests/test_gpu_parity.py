@@ -1,0 +1,295 @@
+"""Parity of the HIP path with the oracle, bit for bit, through the C ABI.
+
+Small shapes run whole (every state byte after every turn); the row kernel
+is checked on ragged shapes, adversarial 64-bit inputs (which take the exact
+64-bit path) and the full 4096 x 4096 sweep.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from workloads import blob as Bl
+from workloads.configs import Shape
+from fixed_point_int8_amd import binding as B
+from fixed_point_int8_amd.device import DeviceModel
+from gpu_helpers import Pair, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# The matrix row, standalone
+
+def gpu_rows(Wm, s, x):
+    torch = require_gpu()
+    rows, cols = Wm.shape
+    batch = x.shape[0]
+    dW = torch.from_numpy(np.ascontiguousarray(Wm)).cuda()
+    dS = torch.from_numpy(np.ascontiguousarray(s).view(np.int32)).cuda()
+    dX = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    dY = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
+    n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
+    dWk = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    e = B.fpi8_matrix_rows(dW, dS, rows, cols, dX, batch, dY, dWk, n)
+    assert e == 0
+    torch.cuda.synchronize()
+    return dY.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,batch", [
+    (16, 64, 1), (1, 1, 1), (37, 172, 3), (100, 300, 17), (256, 512, 32), (129, 4096, 64),
+    (64, 128, 100), (33, 64, 128), (48, 11008, 8), (200, 2048, 65)])
+def test_matrix_rows_random(rows, cols, batch):
+    say(f"matrix_rows {rows}x{cols} batch {batch}")
+    Wm, s, x = W.row_operands(rows, cols, batch, rows * 1000 + cols + batch)
+    assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
+
+
+@pytest.mark.parametrize("rows,cols,batch", [(16, 64, 2), (40, 100, 5), (64, 256, 33)])
+def test_matrix_rows_adversarial_inputs(rows, cols, batch):
+    say(f"matrix_rows adversarial {rows}x{cols} batch {batch}")
+    Wm, s, _ = W.row_operands(rows, cols, batch, 7)
+    x = W.adversarial_row_inputs(batch, cols, rows + cols)
+    Wm[0, :] = 0
+    Wm[1, :] = 255
+    s[0] = 2**32 - 1
+    s[2] = 0
+    assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
+
+
+def test_matrix_rows_three_digit_edges():
+    # Inputs at the edges of the three-digit range, and one just outside it.
+    Wm, s, _ = W.row_operands(32, 128, 4, 3)
+    edge = np.array([-8421504, 8355711, -8421505, 8355712, 8388607, -8388608], dtype=np.int64)
+    x = np.resize(edge, (4, 128)).astype(np.int64)
+    assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
+    x2 = np.resize(edge[:2], (4, 128)).astype(np.int64)
+    assert np.array_equal(gpu_rows(Wm, s, x2), O.rows(Wm, s, x2))
+
+
+@pytest.mark.parametrize("batch", W.ROW_SWEEP_BATCHES)
+def test_matrix_rows_4096_sweep(batch):
+    say(f"matrix_rows 4096x4096 batch {batch}")
+    O.set_threads(16)
+    Wm, s, x = W.row_operands(W.ROW_SWEEP_ROWS, W.ROW_SWEEP_COLS, batch, W.ROW_SWEEP_SEED)
+    try:
+        assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
+    finally:
+        O.set_threads(1)
+
+
+# ---------------------------------------------------------------------------
+# The whole pass on small shapes
+
+def spec(shape, n_runs, prompt, max_tokens, seed=0, temps=None, seeds=None):
+    runs = []
+    for r in range(n_runs):
+        p = prompt[r] if isinstance(prompt, (list, tuple)) else prompt
+        m = max_tokens[r] if isinstance(max_tokens, (list, tuple)) else max_tokens
+        ids = W.prompt_ids(shape.vocab, p, 100 + seed, r)
+        t = temps[r] if temps else 0
+        sd = seeds[r] if seeds else 42 + r
+        runs.append((ids, m, t, sd))
+    return runs
+
+
+def run_pair(shape, blob, runs, cuts, compare_every=True):
+    pair = Pair(shape, blob, runs)
+    try:
+        for k in cuts:
+            pair.turn(k)
+            if compare_every:
+                pair.compare()
+            if pair.complete():
+                break
+        while not pair.complete():
+            pair.turn(1 << 20)
+        pair.compare()
+    finally:
+        pair.model.close()
+    return pair
+
+
+def test_tiny_workload_position_by_position():
+    w = W.TINY
+    say("tiny workload")
+    blob = Bl.build_blob(w.shape, w.blob_seed)
+    runs = [(W.prompt_ids(w.shape.vocab, w.prompt, w.ids_seed, 0), w.max_tokens, 0, w.run_seed)]
+    pair = run_pair(w.shape, blob, runs, [1] * 31)
+    info = O.state_info(pair.ref[0])[1]
+    assert info["complete"] and info["generated"] == 16
+
+
+def test_tiny_prefix_runs_in_one_batch():
+    # P = k ids and one generated token, k = 1..16: runs of sixteen sizes at
+    # one stride; a greedy token at every fed position.
+    w = W.TINY
+    say("tiny prefix runs")
+    blob = Bl.build_blob(w.shape, w.blob_seed)
+    ids = W.prompt_ids(w.shape.vocab, w.prompt, w.ids_seed, 0)
+    runs = [(ids[:k], 1, 0, 0) for k in range(1, 17)]
+    run_pair(w.shape, blob, runs, [3, 5, 100])
+
+
+def test_tiny_context_fills_exactly():
+    w = W.TINY
+    blob = Bl.build_blob(w.shape, w.blob_seed)
+    ids = W.prompt_ids(w.shape.vocab, 16, w.ids_seed, 0)
+    run_pair(w.shape, blob, [(ids, 17, 0, 0)], [40])
+
+
+@pytest.mark.parametrize("name", ["gqa", "ragged", "wide", "h8"])
+def test_small_shapes_greedy(name):
+    shape = W.SMALL_SHAPES[name]
+    say(f"small shape {name}")
+    blob = Bl.build_blob(shape, 11)
+    runs = spec(shape, 5, [1, 4, 7, 2, 9], [9, 5, 3, 12, 1])
+    run_pair(shape, blob, runs, [1, 2, 3, 1, 5])
+
+
+def test_generic_head_size():
+    shape = Shape(120, 200, 2, 6, 3, 300, 24)  # head 20: the generic attention path
+    say("generic head size 20")
+    blob = Bl.build_blob(shape, 12)
+    runs = spec(shape, 4, [3, 6, 1, 10], [6, 4, 9, 2])
+    run_pair(shape, blob, runs, [2, 2, 4])
+
+
+def test_temperature_sampling():
+    shape = W.SMALL_SHAPES["gqa"]
+    say("temperature sampling")
+    blob = Bl.build_blob(shape, 13)
+    temps = [65536, 3 * 65536 // 2, 16 << 16, 1, 0, 32768]
+    seeds = [0, 1, 2**64 - 1, 12345, 7, 99]
+    runs = spec(shape, 6, [2, 5, 3, 8, 4, 1], 10, temps=temps, seeds=seeds)
+    run_pair(shape, blob, runs, [1, 4, 2])
+
+
+def test_wide_batch_two_chunks():
+    # 70 runs: four 16-run tiles per workgroup and a second batch chunk.
+    shape = W.SMALL_SHAPES["tiny"]
+    say("70 runs")
+    blob = Bl.build_blob(shape, 14)
+    runs = spec(shape, 70, [1 + (r % 9) for r in range(70)], [1 + (r % 7) for r in range(70)])
+    run_pair(shape, blob, runs, [2, 3], compare_every=True)
+
+
+def test_exact_path_inside_the_model():
+    # Normalization weights of 64.0 push the normalized vector beyond the
+    # three-digit range, so the matrices take the exact 64-bit path.
+    shape = W.SMALL_SHAPES["ragged"]
+    say("exact path in the model")
+    norm = np.full((2 * shape.layers + 1) * shape.dim, 1 << 30, dtype=np.int32)
+    blob = Bl.build_blob(shape, 15, tables={"norm": norm})
+    runs = spec(shape, 3, [2, 3, 4], 4)
+    run_pair(shape, blob, runs, [1, 1, 10])
+
+
+# ---------------------------------------------------------------------------
+# Errors: the 32-bit cache fit check, invalid states, complete runs
+
+def fit_blob(shape, kind, layer=0, seed=1000):
+    bl = Bl.build_blob(shape, seed)
+    w, s = Bl.matrix_view(bl, shape, kind, layer)
+    w[:] = 255
+    s[:] = 2**32 - 1
+    return bl
+
+
+@pytest.mark.parametrize("kind,layer,phase", [(Bl.KIND_K, 0, 6), (Bl.KIND_V, 0, 7), (Bl.KIND_K, 1, 6)])
+def test_cache_fit_failure(kind, layer, phase):
+    shape = W.SMALL_SHAPES["gqa"]
+    say(f"fit failure kind {kind} layer {layer}")
+    blob = fit_blob(shape, kind, layer)
+    runs = spec(shape, 3, [1, 2, 3], 3)
+    pair = Pair(shape, blob, runs)
+    try:
+        errs = pair.turn(5)
+        assert list(errs) == [8, 8, 8]
+        for i in range(3):
+            gi = pair.batch.info(i)
+            ri = O.state_info(pair.ref[i])[1]
+            assert pair.ref_err[i] == 8
+            assert (gi["error"], gi["phase"], gi["layer"], gi["position"]) == \
+                   (ri["error"], ri["phase"], ri["layer"], ri["position"]) == (8, phase, layer, 0)
+        errs = pair.turn(1)
+        assert list(errs) == [3, 3, 3]
+    finally:
+        pair.model.close()
+
+
+def test_rotary_fit_failure():
+    shape = Shape(8, 16, 1, 1, 1, 16, 4)
+    cos, sin = Bl.rope_tables(shape)
+    c45 = round(2**24 * math.sqrt(0.5))
+    cos[0, :] = c45
+    sin[0, :] = c45
+    bl = Bl.build_blob(shape, 5, tables={"cos": cos, "sin": sin,
+                                         "norm": np.full(3 * 8, 1 << 24, np.int32)})
+    w, s = Bl.matrix_view(bl, shape, Bl.KIND_K, 0)
+    E, sE = Bl.matrix_view(bl, shape, Bl.KIND_EMBED, 0)
+    E[:] = 129
+    sE[:] = 1 << 24
+    w[0::2, :] = 255
+    w[1::2, :] = 1
+    s[:] = int((2**31 - 2**20) / (127 * 8) * 2**24 / 65536)
+    pair = Pair(shape, bl, [(np.array([3], np.uint32), 2, 0, 0)])
+    try:
+        errs = pair.turn(1)
+        assert list(errs) == [8] and pair.ref_err[0] == 8
+        gi = pair.batch.info(0)
+        assert (gi["phase"], gi["layer"], gi["error"]) == (8, 0, 8)
+    finally:
+        pair.model.close()
+
+
+def test_invalid_and_complete_runs_in_a_batch():
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 16)
+    runs = spec(shape, 4, [3, 3, 3, 3], [1, 4, 4, 4])
+    pair = Pair(shape, blob, runs)
+    try:
+        # break run 2's tag on the device
+        pair.batch.d_states[2 * pair.batch.stride] = 0
+        errs = pair.turn(1)
+        assert list(errs) == [0, 0, 3, 0]
+        pair.turn(100, oracle_runs=[0, 1, 3])
+        pair.compare(runs=[0, 1, 3])
+        # run 0 completed in the first turn; a later turn leaves it as it is
+        before = pair.batch.state(0)
+        errs = pair.turn(1, oracle_runs=[])
+        assert errs[0] == 0 and np.array_equal(before, pair.batch.state(0))
+    finally:
+        pair.model.close()
+
+
+def test_stop_token_completes_a_run():
+    shape = W.TINY.shape
+    bl = Bl.build_blob(shape, 1000)
+    w, s = Bl.matrix_view(bl, shape, Bl.KIND_CLS)
+    s[:] = 0
+    s[2] = 1
+    w[2, :] = 255
+    runs = spec(shape, 2, [2, 5], 6)
+    pair = run_pair(shape, bl, runs, [1, 1, 3])
+    for i in range(2):
+        info = O.state_info(pair.ref[i])[1]
+        assert info["complete"] and info["generated"] == 1
+
+
+def test_engine_rejects_bad_artifacts():
+    require_gpu()
+    import torch
+    shape = W.SMALL_SHAPES["gqa"]
+    bl = Bl.build_blob(shape, 17)
+    s0 = Bl.section_zero(bl)
+    d = torch.from_numpy(bl).cuda()
+    bad = s0.copy(); bad[0] = 0
+    assert B.fpi8_engine_create(bad, d, bl.size, 4)[0] == 2
+    assert B.fpi8_engine_create(s0, d, int(Bl.plan(shape).sections[-1][0]) + 8, 4)[0] == 5
+    e, h = B.fpi8_engine_create(s0, d, bl.size, 4)
+    assert e == 0
+    B.fpi8_engine_destroy(h)
