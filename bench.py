@@ -1,0 +1,230 @@
+"""Benchmark: decode throughput of the fixed-point forward pass on one MI355X.
+
+One step is one position of every run of the batch through the whole path:
+embedding, every layer (normalization, query/key/value rows with rotary and
+the cache store, attention, output rows, normalization, gate/up rows with
+SiLU, down rows), the final normalization, the classifier rows and sampling.
+The workload is the 7B-shaped model (dim 4096, 32 layers, 32 heads of 128,
+FFN 11008, vocab 32000) with 64 runs of 512 prompt ids each; the prompts
+are prefilled first (untimed), then W warm-up steps and K timed decode
+steps run.  Inputs are seeded and synthetic and already in HBM when the
+timed region starts.
+
+Also measured: the standalone matrix row at 4096 x 4096 for batches of 1,
+8, 32 and 128 input vectors over a pool of distinct matrices larger than the
+last-level cache, and (unless --no-cpu) the oracle on the host cores over a
+bounded sample of the same workload.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode tokens/s at batch B, bit-exact; int8 row-kernel HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rows_bytes(shape, batch, generating=True):
+    """Algorithmic bytes of every row-kernel launch of one step: weight bytes,
+    Q24 scales, i64 inputs and i64 outputs of each matrix."""
+    d, f, kvd, v, L = shape.dim, shape.hidden, shape.kv_dim, shape.vocab, shape.layers
+    mats = [(d, d), (kvd, d), (kvd, d), (d, d), (f, d), (f, d), (d, f)] * L
+    if generating:
+        mats.append((v, d))
+    total = 0
+    for rows, cols in mats:
+        total += rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
+    return total
+
+
+def attention_bytes(shape, batch, npos):
+    """Algorithmic bytes of one attention launch (one layer): every cached key
+    and value word of the positions so far, the queries read and the outputs
+    written."""
+    return batch * (shape.kv_heads * npos * shape.head_size * 4 * 2 + shape.dim * 8 * 2)
+
+
+def row_sweep(torch, reps=3):
+    """GB/s of the standalone matrix row over a pool of 48 distinct
+    4096 x 4096 matrices (805 MB, over three times the 256 MB last-level
+    cache), one launch per matrix, timed with events on the launch stream."""
+    from fixed_point_int8_amd import binding as B
+    rows = cols = 4096
+    pool = 48
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    W = torch.randint(0, 256, (pool, rows, cols), dtype=torch.uint8, device="cuda", generator=g)
+    S = torch.randint(1 << 14, 1 << 18, (pool, rows), dtype=torch.int32, device="cuda", generator=g)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for batch in (1, 8, 32, 128):
+        x = (torch.randn((batch, cols), device="cuda", generator=g) * 2.0 * 65536).round().to(torch.int64)
+        y = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
+        n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
+        work = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        for i in range(pool):  # warm-up
+            assert B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y, work, n, stream) == 0
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for r in range(reps):
+            for i in range(pool):
+                B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y, work, n, stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / (reps * pool)
+        alg = rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
+        out[str(batch)] = {"us_per_call": round(ms * 1e3, 3), "GB/s": round(alg / ms / 1e6, 1),
+                           "frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
+                           "weight_GB/s": round(rows * cols / ms / 1e6, 1)}
+        del x, y, work
+    del W, S
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(blob, shape, positions=3):
+    """The oracle on the host: one run of the same model from a one-id prompt
+    for `positions` generating positions (each with the classifier), on as
+    many threads as the box gives this job (at most 16)."""
+    import oracle as O
+    import workloads as Wl
+    threads = min(16, os.cpu_count() or 1)
+    O.set_threads(threads)
+    ids = Wl.prompt_ids(shape.vocab, 1, 2003, 0)
+    e, st = O.init_state(shape.as_tuple(), ids, positions, 0, 1)
+    assert e == 0
+    t0 = time.perf_counter()
+    assert O.turn(blob, st, positions) == 0
+    dt = time.perf_counter() - t0
+    gen = O.state_info(st)[1]["generated"]
+    O.set_threads(1)
+    return {"value": round(gen / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one run of the 7B-shaped model, a 1-id prompt, {gen} generating positions "
+                      f"(classifier included), {dt:.1f} s wall; runs are independent, so B runs take "
+                      f"B times as long"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--workload", default="7B-shaped-d4096-L32")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the runs of a batch are "
+              f"independent, and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as Wl
+    from workloads import blob as Bl
+    from fixed_point_int8_amd import binding as B
+    from fixed_point_int8_amd.device import DeviceBatch, DeviceModel
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = Wl.by_name(args.workload)
+    shape = w.shape
+    if args.warmup + args.steps > w.max_tokens - 1:
+        raise SystemExit("warmup + steps exceed the decode positions of the workload")
+
+    t = time.perf_counter()
+    blob = Bl.build_blob(shape, w.blob_seed)
+    log(f"artifact {blob.size / 1e9:.3f} GB in {time.perf_counter() - t:.1f} s")
+    model = DeviceModel(blob, max_runs=w.runs)
+    runs = [(Wl.prompt_ids(shape.vocab, w.prompt, w.ids_seed, r), w.max_tokens, w.temperature_q16,
+             w.run_seed + r) for r in range(w.runs)]
+    t = time.perf_counter()
+    batch = DeviceBatch(shape.as_tuple(), runs)
+    log(f"{w.runs} states of {batch.sizes[0] / 1e6:.1f} MB in {time.perf_counter() - t:.1f} s")
+    stream = torch.cuda.current_stream()
+
+    # Prefill: positions 0 .. prompt-1 (the last one generates the first token).
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    e, errs = batch.turn(model, w.prompt, stream)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t
+    assert e == 0, (e, list(errs))
+    log(f"prefill {w.prompt} positions x {w.runs} runs in {prefill_s:.2f} s")
+
+    e, errs = batch.turn(model, args.warmup, stream)
+    assert e == 0, (e, list(errs))
+    gen0 = sum(batch.info(i)["generated"] for i in range(w.runs))
+    pos0 = batch.info(0)["position"]
+
+    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, True)
+    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e, errs = batch.turn(model, args.steps, stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert e == 0, (e, list(errs))
+    gen1 = sum(batch.info(i)["generated"] for i in range(w.runs))
+    tokens = gen1 - gen0
+    _, rows_ms, rows_n = B.fpi8_engine_timing(model.engine, B.T_ROWS)
+    _, attn_ms, attn_n = B.fpi8_engine_timing(model.engine, B.T_ATTN)
+    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, False)
+    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, False)
+
+    # Algorithmic bytes over the timed steps (positions pos0 .. pos0+steps-1).
+    rows_alg = rows_bytes(shape, w.runs) * args.steps
+    attn_alg = sum(attention_bytes(shape, w.runs, pos0 + k + 1) * shape.layers
+                   for k in range(args.steps))
+    kern = {
+        "rows": {"launches": rows_n, "avg_us": round(rows_ms * 1e3 / max(rows_n, 1), 2),
+                 "GB/s": round(rows_alg / (rows_ms * 1e6), 1),
+                 "bytes_per_launch": int(rows_alg / max(rows_n, 1))},
+        "attention": {"launches": attn_n, "avg_us": round(attn_ms * 1e3 / max(attn_n, 1), 2),
+                      "GB/s": round(attn_alg / (attn_ms * 1e6), 1),
+                      "bytes_per_launch": int(attn_alg / max(attn_n, 1))},
+        "share_of_step": {"rows": round(rows_ms / (dt * 1e3), 3),
+                          "attention": round(attn_ms / (dt * 1e3), 3)},
+    }
+    dom = "attention" if attn_ms > rows_ms else "rows"
+    ach = kern[dom]["GB/s"]
+    roofline = {"kernel": "k_attention" if dom == "attention" else "k_rows", "bound": "hbm",
+                "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+
+    model.close()
+    del batch, model
+    torch.cuda.empty_cache()
+    sweep = None if args.no_sweep else row_sweep(torch)
+    cpu = None if args.no_cpu else cpu_baseline(blob, shape)
+
+    res = {
+        "metric": METRIC, "value": round(tokens / dt, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} decode", "global_batch": w.runs,
+                   "prompt": w.prompt, "decode_positions": [pos0, pos0 + args.steps - 1],
+                   "seq_len": w.prompt + w.max_tokens - 1, "parallelism": "none (one GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
+        "prefill_s": round(prefill_s, 2), "row_sweep_4096": sweep,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

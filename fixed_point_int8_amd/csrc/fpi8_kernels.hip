@@ -251,6 +251,10 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
     vec[mt] = sg.pad != 0;
     rbase[mt] = EPI == EPI_GATEUP ? tile * 16 : (tile - sg.tile0) * 16 * MT + 16 * mt;
   }
+  // Nothing to do for a batch chunk without a run in this phase (the
+  // classifier at prompt positions, finished runs).
+  if (EPI != EPI_RAW && !__syncthreads_or(row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1))) ? 1 : 0))
+    return;
   const bool exact = a.oflag != nullptr && *a.oflag != 0;
 
   int64_t v[MT][BT][4];

@@ -267,12 +267,9 @@ def test_invalid_and_complete_runs_in_a_batch():
 
 
 def test_stop_token_completes_a_run():
+    from test_oracle_pins import stop_token_blob
     shape = W.TINY.shape
-    bl = Bl.build_blob(shape, 1000)
-    w, s = Bl.matrix_view(bl, shape, Bl.KIND_CLS)
-    s[:] = 0
-    s[2] = 1
-    w[2, :] = 255
+    bl = stop_token_blob(shape)
     runs = spec(shape, 2, [2, 5], 6)
     pair = run_pair(shape, bl, runs, [1, 1, 3])
     for i in range(2):

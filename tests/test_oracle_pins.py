@@ -683,15 +683,29 @@ def test_turn_cuts_do_not_change_results():
     assert np.array_equal(a, b)
 
 
-def test_stop_token_completes_the_run():
-    # A classifier that always prefers token 2 (the closing token): the first
-    # sampled token completes the run.
-    shape = W.TINY.shape
-    bl = B.build_blob(shape, 1000)
+def stop_token_blob(shape, seed=1000):
+    """Every activation +127.0 from the embedding, no residual updates, and a
+    classifier whose only nonzero row is the closing token's: token 2 wins."""
+    bl = B.build_blob(shape, seed, tables={"norm": np.full((2 * shape.layers + 1) * shape.dim,
+                                                           1 << 24, np.int32)})
+    E, sE = B.matrix_view(bl, shape, B.KIND_EMBED)
+    E[:] = 255
+    sE[:] = 1 << 24
+    for l in range(shape.layers):
+        for kind in (B.KIND_O, B.KIND_DOWN):
+            B.matrix_view(bl, shape, kind, l)[1][:] = 0
     w, s = B.matrix_view(bl, shape, B.KIND_CLS)
     s[:] = 0
     s[2] = 1
     w[2, :] = 255
+    return bl
+
+
+def test_stop_token_completes_the_run():
+    # A classifier that always prefers token 2 (the closing token): the first
+    # sampled token completes the run.
+    shape = W.TINY.shape
+    bl = stop_token_blob(shape)
     e, st = O.init_state(shape.as_tuple(), [10, 11], 5)
     assert O.run_to_end(bl, st) == 0
     info = O.state_info(st)[1]
