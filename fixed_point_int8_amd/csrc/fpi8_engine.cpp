@@ -49,6 +49,8 @@ struct fpi8_engine {
   uint32_t *d_oflags = nullptr;
   uint32_t n_oflags = 0;
   int32_t *d_run_err = nullptr;
+  int64_t *d_partials = nullptr;   // split-contraction partial sums
+  uint32_t *d_counters = nullptr;  // split-contraction arrival counters
   // pinned host buffers
   RunDesc *h_runs = nullptr;
   uint8_t *h_headers = nullptr;
@@ -91,6 +93,37 @@ struct TimedLaunch {
 
 uint32_t batch_tiles(uint32_t n_runs) { return n_runs <= 16 ? 1 : n_runs <= 32 ? 2 : 4; }
 
+// Launch shape of one row-kernel call: rows per tile (16 * mt), runs per
+// tile (16 * bt), and how many workgroups share a tile's contraction.
+struct RowPlan {
+  int mt, bt;
+  uint32_t chunks, tiles, splits;
+};
+
+constexpr uint32_t kMaxSplitGroups = 1024;  // tiles * chunks * splits when splits > 1
+constexpr uint64_t kPartialValues = 64;     // i64 per lane at most (mt * bt * 4)
+
+// More runs per tile need more rows per tile, so that the byte digits of
+// the inputs (3 bytes per run and column) are read from L2 no more than
+// about three times per weight byte; then the columns are split until the
+// launch has enough workgroups for every compute unit.
+RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup) {
+  RowPlan p;
+  p.bt = (int)batch_tiles(n_runs);
+  p.chunks = (n_runs + 16 * p.bt - 1) / (16 * p.bt);
+  p.mt = p.bt == 4 ? 4 : p.bt == 2 ? 2 : (gateup ? 2 : 1);
+  const uint32_t per_tile = gateup ? 16 * (p.mt / 2) : 16 * p.mt;
+  p.tiles = (rows + per_tile - 1) / per_tile;
+  const uint32_t kblocks = (cols + 63) / 64;
+  p.splits = 1;
+  while (p.tiles * p.chunks * p.splits < 512 && kblocks / (p.splits * 2) >= 8 &&
+         p.tiles * p.chunks * p.splits * 2 <= kMaxSplitGroups)
+    p.splits *= 2;
+  return p;
+}
+
+uint64_t partials_bytes() { return kMaxSplitGroups * 64ull * kPartialValues * 8; }
+
 RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t cols,
                    const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer) {
   RowsArgs a;
@@ -116,22 +149,33 @@ RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t co
   return a;
 }
 
-void add_seg(RowsArgs &a, const Mat &m, uint32_t role, uint32_t rows_per_tile) {
+void add_seg(RowsArgs &a, const Mat &m, uint32_t role) {
   Seg &s = a.seg[a.nseg++];
   s.W = m.W;
   s.S = m.S;
   s.rows = m.rows;
-  s.tile0 = a.ntiles;
   s.role = role;
   s.pad = m.vec ? 1u : 0u;
-  a.ntiles += (m.rows + rows_per_tile - 1) / rows_per_tile;
 }
 
+// Plans the launch over the segments added so far and runs it.
 int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t s) {
-  const uint32_t bt = batch_tiles(n_runs);
-  const uint32_t chunks = (n_runs + 16 * bt - 1) / (16 * bt);
+  const bool gateup = epi == EPI_GATEUP;
+  uint32_t rows = 0;
+  for (uint32_t i = 0; i < a.nseg; i++) rows += a.seg[i].rows;
+  RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup);
+  const uint32_t per_tile = gateup ? 16 * (p.mt / 2) : 16 * p.mt;
+  a.ntiles = 0;
+  for (uint32_t i = 0; i < a.nseg; i++) {
+    a.seg[i].tile0 = gateup ? 0 : a.ntiles;
+    if (!gateup || i == 0) a.ntiles += (a.seg[i].rows + per_tile - 1) / per_tile;
+  }
+  if (p.tiles * p.chunks * p.splits > kMaxSplitGroups) p.splits = 1;
+  a.splits = p.splits;
+  a.partials = e->d_partials;
+  a.counters = e->d_counters;
   TimedLaunch t(e, T_ROWS, s);
-  return launch_rows(epi, epi == EPI_GATEUP ? 2 : 1, (int)bt, a, chunks, s);
+  return launch_rows(epi, p.mt, p.bt, a, p.chunks, s);
 }
 
 // One position of every active run.
@@ -157,9 +201,9 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
     }
     {
       RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 0, IN_W1, l);
-      add_seg(a, e->layer_mat(l, M_Q), ROLE_Q, 16);
-      add_seg(a, e->layer_mat(l, M_K), ROLE_K, 16);
-      add_seg(a, e->layer_mat(l, M_V), ROLE_V, 16);
+      add_seg(a, e->layer_mat(l, M_Q), ROLE_Q);
+      add_seg(a, e->layer_mat(l, M_K), ROLE_K);
+      add_seg(a, e->layer_mat(l, M_V), ROLE_V);
       if ((r = run_rows(e, EPI_QKV, a, n_runs, s))) return r;
     }
     {
@@ -171,7 +215,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
     }
     {
       RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 1, IN_W3, l);
-      add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN, 16);
+      add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_RESID, a, n_runs, s))) return r;
     }
     na.w = e->norm + (uint64_t)(2 * l + 1) * c.dim;
@@ -182,9 +226,8 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
     }
     {
       RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 2, IN_W1, l);
-      add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN, 16);
-      a.ntiles = 0;  // gate and up share the tile index
-      add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN, 16);
+      add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN);
+      add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN);  // shares the gate's row tiles
       a.planes_out = e->d_planes1;
       a.kp_out = e->kp;
       a.oflag_out = fl + 3;
@@ -192,7 +235,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
     }
     {
       RowsArgs a = rows_base(e, states, n_runs, c.hidden, e->d_planes1, fl + 3, IN_GATE, l);
-      add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN, 16);
+      add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_DOWN, a, n_runs, s))) return r;
     }
   }
@@ -205,7 +248,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
   }
   {
     RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, ff, IN_W1, 0);
-    add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN, 16);
+    add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN);
     if ((r = run_rows(e, EPI_CLS, a, n_runs, s))) return r;
   }
   {
@@ -223,6 +266,8 @@ void release(fpi8_engine *e) {
   (void)hipFree(e->d_planes1);
   (void)hipFree(e->d_oflags);
   (void)hipFree(e->d_run_err);
+  (void)hipFree(e->d_partials);
+  (void)hipFree(e->d_counters);
   (void)hipHostFree(e->h_runs);
   (void)hipHostFree(e->h_headers);
   (void)hipHostFree(e->h_err);
@@ -277,6 +322,9 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
       (r = hip_ok(hipMalloc(&e->d_planes1, planes))) ||
       (r = hip_ok(hipMalloc(&e->d_oflags, 4ull * e->n_oflags))) ||
       (r = hip_ok(hipMalloc(&e->d_run_err, 4ull * max_runs))) ||
+      (r = hip_ok(hipMalloc(&e->d_partials, partials_bytes()))) ||
+      (r = hip_ok(hipMalloc(&e->d_counters, 4ull * kMaxSplitGroups))) ||
+      (r = hip_ok(hipMemset(e->d_counters, 0, 4ull * kMaxSplitGroups))) ||
       (r = hip_ok(hipHostMalloc(&e->h_runs, sizeof(RunDesc) * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_headers, 128ull * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_err, 4ull * max_runs))) ||
@@ -372,10 +420,24 @@ int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uin
   return 0;
 }
 
-uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
-  (void)rows;
+// Workspace of the standalone row: [256 B flag][counters][partials][digits].
+static uint64_t rows_work_layout(uint32_t rows, uint32_t cols, uint32_t batch, uint64_t *off_cnt,
+                                 uint64_t *off_part, uint64_t *off_planes, RowPlan *plan) {
+  const RowPlan p = plan_rows(rows, cols, batch, false);
+  const uint64_t groups = (uint64_t)p.tiles * p.chunks;
+  const uint64_t cnt = (groups * 4 + 255) / 256 * 256;
+  const uint64_t part = p.splits > 1 ? groups * p.splits * 64ull * (p.mt * p.bt * 4) * 8 : 0;
   const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
-  return 256 + 3 * bp * kp;
+  *off_cnt = 256;
+  *off_part = 256 + cnt;
+  *off_planes = 256 + cnt + (part + 255) / 256 * 256;
+  if (plan) *plan = p;
+  return *off_planes + 3 * bp * kp;
+}
+
+uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
+  uint64_t a, b, c;
+  return rows_work_layout(rows, cols, batch, &a, &b, &c, nullptr);
 }
 
 int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
@@ -389,9 +451,15 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
     return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   const uint32_t kp = round_up(cols, 64), bp = round_up(batch, 64);
-  uint32_t *flag = reinterpret_cast<uint32_t *>(d_work);
-  int8_t *planes = reinterpret_cast<int8_t *>(d_work) + 256;
-  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
+  uint64_t off_cnt, off_part, off_planes;
+  RowPlan p;
+  rows_work_layout(rows, cols, batch, &off_cnt, &off_part, &off_planes, &p);
+  uint8_t *base = reinterpret_cast<uint8_t *>(d_work);
+  uint32_t *flag = reinterpret_cast<uint32_t *>(base);
+  int8_t *planes = reinterpret_cast<int8_t *>(base + off_planes);
+  int r = launch_zero_words(reinterpret_cast<uint32_t *>(base + off_cnt), p.tiles * p.chunks, s);
+  if (r) return r;
+  r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
   if (r) return r;
   RowsArgs a;
   memset(&a, 0, sizeof a);
@@ -413,10 +481,11 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   sg.role = ROLE_PLAIN;
   sg.pad = (cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0) ? 1u : 0u;
   a.nseg = 1;
-  a.ntiles = (rows + 15) / 16;
-  const uint32_t bt = batch_tiles(batch);
-  const uint32_t chunks = (batch + 16 * bt - 1) / (16 * bt);
-  return launch_rows(EPI_RAW, 1, (int)bt, a, chunks, s);
+  a.ntiles = p.tiles;
+  a.splits = p.splits;
+  a.partials = reinterpret_cast<int64_t *>(base + off_part);
+  a.counters = reinterpret_cast<uint32_t *>(base + off_cnt);
+  return launch_rows(EPI_RAW, p.mt, p.bt, a, p.chunks, s);
 }
 
 }  // extern "C"

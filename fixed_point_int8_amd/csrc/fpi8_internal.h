@@ -114,6 +114,10 @@ struct RowsArgs {
   // standalone matrix rows
   const int64_t *x_raw;     // [n_runs][cols]
   int64_t *y_raw;           // [n_runs][rows]
+  // split contraction
+  uint32_t splits;          // workgroups per row tile, each a share of the columns
+  int64_t *partials;        // [tile * chunks][splits][64 lanes][MT * BT * 4]
+  uint32_t *counters;       // [tile * chunks], zero between launches
 };
 
 struct NormArgs {
@@ -173,6 +177,7 @@ int launch_attention(const AttnArgs &a, void *stream);
 int launch_sample(const SampleArgs &a, void *stream);
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
                       uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream);
+int launch_zero_words(uint32_t *p, uint32_t n, void *stream);
 size_t attention_lds_bytes(uint32_t max_npos, uint32_t head);
 int kernels_init(uint32_t max_npos, uint32_t head);
 

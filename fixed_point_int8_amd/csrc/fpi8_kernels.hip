@@ -175,9 +175,11 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
 // ---------------------------------------------------------------------------
 // The matrix row on the int8 matrix cores.
 //
-// A workgroup of four waves owns 16*MT rows and BT*16 runs; the waves split
-// the 64-column blocks of the contraction round-robin and add their i32
-// partial sums through LDS.  MFMA 16x16x64 lanes: lane (i = lane % 16,
+// A workgroup of four waves owns 16*MT rows, BT*16 runs and a share of the
+// contraction (a split); the waves take its 64-column blocks round-robin,
+// prefetching weights a group of blocks ahead, and add their i32 partial
+// sums in LDS.  With several splits the workgroups of a row tile meet
+// through a counter: the last adds the others' i64 partial sums.  MFMA 16x16x64 lanes: lane (i = lane % 16,
 // g = lane / 16) supplies row i of the weight tile and run i of the digit
 // tile, columns [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of
 // run i.
@@ -228,12 +230,21 @@ __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase
 
 template <int EPI, int MT, int BT>
 __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
+  constexpr int NW = 4;                                // waves per workgroup
+  constexpr int D = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);   // blocks per prefetch group
   constexpr int NACC = MT * 3 * BT;
-  __shared__ v4i red[3][NACC][64];
+  constexpr int HALF = MT / 2;
+  __shared__ int red[NACC * 4][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const uint32_t tile = blockIdx.x;
+  const uint32_t split = blockIdx.x % a.splits;
+  const uint32_t tile = blockIdx.x / a.splits;
   const uint32_t b0 = blockIdx.y * BT * 16;
+
+  // Nothing to do for a batch chunk without a run in this phase (the
+  // classifier at prompt positions, finished runs).
+  if (EPI != EPI_RAW && !__syncthreads_or(row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1))) ? 1 : 0))
+    return;
 
   uint32_t si = 0;
   if (EPI != EPI_GATEUP)
@@ -244,21 +255,22 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   bool vec[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
-    const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt] : a.seg[si];
+    const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[si];
     Wp[mt] = sg.W;
     Sp[mt] = sg.S;
     rcount[mt] = sg.rows;
     vec[mt] = sg.pad != 0;
-    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 : (tile - sg.tile0) * 16 * MT + 16 * mt;
+    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 * HALF + 16 * (mt % HALF)
+                                  : (tile - sg.tile0) * 16 * MT + 16 * mt;
   }
-  // Nothing to do for a batch chunk without a run in this phase (the
-  // classifier at prompt positions, finished runs).
-  if (EPI != EPI_RAW && !__syncthreads_or(row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1))) ? 1 : 0))
-    return;
+  // This workgroup's share of the contraction, in 64-column blocks.
+  const uint32_t kb_lo = (uint32_t)((uint64_t)a.kblocks * split / a.splits);
+  const uint32_t kb_hi = (uint32_t)((uint64_t)a.kblocks * (split + 1) / a.splits);
   const bool exact = a.oflag != nullptr && *a.oflag != 0;
 
   int64_t v[MT][BT][4];
   if (!exact) {
+    for (int i = tid; i < NACC * 4 * 64; i += 256) (&red[0][0])[i] = 0;
     v4i acc[MT][3][BT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -267,52 +279,76 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
         for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
     const uint64_t limb = (uint64_t)a.bp * a.kp;
-    for (uint32_t kb = wave; kb < a.kblocks; kb += 4) {
-      const uint32_t k0 = kb * 64 + lg * 16;
-      v4i A[MT];
+    const int8_t *dig = a.planes + (uint64_t)(b0 + li) * a.kp + lg * 16;
+    // Blocks kb_lo + wave + NW * n, n = 0 .. nkb - 1, prefetched D at a time
+    // into two register buffers so the weight stream keeps many loads in
+    // flight while the matrix cores work on the previous group.
+    const uint32_t first = kb_lo + wave;
+    const uint32_t nkb = kb_hi > first ? (kb_hi - first + NW - 1) / NW : 0;
+    const uint32_t G = (nkb + D - 1) / D;
+    v4i A0[D][MT], A1[D][MT];
+    auto load_group = [&](v4i (&A)[D][MT], uint32_t g) {
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-        A[mt] = load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, k0, vec[mt]);
+      for (int d = 0; d < D; d++) {
+        const uint32_t n = g * D + d;
+        const uint32_t k0 = (first + NW * n) * 64 + lg * 16;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+          A[d][mt] = n < nkb ? load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, k0, vec[mt])
+                             : v4i{0, 0, 0, 0};
+      }
+    };
+    auto compute_group = [&](v4i (&A)[D][MT], uint32_t g) {
+#pragma unroll
+      for (int d = 0; d < D; d++) {
+        const uint32_t n = g * D + d;
+        if (n < nkb) {
+          const uint64_t k0 = (uint64_t)(first + NW * n) * 64;
+#pragma unroll
+          for (int l = 0; l < 3; l++)
+#pragma unroll
+            for (int bt = 0; bt < BT; bt++) {
+              const v4i Bv = *reinterpret_cast<const v4i *>(dig + l * limb + (uint64_t)bt * 16 * a.kp + k0);
+#pragma unroll
+              for (int mt = 0; mt < MT; mt++)
+                acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d][mt], Bv, acc[mt][l][bt], 0, 0, 0);
+            }
+        }
+      }
+    };
+    if (G > 0) load_group(A0, 0);
+    for (uint32_t g = 0; g < G; g += 2) {
+      if (g + 1 < G) load_group(A1, g + 1);
+      compute_group(A0, g);
+      if (g + 2 < G) load_group(A0, g + 2);
+      if (g + 1 < G) compute_group(A1, g + 1);
+    }
+    __syncthreads();
+    // The four waves' i32 partial sums, added in LDS (exact and order-free).
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int l = 0; l < 3; l++)
 #pragma unroll
-        for (int bt = 0; bt < BT; bt++) {
-          const v4i Bv = *reinterpret_cast<const v4i *>(
-              a.planes + l * limb + (uint64_t)(b0 + bt * 16 + li) * a.kp + k0);
+        for (int bt = 0; bt < BT; bt++)
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++)
-            acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mt], Bv, acc[mt][l][bt], 0, 0, 0);
-        }
-    }
-    if (wave > 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int l = 0; l < 3; l++)
-#pragma unroll
-          for (int bt = 0; bt < BT; bt++) red[wave - 1][(mt * 3 + l) * BT + bt][lane] = acc[mt][l][bt];
-    }
+          for (int j = 0; j < 4; j++) atomicAdd(&red[((mt * 3 + l) * BT + bt) * 4 + j][lane], acc[mt][l][bt][j]);
     __syncthreads();
     if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < 3; w++)
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int l = 0; l < 3; l++)
-#pragma unroll
-          for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] += red[w][(mt * 3 + l) * BT + bt][lane];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int bt = 0; bt < BT; bt++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
-                         ((int64_t)acc[mt][2][bt][j] << 16);
+          v[mt][bt][j] = (int64_t)red[((mt * 3 + 0) * BT + bt) * 4 + j][lane] +
+                         ((int64_t)red[((mt * 3 + 1) * BT + bt) * 4 + j][lane] << 8) +
+                         ((int64_t)red[((mt * 3 + 2) * BT + bt) * 4 + j][lane] << 16);
   } else {
-    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products.
+    // Exact 64-bit path over this workgroup's columns:
+    // sum_c (b_c - 128) * x_c with wrapping products.
     if (wave != 0) return;
+    const uint32_t c_lo = kb_lo * 64, c_hi = min(kb_hi * 64, a.cols);
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -326,11 +362,44 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
           int64_t s = 0;
           if (ok && row < rcount[mt]) {
             const uint8_t *w = Wp[mt] + (uint64_t)row * a.cols;
-            for (uint32_t k = 0; k < a.cols; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+            for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
           }
           v[mt][bt][j] = s;
         }
       }
+  }
+
+  // Split contraction: every workgroup of a tile leaves its partial sums;
+  // the last one to arrive adds them all (wrapping, order-free) and runs the
+  // epilogue.
+  if (a.splits > 1) {
+    constexpr int PV = MT * BT * 4;
+    const uint32_t ctr = tile * gridDim.y + blockIdx.y;
+    int64_t *mine = a.partials + (((uint64_t)ctr * a.splits + split) * 64 + lane) * PV;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) mine[(mt * BT + bt) * 4 + j] = v[mt][bt][j];
+    __threadfence();
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(&a.counters[ctr], 1u);
+    prev = __shfl(prev, 0, 64);
+    if (prev != a.splits - 1) return;
+    __threadfence();
+    for (uint32_t s = 0; s < a.splits; s++) {
+      if (s == split) continue;
+      const int64_t *other = a.partials + (((uint64_t)ctr * a.splits + s) * 64 + lane) * PV;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            v[mt][bt][j] = wadd(v[mt][bt][j], __builtin_nontemporal_load(&other[(mt * BT + bt) * 4 + j]));
+    }
+    if (lane == 0) atomicExch(&a.counters[ctr], 0u);
   }
 
   // Epilogue (wave 0): y = (v * scale) >> 24, then the phase's own work.
@@ -346,7 +415,6 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
         const uint32_t row = rbase[mt] + 4 * lg + j;
         y[mt][j] = row < rcount[mt] ? wmul(v[mt][bt][j], (int64_t)(uint64_t)Sp[mt][row]) >> 24 : 0;
       }
-    const uint32_t r0 = rbase[0] + 4 * lg;
     if (EPI == EPI_RAW) {
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
@@ -359,83 +427,82 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
     }
     RunDesc &rd = a.runs[b];
     uint8_t *st = a.states + rd.base;
-    if (EPI == EPI_CLS) {
-      int64_t *lg_out = reinterpret_cast<int64_t *>(st + rd.off_logits);
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (r0 + j < rcount[0]) lg_out[r0 + j] = y[0][j];
-    } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
-      int64_t *x = reinterpret_cast<int64_t *>(st + rd.off_x);
-      int64_t *w1 = reinterpret_cast<int64_t *>(st + rd.off_w1);
+    for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
+      const uint32_t r0 = rbase[mt] + 4 * lg;
+      if (EPI == EPI_CLS) {
+        int64_t *lg_out = reinterpret_cast<int64_t *>(st + rd.off_logits);
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (r0 + j < rcount[0]) {
-          if (EPI == EPI_DOWN) w1[r0 + j] = y[0][j];
-          x[r0 + j] = wadd(x[r0 + j], y[0][j]);
-        }
-    } else if (EPI == EPI_GATEUP) {
-      // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
-      int64_t *gate = reinterpret_cast<int64_t *>(st + rd.off_gate);
-      int64_t *up = reinterpret_cast<int64_t *>(st + rd.off_up);
-      const uint64_t pitch = (uint64_t)a.bp * a.kp_out;
-      const int64_t lim = (int64_t)16 << 16;
+        for (int j = 0; j < 4; j++)
+          if (r0 + j < rcount[mt]) lg_out[r0 + j] = y[mt][j];
+      } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
+        int64_t *x = reinterpret_cast<int64_t *>(st + rd.off_x);
+        int64_t *w1 = reinterpret_cast<int64_t *>(st + rd.off_w1);
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const uint32_t row = r0 + j;
-        if (row >= a.hidden) continue;
-        const int64_t g = y[0][j], u = y[1][j];
-        const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)a.silu[(g + lim) >> 9];
-        const int64_t h = wmul(sg, u) >> 16;
-        gate[row] = h;
-        up[row] = u;
-        put_digits(a.planes_out, pitch, (uint64_t)b * a.kp_out + row, h, a.oflag_out);
-      }
-    } else if (EPI == EPI_QKV) {
-      const uint32_t role = a.seg[si].role;
-      const uint32_t pos = rd.pos;
-      if (role == ROLE_V) {
-        // Phase 7: the value rows into the cache, each checked to fit 32 bits.
-        int32_t *V = reinterpret_cast<int32_t *>(st + rd.off_values);
+        for (int j = 0; j < 4; j++)
+          if (r0 + j < rcount[mt]) {
+            if (EPI == EPI_DOWN) w1[r0 + j] = y[mt][j];
+            x[r0 + j] = wadd(x[r0 + j], y[mt][j]);
+          }
+      } else if (EPI == EPI_GATEUP) {
+        // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
+        int64_t *gate = reinterpret_cast<int64_t *>(st + rd.off_gate);
+        int64_t *up = reinterpret_cast<int64_t *>(st + rd.off_up);
+        const uint64_t pitch = (uint64_t)a.bp * a.kp_out;
+        const int64_t lim = (int64_t)16 << 16;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const uint32_t row = r0 + j;
-          if (row >= rcount[0]) continue;
-          if (!fits32(y[0][j])) { fail(rd, a.layer, 7); continue; }
-          const uint32_t kvh = row / a.head, e = row % a.head;
-          V[(((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e] = (int32_t)y[0][j];
+          if (row >= a.hidden) continue;
+          const int64_t g = y[mt][j], u = y[mt + HALF][j];
+          const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)a.silu[(g + lim) >> 9];
+          const int64_t h = wmul(sg, u) >> 16;
+          gate[row] = h;
+          up[row] = u;
+          put_digits(a.planes_out, pitch, (uint64_t)b * a.kp_out + row, h, a.oflag_out);
         }
-      } else {
-        // Phase 8 on the query (kept in w2) and on the key after its
-        // phase-6 store check: pairs (2p, 2p+1) of each head turned by
-        // position pos's cosine and sine p.
-        const int32_t *cs = a.rope_cos + (uint64_t)pos * a.half;
-        const int32_t *sn = a.rope_sin + (uint64_t)pos * a.half;
-        int64_t *q = reinterpret_cast<int64_t *>(st + rd.off_w2);
-        int32_t *K = reinterpret_cast<int32_t *>(st + rd.off_keys);
+      } else if (EPI == EPI_QKV) {
+        const uint32_t role = a.seg[si].role;
+        const uint32_t pos = rd.pos;
+        if (role == ROLE_V) {
+          // Phase 7: the value rows into the cache, each checked to fit 32 bits.
+          int32_t *V = reinterpret_cast<int32_t *>(st + rd.off_values);
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const uint32_t row = r0 + j;
-          if (row >= rcount[0]) continue;
-          int64_t A0 = y[0][j], B0 = y[0][j + 1];
-          if (role == ROLE_K) {
-            bool ok = true;
-            if (!fits32(A0)) { fail(rd, a.layer, 6); ok = false; }
-            if (!fits32(B0)) { fail(rd, a.layer, 6); ok = false; }
-            if (!ok) continue;
-          }
-          const uint32_t p = (row % a.head) >> 1;
-          const int64_t c = cs[p], s = sn[p];
-          const int64_t ra = wsub(wmul(A0, c), wmul(B0, s)) >> 24;
-          const int64_t rb = wadd(wmul(A0, s), wmul(B0, c)) >> 24;
-          if (role == ROLE_Q) {
-            q[row] = ra;
-            q[row + 1] = rb;
-          } else {
-            if (!fits32(ra) || !fits32(rb)) { fail(rd, a.layer, 8); continue; }
+          for (int j = 0; j < 4; j++) {
+            const uint32_t row = r0 + j;
+            if (row >= rcount[mt]) continue;
+            if (!fits32(y[mt][j])) { fail(rd, a.layer, 7); continue; }
             const uint32_t kvh = row / a.head, e = row % a.head;
-            int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e;
-            dst[0] = (int32_t)ra;
-            dst[1] = (int32_t)rb;
+            V[(((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e] = (int32_t)y[mt][j];
+          }
+        } else {
+          // Phase 8 on the query (kept in w2) and on the key after its
+          // phase-6 store check: pairs (2p, 2p+1) of each head turned by
+          // position pos's cosine and sine p.
+          const int32_t *cs = a.rope_cos + (uint64_t)pos * a.half;
+          const int32_t *sn = a.rope_sin + (uint64_t)pos * a.half;
+          int64_t *q = reinterpret_cast<int64_t *>(st + rd.off_w2);
+          int32_t *K = reinterpret_cast<int32_t *>(st + rd.off_keys);
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const uint32_t row = r0 + j;
+            if (row >= rcount[mt]) continue;
+            const int64_t A0 = y[mt][j], B0 = y[mt][j + 1];
+            if (role == ROLE_K && (!fits32(A0) || !fits32(B0))) { fail(rd, a.layer, 6); continue; }
+            const uint32_t p = (row % a.head) >> 1;
+            const int64_t c = cs[p], s = sn[p];
+            const int64_t ra = wsub(wmul(A0, c), wmul(B0, s)) >> 24;
+            const int64_t rb = wadd(wmul(A0, s), wmul(B0, c)) >> 24;
+            if (role == ROLE_Q) {
+              q[row] = ra;
+              q[row + 1] = rb;
+            } else {
+              if (!fits32(ra) || !fits32(rb)) { fail(rd, a.layer, 8); continue; }
+              const uint32_t kvh = row / a.head, e = row % a.head;
+              int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e;
+              dst[0] = (int32_t)ra;
+              dst[1] = (int32_t)rb;
+            }
           }
         }
       }
@@ -444,7 +511,10 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 }
 
 // Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
-__global__ void k_zero_flag(uint32_t *flag) { *flag = 0; }
+__global__ void k_zero_words(uint32_t *p, uint32_t n) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 __global__ void k_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
                              uint32_t kp, uint32_t bp, uint32_t *oflag) {
@@ -759,7 +829,7 @@ int launch_norm(const NormArgs &a, void *stream) {
 
 template <int EPI, int MT>
 static int rows_bt(int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
-  const dim3 grid(a.ntiles, chunks), block(256);
+  const dim3 grid(a.ntiles * a.splits, chunks), block(256);
   switch (bt) {
     case 1: hipLaunchKernelGGL((k_rows<EPI, MT, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_rows<EPI, MT, 2>), grid, block, 0, s, a); break;
@@ -769,16 +839,26 @@ static int rows_bt(int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
   return ok(hipGetLastError());
 }
 
+template <int EPI>
+static int rows_mt(int mt, int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
+  switch (mt) {
+    case 1: return EPI == EPI_GATEUP ? FPI8_ERR_ARGUMENT : rows_bt<EPI, 1>(bt, a, chunks, s);
+    case 2: return rows_bt<EPI, 2>(bt, a, chunks, s);
+    case 4: return rows_bt<EPI, 4>(bt, a, chunks, s);
+  }
+  return FPI8_ERR_ARGUMENT;
+}
+
 int launch_rows(int epi, int mt, int bt, const RowsArgs &a, uint32_t chunks, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (a.ntiles == 0 || chunks == 0) return 0;
+  if (a.ntiles == 0 || chunks == 0 || a.splits == 0) return 0;
   switch (epi) {
-    case EPI_RAW: return mt == 1 ? rows_bt<EPI_RAW, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
-    case EPI_QKV: return mt == 1 ? rows_bt<EPI_QKV, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
-    case EPI_RESID: return mt == 1 ? rows_bt<EPI_RESID, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
-    case EPI_DOWN: return mt == 1 ? rows_bt<EPI_DOWN, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
-    case EPI_CLS: return mt == 1 ? rows_bt<EPI_CLS, 1>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
-    case EPI_GATEUP: return mt == 2 ? rows_bt<EPI_GATEUP, 2>(bt, a, chunks, s) : FPI8_ERR_ARGUMENT;
+    case EPI_RAW: return rows_mt<EPI_RAW>(mt, bt, a, chunks, s);
+    case EPI_QKV: return rows_mt<EPI_QKV>(mt, bt, a, chunks, s);
+    case EPI_RESID: return rows_mt<EPI_RESID>(mt, bt, a, chunks, s);
+    case EPI_DOWN: return rows_mt<EPI_DOWN>(mt, bt, a, chunks, s);
+    case EPI_CLS: return rows_mt<EPI_CLS>(mt, bt, a, chunks, s);
+    case EPI_GATEUP: return rows_mt<EPI_GATEUP>(mt, bt, a, chunks, s);
   }
   return FPI8_ERR_ARGUMENT;
 }
@@ -828,10 +908,16 @@ int launch_sample(const SampleArgs &a, void *stream) {
   return ok(hipGetLastError());
 }
 
+int launch_zero_words(uint32_t *p, uint32_t n, void *stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, p, n);
+  return ok(hipGetLastError());
+}
+
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
                       uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(1), 0, s, oflag);
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(1), 0, s, oflag, 1u);
   hipLaunchKernelGGL(k_digits_raw, dim3((cols + 255) / 256, n_runs), dim3(256), 0, s, x, n_runs,
                      cols, planes, kp, bp, oflag);
   return ok(hipGetLastError());

@@ -150,6 +150,17 @@ def test_small_shapes_greedy(name):
     run_pair(shape, blob, runs, [1, 2, 3, 1, 5])
 
 
+@pytest.mark.parametrize("n_runs", [3, 20, 40, 70])
+def test_split_contraction_whole_pass(n_runs):
+    # dim 1024 and hidden 2816: every matrix's columns are shared by several
+    # workgroups; 20, 40 and 70 runs take the wider tiles.
+    shape = W.SMALL_SHAPES["split"]
+    say(f"split shape, {n_runs} runs")
+    blob = Bl.build_blob(shape, 21)
+    runs = spec(shape, n_runs, [1 + (r % 5) for r in range(n_runs)], [2 + (r % 4) for r in range(n_runs)])
+    run_pair(shape, blob, runs, [2, 3])
+
+
 def test_generic_head_size():
     shape = Shape(120, 200, 2, 6, 3, 300, 24)  # head 20: the generic attention path
     say("generic head size 20")

@@ -95,6 +95,8 @@ SMALL_SHAPES = {
     "ragged": Shape(160, 392, 2, 5, 5, 1000, 48),
     "wide": Shape(256, 704, 2, 4, 4, 2048, 64),
     "h8": Shape(64, 128, 1, 8, 4, 64, 24),
+    # wide enough that the row kernel splits the columns of every matrix
+    "split": Shape(1024, 2816, 2, 8, 4, 700, 24),
 }
 
 
