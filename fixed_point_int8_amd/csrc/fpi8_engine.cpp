@@ -49,8 +49,6 @@ struct fpi8_engine {
   uint32_t *d_oflags = nullptr;
   uint32_t n_oflags = 0;
   int32_t *d_run_err = nullptr;
-  int64_t *d_partials = nullptr;   // split-contraction partial sums
-  uint32_t *d_counters = nullptr;  // split-contraction arrival counters
   // pinned host buffers
   RunDesc *h_runs = nullptr;
   uint8_t *h_headers = nullptr;
@@ -91,38 +89,44 @@ struct TimedLaunch {
   }
 };
 
-uint32_t batch_tiles(uint32_t n_runs) { return n_runs <= 16 ? 1 : n_runs <= 32 ? 2 : 4; }
 
-// Launch shape of one row-kernel call: rows per tile (16 * mt), runs per
-// tile (16 * bt), and how many workgroups share a tile's contraction.
+// Launch shape of one row-kernel call: rows per wave 16 * mt, runs per
+// workgroup 16 * bt, nw waves per workgroup.
 struct RowPlan {
-  int mt, bt;
-  uint32_t chunks, tiles, splits;
+  int mt, bt, nw;
+  uint32_t chunks, tiles;
 };
 
-constexpr uint32_t kMaxSplitGroups = 1024;  // tiles * chunks * splits when splits > 1
-constexpr uint64_t kPartialValues = 64;     // i64 per lane at most (mt * bt * 4)
-
-// More runs per tile need more rows per tile, so that the byte digits of
-// the inputs (3 bytes per run and column) are read from L2 no more than
-// about three times per weight byte; then the columns are split until the
-// launch has enough workgroups for every compute unit.
+// Picks the shape with the least estimated time.  A launch reads every
+// weight byte once from HBM, and from L2 once per extra batch chunk; every
+// workgroup reads its runs' digits (3 bytes per run and column) from L2.
+// Fewer than four waves per compute unit leave bandwidth unused.
 RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup) {
-  RowPlan p;
-  p.bt = (int)batch_tiles(n_runs);
-  p.chunks = (n_runs + 16 * p.bt - 1) / (16 * p.bt);
-  p.mt = p.bt == 4 ? 4 : p.bt == 2 ? 2 : (gateup ? 2 : 1);
-  const uint32_t per_tile = gateup ? 16 * (p.mt / 2) : 16 * p.mt;
-  p.tiles = (rows + per_tile - 1) / per_tile;
-  const uint32_t kblocks = (cols + 63) / 64;
-  p.splits = 1;
-  while (p.tiles * p.chunks * p.splits < 512 && kblocks / (p.splits * 2) >= 8 &&
-         p.tiles * p.chunks * p.splits * 2 <= kMaxSplitGroups)
-    p.splits *= 2;
-  return p;
+  static const int plain[][3] = {{1, 1, 2}, {1, 2, 2}, {1, 1, 4}, {1, 2, 4}, {1, 4, 4}, {2, 2, 4}, {2, 4, 4}};
+  static const int pairs[][3] = {{2, 1, 2}, {2, 2, 2}, {2, 1, 4}, {2, 2, 4}, {2, 4, 4}};
+  const int (*cand)[3] = gateup ? pairs : plain;
+  const int n = gateup ? 5 : 7;
+  const double hbm = 5.5e12, l2 = 25e12, mfma = 1.5e15;
+  const double W = (double)rows * cols * (gateup ? 2 : 1);
+  RowPlan best{1, 1, 1, 1, 1};
+  double best_t = 1e30;
+  for (int i = 0; i < n; i++) {
+    RowPlan p{cand[i][0], cand[i][1], cand[i][2], 0, 0};
+    const uint32_t bc = 16 * p.bt;
+    p.chunks = (n_runs + bc - 1) / bc;
+    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * p.nw;
+    p.tiles = (rows + per_tile - 1) / per_tile;
+    const double wgs = (double)p.tiles * p.chunks;
+    const double t_hbm = W / hbm;
+    const double t_l2 = (W * p.chunks + wgs * 3.0 * bc * cols) / l2;
+    const double t_mfma = W * 3.0 * bc * p.chunks / mfma;
+    double t = std::max(t_hbm, std::max(t_l2, t_mfma));
+    const double waves = wgs * p.nw;
+    if (waves < 1024) t *= 1024 / waves;
+    if (t < best_t * 0.999) { best_t = t; best = p; }
+  }
+  return best;
 }
-
-uint64_t partials_bytes() { return kMaxSplitGroups * 64ull * kPartialValues * 8; }
 
 RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t cols,
                    const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer) {
@@ -163,19 +167,16 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   const bool gateup = epi == EPI_GATEUP;
   uint32_t rows = 0;
   for (uint32_t i = 0; i < a.nseg; i++) rows += a.seg[i].rows;
-  RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup);
-  const uint32_t per_tile = gateup ? 16 * (p.mt / 2) : 16 * p.mt;
+  const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup);
+  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * p.nw;
   a.ntiles = 0;
   for (uint32_t i = 0; i < a.nseg; i++) {
     a.seg[i].tile0 = gateup ? 0 : a.ntiles;
     if (!gateup || i == 0) a.ntiles += (a.seg[i].rows + per_tile - 1) / per_tile;
   }
-  if (p.tiles * p.chunks * p.splits > kMaxSplitGroups) p.splits = 1;
-  a.splits = p.splits;
-  a.partials = e->d_partials;
-  a.counters = e->d_counters;
+  a.chunks = p.chunks;
   TimedLaunch t(e, T_ROWS, s);
-  return launch_rows(epi, p.mt, p.bt, a, p.chunks, s);
+  return launch_rows(epi, p.mt, p.bt, p.nw, a, s);
 }
 
 // One position of every active run.
@@ -266,8 +267,6 @@ void release(fpi8_engine *e) {
   (void)hipFree(e->d_planes1);
   (void)hipFree(e->d_oflags);
   (void)hipFree(e->d_run_err);
-  (void)hipFree(e->d_partials);
-  (void)hipFree(e->d_counters);
   (void)hipHostFree(e->h_runs);
   (void)hipHostFree(e->h_headers);
   (void)hipHostFree(e->h_err);
@@ -322,9 +321,6 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
       (r = hip_ok(hipMalloc(&e->d_planes1, planes))) ||
       (r = hip_ok(hipMalloc(&e->d_oflags, 4ull * e->n_oflags))) ||
       (r = hip_ok(hipMalloc(&e->d_run_err, 4ull * max_runs))) ||
-      (r = hip_ok(hipMalloc(&e->d_partials, partials_bytes()))) ||
-      (r = hip_ok(hipMalloc(&e->d_counters, 4ull * kMaxSplitGroups))) ||
-      (r = hip_ok(hipMemset(e->d_counters, 0, 4ull * kMaxSplitGroups))) ||
       (r = hip_ok(hipHostMalloc(&e->h_runs, sizeof(RunDesc) * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_headers, 128ull * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_err, 4ull * max_runs))) ||
@@ -420,24 +416,11 @@ int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uin
   return 0;
 }
 
-// Workspace of the standalone row: [256 B flag][counters][partials][digits].
-static uint64_t rows_work_layout(uint32_t rows, uint32_t cols, uint32_t batch, uint64_t *off_cnt,
-                                 uint64_t *off_part, uint64_t *off_planes, RowPlan *plan) {
-  const RowPlan p = plan_rows(rows, cols, batch, false);
-  const uint64_t groups = (uint64_t)p.tiles * p.chunks;
-  const uint64_t cnt = (groups * 4 + 255) / 256 * 256;
-  const uint64_t part = p.splits > 1 ? groups * p.splits * 64ull * (p.mt * p.bt * 4) * 8 : 0;
-  const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
-  *off_cnt = 256;
-  *off_part = 256 + cnt;
-  *off_planes = 256 + cnt + (part + 255) / 256 * 256;
-  if (plan) *plan = p;
-  return *off_planes + 3 * bp * kp;
-}
-
+// Workspace of the standalone row: a 256-byte flag word, then the digits.
 uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
-  uint64_t a, b, c;
-  return rows_work_layout(rows, cols, batch, &a, &b, &c, nullptr);
+  (void)rows;
+  const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
+  return 256 + 3 * bp * kp;
 }
 
 int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
@@ -451,16 +434,12 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
     return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   const uint32_t kp = round_up(cols, 64), bp = round_up(batch, 64);
-  uint64_t off_cnt, off_part, off_planes;
-  RowPlan p;
-  rows_work_layout(rows, cols, batch, &off_cnt, &off_part, &off_planes, &p);
   uint8_t *base = reinterpret_cast<uint8_t *>(d_work);
   uint32_t *flag = reinterpret_cast<uint32_t *>(base);
-  int8_t *planes = reinterpret_cast<int8_t *>(base + off_planes);
-  int r = launch_zero_words(reinterpret_cast<uint32_t *>(base + off_cnt), p.tiles * p.chunks, s);
+  int8_t *planes = reinterpret_cast<int8_t *>(base + 256);
+  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
   if (r) return r;
-  r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
-  if (r) return r;
+  const RowPlan p = plan_rows(rows, cols, batch, false);
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
@@ -482,10 +461,8 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   sg.pad = (cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0) ? 1u : 0u;
   a.nseg = 1;
   a.ntiles = p.tiles;
-  a.splits = p.splits;
-  a.partials = reinterpret_cast<int64_t *>(base + off_part);
-  a.counters = reinterpret_cast<uint32_t *>(base + off_cnt);
-  return launch_rows(EPI_RAW, p.mt, p.bt, a, p.chunks, s);
+  a.chunks = p.chunks;
+  return launch_rows(EPI_RAW, p.mt, p.bt, p.nw, a, s);
 }
 
 }  // extern "C"

@@ -94,7 +94,7 @@ struct RowsArgs {
   uint32_t ntiles;          // row tiles (16 * MT rows each) over all segments
   uint32_t cols;            // contraction length
   uint32_t kblocks;         // ceil(cols / 64)
-  const int8_t *planes;     // [3][bp][kp] signed digits of the input
+  const int8_t *planes;     // [3][bp][kp] signed digits of the input, fragment-major
   uint32_t kp;              // plane pitch in bytes (multiple of 64, >= kblocks * 64)
   uint32_t bp;              // planes per limb (multiple of 16)
   uint32_t n_runs;
@@ -114,10 +114,7 @@ struct RowsArgs {
   // standalone matrix rows
   const int64_t *x_raw;     // [n_runs][cols]
   int64_t *y_raw;           // [n_runs][rows]
-  // split contraction
-  uint32_t splits;          // workgroups per row tile, each a share of the columns
-  int64_t *partials;        // [tile * chunks][splits][64 lanes][MT * BT * 4]
-  uint32_t *counters;       // [tile * chunks], zero between launches
+  uint32_t chunks;          // batch chunks of 16 * BT runs
 };
 
 struct NormArgs {
@@ -172,7 +169,7 @@ int launch_begin(const BeginArgs &a, void *stream);
 int launch_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs, void *stream);
 int launch_embed(const EmbedArgs &a, void *stream);
 int launch_norm(const NormArgs &a, void *stream);
-int launch_rows(int epi, int mt, int bt, const RowsArgs &a, uint32_t batch_chunks, void *stream);
+int launch_rows(int epi, int mt, int bt, int nw, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_sample(const SampleArgs &a, void *stream);
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,

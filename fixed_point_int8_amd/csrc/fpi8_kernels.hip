@@ -52,13 +52,24 @@ __device__ __forceinline__ bool digits3(int64_t x, int8_t &d0, int8_t &d1, int8_
   return fits;
 }
 
-__device__ __forceinline__ void put_digits(int8_t *planes, uint64_t limb_pitch, uint64_t at,
-                                           int64_t x, uint32_t *oflag) {
+// Digit planes are stored fragment-major: the 16 bytes a lane of a
+// 16x16x64 MFMA needs are contiguous, and so are the 1 KB fragments of a
+// 64-column block, so the row kernel stages them with whole-line loads.
+// Byte (run b, column k) of a limb plane:
+//   (((b / 16) * (kp / 64) + k / 64) * 64 + ((k % 64) / 16) * 16 + b % 16) * 16 + k % 16
+__device__ __forceinline__ uint64_t digit_at(uint32_t b, uint32_t k, uint32_t kp) {
+  return ((((uint64_t)(b >> 4) * (kp >> 6) + (k >> 6)) * 64 + ((k & 63) >> 4) * 16 + (b & 15)) << 4) +
+         (k & 15);
+}
+
+__device__ __forceinline__ void put_digits(int8_t *planes, uint32_t bp, uint32_t kp, uint32_t b,
+                                           uint32_t k, int64_t x, uint32_t *oflag) {
   int8_t d0, d1, d2;
   if (!digits3(x, d0, d1, d2)) atomicOr(oflag, 1u);
+  const uint64_t limb = (uint64_t)bp * kp, at = digit_at(b, k, kp);
   planes[at] = d0;
-  planes[limb_pitch + at] = d1;
-  planes[2 * limb_pitch + at] = d2;
+  planes[limb + at] = d1;
+  planes[2 * limb + at] = d2;
 }
 
 __device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
@@ -164,22 +175,22 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   uint64_t r = isqrt64(ss / a.dim + 42950u);
   if (r < 1) r = 1;
   const int64_t rms = (int64_t)r;
-  const uint64_t pitch = (uint64_t)a.bp * a.kp;
   for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) {
     const int64_t v = (wmul(x[i], (int64_t)a.w[i]) / rms) >> 8;
     y[i] = v;
-    put_digits(a.planes, pitch, (uint64_t)b * a.kp + i, v, a.oflag);
+    put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
   }
 }
 
 // ---------------------------------------------------------------------------
 // The matrix row on the int8 matrix cores.
 //
-// A workgroup of four waves owns 16*MT rows, BT*16 runs and a share of the
-// contraction (a split); the waves take its 64-column blocks round-robin,
-// prefetching weights a group of blocks ahead, and add their i32 partial
-// sums in LDS.  With several splits the workgroups of a row tile meet
-// through a counter: the last adds the others' i64 partial sums.  MFMA 16x16x64 lanes: lane (i = lane % 16,
+// A workgroup of NW waves owns 16*MT*NW rows (16*MT per wave) and 16*BT
+// runs.  The digit fragments of a chunk of 64-column blocks are staged in
+// LDS once per workgroup (double-buffered, whole-line loads) and shared by
+// all its waves; each wave streams its own weight rows 16 KB ahead in
+// registers and keeps its sums in the matrix-core accumulators, so no
+// reduction across waves or workgroups is needed.  MFMA 16x16x64 lanes: lane (i = lane % 16,
 // g = lane / 16) supplies row i of the weight tile and run i of the digit
 // tile, columns [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of
 // run i.
@@ -202,6 +213,16 @@ __device__ __forceinline__ v4i load_weights(const uint8_t *W, uint32_t row, uint
     w[t >> 2] |= v << (8 * (t & 3));
   }
   r.x = (int)w[0]; r.y = (int)w[1]; r.z = (int)w[2]; r.w = (int)w[3];
+  return r;
+}
+
+// The same 16 bytes when the whole row tile, the block and the matrix
+// alignment are known good: one unconditional vector load.
+__device__ __forceinline__ v4i load_weights_fast(const uint8_t *W, uint32_t row, uint32_t cols,
+                                                 uint32_t k0) {
+  v4i r = *reinterpret_cast<const v4i *>(W + (uint64_t)row * cols + k0);
+  const int flip = (int)0x80808080u;
+  r.x ^= flip; r.y ^= flip; r.z ^= flip; r.w ^= flip;
   return r;
 }
 
@@ -228,18 +249,36 @@ __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase
   atomicMin(&rd.errkey, (layer << 8) | phase);
 }
 
-template <int EPI, int MT, int BT>
-__global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
-  constexpr int NW = 4;                                // waves per workgroup
-  constexpr int D = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);   // blocks per prefetch group
-  constexpr int NACC = MT * 3 * BT;
-  constexpr int HALF = MT / 2;
-  __shared__ int red[NACC * 4][64];
+// Digits of CD 64-column blocks are staged in LDS per chunk (24 or 48 1 KB
+// fragments); weights stream D blocks ahead per wave (16 KB of loads).
+template <int MT, int BT>
+struct RowsGeom {
+  static constexpr int D = 16 / MT;
+  static constexpr int CD = BT == 1 ? 8 : 4;
+  static constexpr int FR = 3 * BT * CD;
+};
+
+template <int EPI, int MT, int BT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
+  constexpr int D = RowsGeom<MT, BT>::D;
+  constexpr int CD = RowsGeom<MT, BT>::CD;
+  constexpr int FR = RowsGeom<MT, BT>::FR;
+  constexpr int NT = NW * 64;
+  constexpr int UPT = FR * 64 / NT;  // 16-byte staging units per thread
+  constexpr int HALF = MT >= 2 ? MT / 2 : 1;
+  static_assert(D % CD == 0, "a weight group holds whole digit chunks");
+  __shared__ v4i stage[2][FR * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const uint32_t split = blockIdx.x % a.splits;
-  const uint32_t tile = blockIdx.x / a.splits;
-  const uint32_t b0 = blockIdx.y * BT * 16;
+
+  // Workgroup -> (row tile, batch chunk).  The batch chunks of one row tile
+  // get workgroup ids 8 apart, which the dispatcher places on one XCD, so
+  // the tile's weight rows come from HBM once and from that XCD's L2 after.
+  const uint32_t nchunk = a.chunks;
+  const uint32_t grp = blockIdx.x / (8 * nchunk), rem = blockIdx.x % (8 * nchunk);
+  const uint32_t chunk = rem / 8, tile = grp * 8 + rem % 8;
+  if (tile >= a.ntiles) return;
+  const uint32_t b0 = chunk * BT * 16;
 
   // Nothing to do for a batch chunk without a run in this phase (the
   // classifier at prompt positions, finished runs).
@@ -252,25 +291,21 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   const uint8_t *Wp[MT];
   const uint32_t *Sp[MT];
   uint32_t rbase[MT], rcount[MT];
-  bool vec[MT];
+  bool clean = true;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
     const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[si];
     Wp[mt] = sg.W;
     Sp[mt] = sg.S;
     rcount[mt] = sg.rows;
-    vec[mt] = sg.pad != 0;
-    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 * HALF + 16 * (mt % HALF)
-                                  : (tile - sg.tile0) * 16 * MT + 16 * mt;
+    rbase[mt] = EPI == EPI_GATEUP ? (tile * NW + wave) * 16 * HALF + 16 * (mt % HALF)
+                                  : ((tile - sg.tile0) * NW + wave) * 16 * MT + 16 * mt;
+    clean = clean && sg.pad != 0 && rbase[mt] + 16 <= rcount[mt];
   }
-  // This workgroup's share of the contraction, in 64-column blocks.
-  const uint32_t kb_lo = (uint32_t)((uint64_t)a.kblocks * split / a.splits);
-  const uint32_t kb_hi = (uint32_t)((uint64_t)a.kblocks * (split + 1) / a.splits);
   const bool exact = a.oflag != nullptr && *a.oflag != 0;
 
   int64_t v[MT][BT][4];
   if (!exact) {
-    for (int i = tid; i < NACC * 4 * 64; i += 256) (&red[0][0])[i] = 0;
     v4i acc[MT][3][BT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -278,77 +313,109 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
       for (int l = 0; l < 3; l++)
 #pragma unroll
         for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
-    const uint64_t limb = (uint64_t)a.bp * a.kp;
-    const int8_t *dig = a.planes + (uint64_t)(b0 + li) * a.kp + lg * 16;
-    // Blocks kb_lo + wave + NW * n, n = 0 .. nkb - 1, prefetched D at a time
-    // into two register buffers so the weight stream keeps many loads in
-    // flight while the matrix cores work on the previous group.
-    const uint32_t first = kb_lo + wave;
-    const uint32_t nkb = kb_hi > first ? (kb_hi - first + NW - 1) / NW : 0;
-    const uint32_t G = (nkb + D - 1) / D;
-    v4i A0[D][MT], A1[D][MT];
-    auto load_group = [&](v4i (&A)[D][MT], uint32_t g) {
+    const uint32_t nkb = a.kblocks, nch = (nkb + CD - 1) / CD, ng = (nkb + D - 1) / D;
+    const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+    const int8_t *planes = a.planes;
+    // Runs of this workgroup that exist: digit bytes of the others are
+    // never read back into a result, so they are not fetched.
+    const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
+
+    // A chunk's digit fragments (l, bt, c), fragment-major in memory, into
+    // registers and then into LDS in the same order.
+    auto stage_load = [&](uint32_t ch, v4i (&sr)[UPT]) {
 #pragma unroll
-      for (int d = 0; d < D; d++) {
-        const uint32_t n = g * D + d;
-        const uint32_t k0 = (first + NW * n) * 64 + lg * 16;
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-          A[d][mt] = n < nkb ? load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, k0, vec[mt])
-                             : v4i{0, 0, 0, 0};
+      for (int i = 0; i < UPT; i++) {
+        const uint32_t u = tid + NT * i, f = u >> 6, l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
+        const uint32_t kb = ch * CD + c;
+        const uint64_t at = ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + (kb < nkb ? kb : 0)) * 64 + (u & 63)) * 16;
+        if (bt * 16 + (u & 15) < live) sr[i] = *reinterpret_cast<const v4i *>(planes + at);
       }
     };
-    auto compute_group = [&](v4i (&A)[D][MT], uint32_t g) {
+    auto stage_store = [&](uint32_t buf, v4i (&sr)[UPT]) {
+#pragma unroll
+      for (int i = 0; i < UPT; i++) stage[buf][tid + NT * i] = sr[i];
+    };
+    // A group of D weight blocks of a clean tile: plain vector loads (raw
+    // bytes; the top bit is flipped at use).
+    auto a_load = [&](uint32_t g, v4i (&A)[D][MT]) {
+      if (!clean) return;
 #pragma unroll
       for (int d = 0; d < D; d++) {
-        const uint32_t n = g * D + d;
-        if (n < nkb) {
-          const uint64_t k0 = (uint64_t)(first + NW * n) * 64;
+        const uint32_t kb = g * D + d;
+        const uint32_t k0 = (kb < nkb ? kb : 0) * 64 + lg * 16;
 #pragma unroll
-          for (int l = 0; l < 3; l++)
+        for (int mt = 0; mt < MT; mt++)
+          A[d][mt] = *reinterpret_cast<const v4i *>(Wp[mt] + (uint64_t)(rbase[mt] + li) * a.cols + k0);
+      }
+    };
+    v4i sr[UPT];
 #pragma unroll
-            for (int bt = 0; bt < BT; bt++) {
-              const v4i Bv = *reinterpret_cast<const v4i *>(dig + l * limb + (uint64_t)bt * 16 * a.kp + k0);
+    for (int i = 0; i < UPT; i++) sr[i] = v4i{0, 0, 0, 0};
+    // One weight group: its D / CD digit chunks in turn, each computed from
+    // LDS while the next chunk is fetched; the next weight group's loads are
+    // already in flight.
+    auto group = [&](uint32_t g, v4i (&A)[D][MT]) {
+      const int flip = (int)0x80808080u;
 #pragma unroll
-              for (int mt = 0; mt < MT; mt++)
-                acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d][mt], Bv, acc[mt][l][bt], 0, 0, 0);
+      for (int sub = 0; sub < D / CD; sub++) {
+        const uint32_t ch = g * (D / CD) + sub;
+        if (ch < nch) {
+          if (ch + 1 < nch) stage_load(ch + 1, sr);
+          const uint32_t buf = ch & 1;
+#pragma unroll
+          for (int c = 0; c < CD; c++) {
+            const uint32_t kb = ch * CD + c;
+            if (kb < nkb) {
+              v4i w[MT];
+#pragma unroll
+              for (int mt = 0; mt < MT; mt++) {
+                if (clean) {
+                  w[mt] = A[sub * CD + c][mt];
+                  w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+                } else {
+                  w[mt] = load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, kb * 64 + lg * 16, false);
+                }
+              }
+#pragma unroll
+              for (int l = 0; l < 3; l++)
+#pragma unroll
+                for (int bt = 0; bt < BT; bt++) {
+                  const v4i Bv = stage[buf][((l * BT + bt) * CD + c) * 64 + lane];
+#pragma unroll
+                  for (int mt = 0; mt < MT; mt++)
+                    acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Bv, acc[mt][l][bt], 0, 0, 0);
+                }
             }
+          }
+          if (ch + 1 < nch) stage_store(buf ^ 1, sr);
+          __syncthreads();
         }
       }
     };
-    if (G > 0) load_group(A0, 0);
-    for (uint32_t g = 0; g < G; g += 2) {
-      if (g + 1 < G) load_group(A1, g + 1);
-      compute_group(A0, g);
-      if (g + 2 < G) load_group(A0, g + 2);
-      if (g + 1 < G) compute_group(A1, g + 1);
+
+    v4i A0[D][MT], A1[D][MT];
+    stage_load(0, sr);
+    a_load(0, A0);
+    stage_store(0, sr);
+    __syncthreads();
+    for (uint32_t g = 0; g < ng; g += 2) {
+      if (g + 1 < ng) a_load(g + 1, A1);
+      group(g, A0);
+      if (g + 1 < ng) {
+        if (g + 2 < ng) a_load(g + 2, A0);
+        group(g + 1, A1);
+      }
     }
-    __syncthreads();
-    // The four waves' i32 partial sums, added in LDS (exact and order-free).
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int l = 0; l < 3; l++)
-#pragma unroll
-        for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-          for (int j = 0; j < 4; j++) atomicAdd(&red[((mt * 3 + l) * BT + bt) * 4 + j][lane], acc[mt][l][bt][j]);
-    __syncthreads();
-    if (wave != 0) return;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int bt = 0; bt < BT; bt++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          v[mt][bt][j] = (int64_t)red[((mt * 3 + 0) * BT + bt) * 4 + j][lane] +
-                         ((int64_t)red[((mt * 3 + 1) * BT + bt) * 4 + j][lane] << 8) +
-                         ((int64_t)red[((mt * 3 + 2) * BT + bt) * 4 + j][lane] << 16);
+          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
+                         ((int64_t)acc[mt][2][bt][j] << 16);
   } else {
-    // Exact 64-bit path over this workgroup's columns:
-    // sum_c (b_c - 128) * x_c with wrapping products.
-    if (wave != 0) return;
-    const uint32_t c_lo = kb_lo * 64, c_hi = min(kb_hi * 64, a.cols);
+    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products.
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -362,47 +429,15 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
           int64_t s = 0;
           if (ok && row < rcount[mt]) {
             const uint8_t *w = Wp[mt] + (uint64_t)row * a.cols;
-            for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+            for (uint32_t k = 0; k < a.cols; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
           }
           v[mt][bt][j] = s;
         }
       }
   }
 
-  // Split contraction: every workgroup of a tile leaves its partial sums;
-  // the last one to arrive adds them all (wrapping, order-free) and runs the
-  // epilogue.
-  if (a.splits > 1) {
-    constexpr int PV = MT * BT * 4;
-    const uint32_t ctr = tile * gridDim.y + blockIdx.y;
-    int64_t *mine = a.partials + (((uint64_t)ctr * a.splits + split) * 64 + lane) * PV;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) mine[(mt * BT + bt) * 4 + j] = v[mt][bt][j];
-    __threadfence();
-    uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(&a.counters[ctr], 1u);
-    prev = __shfl(prev, 0, 64);
-    if (prev != a.splits - 1) return;
-    __threadfence();
-    for (uint32_t s = 0; s < a.splits; s++) {
-      if (s == split) continue;
-      const int64_t *other = a.partials + (((uint64_t)ctr * a.splits + s) * 64 + lane) * PV;
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-            v[mt][bt][j] = wadd(v[mt][bt][j], __builtin_nontemporal_load(&other[(mt * BT + bt) * 4 + j]));
-    }
-    if (lane == 0) atomicExch(&a.counters[ctr], 0u);
-  }
-
-  // Epilogue (wave 0): y = (v * scale) >> 24, then the phase's own work.
+  // Epilogue (each wave, its own rows): y = (v * scale) >> 24, then the
+  // phase's own work.
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
@@ -448,7 +483,6 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
         // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
         int64_t *gate = reinterpret_cast<int64_t *>(st + rd.off_gate);
         int64_t *up = reinterpret_cast<int64_t *>(st + rd.off_up);
-        const uint64_t pitch = (uint64_t)a.bp * a.kp_out;
         const int64_t lim = (int64_t)16 << 16;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -459,7 +493,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
           const int64_t h = wmul(sg, u) >> 16;
           gate[row] = h;
           up[row] = u;
-          put_digits(a.planes_out, pitch, (uint64_t)b * a.kp_out + row, h, a.oflag_out);
+          put_digits(a.planes_out, a.bp, a.kp_out, b, row, h, a.oflag_out);
         }
       } else if (EPI == EPI_QKV) {
         const uint32_t role = a.seg[si].role;
@@ -521,7 +555,7 @@ __global__ void k_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, i
   const uint32_t b = blockIdx.y;
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= n_runs || i >= cols) return;
-  put_digits(planes, (uint64_t)bp * kp, (uint64_t)b * kp + i, x[(uint64_t)b * cols + i], oflag);
+  put_digits(planes, bp, kp, b, i, x[(uint64_t)b * cols + i], oflag);
 }
 
 // ---------------------------------------------------------------------------
@@ -628,7 +662,6 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   // Stage 3, weighted values: o_i = (sum_j p_j * V_j,i) >> 24.
   int64_t *w3 = reinterpret_cast<int64_t *>(st + rd.off_w3) + (uint64_t)h * hs;
-  const uint64_t pitch = (uint64_t)a.bp * a.kp;
   if constexpr (HS != 0 && HS % 4 == 0) {
     constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
     constexpr int CPL = (NCH + 15) / 16;
@@ -665,7 +698,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       for (int g = 0; g < 16; g++) o = wadd(o, red[g * HS + e]);
       o >>= 24;
       w3[e] = o;
-      put_digits(a.planes, pitch, (uint64_t)b * a.kp + (uint64_t)h * HS + e, o, a.oflag);
+      put_digits(a.planes, a.bp, a.kp, b, h * HS + e, o, a.oflag);
     }
   } else {
     const uint32_t groups = blockDim.x / hs;  // hs <= 256
@@ -680,7 +713,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       for (uint32_t gg = 0; gg < groups; gg++) o = wadd(o, red[gg * hs + tid]);
       o >>= 24;
       w3[tid] = o;
-      put_digits(a.planes, pitch, (uint64_t)b * a.kp + (uint64_t)h * hs + tid, o, a.oflag);
+      put_digits(a.planes, a.bp, a.kp, b, h * hs + tid, o, a.oflag);
     }
   }
 }
@@ -827,38 +860,51 @@ int launch_norm(const NormArgs &a, void *stream) {
   return ok(hipGetLastError());
 }
 
-template <int EPI, int MT>
-static int rows_bt(int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
-  const dim3 grid(a.ntiles * a.splits, chunks), block(256);
-  switch (bt) {
-    case 1: hipLaunchKernelGGL((k_rows<EPI, MT, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_rows<EPI, MT, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_rows<EPI, MT, 4>), grid, block, 0, s, a); break;
-    default: return FPI8_ERR_ARGUMENT;
-  }
+// The launch shapes the planner may pick: rows per wave 16 * MT, runs per
+// workgroup 16 * BT, NW waves per workgroup.
+template <int EPI, int MT, int BT, int NW>
+static int rows_launch(const RowsArgs &a, hipStream_t s) {
+  const uint32_t groups = (a.ntiles + 7) / 8;
+  const dim3 grid(groups * 8 * a.chunks), block(NW * 64);
+  hipLaunchKernelGGL((k_rows<EPI, MT, BT, NW>), grid, block, 0, s, a);
   return ok(hipGetLastError());
 }
 
 template <int EPI>
-static int rows_mt(int mt, int bt, const RowsArgs &a, uint32_t chunks, hipStream_t s) {
-  switch (mt) {
-    case 1: return EPI == EPI_GATEUP ? FPI8_ERR_ARGUMENT : rows_bt<EPI, 1>(bt, a, chunks, s);
-    case 2: return rows_bt<EPI, 2>(bt, a, chunks, s);
-    case 4: return rows_bt<EPI, 4>(bt, a, chunks, s);
+static int rows_shape(int mt, int bt, int nw, const RowsArgs &a, hipStream_t s) {
+  const int key = mt * 100 + bt * 10 + nw;
+  if constexpr (EPI != EPI_GATEUP) {
+    switch (key) {
+      case 112: return rows_launch<EPI, 1, 1, 2>(a, s);
+      case 122: return rows_launch<EPI, 1, 2, 2>(a, s);
+      case 114: return rows_launch<EPI, 1, 1, 4>(a, s);
+      case 124: return rows_launch<EPI, 1, 2, 4>(a, s);
+      case 144: return rows_launch<EPI, 1, 4, 4>(a, s);
+      case 224: return rows_launch<EPI, 2, 2, 4>(a, s);
+      case 244: return rows_launch<EPI, 2, 4, 4>(a, s);
+    }
+  } else {
+    switch (key) {
+      case 212: return rows_launch<EPI, 2, 1, 2>(a, s);
+      case 222: return rows_launch<EPI, 2, 2, 2>(a, s);
+      case 214: return rows_launch<EPI, 2, 1, 4>(a, s);
+      case 224: return rows_launch<EPI, 2, 2, 4>(a, s);
+      case 244: return rows_launch<EPI, 2, 4, 4>(a, s);
+    }
   }
   return FPI8_ERR_ARGUMENT;
 }
 
-int launch_rows(int epi, int mt, int bt, const RowsArgs &a, uint32_t chunks, void *stream) {
+int launch_rows(int epi, int mt, int bt, int nw, const RowsArgs &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (a.ntiles == 0 || chunks == 0 || a.splits == 0) return 0;
+  if (a.ntiles == 0 || a.chunks == 0) return 0;
   switch (epi) {
-    case EPI_RAW: return rows_mt<EPI_RAW>(mt, bt, a, chunks, s);
-    case EPI_QKV: return rows_mt<EPI_QKV>(mt, bt, a, chunks, s);
-    case EPI_RESID: return rows_mt<EPI_RESID>(mt, bt, a, chunks, s);
-    case EPI_DOWN: return rows_mt<EPI_DOWN>(mt, bt, a, chunks, s);
-    case EPI_CLS: return rows_mt<EPI_CLS>(mt, bt, a, chunks, s);
-    case EPI_GATEUP: return rows_mt<EPI_GATEUP>(mt, bt, a, chunks, s);
+    case EPI_RAW: return rows_shape<EPI_RAW>(mt, bt, nw, a, s);
+    case EPI_QKV: return rows_shape<EPI_QKV>(mt, bt, nw, a, s);
+    case EPI_RESID: return rows_shape<EPI_RESID>(mt, bt, nw, a, s);
+    case EPI_DOWN: return rows_shape<EPI_DOWN>(mt, bt, nw, a, s);
+    case EPI_CLS: return rows_shape<EPI_CLS>(mt, bt, nw, a, s);
+    case EPI_GATEUP: return rows_shape<EPI_GATEUP>(mt, bt, nw, a, s);
   }
   return FPI8_ERR_ARGUMENT;
 }
