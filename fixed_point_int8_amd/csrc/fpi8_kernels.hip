@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/fpi8.h"
 #include "fpi8_internal.h"
 
@@ -596,35 +598,64 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   if constexpr (HS != 0 && HS % 4 == 0) {
     constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
     constexpr int CPL = (NCH + 15) / 16;
+    constexpr int U = 4;  // positions per group in flight
     int64_t qr[CPL][4];
+    bool fits = true;
 #pragma unroll
     for (int t = 0; t < CPL; t++)
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int c = l16 + 16 * t;
         qr[t][u] = c < NCH ? qs[4 * c + u] : 0;
+        fits = fits && qr[t][u] >= INT32_MIN && qr[t][u] <= INT32_MAX;
       }
-    for (uint32_t j = grp; j < npos; j += 16) {
-      const int32_t *kr = K + (uint64_t)j * HS;
-      int64_t dot = 0;
+    // Queries that fit 32 bits (the usual case) multiply as 32 x 32 -> 64.
+    const bool q32 = __syncthreads_and(fits ? 1 : 0) != 0;
+    auto scores = [&](auto narrow) {
+      for (uint32_t j0 = grp; j0 < npos; j0 += 16 * U) {
+        v4i kv[U][CPL];
 #pragma unroll
-      for (int t = 0; t < CPL; t++) {
-        const int c = l16 + 16 * t;
-        if (c < NCH) {
-          const int4 kv = *reinterpret_cast<const int4 *>(kr + 4 * c);
-          dot = wadd(dot, wmul(qr[t][0], kv.x));
-          dot = wadd(dot, wmul(qr[t][1], kv.y));
-          dot = wadd(dot, wmul(qr[t][2], kv.z));
-          dot = wadd(dot, wmul(qr[t][3], kv.w));
+        for (int u = 0; u < U; u++) {
+          const uint32_t j = j0 + 16 * u < npos ? j0 + 16 * u : j0;
+          const int32_t *kr = K + (uint64_t)j * HS;
+#pragma unroll
+          for (int t = 0; t < CPL; t++) {
+            const int c = l16 + 16 * t;
+            if (c < NCH) kv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(kr + 4 * c));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          int64_t dot = 0;
+#pragma unroll
+          for (int t = 0; t < CPL; t++) {
+            const int c = l16 + 16 * t;
+            if (c < NCH) {
+              if constexpr (decltype(narrow)::value) {
+                dot = wadd(dot, (int64_t)(int32_t)qr[t][0] * kv[u][t].x);
+                dot = wadd(dot, (int64_t)(int32_t)qr[t][1] * kv[u][t].y);
+                dot = wadd(dot, (int64_t)(int32_t)qr[t][2] * kv[u][t].z);
+                dot = wadd(dot, (int64_t)(int32_t)qr[t][3] * kv[u][t].w);
+              } else {
+                dot = wadd(dot, wmul(qr[t][0], kv[u][t].x));
+                dot = wadd(dot, wmul(qr[t][1], kv[u][t].y));
+                dot = wadd(dot, wmul(qr[t][2], kv[u][t].z));
+                dot = wadd(dot, wmul(qr[t][3], kv[u][t].w));
+              }
+            }
+          }
+          for (int o = 8; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, 16));
+          const uint32_t j = j0 + 16 * u;
+          if (l16 == 0 && j < npos) {
+            const int64_t s = wmul(dot >> 16, inv) >> 24;
+            sc[j] = s;
+            lmax = s > lmax ? s : lmax;
+          }
         }
       }
-      for (int o = 8; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, 16));
-      if (l16 == 0) {
-        const int64_t s = wmul(dot >> 16, inv) >> 24;
-        sc[j] = s;
-        lmax = s > lmax ? s : lmax;
-      }
-    }
+    };
+    if (q32) scores(std::true_type{});
+    else scores(std::false_type{});
   } else {
     for (uint32_t j = grp; j < npos; j += 16) {
       const int32_t *kr = K + (uint64_t)j * hs;
@@ -665,23 +696,38 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   if constexpr (HS != 0 && HS % 4 == 0) {
     constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
     constexpr int CPL = (NCH + 15) / 16;
+    constexpr int U = 4;  // positions per group in flight
     int64_t acc[CPL][4];
 #pragma unroll
     for (int t = 0; t < CPL; t++)
 #pragma unroll
       for (int u = 0; u < 4; u++) acc[t][u] = 0;
-    for (uint32_t j = grp; j < npos; j += 16) {
-      const int32_t *vr = V + (uint64_t)j * HS;
-      const int32_t p = (int32_t)sc[j];
+    for (uint32_t j0 = grp; j0 < npos; j0 += 16 * U) {
+      v4i vv[U][CPL];
 #pragma unroll
-      for (int t = 0; t < CPL; t++) {
-        const int c = l16 + 16 * t;
-        if (c < NCH) {
-          const int4 vv = *reinterpret_cast<const int4 *>(vr + 4 * c);
-          acc[t][0] = wadd(acc[t][0], (int64_t)p * vv.x);
-          acc[t][1] = wadd(acc[t][1], (int64_t)p * vv.y);
-          acc[t][2] = wadd(acc[t][2], (int64_t)p * vv.z);
-          acc[t][3] = wadd(acc[t][3], (int64_t)p * vv.w);
+      for (int u = 0; u < U; u++) {
+        const uint32_t j = j0 + 16 * u < npos ? j0 + 16 * u : j0;
+        const int32_t *vr = V + (uint64_t)j * HS;
+#pragma unroll
+        for (int t = 0; t < CPL; t++) {
+          const int c = l16 + 16 * t;
+          if (c < NCH) vv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(vr + 4 * c));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t j = j0 + 16 * u;
+        // a position past the end weighs nothing
+        const int32_t p = j < npos ? (int32_t)sc[j] : 0;
+#pragma unroll
+        for (int t = 0; t < CPL; t++) {
+          const int c = l16 + 16 * t;
+          if (c < NCH) {
+            acc[t][0] = wadd(acc[t][0], (int64_t)p * vv[u][t].x);
+            acc[t][1] = wadd(acc[t][1], (int64_t)p * vv[u][t].y);
+            acc[t][2] = wadd(acc[t][2], (int64_t)p * vv[u][t].z);
+            acc[t][3] = wadd(acc[t][3], (int64_t)p * vv[u][t].w);
+          }
         }
       }
     }
