@@ -91,7 +91,7 @@ struct TimedLaunch {
 
 
 // Launch shape of one row-kernel call: rows per wave 16 * mt, runs per
-// workgroup 16 * bt, nw waves per workgroup.
+// workgroup 16 * bt, nw compute waves per workgroup (plus one staging wave).
 struct RowPlan {
   int mt, bt, nw;
   uint32_t chunks, tiles;
@@ -102,10 +102,10 @@ struct RowPlan {
 // workgroup reads its runs' digits (3 bytes per run and column) from L2.
 // Fewer than four waves per compute unit leave bandwidth unused.
 RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup) {
-  static const int plain[][3] = {{1, 1, 2}, {1, 2, 2}, {1, 1, 4}, {1, 2, 4}, {1, 4, 4}, {2, 2, 4}, {2, 4, 4}};
-  static const int pairs[][3] = {{2, 1, 2}, {2, 2, 2}, {2, 1, 4}, {2, 2, 4}, {2, 4, 4}};
+  static const int plain[][3] = {{1, 1, 7}, {1, 2, 7}, {1, 1, 3}, {1, 2, 3}, {1, 4, 3}, {2, 2, 3}, {2, 4, 3}};
+  static const int pairs[][3] = {{2, 1, 7}, {2, 1, 3}, {2, 2, 3}, {2, 4, 3}};
   const int (*cand)[3] = gateup ? pairs : plain;
-  const int n = gateup ? 5 : 7;
+  const int n = gateup ? 4 : 7;
   const double hbm = 5.5e12, l2 = 25e12, mfma = 1.5e15;
   const double W = (double)rows * cols * (gateup ? 2 : 1);
   RowPlan best{1, 1, 1, 1, 1};

@@ -176,9 +176,21 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   ss = block_sum_u64(ss, scratch);
   uint64_t r = isqrt64(ss / a.dim + 42950u);
   if (r < 1) r = 1;
-  const int64_t rms = (int64_t)r;
+  // Truncating division by rms through its 64-bit reciprocal
+  // m = floor(2^64 / rms): q = mulhi(|p|, m) is the quotient or one less,
+  // and one remainder test fixes it (Granlund and Montgomery, "Division by
+  // invariant integers using multiplication", 1994).
+  uint64_t m = ~0ull / r;
+  if (~0ull % r == r - 1) m++;
   for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) {
-    const int64_t v = (wmul(x[i], (int64_t)a.w[i]) / rms) >> 8;
+    const int64_t p = wmul(x[i], (int64_t)a.w[i]);
+    const uint64_t n = p < 0 ? 0ull - (uint64_t)p : (uint64_t)p;
+    uint64_t q = n;
+    if (r > 1) {
+      q = __umul64hi(n, m);
+      if (n - q * r >= r) q++;
+    }
+    const int64_t v = (p < 0 ? (int64_t)(0ull - q) : (int64_t)q) >> 8;
     y[i] = v;
     put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
   }
@@ -187,12 +199,13 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
 // ---------------------------------------------------------------------------
 // The matrix row on the int8 matrix cores.
 //
-// A workgroup of NW waves owns 16*MT*NW rows (16*MT per wave) and 16*BT
-// runs.  The digit fragments of a chunk of 64-column blocks are staged in
-// LDS once per workgroup (double-buffered, whole-line loads) and shared by
-// all its waves; each wave streams its own weight rows 16 KB ahead in
-// registers and keeps its sums in the matrix-core accumulators, so no
-// reduction across waves or workgroups is needed.  MFMA 16x16x64 lanes: lane (i = lane % 16,
+// A workgroup of NW compute waves owns 16*MT*NW rows (16*MT per wave) and
+// 16*BT runs.  One more wave stages the digit fragments of each chunk of
+// 64-column blocks in LDS with direct global-to-LDS loads (double-buffered),
+// shared by all compute waves; each compute wave streams its own weight rows
+// 16 KB ahead in registers, never waiting on the staging loads, and keeps its
+// sums in the matrix-core accumulators, so no reduction across waves or
+// workgroups is needed.  MFMA 16x16x64 lanes: lane (i = lane % 16,
 // g = lane / 16) supplies row i of the weight tile and run i of the digit
 // tile, columns [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of
 // run i.
@@ -252,7 +265,7 @@ __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase
 }
 
 // Digits of CD 64-column blocks are staged in LDS per chunk (24 or 48 1 KB
-// fragments); weights stream D blocks ahead per wave (16 KB of loads).
+// fragments); weights stream D blocks ahead per compute wave (16 KB).
 template <int MT, int BT>
 struct RowsGeom {
   static constexpr int D = 16 / MT;
@@ -260,18 +273,19 @@ struct RowsGeom {
   static constexpr int FR = 3 * BT * CD;
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int EPI, int MT, int BT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
+__global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
   constexpr int D = RowsGeom<MT, BT>::D;
   constexpr int CD = RowsGeom<MT, BT>::CD;
   constexpr int FR = RowsGeom<MT, BT>::FR;
-  constexpr int NT = NW * 64;
-  constexpr int UPT = FR * 64 / NT;  // 16-byte staging units per thread
   constexpr int HALF = MT >= 2 ? MT / 2 : 1;
   static_assert(D % CD == 0, "a weight group holds whole digit chunks");
   __shared__ v4i stage[2][FR * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
+  const bool producer = wave == NW;  // the last wave stages digits; the others compute
 
   // Workgroup -> (row tile, batch chunk).  The batch chunks of one row tile
   // get workgroup ids 8 apart, which the dispatcher places on one XCD, so
@@ -290,6 +304,7 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
   uint32_t si = 0;
   if (EPI != EPI_GATEUP)
     while (si + 1 < a.nseg && tile >= a.seg[si + 1].tile0) ++si;
+  const int cw = producer ? 0 : wave;  // the producer borrows wave 0's rows, never used
   const uint8_t *Wp[MT];
   const uint32_t *Sp[MT];
   uint32_t rbase[MT], rcount[MT];
@@ -300,14 +315,44 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
     Wp[mt] = sg.W;
     Sp[mt] = sg.S;
     rcount[mt] = sg.rows;
-    rbase[mt] = EPI == EPI_GATEUP ? (tile * NW + wave) * 16 * HALF + 16 * (mt % HALF)
-                                  : ((tile - sg.tile0) * NW + wave) * 16 * MT + 16 * mt;
+    rbase[mt] = EPI == EPI_GATEUP ? (tile * NW + cw) * 16 * HALF + 16 * (mt % HALF)
+                                  : ((tile - sg.tile0) * NW + cw) * 16 * MT + 16 * mt;
     clean = clean && sg.pad != 0 && rbase[mt] + 16 <= rcount[mt];
   }
   const bool exact = a.oflag != nullptr && *a.oflag != 0;
 
   int64_t v[MT][BT][4];
   if (!exact) {
+    const uint32_t nkb = a.kblocks, nch = (nkb + CD - 1) / CD, ng = (nkb + D - 1) / D;
+    if (producer) {
+      // The digit fragments (l, bt, c) of each chunk, fragment-major in
+      // memory, straight into LDS (64 lanes x 16 bytes per fragment).  Lanes
+      // of runs that do not exist bring nothing; their columns of the
+      // product are never read back.
+      const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+      const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
+      auto fetch = [&](uint32_t ch) {
+        const uint32_t buf = ch & 1;
+#pragma unroll
+        for (int f = 0; f < FR; f++) {
+          const uint32_t l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
+          const uint32_t kb = ch * CD + c;
+          if (kb < nkb && bt * 16 + li < live) {
+            const int8_t *src = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + kb) * 64 + lane) * 16;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)&stage[buf][f * 64], 16, 0, 0);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+      };
+      fetch(0);
+      __syncthreads();
+      for (uint32_t ch = 0; ch < nch; ch++) {
+        if (ch + 1 < nch) fetch(ch + 1);
+        __syncthreads();
+      }
+      return;
+    }
+
     v4i acc[MT][3][BT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -315,28 +360,7 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
       for (int l = 0; l < 3; l++)
 #pragma unroll
         for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
-    const uint32_t nkb = a.kblocks, nch = (nkb + CD - 1) / CD, ng = (nkb + D - 1) / D;
-    const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
-    const int8_t *planes = a.planes;
-    // Runs of this workgroup that exist: digit bytes of the others are
-    // never read back into a result, so they are not fetched.
-    const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
 
-    // A chunk's digit fragments (l, bt, c), fragment-major in memory, into
-    // registers and then into LDS in the same order.
-    auto stage_load = [&](uint32_t ch, v4i (&sr)[UPT]) {
-#pragma unroll
-      for (int i = 0; i < UPT; i++) {
-        const uint32_t u = tid + NT * i, f = u >> 6, l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
-        const uint32_t kb = ch * CD + c;
-        const uint64_t at = ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + (kb < nkb ? kb : 0)) * 64 + (u & 63)) * 16;
-        if (bt * 16 + (u & 15) < live) sr[i] = *reinterpret_cast<const v4i *>(planes + at);
-      }
-    };
-    auto stage_store = [&](uint32_t buf, v4i (&sr)[UPT]) {
-#pragma unroll
-      for (int i = 0; i < UPT; i++) stage[buf][tid + NT * i] = sr[i];
-    };
     // A group of D weight blocks of a clean tile: plain vector loads (raw
     // bytes; the top bit is flipped at use).
     auto a_load = [&](uint32_t g, v4i (&A)[D][MT]) {
@@ -350,11 +374,8 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
           A[d][mt] = *reinterpret_cast<const v4i *>(Wp[mt] + (uint64_t)(rbase[mt] + li) * a.cols + k0);
       }
     };
-    v4i sr[UPT];
-#pragma unroll
-    for (int i = 0; i < UPT; i++) sr[i] = v4i{0, 0, 0, 0};
-    // One weight group: its D / CD digit chunks in turn, each computed from
-    // LDS while the next chunk is fetched; the next weight group's loads are
+    // One weight group: its D / CD digit chunks in turn, each read from LDS
+    // while the producer stages the next; the next weight group's loads are
     // already in flight.
     auto group = [&](uint32_t g, v4i (&A)[D][MT]) {
       const int flip = (int)0x80808080u;
@@ -362,7 +383,6 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
       for (int sub = 0; sub < D / CD; sub++) {
         const uint32_t ch = g * (D / CD) + sub;
         if (ch < nch) {
-          if (ch + 1 < nch) stage_load(ch + 1, sr);
           const uint32_t buf = ch & 1;
 #pragma unroll
           for (int c = 0; c < CD; c++) {
@@ -389,16 +409,13 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
                 }
             }
           }
-          if (ch + 1 < nch) stage_store(buf ^ 1, sr);
           __syncthreads();
         }
       }
     };
 
     v4i A0[D][MT], A1[D][MT];
-    stage_load(0, sr);
     a_load(0, A0);
-    stage_store(0, sr);
     __syncthreads();
     for (uint32_t g = 0; g < ng; g += 2) {
       if (g + 1 < ng) a_load(g + 1, A1);
@@ -418,6 +435,7 @@ __global__ __launch_bounds__(NW * 64) void k_rows(RowsArgs a) {
                          ((int64_t)acc[mt][2][bt][j] << 16);
   } else {
     // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products.
+    if (producer) return;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -911,7 +929,7 @@ int launch_norm(const NormArgs &a, void *stream) {
 template <int EPI, int MT, int BT, int NW>
 static int rows_launch(const RowsArgs &a, hipStream_t s) {
   const uint32_t groups = (a.ntiles + 7) / 8;
-  const dim3 grid(groups * 8 * a.chunks), block(NW * 64);
+  const dim3 grid(groups * 8 * a.chunks), block((NW + 1) * 64);
   hipLaunchKernelGGL((k_rows<EPI, MT, BT, NW>), grid, block, 0, s, a);
   return ok(hipGetLastError());
 }
@@ -921,21 +939,20 @@ static int rows_shape(int mt, int bt, int nw, const RowsArgs &a, hipStream_t s) 
   const int key = mt * 100 + bt * 10 + nw;
   if constexpr (EPI != EPI_GATEUP) {
     switch (key) {
-      case 112: return rows_launch<EPI, 1, 1, 2>(a, s);
-      case 122: return rows_launch<EPI, 1, 2, 2>(a, s);
-      case 114: return rows_launch<EPI, 1, 1, 4>(a, s);
-      case 124: return rows_launch<EPI, 1, 2, 4>(a, s);
-      case 144: return rows_launch<EPI, 1, 4, 4>(a, s);
-      case 224: return rows_launch<EPI, 2, 2, 4>(a, s);
-      case 244: return rows_launch<EPI, 2, 4, 4>(a, s);
+      case 117: return rows_launch<EPI, 1, 1, 7>(a, s);
+      case 127: return rows_launch<EPI, 1, 2, 7>(a, s);
+      case 113: return rows_launch<EPI, 1, 1, 3>(a, s);
+      case 123: return rows_launch<EPI, 1, 2, 3>(a, s);
+      case 143: return rows_launch<EPI, 1, 4, 3>(a, s);
+      case 223: return rows_launch<EPI, 2, 2, 3>(a, s);
+      case 243: return rows_launch<EPI, 2, 4, 3>(a, s);
     }
   } else {
     switch (key) {
-      case 212: return rows_launch<EPI, 2, 1, 2>(a, s);
-      case 222: return rows_launch<EPI, 2, 2, 2>(a, s);
-      case 214: return rows_launch<EPI, 2, 1, 4>(a, s);
-      case 224: return rows_launch<EPI, 2, 2, 4>(a, s);
-      case 244: return rows_launch<EPI, 2, 4, 4>(a, s);
+      case 217: return rows_launch<EPI, 2, 1, 7>(a, s);
+      case 213: return rows_launch<EPI, 2, 1, 3>(a, s);
+      case 223: return rows_launch<EPI, 2, 2, 3>(a, s);
+      case 243: return rows_launch<EPI, 2, 4, 3>(a, s);
     }
   }
   return FPI8_ERR_ARGUMENT;
