@@ -90,39 +90,44 @@ struct TimedLaunch {
 };
 
 
-// Launch shape of one row-kernel call: rows per wave 16 * mt, runs per
-// workgroup 16 * bt, nw compute waves per workgroup (plus one staging wave).
+// Launch shape of one row-kernel call: 16 * mt rows and 16 * bt runs per
+// workgroup of four waves, which split the contraction.
 struct RowPlan {
-  int mt, bt, nw;
+  int mt, bt;
   uint32_t chunks, tiles;
 };
 
-// Picks the shape with the least estimated time.  A launch reads every
-// weight byte once from HBM, and from L2 once per extra batch chunk; every
-// workgroup reads its runs' digits (3 bytes per run and column) from L2.
-// Fewer than four waves per compute unit leave bandwidth unused.
+// Picks the shape with the least estimated time.  Every workgroup streams
+// its weight rows and its runs' digits (3 bytes per run and column) through
+// L2; the weights come from HBM once, at about 20 GB/s per compute unit, so
+// a launch wants a workgroup on each of the 256 compute units.  The rate at
+// which one compute unit draws a workgroup's bytes depends on the shape
+// (registers left for loads in flight, sums per wave); the figures are
+// measured on MI355X with the 7B-shaped matrices at 64 runs.
 RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup) {
-  static const int plain[][3] = {{1, 1, 7}, {1, 2, 7}, {1, 1, 3}, {1, 2, 3}, {1, 4, 3}, {2, 2, 3}, {2, 4, 3}};
-  static const int pairs[][3] = {{2, 1, 7}, {2, 1, 3}, {2, 2, 3}, {2, 4, 3}};
-  const int (*cand)[3] = gateup ? pairs : plain;
-  const int n = gateup ? 4 : 7;
-  const double hbm = 5.5e12, l2 = 25e12, mfma = 1.5e15;
-  const double W = (double)rows * cols * (gateup ? 2 : 1);
-  RowPlan best{1, 1, 1, 1, 1};
+  struct Cand { int mt, bt; double gbs; };
+  static const Cand plain[] = {{1, 1, 32}, {1, 2, 48}, {1, 4, 53}, {2, 1, 33}, {2, 2, 38},
+                               {2, 4, 42}, {3, 2, 31}, {4, 1, 29}, {4, 2, 29}};
+  static const Cand pairs[] = {{2, 1, 33}, {2, 2, 38}, {2, 4, 42}, {4, 1, 29}, {4, 2, 29}};
+  const Cand *cand = gateup ? pairs : plain;
+  const int n = gateup ? 5 : 9;
+  const double cus = 256, hbm_cu = 20e9;
+  RowPlan best{1, 1, 1, 1};
   double best_t = 1e30;
   for (int i = 0; i < n; i++) {
-    RowPlan p{cand[i][0], cand[i][1], cand[i][2], 0, 0};
+    RowPlan p{cand[i].mt, cand[i].bt, 0, 0};
     const uint32_t bc = 16 * p.bt;
     p.chunks = (n_runs + bc - 1) / bc;
-    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * p.nw;
+    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt);
     p.tiles = (rows + per_tile - 1) / per_tile;
     const double wgs = (double)p.tiles * p.chunks;
-    const double t_hbm = W / hbm;
-    const double t_l2 = (W * p.chunks + wgs * 3.0 * bc * cols) / l2;
-    const double t_mfma = W * 3.0 * bc * p.chunks / mfma;
-    double t = std::max(t_hbm, std::max(t_l2, t_mfma));
-    const double waves = wgs * p.nw;
-    if (waves < 1024) t *= 1024 / waves;
+    const double act = wgs < cus ? wgs : cus;
+    // Each 64-column block costs a wave one 1 KB load per weight tile and
+    // per digit tile, whether or not all its runs exist.
+    const double per_wg = 1024.0 * (p.mt + 3 * p.bt) * ((cols + 63) / 64);
+    const double t_hbm = (double)rows * cols * (gateup ? 2 : 1) / (act * hbm_cu);
+    const double t_l2 = wgs / act * per_wg / (cand[i].gbs * 1e9);
+    const double t = std::max(t_hbm, t_l2);
     if (t < best_t * 0.999) { best_t = t; best = p; }
   }
   return best;
@@ -168,7 +173,7 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   uint32_t rows = 0;
   for (uint32_t i = 0; i < a.nseg; i++) rows += a.seg[i].rows;
   const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup);
-  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * p.nw;
+  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt);
   a.ntiles = 0;
   for (uint32_t i = 0; i < a.nseg; i++) {
     a.seg[i].tile0 = gateup ? 0 : a.ntiles;
@@ -176,7 +181,7 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   }
   a.chunks = p.chunks;
   TimedLaunch t(e, T_ROWS, s);
-  return launch_rows(epi, p.mt, p.bt, p.nw, a, s);
+  return launch_rows(epi, p.mt, p.bt, a, s);
 }
 
 // One position of every active run.
@@ -462,7 +467,7 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   a.nseg = 1;
   a.ntiles = p.tiles;
   a.chunks = p.chunks;
-  return launch_rows(EPI_RAW, p.mt, p.bt, p.nw, a, s);
+  return launch_rows(EPI_RAW, p.mt, p.bt, a, s);
 }
 
 }  // extern "C"

@@ -169,7 +169,7 @@ int launch_begin(const BeginArgs &a, void *stream);
 int launch_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs, void *stream);
 int launch_embed(const EmbedArgs &a, void *stream);
 int launch_norm(const NormArgs &a, void *stream);
-int launch_rows(int epi, int mt, int bt, int nw, const RowsArgs &a, void *stream);
+int launch_rows(int epi, int mt, int bt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_sample(const SampleArgs &a, void *stream);
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,

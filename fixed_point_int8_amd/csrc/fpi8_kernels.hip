@@ -199,45 +199,31 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
 // ---------------------------------------------------------------------------
 // The matrix row on the int8 matrix cores.
 //
-// A workgroup of NW compute waves owns 16*MT*NW rows (16*MT per wave) and
-// 16*BT runs.  One more wave stages the digit fragments of each chunk of
-// 64-column blocks in LDS with direct global-to-LDS loads (double-buffered),
-// shared by all compute waves; each compute wave streams its own weight rows
-// 16 KB ahead in registers, never waiting on the staging loads, and keeps its
-// sums in the matrix-core accumulators, so no reduction across waves or
-// workgroups is needed.  MFMA 16x16x64 lanes: lane (i = lane % 16,
-// g = lane / 16) supplies row i of the weight tile and run i of the digit
-// tile, columns [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of
-// run i.
+// A workgroup owns 16*MT rows and 16*BT runs; its four waves split the
+// contraction into four contiguous ranges of 64-column blocks.  Each wave
+// streams the weight and digit fragments of its range straight into
+// registers, P blocks ahead, and keeps exact i32 sums per digit in the
+// matrix-core accumulators; at the end the four partial sums meet in LDS and
+// wave 0 runs the epilogue.  No wave waits on another inside the loop, and a
+// row tile of only 16 rows still spreads a small matrix over every compute
+// unit.  MFMA 16x16x64 lanes: lane (i = lane % 16, g = lane / 16) supplies
+// row i of the weight tile and run i of the digit tile, columns
+// [16g, 16g + 16) of the block; it receives rows 4g..4g+3 of run i.
 
-__device__ __forceinline__ v4i load_weights(const uint8_t *W, uint32_t row, uint32_t rows,
-                                            uint32_t cols, uint32_t k0, bool vec) {
-  v4i r = {0, 0, 0, 0};
+// 16 raw weight bytes (weight + 128) of one row; bytes outside the matrix
+// read as 0x80, which is the weight 0.
+__device__ __forceinline__ v4i load_weights_raw(const uint8_t *W, uint32_t row, uint32_t rows,
+                                                uint32_t cols, uint32_t k0, bool vec) {
+  v4i r = {(int)0x80808080u, (int)0x80808080u, (int)0x80808080u, (int)0x80808080u};
   if (row >= rows) return r;
   const uint8_t *p = W + (uint64_t)row * cols + k0;
-  if (vec && k0 + 16 <= cols) {
-    r = *reinterpret_cast<const v4i *>(p);
-    const int flip = (int)0x80808080u;
-    r.x ^= flip; r.y ^= flip; r.z ^= flip; r.w ^= flip;
-    return r;
-  }
-  uint32_t w[4] = {0, 0, 0, 0};
+  if (vec && k0 + 16 <= cols) return *reinterpret_cast<const v4i *>(p);
+  uint32_t w[4] = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
   for (int t = 0; t < 16; t++) {
     const uint32_t k = k0 + t;
-    const uint32_t v = k < cols ? (uint32_t)(p[t] ^ 0x80u) : 0u;
-    w[t >> 2] |= v << (8 * (t & 3));
+    if (k < cols) w[t >> 2] = (w[t >> 2] & ~(0xFFu << (8 * (t & 3)))) | ((uint32_t)p[t] << (8 * (t & 3)));
   }
   r.x = (int)w[0]; r.y = (int)w[1]; r.z = (int)w[2]; r.w = (int)w[3];
-  return r;
-}
-
-// The same 16 bytes when the whole row tile, the block and the matrix
-// alignment are known good: one unconditional vector load.
-__device__ __forceinline__ v4i load_weights_fast(const uint8_t *W, uint32_t row, uint32_t cols,
-                                                 uint32_t k0) {
-  v4i r = *reinterpret_cast<const v4i *>(W + (uint64_t)row * cols + k0);
-  const int flip = (int)0x80808080u;
-  r.x ^= flip; r.y ^= flip; r.z ^= flip; r.w ^= flip;
   return r;
 }
 
@@ -264,28 +250,22 @@ __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase
   atomicMin(&rd.errkey, (layer << 8) | phase);
 }
 
-// Digits of CD 64-column blocks are staged in LDS per chunk (24 or 48 1 KB
-// fragments); weights stream D blocks ahead per compute wave (16 KB).
+// Blocks in flight per wave: the fragments of a block take 4 * (MT + 3 BT)
+// VGPRs, and about 190 of them hold the prefetch ring.
 template <int MT, int BT>
 struct RowsGeom {
-  static constexpr int D = 16 / MT;
-  static constexpr int CD = BT == 1 ? 8 : 4;
-  static constexpr int FR = 3 * BT * CD;
+  static constexpr int FRAG = MT + 3 * BT;
+  static constexpr int P0 = 48 / FRAG;
+  static constexpr int P = P0 < 2 ? 2 : P0 > 12 ? 12 : P0;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int EPI, int MT, int BT, int NW>
-__global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
-  constexpr int D = RowsGeom<MT, BT>::D;
-  constexpr int CD = RowsGeom<MT, BT>::CD;
-  constexpr int FR = RowsGeom<MT, BT>::FR;
+template <int EPI, int MT, int BT>
+__global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
+  constexpr int P = RowsGeom<MT, BT>::P;
   constexpr int HALF = MT >= 2 ? MT / 2 : 1;
-  static_assert(D % CD == 0, "a weight group holds whole digit chunks");
-  __shared__ v4i stage[2][FR * 64];
+  __shared__ int64_t red[3][MT * BT * 4 * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const bool producer = wave == NW;  // the last wave stages digits; the others compute
 
   // Workgroup -> (row tile, batch chunk).  The batch chunks of one row tile
   // get workgroup ids 8 apart, which the dispatcher places on one XCD, so
@@ -296,135 +276,171 @@ __global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
   if (tile >= a.ntiles) return;
   const uint32_t b0 = chunk * BT * 16;
 
-  // Nothing to do for a batch chunk without a run in this phase (the
-  // classifier at prompt positions, finished runs).
-  if (EPI != EPI_RAW && !__syncthreads_or(row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1))) ? 1 : 0))
-    return;
+  // Whether this batch chunk has a run in this phase (the classifier skips
+  // prompt positions and finished runs); read first, tested after the first
+  // loads are on their way.
+  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
 
   uint32_t si = 0;
   if (EPI != EPI_GATEUP)
     while (si + 1 < a.nseg && tile >= a.seg[si + 1].tile0) ++si;
-  const int cw = producer ? 0 : wave;  // the producer borrows wave 0's rows, never used
   const uint8_t *Wp[MT];
   const uint32_t *Sp[MT];
   uint32_t rbase[MT], rcount[MT];
-  bool clean = true;
+  bool vecw[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
     const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[si];
     Wp[mt] = sg.W;
     Sp[mt] = sg.S;
     rcount[mt] = sg.rows;
-    rbase[mt] = EPI == EPI_GATEUP ? (tile * NW + cw) * 16 * HALF + 16 * (mt % HALF)
-                                  : ((tile - sg.tile0) * NW + cw) * 16 * MT + 16 * mt;
-    clean = clean && sg.pad != 0 && rbase[mt] + 16 <= rcount[mt];
+    vecw[mt] = sg.pad != 0;
+    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 * HALF + 16 * (mt % HALF)
+                                  : (tile - sg.tile0) * 16 * MT + 16 * mt;
   }
-  const bool exact = a.oflag != nullptr && *a.oflag != 0;
+  // The scales of the rows this lane finishes, fetched now for the epilogue.
+  uint32_t sc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t row = rbase[mt] + 4 * lg + j;
+      sc[mt][j] = Sp[mt][row < rcount[mt] ? row : rcount[mt] - 1];
+    }
+
+  // This wave's blocks [k_lo, k_lo + n).
+  const uint32_t nkb = a.kblocks, per = (nkb + 3) / 4;
+  const uint32_t k_lo = wave * per < nkb ? wave * per : nkb;
+  const uint32_t n = (k_lo + per < nkb ? k_lo + per : nkb) - k_lo;
+
+  v4i acc[MT][3][BT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
+
+  // Digit fragments (l, bt, kb) are 1 KB apart per block in the
+  // fragment-major planes.  Lanes of runs that do not exist load run 0's
+  // bytes (the same address as a live lane, so no extra traffic), and rows
+  // past the end of a segment re-read its last row: both only fill
+  // product entries that are never stored.  Every load is unconditional,
+  // which keeps the prefetch ring free of branches.
+  const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
+  const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+  const int8_t *dsrc[3][BT];
+#pragma unroll
+  for (int bt = 0; bt < BT; bt++) {
+    const uint32_t ie = bt * 16 + li < live ? li : 0;
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+      dsrc[l][bt] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
+  }
+  const uint8_t *wsrc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    const uint32_t row = rbase[mt] + li < rcount[mt] ? rbase[mt] + li : rcount[mt] - 1;
+    wsrc[mt] = Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
+  }
+
+  v4i Wr[P][MT], Dr[P][3][BT];
+  auto load_digits = [&](int s, uint32_t i) {
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * 1024);
+  };
+  // Block k_lo + i into ring slot s: whole 16-byte pieces of aligned rows.
+  // The scheduling fences keep each slot's loads together and in ring
+  // order, so the oldest slot is always the next one computed.
+  auto load = [&](int s, uint32_t i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Wr[s][mt] = *reinterpret_cast<const v4i *>(wsrc[mt] + (uint64_t)i * 64);
+    load_digits(s, i);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The same with every byte checked against the matrix (bytes outside
+  // it read as the weight 0).
+  auto load_checked = [&](int s, uint32_t i) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+      Wr[s][mt] = load_weights_raw(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, (k_lo + i) * 64 + lg * 16, vecw[mt]);
+    load_digits(s, i);
+  };
+  auto compute = [&](int s) {
+    const int flip = (int)0x80808080u;
+    v4i w[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      w[mt] = Wr[s][mt];
+      w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+    }
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Dr[s][l][bt], acc[mt][l][bt], 0, 0, 0);
+  };
+
+  // Whole 64-column blocks of this wave, then (for the wave that owns it)
+  // the partial block at the end of the rows.
+  const uint32_t nfull = a.cols / 64;
+  const uint32_t n_main = k_lo >= nfull ? 0 : (k_lo + n < nfull ? n : nfull - k_lo);
+  bool fast = true;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) fast = fast && vecw[mt];
+  // The ring's first P blocks go out before anything waits.
+  const uint32_t last = n_main ? n_main - 1 : 0;
+  if (fast && n_main > 0) {
+#pragma unroll
+    for (int s = 0; s < P; s++) load(s, (uint32_t)s < n_main ? (uint32_t)s : last);
+  }
+
+  // The input needs more than three digits somewhere: exact path (a scalar
+  // read, so it does not wait behind the loads above).
+  const bool exact =
+      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
+  if (EPI != EPI_RAW && !__syncthreads_or(busy ? 1 : 0)) return;
 
   int64_t v[MT][BT][4];
   if (!exact) {
-    const uint32_t nkb = a.kblocks, nch = (nkb + CD - 1) / CD, ng = (nkb + D - 1) / D;
-    if (producer) {
-      // The digit fragments (l, bt, c) of each chunk, fragment-major in
-      // memory, straight into LDS (64 lanes x 16 bytes per fragment).  Lanes
-      // of runs that do not exist bring nothing; their columns of the
-      // product are never read back.
-      const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
-      const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
-      auto fetch = [&](uint32_t ch) {
-        const uint32_t buf = ch & 1;
+    if (fast && n_main > 0) {
+      // P blocks in flight; the loop body has no branches, so the compiler
+      // waits only for the slot about to be used.
+      uint32_t i = 0;
+      for (; i + 2 * P <= n_main; i += P) {
 #pragma unroll
-        for (int f = 0; f < FR; f++) {
-          const uint32_t l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
-          const uint32_t kb = ch * CD + c;
-          if (kb < nkb && bt * 16 + li < live) {
-            const int8_t *src = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + kb) * 64 + lane) * 16;
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)&stage[buf][f * 64], 16, 0, 0);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-      };
-      fetch(0);
-      __syncthreads();
-      for (uint32_t ch = 0; ch < nch; ch++) {
-        if (ch + 1 < nch) fetch(ch + 1);
-        __syncthreads();
-      }
-      return;
-    }
-
-    v4i acc[MT][3][BT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int l = 0; l < 3; l++)
-#pragma unroll
-        for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
-
-    // A group of D weight blocks of a clean tile: plain vector loads (raw
-    // bytes; the top bit is flipped at use).
-    auto a_load = [&](uint32_t g, v4i (&A)[D][MT]) {
-      if (!clean) return;
-#pragma unroll
-      for (int d = 0; d < D; d++) {
-        const uint32_t kb = g * D + d;
-        const uint32_t k0 = (kb < nkb ? kb : 0) * 64 + lg * 16;
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-          A[d][mt] = *reinterpret_cast<const v4i *>(Wp[mt] + (uint64_t)(rbase[mt] + li) * a.cols + k0);
-      }
-    };
-    // One weight group: its D / CD digit chunks in turn, each read from LDS
-    // while the producer stages the next; the next weight group's loads are
-    // already in flight.
-    auto group = [&](uint32_t g, v4i (&A)[D][MT]) {
-      const int flip = (int)0x80808080u;
-#pragma unroll
-      for (int sub = 0; sub < D / CD; sub++) {
-        const uint32_t ch = g * (D / CD) + sub;
-        if (ch < nch) {
-          const uint32_t buf = ch & 1;
-#pragma unroll
-          for (int c = 0; c < CD; c++) {
-            const uint32_t kb = ch * CD + c;
-            if (kb < nkb) {
-              v4i w[MT];
-#pragma unroll
-              for (int mt = 0; mt < MT; mt++) {
-                if (clean) {
-                  w[mt] = A[sub * CD + c][mt];
-                  w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
-                } else {
-                  w[mt] = load_weights(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, kb * 64 + lg * 16, false);
-                }
-              }
-#pragma unroll
-              for (int l = 0; l < 3; l++)
-#pragma unroll
-                for (int bt = 0; bt < BT; bt++) {
-                  const v4i Bv = stage[buf][((l * BT + bt) * CD + c) * 64 + lane];
-#pragma unroll
-                  for (int mt = 0; mt < MT; mt++)
-                    acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Bv, acc[mt][l][bt], 0, 0, 0);
-                }
-            }
-          }
-          __syncthreads();
+        for (int s = 0; s < P; s++) {
+          compute(s);
+          load(s, i + s + P);
         }
       }
-    };
-
-    v4i A0[D][MT], A1[D][MT];
-    a_load(0, A0);
-    __syncthreads();
-    for (uint32_t g = 0; g < ng; g += 2) {
-      if (g + 1 < ng) a_load(g + 1, A1);
-      group(g, A0);
-      if (g + 1 < ng) {
-        if (g + 2 < ng) a_load(g + 2, A0);
-        group(g + 1, A1);
+#pragma unroll
+      for (int s = 0; s < P; s++) {
+        if (i + s < n_main) compute(s);
+        const uint32_t nx = i + s + P;
+        load(s, nx < n_main ? nx : last);
+      }
+      i += P;
+#pragma unroll
+      for (int s = 0; s < P; s++)
+        if (i + s < n_main) compute(s);
+    } else {
+      for (uint32_t i = 0; i < n_main; i++) {
+        load_checked(0, i);
+        compute(0);
       }
     }
+    if (nfull < nkb && k_lo <= nfull && nfull < k_lo + n) {
+      load_checked(0, nfull - k_lo);
+      compute(0);
+    }
+
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -434,8 +450,9 @@ __global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
           v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
                          ((int64_t)acc[mt][2][bt][j] << 16);
   } else {
-    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products.
-    if (producer) return;
+    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products,
+    // over this wave's columns.
+    const uint32_t c_lo = k_lo * 64, c_hi = (k_lo + n) * 64 < a.cols ? (k_lo + n) * 64 : a.cols;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -449,14 +466,34 @@ __global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
           int64_t s = 0;
           if (ok && row < rcount[mt]) {
             const uint8_t *w = Wp[mt] + (uint64_t)row * a.cols;
-            for (uint32_t k = 0; k < a.cols; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+            for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
           }
           v[mt][bt][j] = s;
         }
       }
   }
 
-  // Epilogue (each wave, its own rows): y = (v * scale) >> 24, then the
+  // The four waves' sums meet in wave 0 (wrapping adds).
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) red[wave - 1][((mt * BT + bt) * 4 + j) * 64 + lane] = v[mt][bt][j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; w++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) v[mt][bt][j] = wadd(v[mt][bt][j], red[w][((mt * BT + bt) * 4 + j) * 64 + lane]);
+
+  // Epilogue (wave 0): y = (v * scale) >> 24, then the
   // phase's own work.
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
@@ -468,7 +505,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void k_rows(RowsArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const uint32_t row = rbase[mt] + 4 * lg + j;
-        y[mt][j] = row < rcount[mt] ? wmul(v[mt][bt][j], (int64_t)(uint64_t)Sp[mt][row]) >> 24 : 0;
+        y[mt][j] = row < rcount[mt] ? wmul(v[mt][bt][j], (int64_t)(uint64_t)sc[mt][j]) >> 24 : 0;
       }
     if (EPI == EPI_RAW) {
 #pragma unroll
@@ -924,50 +961,53 @@ int launch_norm(const NormArgs &a, void *stream) {
   return ok(hipGetLastError());
 }
 
-// The launch shapes the planner may pick: rows per wave 16 * MT, runs per
-// workgroup 16 * BT, NW waves per workgroup.
-template <int EPI, int MT, int BT, int NW>
+// The launch shapes the planner may pick: 16 * MT rows and 16 * BT runs per
+// workgroup of four waves.
+template <int EPI, int MT, int BT>
 static int rows_launch(const RowsArgs &a, hipStream_t s) {
   const uint32_t groups = (a.ntiles + 7) / 8;
-  const dim3 grid(groups * 8 * a.chunks), block((NW + 1) * 64);
-  hipLaunchKernelGGL((k_rows<EPI, MT, BT, NW>), grid, block, 0, s, a);
+  const dim3 grid(groups * 8 * a.chunks), block(256);
+  hipLaunchKernelGGL((k_rows<EPI, MT, BT>), grid, block, 0, s, a);
   return ok(hipGetLastError());
 }
 
 template <int EPI>
-static int rows_shape(int mt, int bt, int nw, const RowsArgs &a, hipStream_t s) {
-  const int key = mt * 100 + bt * 10 + nw;
+static int rows_shape(int mt, int bt, const RowsArgs &a, hipStream_t s) {
+  const int key = mt * 10 + bt;
   if constexpr (EPI != EPI_GATEUP) {
     switch (key) {
-      case 117: return rows_launch<EPI, 1, 1, 7>(a, s);
-      case 127: return rows_launch<EPI, 1, 2, 7>(a, s);
-      case 113: return rows_launch<EPI, 1, 1, 3>(a, s);
-      case 123: return rows_launch<EPI, 1, 2, 3>(a, s);
-      case 143: return rows_launch<EPI, 1, 4, 3>(a, s);
-      case 223: return rows_launch<EPI, 2, 2, 3>(a, s);
-      case 243: return rows_launch<EPI, 2, 4, 3>(a, s);
+      case 11: return rows_launch<EPI, 1, 1>(a, s);
+      case 12: return rows_launch<EPI, 1, 2>(a, s);
+      case 14: return rows_launch<EPI, 1, 4>(a, s);
+      case 21: return rows_launch<EPI, 2, 1>(a, s);
+      case 22: return rows_launch<EPI, 2, 2>(a, s);
+      case 24: return rows_launch<EPI, 2, 4>(a, s);
+      case 32: return rows_launch<EPI, 3, 2>(a, s);
+      case 41: return rows_launch<EPI, 4, 1>(a, s);
+      case 42: return rows_launch<EPI, 4, 2>(a, s);
     }
   } else {
     switch (key) {
-      case 217: return rows_launch<EPI, 2, 1, 7>(a, s);
-      case 213: return rows_launch<EPI, 2, 1, 3>(a, s);
-      case 223: return rows_launch<EPI, 2, 2, 3>(a, s);
-      case 243: return rows_launch<EPI, 2, 4, 3>(a, s);
+      case 21: return rows_launch<EPI, 2, 1>(a, s);
+      case 22: return rows_launch<EPI, 2, 2>(a, s);
+      case 24: return rows_launch<EPI, 2, 4>(a, s);
+      case 41: return rows_launch<EPI, 4, 1>(a, s);
+      case 42: return rows_launch<EPI, 4, 2>(a, s);
     }
   }
   return FPI8_ERR_ARGUMENT;
 }
 
-int launch_rows(int epi, int mt, int bt, int nw, const RowsArgs &a, void *stream) {
+int launch_rows(int epi, int mt, int bt, const RowsArgs &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.ntiles == 0 || a.chunks == 0) return 0;
   switch (epi) {
-    case EPI_RAW: return rows_shape<EPI_RAW>(mt, bt, nw, a, s);
-    case EPI_QKV: return rows_shape<EPI_QKV>(mt, bt, nw, a, s);
-    case EPI_RESID: return rows_shape<EPI_RESID>(mt, bt, nw, a, s);
-    case EPI_DOWN: return rows_shape<EPI_DOWN>(mt, bt, nw, a, s);
-    case EPI_CLS: return rows_shape<EPI_CLS>(mt, bt, nw, a, s);
-    case EPI_GATEUP: return rows_shape<EPI_GATEUP>(mt, bt, nw, a, s);
+    case EPI_RAW: return rows_shape<EPI_RAW>(mt, bt, a, s);
+    case EPI_QKV: return rows_shape<EPI_QKV>(mt, bt, a, s);
+    case EPI_RESID: return rows_shape<EPI_RESID>(mt, bt, a, s);
+    case EPI_DOWN: return rows_shape<EPI_DOWN>(mt, bt, a, s);
+    case EPI_CLS: return rows_shape<EPI_CLS>(mt, bt, a, s);
+    case EPI_GATEUP: return rows_shape<EPI_GATEUP>(mt, bt, a, s);
   }
   return FPI8_ERR_ARGUMENT;
 }
