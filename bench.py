@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--kernel-steps", type=int, default=8,
+                    help="extra steps after the timed ones, with per-launch kernel timing")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--workload", default="7B-shaped-d4096-L32")
@@ -143,8 +145,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = Wl.by_name(args.workload)
     shape = w.shape
-    if args.warmup + args.steps > w.max_tokens - 1:
-        raise SystemExit("warmup + steps exceed the decode positions of the workload")
+    if args.warmup + args.steps + args.kernel_steps > w.max_tokens - 1:
+        raise SystemExit("warmup + steps + kernel steps exceed the decode positions of the workload")
 
     t = time.perf_counter()
     blob = Bl.build_blob(shape, w.blob_seed)
@@ -171,8 +173,7 @@ def main():
     gen0 = sum(batch.info(i)["generated"] for i in range(w.runs))
     pos0 = batch.info(0)["position"]
 
-    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, True)
-    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, True)
+    # The timed steps: nothing but the launches of the path.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e, errs = batch.turn(model, args.steps, stream)
@@ -181,24 +182,37 @@ def main():
     assert e == 0, (e, list(errs))
     gen1 = sum(batch.info(i)["generated"] for i in range(w.runs))
     tokens = gen1 - gen0
+
+    # Kernel times: a few more steps with every row-kernel and attention
+    # launch bracketed by HIP events on its stream.
+    pos1 = batch.info(0)["position"]
+    ks = args.kernel_steps
+    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, True)
+    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, True)
+    torch.cuda.synchronize()
+    tk = time.perf_counter()
+    e, errs = batch.turn(model, ks, stream)
+    torch.cuda.synchronize()
+    dk = time.perf_counter() - tk
+    assert e == 0, (e, list(errs))
     _, rows_ms, rows_n = B.fpi8_engine_timing(model.engine, B.T_ROWS)
     _, attn_ms, attn_n = B.fpi8_engine_timing(model.engine, B.T_ATTN)
     B.fpi8_engine_set_timing(model.engine, B.T_ROWS, False)
     B.fpi8_engine_set_timing(model.engine, B.T_ATTN, False)
 
-    # Algorithmic bytes over the timed steps (positions pos0 .. pos0+steps-1).
-    rows_alg = rows_bytes(shape, w.runs) * args.steps
-    attn_alg = sum(attention_bytes(shape, w.runs, pos0 + k + 1) * shape.layers
-                   for k in range(args.steps))
+    # Algorithmic bytes over the kernel-timed steps (positions pos1 .. pos1+ks-1).
+    rows_alg = rows_bytes(shape, w.runs) * ks
+    attn_alg = sum(attention_bytes(shape, w.runs, pos1 + k + 1) * shape.layers for k in range(ks))
     kern = {
+        "steps": ks, "positions": [pos1, pos1 + ks - 1],
         "rows": {"launches": rows_n, "avg_us": round(rows_ms * 1e3 / max(rows_n, 1), 2),
                  "GB/s": round(rows_alg / (rows_ms * 1e6), 1),
                  "bytes_per_launch": int(rows_alg / max(rows_n, 1))},
         "attention": {"launches": attn_n, "avg_us": round(attn_ms * 1e3 / max(attn_n, 1), 2),
                       "GB/s": round(attn_alg / (attn_ms * 1e6), 1),
                       "bytes_per_launch": int(attn_alg / max(attn_n, 1))},
-        "share_of_step": {"rows": round(rows_ms / (dt * 1e3), 3),
-                          "attention": round(attn_ms / (dt * 1e3), 3)},
+        "share_of_step": {"rows": round(rows_ms / (dk * 1e3), 3),
+                          "attention": round(attn_ms / (dk * 1e3), 3)},
     }
     dom = "attention" if attn_ms > rows_ms else "rows"
     ach = kern[dom]["GB/s"]

@@ -162,9 +162,10 @@ __global__ void k_embed(EmbedArgs a) {
 // Phases 4, 11 (normalization part) and 17: RMS normalization of x into w1,
 // rms = isqrt(sum(x*x) / dim + 42,950) at least 1, y = ((x * w) / rms) >> 8;
 // also writes the digits of w1 for the next matrix.
-__global__ __launch_bounds__(256) void k_norm(NormArgs a) {
+__global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   __shared__ uint64_t scratch[8];
-  const uint32_t b = blockIdx.x;
+  constexpr int U = 8;  // loads in flight per thread
+  const uint32_t b = blockIdx.x, nt = blockDim.x;
   const RunDesc &rd = a.runs[b];
   const uint32_t need = a.final_norm ? RUN_GEN : RUN_ACTIVE;
   if (!(rd.flags & need)) return;
@@ -172,7 +173,16 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
   int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
   uint64_t ss = 0;
-  for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) ss += (uint64_t)wmul(x[i], x[i]);
+  for (uint32_t base = threadIdx.x; base < a.dim; base += nt * U) {
+    int64_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = base + u * nt;
+      v[u] = i < a.dim ? x[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) ss += (uint64_t)wmul(v[u], v[u]);
+  }
   ss = block_sum_u64(ss, scratch);
   uint64_t r = isqrt64(ss / a.dim + 42950u);
   if (r < 1) r = 1;
@@ -182,17 +192,30 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   // invariant integers using multiplication", 1994).
   uint64_t m = ~0ull / r;
   if (~0ull % r == r - 1) m++;
-  for (uint32_t i = threadIdx.x; i < a.dim; i += blockDim.x) {
-    const int64_t p = wmul(x[i], (int64_t)a.w[i]);
-    const uint64_t n = p < 0 ? 0ull - (uint64_t)p : (uint64_t)p;
-    uint64_t q = n;
-    if (r > 1) {
-      q = __umul64hi(n, m);
-      if (n - q * r >= r) q++;
+  for (uint32_t base = threadIdx.x; base < a.dim; base += nt * U) {
+    int64_t xv[U];
+    int32_t wv[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = base + u * nt;
+      xv[u] = i < a.dim ? x[i] : 0;
+      wv[u] = i < a.dim ? a.w[i] : 0;
     }
-    const int64_t v = (p < 0 ? (int64_t)(0ull - q) : (int64_t)q) >> 8;
-    y[i] = v;
-    put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = base + u * nt;
+      if (i >= a.dim) continue;
+      const int64_t p = wmul(xv[u], (int64_t)wv[u]);
+      const uint64_t n = p < 0 ? 0ull - (uint64_t)p : (uint64_t)p;
+      uint64_t q = n;
+      if (r > 1) {
+        q = __umul64hi(n, m);
+        if (n - q * r >= r) q++;
+      }
+      const int64_t v = (p < 0 ? (int64_t)(0ull - q) : (int64_t)q) >> 8;
+      y[i] = v;
+      put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
+    }
   }
 }
 
@@ -957,7 +980,7 @@ int launch_embed(const EmbedArgs &a, void *stream) {
 }
 
 int launch_norm(const NormArgs &a, void *stream) {
-  hipLaunchKernelGGL(k_norm, dim3(a.n_runs), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(k_norm, dim3(a.n_runs), dim3(512), 0, (hipStream_t)stream, a);
   return ok(hipGetLastError());
 }
 
