@@ -54,6 +54,13 @@ struct fpi8_engine {
   uint8_t *h_headers = nullptr;
   int32_t *h_err = nullptr;
   Timer timers[kTimingClasses];
+  // One position's launches recorded as a graph on a stream of the
+  // engine's own (capture runs nothing) and replayed on the caller's
+  // stream; valid for one (state arena, run count).
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t graph = nullptr;
+  uint8_t *graph_states = nullptr;
+  uint32_t graph_runs = 0;
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -265,8 +272,42 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
   return 0;
 }
 
+// Records one position of the launch sequence as a graph (once per state
+// arena and run count).  Every launch of a position reads the run
+// descriptors on the device, so the same graph serves every position.
+int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
+  if (e->graph && e->graph_states == states && e->graph_runs == n_runs) return 0;
+  if (e->graph) {
+    (void)hipGraphExecDestroy(e->graph);
+    e->graph = nullptr;
+  }
+  int r;
+  if (!e->cap_stream && (r = hip_ok(hipStreamCreateWithFlags(&e->cap_stream, hipStreamNonBlocking))))
+    return r;
+  if ((r = hip_ok(hipStreamBeginCapture(e->cap_stream, hipStreamCaptureModeThreadLocal)))) return r;
+  const int rs = step(e, states, n_runs, e->cap_stream);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(e->cap_stream, &g);
+  if (rs) {
+    if (g) (void)hipGraphDestroy(g);
+    return rs;
+  }
+  if ((r = hip_ok(ec))) return r;
+  const hipError_t ei = hipGraphInstantiate(&e->graph, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if ((r = hip_ok(ei))) {
+    e->graph = nullptr;
+    return r;
+  }
+  e->graph_states = states;
+  e->graph_runs = n_runs;
+  return 0;
+}
+
 void release(fpi8_engine *e) {
   if (!e) return;
+  if (e->graph) (void)hipGraphExecDestroy(e->graph);
+  if (e->cap_stream) (void)hipStreamDestroy(e->cap_stream);
   (void)hipFree(e->d_runs);
   (void)hipFree(e->d_planes0);
   (void)hipFree(e->d_planes1);
@@ -385,8 +426,16 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
       (r = hip_ok(hipMemcpyAsync(e->d_run_err, e->h_err, 4ull * n_runs, hipMemcpyHostToDevice, s))))
     return r;
   if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
-  for (uint32_t k = 0; k < steps; k++)
-    if ((r = step(e, d_states, n_runs, s))) return r;
+  bool timing = false;
+  for (const Timer &t : e->timers) timing = timing || t.on;
+  if (steps > 0 && !timing) {
+    if ((r = step_graph(e, d_states, n_runs))) return r;
+    for (uint32_t k = 0; k < steps; k++)
+      if ((r = hip_ok(hipGraphLaunch(e->graph, s)))) return r;
+  } else {
+    for (uint32_t k = 0; k < steps; k++)
+      if ((r = step(e, d_states, n_runs, s))) return r;
+  }
   if ((r = hip_ok(hipMemcpyAsync(e->h_err, e->d_run_err, 4ull * n_runs, hipMemcpyDeviceToHost, s))) ||
       (r = hip_ok(hipStreamSynchronize(s))))
     return r;
