@@ -61,6 +61,7 @@ struct fpi8_engine {
   hipGraphExec_t graph = nullptr;
   uint8_t *graph_states = nullptr;
   uint32_t graph_runs = 0;
+  int row_kind = 0;  // 0 planner's choice, 1 or 2 restrict it (fpi8_engine_set_row_kernel)
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -97,10 +98,12 @@ struct TimedLaunch {
 };
 
 
-// Launch shape of one row-kernel call: 16 * mt rows and 16 * bt runs per
-// workgroup of four waves, which split the contraction.
+// Launch shape of one row-kernel call.  kind 0: 16 * mt rows and 16 * bt
+// runs per workgroup of four waves, which split the contraction; kind 1:
+// 4 * 16 * mt rows (16 * mt per wave) sharing their runs' digits through
+// LDS.
 struct RowPlan {
-  int mt, bt;
+  int kind, mt, bt;
   uint32_t chunks, tiles;
 };
 
@@ -109,29 +112,40 @@ struct RowPlan {
 // L2; the weights come from HBM once, at about 20 GB/s per compute unit, so
 // a launch wants a workgroup on each of the 256 compute units.  The rate at
 // which one compute unit draws a workgroup's bytes depends on the shape
-// (registers left for loads in flight, sums per wave); the figures are
-// measured on MI355X with the 7B-shaped matrices at 64 runs.
-RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup) {
-  struct Cand { int mt, bt; double gbs; };
-  static const Cand plain[] = {{1, 1, 32}, {1, 2, 48}, {1, 4, 53}, {2, 1, 33}, {2, 2, 38},
-                               {2, 4, 42}, {3, 2, 31}, {4, 1, 29}, {4, 2, 29}};
-  static const Cand pairs[] = {{2, 1, 33}, {2, 2, 38}, {2, 4, 42}, {4, 1, 29}, {4, 2, 29}};
+// (registers left for loads in flight, sums per wave, one workgroup's digits
+// serving four waves' rows); the figures are measured on MI355X with the
+// 7B-shaped matrices at 64 runs.  shared_ok: the shared-digit kernel can run
+// (columns a multiple of 128, aligned rows); force 1 or 2 restricts the
+// choice to kind 0 or kind 1.
+RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bool shared_ok,
+                  int force) {
+  struct Cand { int kind, mt, bt; double gbs; };
+  static const Cand plain[] = {{0, 1, 1, 32}, {0, 1, 2, 48}, {0, 1, 4, 53}, {0, 2, 1, 33},
+                               {0, 2, 2, 38}, {0, 2, 4, 42}, {0, 3, 2, 31}, {0, 4, 1, 29},
+                               {0, 4, 2, 29}, {1, 1, 2, 28}, {1, 1, 4, 28}, {1, 2, 2, 28},
+                               {1, 2, 4, 24}};
+  static const Cand pairs[] = {{0, 2, 1, 33}, {0, 2, 2, 38}, {0, 2, 4, 42}, {0, 4, 1, 29},
+                               {0, 4, 2, 29}, {1, 2, 2, 28}, {1, 2, 4, 24}};
   const Cand *cand = gateup ? pairs : plain;
-  const int n = gateup ? 5 : 9;
+  const int n = gateup ? 7 : 13;
   const double cus = 256, hbm_cu = 20e9;
-  RowPlan best{1, 1, 1, 1};
+  RowPlan best{0, 1, 1, 1, 1};
   double best_t = 1e30;
   for (int i = 0; i < n; i++) {
-    RowPlan p{cand[i].mt, cand[i].bt, 0, 0};
+    const int kind = cand[i].kind;
+    if (kind == 1 && !shared_ok) continue;
+    if ((force == 1 && kind != 0) || (force == 2 && shared_ok && kind != 1)) continue;
+    RowPlan p{kind, cand[i].mt, cand[i].bt, 0, 0};
     const uint32_t bc = 16 * p.bt;
     p.chunks = (n_runs + bc - 1) / bc;
-    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt);
+    const uint32_t waves_rows = kind ? 4 : 1;
+    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * waves_rows;
     p.tiles = (rows + per_tile - 1) / per_tile;
     const double wgs = (double)p.tiles * p.chunks;
     const double act = wgs < cus ? wgs : cus;
-    // Each 64-column block costs a wave one 1 KB load per weight tile and
-    // per digit tile, whether or not all its runs exist.
-    const double per_wg = 1024.0 * (p.mt + 3 * p.bt) * ((cols + 63) / 64);
+    // Each 64-column block costs a workgroup one 1 KB load per weight tile
+    // and per digit tile, whether or not all its runs exist.
+    const double per_wg = 1024.0 * (waves_rows * p.mt + 3 * p.bt) * ((cols + 63) / 64);
     const double t_hbm = (double)rows * cols * (gateup ? 2 : 1) / (act * hbm_cu);
     const double t_l2 = wgs / act * per_wg / (cand[i].gbs * 1e9);
     const double t = std::max(t_hbm, t_l2);
@@ -179,8 +193,11 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   const bool gateup = epi == EPI_GATEUP;
   uint32_t rows = 0;
   for (uint32_t i = 0; i < a.nseg; i++) rows += a.seg[i].rows;
-  const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup);
-  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt);
+  bool shared_ok = a.cols % 128 == 0;
+  for (uint32_t i = 0; i < a.nseg; i++) shared_ok = shared_ok && a.seg[i].pad != 0;
+  const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup, shared_ok,
+                              e->row_kind);
+  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * (p.kind ? 4 : 1);
   a.ntiles = 0;
   for (uint32_t i = 0; i < a.nseg; i++) {
     a.seg[i].tile0 = gateup ? 0 : a.ntiles;
@@ -188,7 +205,7 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   }
   a.chunks = p.chunks;
   TimedLaunch t(e, T_ROWS, s);
-  return launch_rows(epi, p.mt, p.bt, a, s);
+  return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
 }
 
 // One position of every active run.
@@ -447,6 +464,16 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
   return first;
 }
 
+int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
+  if (!e || kind < 0 || kind > 2) return FPI8_ERR_ARGUMENT;
+  if (e->row_kind != kind) {
+    e->row_kind = kind;
+    e->graph_states = nullptr;  // record the position again with the new shapes
+    e->graph_runs = 0;
+  }
+  return 0;
+}
+
 int32_t fpi8_engine_set_timing(fpi8_engine *e, int32_t kernel, int32_t enable) {
   if (!e || kernel < 0 || kernel >= kTimingClasses) return FPI8_ERR_ARGUMENT;
   Timer &t = e->timers[kernel];
@@ -493,7 +520,8 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   int8_t *planes = reinterpret_cast<int8_t *>(base + 256);
   int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
   if (r) return r;
-  const RowPlan p = plan_rows(rows, cols, batch, false);
+  const bool aligned = cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0;
+  const RowPlan p = plan_rows(rows, cols, batch, false, aligned && cols % 128 == 0, 0);
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
@@ -516,7 +544,7 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   a.nseg = 1;
   a.ntiles = p.tiles;
   a.chunks = p.chunks;
-  return launch_rows(EPI_RAW, p.mt, p.bt, a, s);
+  return launch_rows(EPI_RAW, p.kind, p.mt, p.bt, a, s);
 }
 
 }  // extern "C"

@@ -169,7 +169,10 @@ int launch_begin(const BeginArgs &a, void *stream);
 int launch_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs, void *stream);
 int launch_embed(const EmbedArgs &a, void *stream);
 int launch_norm(const NormArgs &a, void *stream);
-int launch_rows(int epi, int mt, int bt, const RowsArgs &a, void *stream);
+// kind 0: the four waves of a workgroup split the contraction of 16 * mt
+// rows; kind 1: they own 16 * mt rows each and share the digits through LDS
+// (columns a multiple of 128, 16-byte aligned rows).
+int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_sample(const SampleArgs &a, void *stream);
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,

@@ -273,251 +273,81 @@ __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase
   atomicMin(&rd.errkey, (layer << 8) | phase);
 }
 
-// Blocks in flight per wave: the fragments of a block take 4 * (MT + 3 BT)
-// VGPRs, and about 190 of them hold the prefetch ring.
-template <int MT, int BT>
-struct RowsGeom {
-  static constexpr int FRAG = MT + 3 * BT;
-  static constexpr int P0 = 48 / FRAG;
-  static constexpr int P = P0 < 2 ? 2 : P0 > 12 ? 12 : P0;
-};
-
-template <int EPI, int MT, int BT>
-__global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
-  constexpr int P = RowsGeom<MT, BT>::P;
-  constexpr int HALF = MT >= 2 ? MT / 2 : 1;
-  __shared__ int64_t red[3][MT * BT * 4 * 64];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, lg = lane >> 4;
-
-  // Workgroup -> (row tile, batch chunk).  The batch chunks of one row tile
-  // get workgroup ids 8 apart, which the dispatcher places on one XCD, so
-  // the tile's weight rows come from HBM once and from that XCD's L2 after.
-  const uint32_t nchunk = a.chunks;
-  const uint32_t grp = blockIdx.x / (8 * nchunk), rem = blockIdx.x % (8 * nchunk);
-  const uint32_t chunk = rem / 8, tile = grp * 8 + rem % 8;
-  if (tile >= a.ntiles) return;
-  const uint32_t b0 = chunk * BT * 16;
-
-  // Whether this batch chunk has a run in this phase (the classifier skips
-  // prompt positions and finished runs); read first, tested after the first
-  // loads are on their way.
-  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
-
-  uint32_t si = 0;
-  if (EPI != EPI_GATEUP)
-    while (si + 1 < a.nseg && tile >= a.seg[si + 1].tile0) ++si;
+// The rows one wave finishes: 16 * MT rows in MT tiles of 16, from the
+// segment (matrix) that holds them; for the gate/up pair, HALF tiles of the
+// gate matrix and the same rows of the up matrix.  unit numbers the 16*MT-row
+// units of the launch: a workgroup tile holds `per` of them, and this wave
+// finishes unit tile * per + sub.  The scales of the rows this lane
+// finishes are fetched here, long before the epilogue needs them.
+template <int MT>
+struct RowTile {
+  uint32_t si;
   const uint8_t *Wp[MT];
-  const uint32_t *Sp[MT];
   uint32_t rbase[MT], rcount[MT];
   bool vecw[MT];
+  uint32_t sc[MT][4];
+};
+
+template <int EPI, int MT>
+__device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t tile, uint32_t per,
+                                         uint32_t sub, int lg, RowTile<MT> &t) {
+  constexpr int HALF = MT >= 2 ? MT / 2 : 1;
+  t.si = 0;
+  if (EPI != EPI_GATEUP)
+    while (t.si + 1 < a.nseg && tile >= a.seg[t.si + 1].tile0) ++t.si;
+  const uint32_t unit = tile * per + sub;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
-    const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[si];
-    Wp[mt] = sg.W;
-    Sp[mt] = sg.S;
-    rcount[mt] = sg.rows;
-    vecw[mt] = sg.pad != 0;
-    rbase[mt] = EPI == EPI_GATEUP ? tile * 16 * HALF + 16 * (mt % HALF)
-                                  : (tile - sg.tile0) * 16 * MT + 16 * mt;
-  }
-  // The scales of the rows this lane finishes, fetched now for the epilogue.
-  uint32_t sc[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++)
+    const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[t.si];
+    t.Wp[mt] = sg.W;
+    t.rcount[mt] = sg.rows;
+    t.vecw[mt] = sg.pad != 0;
+    t.rbase[mt] = EPI == EPI_GATEUP ? unit * 16 * HALF + 16 * (mt % HALF)
+                                    : (unit - sg.tile0 * per) * 16 * MT + 16 * mt;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const uint32_t row = rbase[mt] + 4 * lg + j;
-      sc[mt][j] = Sp[mt][row < rcount[mt] ? row : rcount[mt] - 1];
+      const uint32_t row = t.rbase[mt] + 4 * lg + j;
+      t.sc[mt][j] = sg.S[row < t.rcount[mt] ? row : t.rcount[mt] - 1];
     }
+  }
+}
 
-  // This wave's blocks [k_lo, k_lo + n).
-  const uint32_t nkb = a.kblocks, per = (nkb + 3) / 4;
-  const uint32_t k_lo = wave * per < nkb ? wave * per : nkb;
-  const uint32_t n = (k_lo + per < nkb ? k_lo + per : nkb) - k_lo;
-
-  v4i acc[MT][3][BT];
+// Exact 64-bit path: sum_c (b_c - 128) * x_c over columns [c_lo, c_hi) with
+// wrapping products, for the outputs this lane holds.
+template <int EPI, int MT, int BT>
+__device__ __forceinline__ void rows_exact(const RowsArgs &a, const RowTile<MT> &t, uint32_t b0,
+                                           uint32_t c_lo, uint32_t c_hi, int li, int lg,
+                                           int64_t (&v)[MT][BT][4]) {
 #pragma unroll
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-    for (int l = 0; l < 3; l++)
+    for (int bt = 0; bt < BT; bt++) {
+      const uint32_t b = b0 + bt * 16 + li;
+      const bool ok = row_run_ok<EPI>(a, b);
+      const int64_t *x = ok ? row_input<EPI>(a, b) : nullptr;
 #pragma unroll
-      for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
-
-  // Digit fragments (l, bt, kb) are 1 KB apart per block in the
-  // fragment-major planes.  Lanes of runs that do not exist load run 0's
-  // bytes (the same address as a live lane, so no extra traffic), and rows
-  // past the end of a segment re-read its last row: both only fill
-  // product entries that are never stored.  Every load is unconditional,
-  // which keeps the prefetch ring free of branches.
-  const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
-  const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
-  const int8_t *dsrc[3][BT];
-#pragma unroll
-  for (int bt = 0; bt < BT; bt++) {
-    const uint32_t ie = bt * 16 + li < live ? li : 0;
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-      dsrc[l][bt] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
-  }
-  const uint8_t *wsrc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++) {
-    const uint32_t row = rbase[mt] + li < rcount[mt] ? rbase[mt] + li : rcount[mt] - 1;
-    wsrc[mt] = Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
-  }
-
-  v4i Wr[P][MT], Dr[P][3][BT];
-  auto load_digits = [&](int s, uint32_t i) {
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * 1024);
-  };
-  // Block k_lo + i into ring slot s: whole 16-byte pieces of aligned rows.
-  // The scheduling fences keep each slot's loads together and in ring
-  // order, so the oldest slot is always the next one computed.
-  auto load = [&](int s, uint32_t i) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) Wr[s][mt] = *reinterpret_cast<const v4i *>(wsrc[mt] + (uint64_t)i * 64);
-    load_digits(s, i);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // The same with every byte checked against the matrix (bytes outside
-  // it read as the weight 0).
-  auto load_checked = [&](int s, uint32_t i) {
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-      Wr[s][mt] = load_weights_raw(Wp[mt], rbase[mt] + li, rcount[mt], a.cols, (k_lo + i) * 64 + lg * 16, vecw[mt]);
-    load_digits(s, i);
-  };
-  auto compute = [&](int s) {
-    const int flip = (int)0x80808080u;
-    v4i w[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      w[mt] = Wr[s][mt];
-      w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
-    }
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Dr[s][l][bt], acc[mt][l][bt], 0, 0, 0);
-  };
-
-  // Whole 64-column blocks of this wave, then (for the wave that owns it)
-  // the partial block at the end of the rows.
-  const uint32_t nfull = a.cols / 64;
-  const uint32_t n_main = k_lo >= nfull ? 0 : (k_lo + n < nfull ? n : nfull - k_lo);
-  bool fast = true;
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++) fast = fast && vecw[mt];
-  // The ring's first P blocks go out before anything waits.
-  const uint32_t last = n_main ? n_main - 1 : 0;
-  if (fast && n_main > 0) {
-#pragma unroll
-    for (int s = 0; s < P; s++) load(s, (uint32_t)s < n_main ? (uint32_t)s : last);
-  }
-
-  // The input needs more than three digits somewhere: exact path (a scalar
-  // read, so it does not wait behind the loads above).
-  const bool exact =
-      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
-  if (EPI != EPI_RAW && !__syncthreads_or(busy ? 1 : 0)) return;
-
-  int64_t v[MT][BT][4];
-  if (!exact) {
-    if (fast && n_main > 0) {
-      // P blocks in flight; the loop body has no branches, so the compiler
-      // waits only for the slot about to be used.
-      uint32_t i = 0;
-      for (; i + 2 * P <= n_main; i += P) {
-#pragma unroll
-        for (int s = 0; s < P; s++) {
-          compute(s);
-          load(s, i + s + P);
+      for (int j = 0; j < 4; j++) {
+        const uint32_t row = t.rbase[mt] + 4 * lg + j;
+        int64_t s = 0;
+        if (ok && row < t.rcount[mt]) {
+          const uint8_t *w = t.Wp[mt] + (uint64_t)row * a.cols;
+          for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
         }
-      }
-#pragma unroll
-      for (int s = 0; s < P; s++) {
-        if (i + s < n_main) compute(s);
-        const uint32_t nx = i + s + P;
-        load(s, nx < n_main ? nx : last);
-      }
-      i += P;
-#pragma unroll
-      for (int s = 0; s < P; s++)
-        if (i + s < n_main) compute(s);
-    } else {
-      for (uint32_t i = 0; i < n_main; i++) {
-        load_checked(0, i);
-        compute(0);
+        v[mt][bt][j] = s;
       }
     }
-    if (nfull < nkb && k_lo <= nfull && nfull < k_lo + n) {
-      load_checked(0, nfull - k_lo);
-      compute(0);
-    }
+}
 
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
-                         ((int64_t)acc[mt][2][bt][j] << 16);
-  } else {
-    // Exact 64-bit path: sum_c (b_c - 128) * x_c with wrapping products,
-    // over this wave's columns.
-    const uint32_t c_lo = k_lo * 64, c_hi = (k_lo + n) * 64 < a.cols ? (k_lo + n) * 64 : a.cols;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++) {
-        const uint32_t b = b0 + bt * 16 + li;
-        const bool ok = row_run_ok<EPI>(a, b);
-        const int64_t *x = ok ? row_input<EPI>(a, b) : nullptr;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const uint32_t row = rbase[mt] + 4 * lg + j;
-          int64_t s = 0;
-          if (ok && row < rcount[mt]) {
-            const uint8_t *w = Wp[mt] + (uint64_t)row * a.cols;
-            for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
-          }
-          v[mt][bt][j] = s;
-        }
-      }
-  }
-
-  // The four waves' sums meet in wave 0 (wrapping adds).
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) red[wave - 1][((mt * BT + bt) * 4 + j) * 64 + lane] = v[mt][bt][j];
-  }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < 3; w++)
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) v[mt][bt][j] = wadd(v[mt][bt][j], red[w][((mt * BT + bt) * 4 + j) * 64 + lane]);
-
-  // Epilogue (wave 0): y = (v * scale) >> 24, then the
-  // phase's own work.
+// Epilogue of the outputs this lane holds: y = (v * scale) >> 24, then the
+// phase's own work.
+template <int EPI, int MT, int BT>
+__device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<MT> &t, uint32_t b0,
+                                              const int64_t (&v)[MT][BT][4], int li, int lg) {
+  constexpr int HALF = MT >= 2 ? MT / 2 : 1;
+  const uint32_t si = t.si;
+  const auto &rbase = t.rbase;
+  const auto &rcount = t.rcount;
+  const auto &sc = t.sc;
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
@@ -622,6 +452,390 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
       }
     }
   }
+}
+
+// Waits until at most N vector memory operations of this wave are still
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Blocks in flight per wave: the fragments of a block take 4 * (MT + 3 BT)
+// VGPRs, and about 190 of them hold the prefetch ring.
+template <int MT, int BT>
+struct RowsGeom {
+  static constexpr int FRAG = MT + 3 * BT;
+  static constexpr int P0 = 48 / FRAG;
+  static constexpr int P = P0 < 2 ? 2 : P0 > 12 ? 12 : P0;
+};
+
+template <int EPI, int MT, int BT>
+__global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
+  constexpr int P = RowsGeom<MT, BT>::P;
+  __shared__ int64_t red[3][MT * BT * 4 * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+
+  // Workgroup -> (row tile, batch chunk).  The batch chunks of one row tile
+  // get workgroup ids 8 apart, which the dispatcher places on one XCD, so
+  // the tile's weight rows come from HBM once and from that XCD's L2 after.
+  const uint32_t nchunk = a.chunks;
+  const uint32_t grp = blockIdx.x / (8 * nchunk), rem = blockIdx.x % (8 * nchunk);
+  const uint32_t chunk = rem / 8, tile = grp * 8 + rem % 8;
+  if (tile >= a.ntiles) return;
+  const uint32_t b0 = chunk * BT * 16;
+
+  // Whether this batch chunk has a run in this phase (the classifier skips
+  // prompt positions and finished runs); read first, tested after the first
+  // loads are on their way.
+  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
+
+  RowTile<MT> t;
+  row_tile<EPI, MT>(a, tile, 1, 0, lg, t);
+
+  // This wave's blocks [k_lo, k_lo + n).
+  const uint32_t nkb = a.kblocks, per = (nkb + 3) / 4;
+  const uint32_t k_lo = wave * per < nkb ? wave * per : nkb;
+  const uint32_t n = (k_lo + per < nkb ? k_lo + per : nkb) - k_lo;
+
+  v4i acc[MT][3][BT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
+
+  // Digit fragments (l, bt, kb) are 1 KB apart per block in the
+  // fragment-major planes.  Lanes of runs that do not exist load run 0's
+  // bytes (the same address as a live lane, so no extra traffic), and rows
+  // past the end of a segment re-read its last row: both only fill
+  // product entries that are never stored.  Every load is unconditional,
+  // which keeps the prefetch ring free of branches.
+  const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
+  const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+  const int8_t *dsrc[3][BT];
+#pragma unroll
+  for (int bt = 0; bt < BT; bt++) {
+    const uint32_t ie = bt * 16 + li < live ? li : 0;
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+      dsrc[l][bt] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
+  }
+  const uint8_t *wsrc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
+    wsrc[mt] = t.Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
+  }
+
+  v4i Wr[P][MT], Dr[P][3][BT];
+  auto load_digits = [&](int s, uint32_t i) {
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * 1024);
+  };
+  // Block k_lo + i into ring slot s: whole 16-byte pieces of aligned rows.
+  // The scheduling fences keep each slot's loads together and in ring
+  // order, so the oldest slot is always the next one computed.
+  auto load = [&](int s, uint32_t i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Wr[s][mt] = *reinterpret_cast<const v4i *>(wsrc[mt] + (uint64_t)i * 64);
+    load_digits(s, i);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The same with every byte checked against the matrix (bytes outside
+  // it read as the weight 0).
+  auto load_checked = [&](int s, uint32_t i) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+      Wr[s][mt] = load_weights_raw(t.Wp[mt], t.rbase[mt] + li, t.rcount[mt], a.cols, (k_lo + i) * 64 + lg * 16, t.vecw[mt]);
+    load_digits(s, i);
+  };
+  auto compute = [&](int s) {
+    const int flip = (int)0x80808080u;
+    v4i w[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      w[mt] = Wr[s][mt];
+      w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+    }
+#pragma unroll
+    for (int l = 0; l < 3; l++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Dr[s][l][bt], acc[mt][l][bt], 0, 0, 0);
+  };
+
+  // Whole 64-column blocks of this wave, then (for the wave that owns it)
+  // the partial block at the end of the rows.
+  const uint32_t nfull = a.cols / 64;
+  const uint32_t n_main = k_lo >= nfull ? 0 : (k_lo + n < nfull ? n : nfull - k_lo);
+  bool fast = true;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) fast = fast && t.vecw[mt];
+  // The ring's first P blocks go out before anything waits.
+  const uint32_t last = n_main ? n_main - 1 : 0;
+  if (fast && n_main > 0) {
+#pragma unroll
+    for (int s = 0; s < P; s++) load(s, (uint32_t)s < n_main ? (uint32_t)s : last);
+  }
+
+  // The input needs more than three digits somewhere: exact path (a scalar
+  // read, so it does not wait behind the loads above).
+  const bool exact =
+      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
+  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) return;  // every wave sees all runs of the chunk
+
+  int64_t v[MT][BT][4];
+  if (!exact) {
+    if (fast && n_main > 0) {
+      // P blocks in flight; the loop body has no branches, so the compiler
+      // waits only for the slot about to be used.
+      uint32_t i = 0;
+      for (; i + 2 * P <= n_main; i += P) {
+#pragma unroll
+        for (int s = 0; s < P; s++) {
+          compute(s);
+          load(s, i + s + P);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < P; s++) {
+        if (i + s < n_main) compute(s);
+        const uint32_t nx = i + s + P;
+        load(s, nx < n_main ? nx : last);
+      }
+      i += P;
+#pragma unroll
+      for (int s = 0; s < P; s++)
+        if (i + s < n_main) compute(s);
+    } else {
+      for (uint32_t i = 0; i < n_main; i++) {
+        load_checked(0, i);
+        compute(0);
+      }
+    }
+    if (nfull < nkb && k_lo <= nfull && nfull < k_lo + n) {
+      load_checked(0, nfull - k_lo);
+      compute(0);
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
+                         ((int64_t)acc[mt][2][bt][j] << 16);
+  } else {
+    // Exact 64-bit path over this wave's columns.
+    const uint32_t c_lo = k_lo * 64, c_hi = (k_lo + n) * 64 < a.cols ? (k_lo + n) * 64 : a.cols;
+    rows_exact<EPI, MT, BT>(a, t, b0, c_lo, c_hi, li, lg, v);
+  }
+
+  // The four waves' sums meet in wave 0 (wrapping adds).
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) red[wave - 1][((mt * BT + bt) * 4 + j) * 64 + lane] = v[mt][bt][j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; w++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) v[mt][bt][j] = wadd(v[mt][bt][j], red[w][((mt * BT + bt) * 4 + j) * 64 + lane]);
+
+  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg);
+}
+
+// The matrix row with the digits shared through LDS.  A workgroup of four
+// waves owns 4 * 16 * MT rows (each wave its own 16 * MT) and 16 * BT runs,
+// over the whole contraction.  The four waves stage each run of CD
+// 64-column blocks of digit fragments into an LDS ring with direct
+// global-to-LDS loads (a quarter of the fragments each), P stages ahead,
+// and every wave streams its own weight rows into a register ring of the
+// same depth; one barrier per stage.  The digits then cross L2 once per
+// 64 * MT rows rather than once per 16 * MT.  For matrices whose rows are
+// 16-byte aligned and whose column count is a multiple of 64 * CD.
+template <int BT>
+struct SharedGeom {
+  static constexpr int CD = 2;                 // 64-column blocks per stage
+  static constexpr int FR = 3 * BT * CD;       // digit fragments per stage
+  static constexpr int FW = FR / 4;            // fragments each wave stages
+  static constexpr int P = BT >= 4 ? 3 : 4;    // stages in flight
+  static constexpr int NB = P + 1;             // stage buffers (LDS and registers)
+};
+
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() would
+// also wait for every outstanding global load of the wave (its release
+// fence), which would empty the prefetch ring at each stage; the staging
+// loads a stage needs are awaited explicitly before this barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Stage buffer I of the LDS ring: one distinct LDS object per buffer, so the
+// compiler can tell which staging loads a read of the buffer waits for.
+template <int I, int N>
+__device__ __forceinline__ v4i *ring_buf() {
+  __shared__ v4i buf[N];
+  return buf;
+}
+
+template <int EPI, int MT, int BT>
+__global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
+  using G = SharedGeom<BT>;
+  constexpr int CD = G::CD, FR = G::FR, FW = G::FW, P = G::P, NB = G::NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+
+  // Workgroup -> (row tile, batch chunk), chunks of a tile 8 ids apart.
+  const uint32_t nchunk = a.chunks;
+  const uint32_t grp = blockIdx.x / (8 * nchunk), rem = blockIdx.x % (8 * nchunk);
+  const uint32_t chunk = rem / 8, tile = grp * 8 + rem % 8;
+  if (tile >= a.ntiles) return;
+  const uint32_t b0 = chunk * BT * 16;
+  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
+
+  RowTile<MT> t;
+  row_tile<EPI, MT>(a, tile, 4, wave, lg, t);
+  const bool exact =
+      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
+  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) return;  // every wave sees all runs of the chunk
+
+  int64_t v[MT][BT][4];
+  if (exact) {
+    rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
+  } else {
+    v4i acc[MT][3][BT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int l = 0; l < 3; l++)
+#pragma unroll
+        for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
+
+    const uint32_t nch = a.kblocks / CD;
+    const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+    const uint8_t *wsrc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
+      wsrc[mt] = t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
+    }
+    // This wave stages fragments f = wave + 4q of every stage; fragment f
+    // is (limb l, run tile bt, block c).  Runs past the batch bring
+    // whatever their plane rows hold; those product columns are never stored.
+    const int8_t *dsrc[FW];
+#pragma unroll
+    for (int q = 0; q < FW; q++) {
+      const int f = wave + 4 * q;
+      const int l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
+      dsrc[q] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + c) * 64 + lane) * 16;
+    }
+    v4i *ring[NB];
+    ring[0] = ring_buf<0, FR * 64>();
+    ring[1] = ring_buf<1, FR * 64>();
+    ring[2] = ring_buf<2, FR * 64>();
+    ring[3] = ring_buf<3, FR * 64>();
+    if constexpr (NB > 4) ring[4] = ring_buf<4, FR * 64>();
+
+    v4i Wr[NB][MT][CD];
+    // Stage st into buffer s (weights into register slot s, digits into
+    // LDS buffer s).
+    auto issue = [&](int s, uint32_t st) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int c = 0; c < CD; c++)
+          Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * 64);
+#pragma unroll
+      for (int q = 0; q < FW; q++)
+        __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
+                                         (lds_void *)(ring[s] + (wave + 4 * q) * 64), 16, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](int s) {
+      const int flip = (int)0x80808080u;
+      const v4i *buf = ring[s];
+#pragma unroll
+      for (int c = 0; c < CD; c++) {
+        v4i w[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          w[mt] = Wr[s][mt][c];
+          w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+        }
+#pragma unroll
+        for (int l = 0; l < 3; l++)
+#pragma unroll
+          for (int bt = 0; bt < BT; bt++) {
+            const v4i Bv = buf[((l * BT + bt) * CD + c) * 64 + lane];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+              acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Bv, acc[mt][l][bt], 0, 0, 0);
+          }
+      }
+    };
+    // Stage k lives in buffer k % NB.  Once stage k has landed and every
+    // wave has passed the barrier (so all have finished stage k - 1), a wave
+    // issues stage k + P (the last stage again when there is no further
+    // one) into buffer (k + P) % NB, the one stage k - 1 used, then computes
+    // stage k.  P - 1 younger stages are in flight at every wait.
+    const uint32_t last = nch - 1;
+#pragma unroll
+    for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
+    uint32_t ch = 0;
+    for (; ch + NB <= nch; ch += NB) {
+#pragma unroll
+      for (int s = 0; s < NB; s++) {
+        wait_vm<(P - 1) * (MT * CD + FW)>();
+        lds_barrier();
+        const uint32_t nx = ch + s + P;
+        issue((s + P) % NB, nx < nch ? nx : last);
+        compute(s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NB; s++) {
+      if (ch + s < nch) {
+        wait_vm<(P - 1) * (MT * CD + FW)>();
+        lds_barrier();
+        const uint32_t nx = ch + s + P;
+        issue((s + P) % NB, nx < nch ? nx : last);
+        compute(s);
+      }
+    }
+    // No staging load may still be landing in LDS when the workgroup ends.
+    wait_vm<0>();
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int bt = 0; bt < BT; bt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
+                         ((int64_t)acc[mt][2][bt][j] << 16);
+  }
+  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg);
 }
 
 // Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
@@ -994,9 +1208,17 @@ static int rows_launch(const RowsArgs &a, hipStream_t s) {
   return ok(hipGetLastError());
 }
 
+template <int EPI, int MT, int BT>
+static int rows_launch_shared(const RowsArgs &a, hipStream_t s) {
+  const uint32_t groups = (a.ntiles + 7) / 8;
+  const dim3 grid(groups * 8 * a.chunks), block(256);
+  hipLaunchKernelGGL((k_rows_shared<EPI, MT, BT>), grid, block, 0, s, a);
+  return ok(hipGetLastError());
+}
+
 template <int EPI>
-static int rows_shape(int mt, int bt, const RowsArgs &a, hipStream_t s) {
-  const int key = mt * 10 + bt;
+static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s) {
+  const int key = kind * 100 + mt * 10 + bt;
   if constexpr (EPI != EPI_GATEUP) {
     switch (key) {
       case 11: return rows_launch<EPI, 1, 1>(a, s);
@@ -1008,6 +1230,10 @@ static int rows_shape(int mt, int bt, const RowsArgs &a, hipStream_t s) {
       case 32: return rows_launch<EPI, 3, 2>(a, s);
       case 41: return rows_launch<EPI, 4, 1>(a, s);
       case 42: return rows_launch<EPI, 4, 2>(a, s);
+      case 112: return rows_launch_shared<EPI, 1, 2>(a, s);
+      case 114: return rows_launch_shared<EPI, 1, 4>(a, s);
+      case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
+      case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
     }
   } else {
     switch (key) {
@@ -1016,21 +1242,23 @@ static int rows_shape(int mt, int bt, const RowsArgs &a, hipStream_t s) {
       case 24: return rows_launch<EPI, 2, 4>(a, s);
       case 41: return rows_launch<EPI, 4, 1>(a, s);
       case 42: return rows_launch<EPI, 4, 2>(a, s);
+      case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
+      case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
     }
   }
   return FPI8_ERR_ARGUMENT;
 }
 
-int launch_rows(int epi, int mt, int bt, const RowsArgs &a, void *stream) {
+int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.ntiles == 0 || a.chunks == 0) return 0;
   switch (epi) {
-    case EPI_RAW: return rows_shape<EPI_RAW>(mt, bt, a, s);
-    case EPI_QKV: return rows_shape<EPI_QKV>(mt, bt, a, s);
-    case EPI_RESID: return rows_shape<EPI_RESID>(mt, bt, a, s);
-    case EPI_DOWN: return rows_shape<EPI_DOWN>(mt, bt, a, s);
-    case EPI_CLS: return rows_shape<EPI_CLS>(mt, bt, a, s);
-    case EPI_GATEUP: return rows_shape<EPI_GATEUP>(mt, bt, a, s);
+    case EPI_RAW: return rows_shape<EPI_RAW>(kind, mt, bt, a, s);
+    case EPI_QKV: return rows_shape<EPI_QKV>(kind, mt, bt, a, s);
+    case EPI_RESID: return rows_shape<EPI_RESID>(kind, mt, bt, a, s);
+    case EPI_DOWN: return rows_shape<EPI_DOWN>(kind, mt, bt, a, s);
+    case EPI_CLS: return rows_shape<EPI_CLS>(kind, mt, bt, a, s);
+    case EPI_GATEUP: return rows_shape<EPI_GATEUP>(kind, mt, bt, a, s);
   }
   return FPI8_ERR_ARGUMENT;
 }

@@ -144,6 +144,14 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
                   uint32_t n_runs, uint32_t max_positions, void *stream,
                   int32_t *h_run_errors);
 
+/* Which matrix-row kernel the engine's launches use: 0 the planner's choice
+ * (the default), 1 always the kernel whose four waves split the contraction,
+ * 2 the kernel whose waves share their runs' digits through LDS wherever it
+ * can run (columns a multiple of 128, 16-byte aligned rows).  Results are
+ * identical under every setting; it exists for tests and tuning.  Error 102
+ * for another value. */
+int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
+
 /* Kernel timing for measurement: while enabled, every launch of the kernel
  * class `kernel` is bracketed by HIP events on its stream.  Classes: 0 row
  * kernel (all matrices), 1 attention, 2 normalization, 3 sampling, 4 embedding.

@@ -96,8 +96,9 @@ def spec(shape, n_runs, prompt, max_tokens, seed=0, temps=None, seeds=None):
     return runs
 
 
-def run_pair(shape, blob, runs, cuts, compare_every=True):
+def run_pair(shape, blob, runs, cuts, compare_every=True, row_kernel=0):
     pair = Pair(shape, blob, runs)
+    assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
     try:
         for k in cuts:
             pair.turn(k)
@@ -159,6 +160,67 @@ def test_split_contraction_whole_pass(n_runs):
     blob = Bl.build_blob(shape, 21)
     runs = spec(shape, n_runs, [1 + (r % 5) for r in range(n_runs)], [2 + (r % 4) for r in range(n_runs)])
     run_pair(shape, blob, runs, [2, 3])
+
+
+@pytest.mark.parametrize("row_kernel", [1, 2])
+@pytest.mark.parametrize("n_runs", [3, 20, 70])
+def test_row_kernels_whole_pass(n_runs, row_kernel):
+    # Every matrix of the split shape has a column count that is a multiple
+    # of 128, so both row kernels can run all of them: 1 forces the kernel
+    # whose waves split the contraction, 2 the one that shares digits in LDS.
+    shape = W.SMALL_SHAPES["split"]
+    say(f"split shape, {n_runs} runs, row kernel {row_kernel}")
+    blob = Bl.build_blob(shape, 22)
+    runs = spec(shape, n_runs, [1 + (r % 4) for r in range(n_runs)], [2 + (r % 3) for r in range(n_runs)])
+    run_pair(shape, blob, runs, [1, 3], row_kernel=row_kernel)
+
+
+def test_shared_kernel_exact_path():
+    shape = W.SMALL_SHAPES["split"]
+    say("exact path, shared-digit row kernel")
+    norm = np.full((2 * shape.layers + 1) * shape.dim, 1 << 30, dtype=np.int32)
+    blob = Bl.build_blob(shape, 23, tables={"norm": norm})
+    runs = spec(shape, 5, [2, 3, 1, 4, 2], 3)
+    run_pair(shape, blob, runs, [1, 10], row_kernel=2)
+
+
+def test_long_context_attention():
+    # 3000 prompt ids: attention over thousands of cached positions.
+    shape = Shape(256, 512, 2, 2, 2, 300, 4096)
+    say("long context, 3000 ids")
+    blob = Bl.build_blob(shape, 24)
+    runs = [(W.prompt_ids(shape.vocab, 3000, 124, 0), 3, 0, 1),
+            (W.prompt_ids(shape.vocab, 700, 124, 1), 2, 0, 2)]
+    O.set_threads(16)
+    try:
+        run_pair(shape, blob, runs, [1500, 10000], compare_every=False)
+    finally:
+        O.set_threads(1)
+
+
+@pytest.mark.parametrize("name", ["1.1B-shaped-d2048-L22", "7B-shaped-d4096-L32"])
+def test_full_size_first_positions(name):
+    # The model and batch width of the workload; prompts of 1 to 3 ids so
+    # that the first positions generate (classifier and sampling at full
+    # size).  Every run advances on the GPU; a sample of runs is checked
+    # against the oracle, state for state.
+    w = W.by_name(name)
+    shape = w.shape
+    say(f"full size {name}: artifact")
+    blob = Bl.build_blob(shape, w.blob_seed)
+    runs = [(W.prompt_ids(shape.vocab, 1 + (r % 3), w.ids_seed, r), 3, 0, w.run_seed + r)
+            for r in range(w.runs)]
+    sample = sorted({0, 1, 2, w.runs // 2 + 1, w.runs - 1})
+    O.set_threads(16)
+    pair = Pair(shape, blob, runs)
+    try:
+        for k in (1, 2):
+            say(f"full size {name}: turn of {k}")
+            pair.turn(k, oracle_runs=sample)
+            pair.compare(sample)
+    finally:
+        pair.model.close()
+        O.set_threads(1)
 
 
 def test_generic_head_size():
