@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "../../include/fpi8.h"
@@ -119,15 +120,17 @@ struct RowPlan {
 // choice to kind 0 or kind 1.
 RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bool shared_ok,
                   int force) {
-  struct Cand { int kind, mt, bt; double gbs; };
-  static const Cand plain[] = {{0, 1, 1, 32}, {0, 1, 2, 48}, {0, 1, 4, 53}, {0, 2, 1, 33},
-                               {0, 2, 2, 38}, {0, 2, 4, 42}, {0, 3, 2, 31}, {0, 4, 1, 29},
-                               {0, 4, 2, 29}, {1, 1, 2, 28}, {1, 1, 4, 28}, {1, 2, 2, 28},
-                               {1, 2, 4, 24}};
-  static const Cand pairs[] = {{0, 2, 1, 33}, {0, 2, 2, 38}, {0, 2, 4, 42}, {0, 4, 1, 29},
-                               {0, 4, 2, 29}, {1, 2, 2, 28}, {1, 2, 4, 24}};
+  // rate: GB/s one compute unit draws for the shape; occ: workgroups of the
+  // shape that fit on one compute unit (registers, LDS).
+  struct Cand { int kind, mt, bt; double gbs; int occ; };
+  static const Cand plain[] = {{0, 1, 1, 26, 1}, {0, 1, 2, 44, 2}, {0, 1, 4, 46, 1},
+                               {0, 2, 2, 37, 1}, {0, 2, 4, 42, 1}, {0, 4, 2, 28, 1},
+                               {1, 1, 2, 36, 2}, {1, 1, 4, 30, 1}, {1, 2, 2, 29, 2},
+                               {1, 2, 4, 24, 1}};
+  static const Cand pairs[] = {{0, 2, 2, 37, 1}, {0, 2, 4, 42, 1}, {0, 4, 2, 28, 1},
+                               {1, 2, 2, 29, 2}, {1, 2, 4, 24, 1}};
   const Cand *cand = gateup ? pairs : plain;
-  const int n = gateup ? 7 : 13;
+  const int n = gateup ? 5 : 10;
   const double cus = 256, hbm_cu = 20e9;
   RowPlan best{0, 1, 1, 1, 1};
   double best_t = 1e30;
@@ -144,10 +147,14 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
     const double wgs = (double)p.tiles * p.chunks;
     const double act = wgs < cus ? wgs : cus;
     // Each 64-column block costs a workgroup one 1 KB load per weight tile
-    // and per digit tile, whether or not all its runs exist.
+    // and per digit tile, whether or not all its runs exist.  Workgroups run
+    // in rounds of 256 * occ; a compute unit holding k of them shares its
+    // rate among them.
     const double per_wg = 1024.0 * (waves_rows * p.mt + 3 * p.bt) * ((cols + 63) / 64);
+    const double rounds = std::ceil(wgs / (cus * cand[i].occ));
+    const double per_cu = std::min((double)cand[i].occ, std::ceil(wgs / cus));
     const double t_hbm = (double)rows * cols * (gateup ? 2 : 1) / (act * hbm_cu);
-    const double t_l2 = wgs / act * per_wg / (cand[i].gbs * 1e9);
+    const double t_l2 = rounds * per_cu * per_wg / (cand[i].gbs * 1e9);
     const double t = std::max(t_hbm, t_l2);
     if (t < best_t * 0.999) { best_t = t; best = p; }
   }

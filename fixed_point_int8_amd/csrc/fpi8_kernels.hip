@@ -1224,11 +1224,8 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 11: return rows_launch<EPI, 1, 1>(a, s);
       case 12: return rows_launch<EPI, 1, 2>(a, s);
       case 14: return rows_launch<EPI, 1, 4>(a, s);
-      case 21: return rows_launch<EPI, 2, 1>(a, s);
       case 22: return rows_launch<EPI, 2, 2>(a, s);
       case 24: return rows_launch<EPI, 2, 4>(a, s);
-      case 32: return rows_launch<EPI, 3, 2>(a, s);
-      case 41: return rows_launch<EPI, 4, 1>(a, s);
       case 42: return rows_launch<EPI, 4, 2>(a, s);
       case 112: return rows_launch_shared<EPI, 1, 2>(a, s);
       case 114: return rows_launch_shared<EPI, 1, 4>(a, s);
@@ -1237,10 +1234,8 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
     }
   } else {
     switch (key) {
-      case 21: return rows_launch<EPI, 2, 1>(a, s);
       case 22: return rows_launch<EPI, 2, 2>(a, s);
       case 24: return rows_launch<EPI, 2, 4>(a, s);
-      case 41: return rows_launch<EPI, 4, 1>(a, s);
       case 42: return rows_launch<EPI, 4, 2>(a, s);
       case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
       case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
