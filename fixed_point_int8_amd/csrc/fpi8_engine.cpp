@@ -62,6 +62,8 @@ struct fpi8_engine {
   hipGraphExec_t graph = nullptr;
   uint8_t *graph_states = nullptr;
   uint32_t graph_runs = 0;
+  uint32_t graph_cap = 0;
+  uint32_t score_cap = 0;  // attention's LDS score slots for the current turn
   int row_kind = 0;  // 0 planner's choice, 1 or 2 restrict it (fpi8_engine_set_row_kernel)
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
@@ -246,7 +248,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
     {
       AttnArgs a{states, e->d_runs, n_runs, l, c.heads, c.kv_heads, c.head,
                  c.heads / c.kv_heads, e->model.inv, e->exp_tab, e->d_planes0, e->kp, e->bp,
-                 fl + 1, e->max_npos};
+                 fl + 1, e->score_cap};
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
     }
@@ -300,7 +302,8 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
 // arena and run count).  Every launch of a position reads the run
 // descriptors on the device, so the same graph serves every position.
 int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
-  if (e->graph && e->graph_states == states && e->graph_runs == n_runs) return 0;
+  if (e->graph && e->graph_states == states && e->graph_runs == n_runs && e->graph_cap == e->score_cap)
+    return 0;
   if (e->graph) {
     (void)hipGraphExecDestroy(e->graph);
     e->graph = nullptr;
@@ -325,6 +328,7 @@ int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   }
   e->graph_states = states;
   e->graph_runs = n_runs;
+  e->graph_cap = e->score_cap;
   return 0;
 }
 
@@ -445,6 +449,13 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
     steps = std::max(steps, L.cachepos - v);
   }
   steps = std::min(steps, max_positions);
+  // Attention keeps one score per cached position in LDS: size it for the
+  // longest cache of the batch (in steps of 256, so a graph recorded for one
+  // turn serves the next).
+  uint32_t cap = 256;
+  for (uint32_t b = 0; b < n_runs; b++)
+    if (e->h_runs[b].valid) cap = std::max(cap, (e->h_runs[b].cachepos + 255) / 256 * 256);
+  e->score_cap = std::min(cap, e->max_npos);
   if ((r = hip_ok(hipMemcpyAsync(e->d_runs, e->h_runs, sizeof(RunDesc) * n_runs,
                                  hipMemcpyHostToDevice, s))) ||
       (r = hip_ok(hipMemcpyAsync(e->d_run_err, e->h_err, 4ull * n_runs, hipMemcpyHostToDevice, s))))

@@ -145,7 +145,7 @@ struct AttnArgs {
   int8_t *planes;
   uint32_t kp, bp;
   uint32_t *oflag;
-  uint32_t max_npos;        // LDS sized for this many positions
+  uint32_t max_npos;        // LDS score slots: at least every run's cache positions
 };
 
 struct SampleArgs {

@@ -862,8 +862,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   __shared__ uint64_t scratch[8];
   __shared__ int64_t qs[256];
   extern __shared__ __align__(16) uint8_t lds[];
-  uint32_t *exps = reinterpret_cast<uint32_t *>(lds);
-  int64_t *sc = reinterpret_cast<int64_t *>(lds + 16400);
+  int64_t *sc = reinterpret_cast<int64_t *>(lds);  // scores, then exponentials, then probabilities
   int64_t *red = sc + a.max_npos;
 
   const uint32_t h = blockIdx.x, b = blockIdx.y;
@@ -879,7 +878,6 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   const int32_t *K = reinterpret_cast<const int32_t *>(st + rd.off_keys) + head_base;
   const int32_t *V = reinterpret_cast<const int32_t *>(st + rd.off_values) + head_base;
 
-  for (uint32_t i = tid; i < 4097; i += blockDim.x) exps[i] = a.exp_tab[i];
   for (uint32_t i = tid; i < hs; i += blockDim.x) qs[i] = q[i];
   __syncthreads();
 
@@ -968,7 +966,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   for (uint32_t j = tid; j < npos; j += blockDim.x) {
     const uint64_t d = (uint64_t)m - (uint64_t)sc[j];
     const uint64_t idx = d >> 8;
-    const uint32_t e = exps[idx > 4096 ? 4096 : idx];
+    const uint32_t e = a.exp_tab[idx > 4096 ? 4096 : idx];  // 16 KB table, hot in L2
     sc[j] = e;
     lsum += e;
   }
@@ -1260,7 +1258,7 @@ int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stre
 
 size_t attention_lds_bytes(uint32_t max_npos, uint32_t head) {
   const size_t red = (head % 4 == 0 && (head & (head - 1)) == 0) ? 16ull * head : 256ull;
-  return 16400 + 8ull * max_npos + 8ull * red;
+  return 8ull * max_npos + 8ull * red;
 }
 
 static bool pow2_head(uint32_t h) { return h >= 4 && h <= 256 && (h & (h - 1)) == 0; }
