@@ -338,11 +338,106 @@ __device__ __forceinline__ void rows_exact(const RowsArgs &a, const RowTile<MT> 
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// What a lane's epilogue needs besides its sums, fetched while the matrix
+// streams so that the epilogue waits on nothing: the descriptor fields of
+// its runs (issued first), then the state or table values the phase reads
+// (issued after the first matrix loads).  Runs that do not exist read
+// offsets 0 and clamped rows: valid addresses whose values are never used.
+template <int EPI, int MT, int BT>
+struct EpiIn {
+  static constexpr int NX = (EPI == EPI_RESID || EPI == EPI_DOWN) ? MT : 1;
+  static constexpr int NR = EPI == EPI_QKV ? MT : 1;
+  uint32_t flags[BT], pos[BT], cache[BT];
+  uint64_t base[BT], o1[BT], o2[BT], o3[BT];
+  int64_t x[NX][BT][4];
+  int32_t c[NR][BT][2], s[NR][BT][2];
+};
+
+template <int EPI, int MT, int BT>
+__device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li,
+                                          EpiIn<EPI, MT, BT> &in) {
+#pragma unroll
+  for (int bt = 0; bt < BT; bt++) {
+    const uint32_t b = b0 + bt * 16 + li;
+    in.flags[bt] = 0; in.pos[bt] = 0; in.cache[bt] = 0;
+    in.base[bt] = 0; in.o1[bt] = 0; in.o2[bt] = 0; in.o3[bt] = 0;
+    if (EPI == EPI_RAW) {
+      in.flags[bt] = b < a.n_runs ? 1u : 0u;
+      continue;
+    }
+    const RunDesc &rd = a.runs[b < a.n_runs ? b : 0];
+    in.flags[bt] = b < a.n_runs ? rd.flags : 0u;
+    in.base[bt] = rd.base;
+    if (EPI == EPI_CLS) in.o1[bt] = rd.off_logits;
+    if (EPI == EPI_RESID || EPI == EPI_DOWN) in.o1[bt] = rd.off_x;
+    if (EPI == EPI_DOWN) in.o2[bt] = rd.off_w1;
+    if (EPI == EPI_GATEUP) { in.o1[bt] = rd.off_gate; in.o2[bt] = rd.off_up; }
+    if (EPI == EPI_QKV) {
+      in.pos[bt] = rd.pos;
+      in.cache[bt] = rd.cachepos;
+      in.o1[bt] = rd.off_w2; in.o2[bt] = rd.off_keys; in.o3[bt] = rd.off_values;
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ bool epi_live(uint32_t flags) {
+  if (EPI == EPI_RAW) return flags != 0;
+  return EPI == EPI_CLS ? (flags & RUN_GEN) != 0 : (flags & RUN_ACTIVE) != 0;
+}
+
+template <int EPI, int MT, int BT>
+__device__ __forceinline__ void epi_fetch(const RowsArgs &a, const RowTile<MT> &t, int lg,
+                                          EpiIn<EPI, MT, BT> &in) {
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DOWN) {
+#pragma unroll
+    for (int bt = 0; bt < BT; bt++) {
+      const int64_t *x = reinterpret_cast<const int64_t *>(a.states + in.base[bt] + in.o1[bt]);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t row = t.rbase[mt] + 4 * lg + j;
+          in.x[mt][bt][j] = x[row < t.rcount[mt] ? row : t.rcount[mt] - 1];
+        }
+    }
+  }
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int bt = 0; bt < BT; bt++) {
+      const int32_t *cs = a.rope_cos + (uint64_t)in.pos[bt] * a.half;
+      const int32_t *sn = a.rope_sin + (uint64_t)in.pos[bt] * a.half;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int jp = 0; jp < 2; jp++) {
+          const uint32_t row = t.rbase[mt] + 4 * lg + 2 * jp;
+          const uint32_t p = ((row < t.rcount[mt] ? row : 0) % a.head) >> 1;
+          in.c[mt][bt][jp] = cs[p];
+          in.s[mt][bt][jp] = sn[p];
+        }
+    }
+  }
+}
+
+// The first 4096 entries of the SiLU table (the only ones an index can
+// reach) into LDS with direct global-to-LDS loads: 16 of 1 KB, shared out
+// over the workgroup's waves.
+__device__ __forceinline__ void silu_to_lds(const int32_t *silu, int32_t *lds, int wave, int nwaves,
+                                            int lane) {
+  for (int i = wave; i < 16; i += nwaves)
+    __builtin_amdgcn_global_load_lds((const void *)(silu + i * 256 + lane * 4),
+                                     (lds_void *)(lds + i * 256), 16, 0, 0);
+}
+
 // Epilogue of the outputs this lane holds: y = (v * scale) >> 24, then the
 // phase's own work.
 template <int EPI, int MT, int BT>
 __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<MT> &t, uint32_t b0,
-                                              const int64_t (&v)[MT][BT][4], int li, int lg) {
+                                              const int64_t (&v)[MT][BT][4], int li, int lg,
+                                              const EpiIn<EPI, MT, BT> &in, const int32_t *silu) {
   constexpr int HALF = MT >= 2 ? MT / 2 : 1;
   const uint32_t si = t.si;
   const auto &rbase = t.rbase;
@@ -351,7 +446,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
-    if (!row_run_ok<EPI>(a, b)) continue;
+    if (!epi_live<EPI>(in.flags[bt])) continue;
     int64_t y[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -370,36 +465,36 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
         }
       continue;
     }
-    RunDesc &rd = a.runs[b];
-    uint8_t *st = a.states + rd.base;
+    RunDesc &rd = a.runs[b];  // only for recording a fit failure
+    uint8_t *st = a.states + in.base[bt];
 #pragma unroll
     for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
       const uint32_t r0 = rbase[mt] + 4 * lg;
       if (EPI == EPI_CLS) {
-        int64_t *lg_out = reinterpret_cast<int64_t *>(st + rd.off_logits);
+        int64_t *lg_out = reinterpret_cast<int64_t *>(st + in.o1[bt]);
 #pragma unroll
         for (int j = 0; j < 4; j++)
           if (r0 + j < rcount[mt]) lg_out[r0 + j] = y[mt][j];
       } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
-        int64_t *x = reinterpret_cast<int64_t *>(st + rd.off_x);
-        int64_t *w1 = reinterpret_cast<int64_t *>(st + rd.off_w1);
+        int64_t *x = reinterpret_cast<int64_t *>(st + in.o1[bt]);
+        int64_t *w1 = reinterpret_cast<int64_t *>(st + in.o2[bt]);
 #pragma unroll
         for (int j = 0; j < 4; j++)
           if (r0 + j < rcount[mt]) {
             if (EPI == EPI_DOWN) w1[r0 + j] = y[mt][j];
-            x[r0 + j] = wadd(x[r0 + j], y[mt][j]);
+            x[r0 + j] = wadd(in.x[EPI == EPI_RESID || EPI == EPI_DOWN ? mt : 0][bt][j], y[mt][j]);
           }
       } else if (EPI == EPI_GATEUP) {
         // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
-        int64_t *gate = reinterpret_cast<int64_t *>(st + rd.off_gate);
-        int64_t *up = reinterpret_cast<int64_t *>(st + rd.off_up);
+        int64_t *gate = reinterpret_cast<int64_t *>(st + in.o1[bt]);
+        int64_t *up = reinterpret_cast<int64_t *>(st + in.o2[bt]);
         const int64_t lim = (int64_t)16 << 16;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const uint32_t row = r0 + j;
           if (row >= a.hidden) continue;
           const int64_t g = y[mt][j], u = y[mt + HALF][j];
-          const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)a.silu[(g + lim) >> 9];
+          const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)silu[(g + lim) >> 9];
           const int64_t h = wmul(sg, u) >> 16;
           gate[row] = h;
           up[row] = u;
@@ -407,34 +502,32 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
         }
       } else if (EPI == EPI_QKV) {
         const uint32_t role = a.seg[si].role;
-        const uint32_t pos = rd.pos;
+        const uint32_t pos = in.pos[bt];
         if (role == ROLE_V) {
           // Phase 7: the value rows into the cache, each checked to fit 32 bits.
-          int32_t *V = reinterpret_cast<int32_t *>(st + rd.off_values);
+          int32_t *V = reinterpret_cast<int32_t *>(st + in.o3[bt]);
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const uint32_t row = r0 + j;
             if (row >= rcount[mt]) continue;
             if (!fits32(y[mt][j])) { fail(rd, a.layer, 7); continue; }
             const uint32_t kvh = row / a.head, e = row % a.head;
-            V[(((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e] = (int32_t)y[mt][j];
+            V[(((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e] = (int32_t)y[mt][j];
           }
         } else {
           // Phase 8 on the query (kept in w2) and on the key after its
           // phase-6 store check: pairs (2p, 2p+1) of each head turned by
           // position pos's cosine and sine p.
-          const int32_t *cs = a.rope_cos + (uint64_t)pos * a.half;
-          const int32_t *sn = a.rope_sin + (uint64_t)pos * a.half;
-          int64_t *q = reinterpret_cast<int64_t *>(st + rd.off_w2);
-          int32_t *K = reinterpret_cast<int32_t *>(st + rd.off_keys);
+          int64_t *q = reinterpret_cast<int64_t *>(st + in.o1[bt]);
+          int32_t *K = reinterpret_cast<int32_t *>(st + in.o2[bt]);
 #pragma unroll
           for (int j = 0; j < 4; j += 2) {
             const uint32_t row = r0 + j;
             if (row >= rcount[mt]) continue;
             const int64_t A0 = y[mt][j], B0 = y[mt][j + 1];
             if (role == ROLE_K && (!fits32(A0) || !fits32(B0))) { fail(rd, a.layer, 6); continue; }
-            const uint32_t p = (row % a.head) >> 1;
-            const int64_t c = cs[p], s = sn[p];
+            const int64_t c = in.c[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
+            const int64_t s = in.s[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
             const int64_t ra = wsub(wmul(A0, c), wmul(B0, s)) >> 24;
             const int64_t rb = wadd(wmul(A0, s), wmul(B0, c)) >> 24;
             if (role == ROLE_Q) {
@@ -443,7 +536,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             } else {
               if (!fits32(ra) || !fits32(rb)) { fail(rd, a.layer, 8); continue; }
               const uint32_t kvh = row / a.head, e = row % a.head;
-              int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * rd.cachepos + pos) * a.head + e;
+              int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
               dst[0] = (int32_t)ra;
               dst[1] = (int32_t)rb;
             }
@@ -462,7 +555,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Blocks in flight per wave: the fragments of a block take 4 * (MT + 3 BT)
 // VGPRs, and about 190 of them hold the prefetch ring.
@@ -477,6 +569,7 @@ template <int EPI, int MT, int BT>
 __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   constexpr int P = RowsGeom<MT, BT>::P;
   __shared__ int64_t red[3][MT * BT * 4 * 64];
+  __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
 
@@ -496,6 +589,9 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile, 1, 0, lg, t);
+  EpiIn<EPI, MT, BT> in;
+  epi_begin<EPI, MT, BT>(a, b0, li, in);
+  if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
 
   // This wave's blocks [k_lo, k_lo + n).
   const uint32_t nkb = a.kblocks, per = (nkb + 3) / 4;
@@ -589,12 +685,16 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
     for (int s = 0; s < P; s++) load(s, (uint32_t)s < n_main ? (uint32_t)s : last);
   }
+  epi_fetch<EPI, MT, BT>(a, t, lg, in);
 
   // The input needs more than three digits somewhere: exact path (a scalar
   // read, so it does not wait behind the loads above).
   const bool exact =
       a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
-  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) return;  // every wave sees all runs of the chunk
+  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
+    wait_vm<0>();  // no table load may still be landing in LDS
+    return;
+  }
 
   int64_t v[MT][BT][4];
   if (!exact) {
@@ -664,7 +764,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; j++) v[mt][bt][j] = wadd(v[mt][bt][j], red[w][((mt * BT + bt) * 4 + j) * 64 + lane]);
 
-  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg);
+  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
 // The matrix row with the digits shared through LDS.  A workgroup of four
@@ -714,14 +814,22 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
   const uint32_t b0 = chunk * BT * 16;
   const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
 
+  __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile, 4, wave, lg, t);
+  EpiIn<EPI, MT, BT> in;
+  epi_begin<EPI, MT, BT>(a, b0, li, in);
+  if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
   const bool exact =
       a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
-  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) return;  // every wave sees all runs of the chunk
+  if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
+    wait_vm<0>();  // no table load may still be landing in LDS
+    return;
+  }
 
   int64_t v[MT][BT][4];
   if (exact) {
+    epi_fetch<EPI, MT, BT>(a, t, lg, in);
     rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
   } else {
     v4i acc[MT][3][BT];
@@ -803,6 +911,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
     const uint32_t last = nch - 1;
 #pragma unroll
     for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
+    epi_fetch<EPI, MT, BT>(a, t, lg, in);
     uint32_t ch = 0;
     for (; ch + NB <= nch; ch += NB) {
 #pragma unroll
@@ -835,7 +944,11 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
           v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
                          ((int64_t)acc[mt][2][bt][j] << 16);
   }
-  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg);
+  if constexpr (EPI == EPI_GATEUP) {
+    wait_vm<0>();
+    lds_barrier();  // every wave's share of the SiLU table has landed
+  }
+  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
 // Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
