@@ -187,6 +187,8 @@ def main():
     # launch bracketed by HIP events on its stream.
     pos1 = batch.info(0)["position"]
     ks = args.kernel_steps
+    # One stream here, so that no other kernel runs beside the one timed.
+    B.fpi8_engine_set_streams(model.engine, 1)
     B.fpi8_engine_set_timing(model.engine, B.T_ROWS, True)
     B.fpi8_engine_set_timing(model.engine, B.T_ATTN, True)
     torch.cuda.synchronize()

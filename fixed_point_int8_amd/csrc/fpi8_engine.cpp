@@ -46,8 +46,8 @@ struct fpi8_engine {
   std::vector<Mat> mats;  // [0] embedding, [1 + 7l + kind - 1], [1 + 7L] classifier
   // device workspace
   RunDesc *d_runs = nullptr;
-  int8_t *d_planes0 = nullptr, *d_planes1 = nullptr;
-  uint32_t *d_oflags = nullptr;
+  int8_t *d_planes0 = nullptr, *d_planes1 = nullptr;  // per run group: [2][3][bp][kp]
+  uint32_t *d_oflags = nullptr;                        // per run group: [2][n_oflags]
   uint32_t n_oflags = 0;
   int32_t *d_run_err = nullptr;
   // pinned host buffers
@@ -65,6 +65,14 @@ struct fpi8_engine {
   uint32_t graph_cap = 0;
   uint32_t score_cap = 0;  // attention's LDS score slots for the current turn
   int row_kind = 0;  // 0 planner's choice, 1 or 2 restrict it (fpi8_engine_set_row_kernel)
+  // Runs split into two groups advanced on two streams, so one group's
+  // row kernels overlap the other's attention (2); one stream (0, 1).
+  // Measured on the 7B-shaped decode at 64 runs, two groups are slower:
+  // the row kernels at 32 runs read every weight twice.
+  int streams = 0;
+  uint32_t graph_groups = 0;
+  hipStream_t side_stream = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -163,8 +171,25 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
   return best;
 }
 
-RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t cols,
+// The runs [r0, r0 + n) of a batch with their own digit planes and flags:
+// every kernel of a position sees them as a batch of n runs.
+struct Group {
+  uint32_t n;
+  RunDesc *runs;
+  int8_t *planes0, *planes1;
+  uint32_t *oflags;
+  int32_t *run_err;
+};
+
+Group group(fpi8_engine *e, int g, uint32_t r0, uint32_t n) {
+  const size_t planes = 3ull * e->bp * e->kp;
+  return Group{n, e->d_runs + r0, e->d_planes0 + g * planes, e->d_planes1 + g * planes,
+               e->d_oflags + g * e->n_oflags, e->d_run_err + r0};
+}
+
+RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t cols,
                    const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer) {
+  const uint32_t n_runs = G.n;
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
@@ -176,7 +201,7 @@ RowsArgs rows_base(fpi8_engine *e, uint8_t *states, uint32_t n_runs, uint32_t co
   a.in_sel = in_sel;
   a.oflag = oflag;
   a.states = states;
-  a.runs = e->d_runs;
+  a.runs = G.runs;
   a.layer = layer;
   a.rope_cos = e->cos_t;
   a.rope_sin = e->sin_t;
@@ -217,43 +242,44 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
 }
 
-// One position of every active run.
-int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
+// One position of every active run of a group.
+int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s) {
   const Cfg &c = e->c;
+  const uint32_t n_runs = G.n;
   int r;
   {
-    BeginArgs a{states, e->d_runs, n_runs, e->d_oflags, e->n_oflags};
+    BeginArgs a{states, G.runs, n_runs, G.oflags, e->n_oflags};
     if ((r = launch_begin(a, s))) return r;
   }
   {
-    EmbedArgs a{states, e->d_runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S};
+    EmbedArgs a{states, G.runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S};
     TimedLaunch t(e, T_EMBED, s);
     if ((r = launch_embed(a, s))) return r;
   }
   for (uint32_t l = 0; l < c.layers; l++) {
-    uint32_t *fl = e->d_oflags + 4 * l;
-    NormArgs na{states, e->d_runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
-                e->d_planes0, e->kp, e->bp, fl + 0, 0};
+    uint32_t *fl = G.oflags + 4 * l;
+    NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
+                G.planes0, e->kp, e->bp, fl + 0, 0};
     {
       TimedLaunch t(e, T_NORM, s);
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 0, IN_W1, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 0, IN_W1, l);
       add_seg(a, e->layer_mat(l, M_Q), ROLE_Q);
       add_seg(a, e->layer_mat(l, M_K), ROLE_K);
       add_seg(a, e->layer_mat(l, M_V), ROLE_V);
       if ((r = run_rows(e, EPI_QKV, a, n_runs, s))) return r;
     }
     {
-      AttnArgs a{states, e->d_runs, n_runs, l, c.heads, c.kv_heads, c.head,
-                 c.heads / c.kv_heads, e->model.inv, e->exp_tab, e->d_planes0, e->kp, e->bp,
+      AttnArgs a{states, G.runs, n_runs, l, c.heads, c.kv_heads, c.head,
+                 c.heads / c.kv_heads, e->model.inv, e->exp_tab, G.planes0, e->kp, e->bp,
                  fl + 1, e->score_cap};
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 1, IN_W3, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l);
       add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_RESID, a, n_runs, s))) return r;
     }
@@ -264,37 +290,60 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, fl + 2, IN_W1, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 2, IN_W1, l);
       add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN);
       add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN);  // shares the gate's row tiles
-      a.planes_out = e->d_planes1;
+      a.planes_out = G.planes1;
       a.kp_out = e->kp;
       a.oflag_out = fl + 3;
       if ((r = run_rows(e, EPI_GATEUP, a, n_runs, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, states, n_runs, c.hidden, e->d_planes1, fl + 3, IN_GATE, l);
+      RowsArgs a = rows_base(e, G, states, c.hidden, G.planes1, fl + 3, IN_GATE, l);
       add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_DOWN, a, n_runs, s))) return r;
     }
   }
-  uint32_t *ff = e->d_oflags + 4 * c.layers;
+  uint32_t *ff = G.oflags + 4 * c.layers;
   {
-    NormArgs na{states, e->d_runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
-                e->d_planes0, e->kp, e->bp, ff, 1};
+    NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
+                G.planes0, e->kp, e->bp, ff, 1};
     TimedLaunch t(e, T_NORM, s);
     if ((r = launch_norm(na, s))) return r;
   }
   {
-    RowsArgs a = rows_base(e, states, n_runs, c.dim, e->d_planes0, ff, IN_W1, 0);
+    RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, ff, IN_W1, 0);
     add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN);
     if ((r = run_rows(e, EPI_CLS, a, n_runs, s))) return r;
   }
   {
-    SampleArgs a{states, e->d_runs, n_runs, c.vocab, e->exp_tab, e->d_run_err};
+    SampleArgs a{states, G.runs, n_runs, c.vocab, e->exp_tab, G.run_err};
     TimedLaunch t(e, T_SAMPLE, s);
     if ((r = launch_sample(a, s))) return r;
   }
+  return 0;
+}
+
+// How many run groups a turn of n_runs uses.
+uint32_t n_groups(const fpi8_engine *e, uint32_t n_runs) {
+  if (n_runs < 2) return 1;
+  return e->streams == 2 ? 2 : 1;
+}
+
+// One position of every active run: one group on stream s, or two, the
+// second on the engine's side stream, forked from and joined back to s.
+int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
+  if (n_groups(e, n_runs) == 1) return step_group(e, group(e, 0, 0, n_runs), states, s);
+  int r;
+  const uint32_t h = (n_runs / 2 + 15) / 16 * 16 < n_runs ? (n_runs / 2 + 15) / 16 * 16 : n_runs / 2;
+  if ((r = hip_ok(hipEventRecord(e->ev_fork, s))) ||
+      (r = hip_ok(hipStreamWaitEvent(e->side_stream, e->ev_fork, 0))))
+    return r;
+  if ((r = step_group(e, group(e, 0, 0, h), states, s))) return r;
+  if ((r = step_group(e, group(e, 1, h, n_runs - h), states, e->side_stream))) return r;
+  if ((r = hip_ok(hipEventRecord(e->ev_join, e->side_stream))) ||
+      (r = hip_ok(hipStreamWaitEvent(s, e->ev_join, 0))))
+    return r;
   return 0;
 }
 
@@ -302,7 +351,8 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
 // arena and run count).  Every launch of a position reads the run
 // descriptors on the device, so the same graph serves every position.
 int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
-  if (e->graph && e->graph_states == states && e->graph_runs == n_runs && e->graph_cap == e->score_cap)
+  if (e->graph && e->graph_states == states && e->graph_runs == n_runs && e->graph_cap == e->score_cap &&
+      e->graph_groups == n_groups(e, n_runs))
     return 0;
   if (e->graph) {
     (void)hipGraphExecDestroy(e->graph);
@@ -329,6 +379,7 @@ int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   e->graph_states = states;
   e->graph_runs = n_runs;
   e->graph_cap = e->score_cap;
+  e->graph_groups = n_groups(e, n_runs);
   return 0;
 }
 
@@ -336,6 +387,9 @@ void release(fpi8_engine *e) {
   if (!e) return;
   if (e->graph) (void)hipGraphExecDestroy(e->graph);
   if (e->cap_stream) (void)hipStreamDestroy(e->cap_stream);
+  if (e->side_stream) (void)hipStreamDestroy(e->side_stream);
+  if (e->ev_fork) (void)hipEventDestroy(e->ev_fork);
+  if (e->ev_join) (void)hipEventDestroy(e->ev_join);
   (void)hipFree(e->d_runs);
   (void)hipFree(e->d_planes0);
   (void)hipFree(e->d_planes1);
@@ -391,16 +445,19 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
   e->n_oflags = 4 * c.layers + 1;
   const size_t planes = 3ull * e->bp * e->kp;
   if ((r = hip_ok(hipMalloc(&e->d_runs, sizeof(RunDesc) * max_runs))) ||
-      (r = hip_ok(hipMalloc(&e->d_planes0, planes))) ||
-      (r = hip_ok(hipMalloc(&e->d_planes1, planes))) ||
-      (r = hip_ok(hipMalloc(&e->d_oflags, 4ull * e->n_oflags))) ||
+      (r = hip_ok(hipMalloc(&e->d_planes0, 2 * planes))) ||
+      (r = hip_ok(hipMalloc(&e->d_planes1, 2 * planes))) ||
+      (r = hip_ok(hipMalloc(&e->d_oflags, 2 * 4ull * e->n_oflags))) ||
       (r = hip_ok(hipMalloc(&e->d_run_err, 4ull * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_runs, sizeof(RunDesc) * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_headers, 128ull * max_runs))) ||
       (r = hip_ok(hipHostMalloc(&e->h_err, 4ull * max_runs))) ||
-      (r = hip_ok(hipMemset(e->d_planes0, 0, planes))) ||
-      (r = hip_ok(hipMemset(e->d_planes1, 0, planes))) ||
-      (r = hip_ok(hipMemset(e->d_oflags, 0, 4ull * e->n_oflags))) ||
+      (r = hip_ok(hipMemset(e->d_planes0, 0, 2 * planes))) ||
+      (r = hip_ok(hipMemset(e->d_planes1, 0, 2 * planes))) ||
+      (r = hip_ok(hipMemset(e->d_oflags, 0, 2 * 4ull * e->n_oflags))) ||
+      (r = hip_ok(hipStreamCreateWithFlags(&e->side_stream, hipStreamNonBlocking))) ||
+      (r = hip_ok(hipEventCreateWithFlags(&e->ev_fork, hipEventDisableTiming))) ||
+      (r = hip_ok(hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming))) ||
       (r = kernels_init(e->max_npos, c.head))) {
     release(e);
     return r;
@@ -489,6 +546,12 @@ int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
     e->graph_states = nullptr;  // record the position again with the new shapes
     e->graph_runs = 0;
   }
+  return 0;
+}
+
+int32_t fpi8_engine_set_streams(fpi8_engine *e, int32_t streams) {
+  if (!e || streams < 0 || streams > 2) return FPI8_ERR_ARGUMENT;
+  e->streams = streams;
   return 0;
 }
 

@@ -152,6 +152,13 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
  * for another value. */
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
 
+/* How a turn spreads a batch over streams: 0 (the default) or 1 one stream;
+ * 2 the runs split in two groups, each advanced by its own launch sequence
+ * on its own stream (the caller's and one of the engine's), so one group's
+ * matrix rows can overlap the other's attention.  Results are identical
+ * under every setting.  Error 102 for another value. */
+int32_t fpi8_engine_set_streams(fpi8_engine *engine, int32_t streams);
+
 /* Kernel timing for measurement: while enabled, every launch of the kernel
  * class `kernel` is bracketed by HIP events on its stream.  Classes: 0 row
  * kernel (all matrices), 1 attention, 2 normalization, 3 sampling, 4 embedding.

@@ -96,9 +96,10 @@ def spec(shape, n_runs, prompt, max_tokens, seed=0, temps=None, seeds=None):
     return runs
 
 
-def run_pair(shape, blob, runs, cuts, compare_every=True, row_kernel=0):
+def run_pair(shape, blob, runs, cuts, compare_every=True, row_kernel=0, streams=0):
     pair = Pair(shape, blob, runs)
     assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    assert B.fpi8_engine_set_streams(pair.model.engine, streams) == 0
     try:
         for k in cuts:
             pair.turn(k)
@@ -173,6 +174,17 @@ def test_row_kernels_whole_pass(n_runs, row_kernel):
     blob = Bl.build_blob(shape, 22)
     runs = spec(shape, n_runs, [1 + (r % 4) for r in range(n_runs)], [2 + (r % 3) for r in range(n_runs)])
     run_pair(shape, blob, runs, [1, 3], row_kernel=row_kernel)
+
+
+@pytest.mark.parametrize("streams,n_runs", [(2, 5), (2, 20), (1, 70)])
+def test_run_groups_on_two_streams(streams, n_runs):
+    # The batch split in two groups, each advanced on its own stream (or,
+    # for 70 runs, kept on one stream although the default would split it).
+    shape = W.SMALL_SHAPES["gqa"]
+    say(f"{n_runs} runs on {streams} stream(s)")
+    blob = Bl.build_blob(shape, 25)
+    runs = spec(shape, n_runs, [1 + (r % 6) for r in range(n_runs)], [1 + (r % 5) for r in range(n_runs)])
+    run_pair(shape, blob, runs, [1, 2, 4], streams=streams)
 
 
 def test_shared_kernel_exact_path():
