@@ -178,8 +178,8 @@ def test_row_kernels_whole_pass(n_runs, row_kernel):
 
 @pytest.mark.parametrize("streams,n_runs", [(2, 5), (2, 20), (1, 70)])
 def test_run_groups_on_two_streams(streams, n_runs):
-    # The batch split in two groups, each advanced on its own stream (or,
-    # for 70 runs, kept on one stream although the default would split it).
+    # The batch split in two groups, each advanced on its own stream, and a
+    # wide batch on one stream.
     shape = W.SMALL_SHAPES["gqa"]
     say(f"{n_runs} runs on {streams} stream(s)")
     blob = Bl.build_blob(shape, 25)
