@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--workload", default="7B-shaped-d4096-L32")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel itself instead of replaying a recorded position "
+                         "(for profilers that cannot follow graph launches)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the runs of a batch are "
@@ -152,6 +155,8 @@ def main():
     blob = Bl.build_blob(shape, w.blob_seed)
     log(f"artifact {blob.size / 1e9:.3f} GB in {time.perf_counter() - t:.1f} s")
     model = DeviceModel(blob, max_runs=w.runs)
+    if args.eager:
+        B.fpi8_engine_set_graph(model.engine, False)
     runs = [(Wl.prompt_ids(shape.vocab, w.prompt, w.ids_seed, r), w.max_tokens, w.temperature_q16,
              w.run_seed + r) for r in range(w.runs)]
     t = time.perf_counter()

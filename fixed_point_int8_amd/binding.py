@@ -28,7 +28,8 @@ UINT64_MAX = (1 << 64) - 1
 # Symbols include/fpi8.h declares.
 EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_init_state",
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
-           "fpi8_engine_destroy", "fpi8_turn", "fpi8_engine_set_row_kernel", "fpi8_engine_set_streams",
+           "fpi8_engine_destroy", "fpi8_turn", "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
+           "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows")
@@ -68,6 +69,7 @@ def lib():
             "fpi8_turn": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
+            "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_timing": (C.c_int32, [_P, C.c_int32, C.c_int32]),
             "fpi8_engine_timing": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_double),
                                                C.POINTER(C.c_uint64)]),
@@ -173,6 +175,10 @@ def fpi8_turn(engine, d_states, state_stride: int, n_runs: int, max_positions: i
 
 def fpi8_engine_set_row_kernel(engine, kind: int) -> int:
     return lib().fpi8_engine_set_row_kernel(engine, kind)
+
+
+def fpi8_engine_set_graph(engine, enable: bool) -> int:
+    return lib().fpi8_engine_set_graph(engine, 1 if enable else 0)
 
 
 def fpi8_engine_set_streams(engine, streams: int) -> int:

@@ -70,6 +70,7 @@ struct fpi8_engine {
   // Measured on the 7B-shaped decode at 64 runs, two groups are slower:
   // the row kernels at 32 runs read every weight twice.
   int streams = 0;
+  bool use_graph = true;  // replay a recorded position (fpi8_engine_set_graph)
   uint32_t graph_groups = 0;
   hipStream_t side_stream = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -520,7 +521,7 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
   if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
   bool timing = false;
   for (const Timer &t : e->timers) timing = timing || t.on;
-  if (steps > 0 && !timing) {
+  if (steps > 0 && !timing && e->use_graph) {
     if ((r = step_graph(e, d_states, n_runs))) return r;
     for (uint32_t k = 0; k < steps; k++)
       if ((r = hip_ok(hipGraphLaunch(e->graph, s)))) return r;
@@ -546,6 +547,12 @@ int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
     e->graph_states = nullptr;  // record the position again with the new shapes
     e->graph_runs = 0;
   }
+  return 0;
+}
+
+int32_t fpi8_engine_set_graph(fpi8_engine *e, int32_t enable) {
+  if (!e) return FPI8_ERR_ARGUMENT;
+  e->use_graph = enable != 0;
   return 0;
 }
 

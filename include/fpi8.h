@@ -152,6 +152,11 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
  * for another value. */
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
 
+/* Whether a turn replays one position recorded as a HIP graph (nonzero, the
+ * default) or launches every kernel of every position itself (0, also the
+ * case while kernel timing is on).  Results are identical either way. */
+int32_t fpi8_engine_set_graph(fpi8_engine *engine, int32_t enable);
+
 /* How a turn spreads a batch over streams: 0 (the default) or 1 one stream;
  * 2 the runs split in two groups, each advanced by its own launch sequence
  * on its own stream (the caller's and one of the engine's), so one group's

@@ -41,7 +41,7 @@ def gpu_rows(Wm, s, x):
 
 @pytest.mark.parametrize("rows,cols,batch", [
     (16, 64, 1), (1, 1, 1), (37, 172, 3), (100, 300, 17), (256, 512, 32), (129, 4096, 64),
-    (64, 128, 100), (33, 64, 128), (48, 11008, 8), (200, 2048, 65)])
+    (64, 128, 100), (33, 64, 128), (48, 11008, 8), (200, 2048, 65), (24, 65536, 3)])
 def test_matrix_rows_random(rows, cols, batch):
     say(f"matrix_rows {rows}x{cols} batch {batch}")
     Wm, s, x = W.row_operands(rows, cols, batch, rows * 1000 + cols + batch)
@@ -96,10 +96,11 @@ def spec(shape, n_runs, prompt, max_tokens, seed=0, temps=None, seeds=None):
     return runs
 
 
-def run_pair(shape, blob, runs, cuts, compare_every=True, row_kernel=0, streams=0):
+def run_pair(shape, blob, runs, cuts, compare_every=True, row_kernel=0, streams=0, graph=True):
     pair = Pair(shape, blob, runs)
     assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
     assert B.fpi8_engine_set_streams(pair.model.engine, streams) == 0
+    assert B.fpi8_engine_set_graph(pair.model.engine, graph) == 0
     try:
         for k in cuts:
             pair.turn(k)
@@ -176,15 +177,16 @@ def test_row_kernels_whole_pass(n_runs, row_kernel):
     run_pair(shape, blob, runs, [1, 3], row_kernel=row_kernel)
 
 
-@pytest.mark.parametrize("streams,n_runs", [(2, 5), (2, 20), (1, 70)])
-def test_run_groups_on_two_streams(streams, n_runs):
+@pytest.mark.parametrize("streams,n_runs,graph", [(2, 5, True), (2, 20, True), (1, 70, True),
+                                                  (1, 20, False), (2, 20, False)])
+def test_run_groups_on_two_streams(streams, n_runs, graph):
     # The batch split in two groups, each advanced on its own stream, and a
     # wide batch on one stream.
     shape = W.SMALL_SHAPES["gqa"]
-    say(f"{n_runs} runs on {streams} stream(s)")
+    say(f"{n_runs} runs on {streams} stream(s), graph {graph}")
     blob = Bl.build_blob(shape, 25)
     runs = spec(shape, n_runs, [1 + (r % 6) for r in range(n_runs)], [1 + (r % 5) for r in range(n_runs)])
-    run_pair(shape, blob, runs, [1, 2, 4], streams=streams)
+    run_pair(shape, blob, runs, [1, 2, 4], streams=streams, graph=graph)
 
 
 def test_shared_kernel_exact_path():
@@ -197,20 +199,43 @@ def test_shared_kernel_exact_path():
 
 
 def test_long_context_attention():
-    # 3000 prompt ids: attention over thousands of cached positions.
+    # Attention over thousands of cached positions, with a shorter run
+    # beside the long one.
     shape = Shape(256, 512, 2, 2, 2, 300, 4096)
-    say("long context, 3000 ids")
+    say("long context 4096, 3000 ids")
     blob = Bl.build_blob(shape, 24)
     runs = [(W.prompt_ids(shape.vocab, 3000, 124, 0), 3, 0, 1),
             (W.prompt_ids(shape.vocab, 700, 124, 1), 2, 0, 2)]
     O.set_threads(16)
     try:
-        run_pair(shape, blob, runs, [1500, 10000], compare_every=False)
+        run_pair(shape, blob, runs, [1500, 100000], compare_every=False)
     finally:
         O.set_threads(1)
 
 
-@pytest.mark.parametrize("name", ["1.1B-shaped-d2048-L22", "7B-shaped-d4096-L32"])
+def test_full_context_score_buffer():
+    # A run whose cache spans the whole 8192-entry context (the long-context
+    # workload's): attention keeps 8192 scores in LDS, the largest buffer.
+    # The first 4003 positions (4000 prompt ids, 3 generated) are checked.
+    shape = Shape(128, 256, 1, 1, 1, 300, 8192)
+    say("full 8192 context")
+    blob = Bl.build_blob(shape, 26)
+    runs = [(W.prompt_ids(shape.vocab, 4000, 126, 0), 4193, 0, 1),
+            (W.prompt_ids(shape.vocab, 100, 126, 1), 3, 0, 2)]
+    O.set_threads(16)
+    pair = Pair(shape, blob, runs)
+    try:
+        pair.turn(2000)
+        pair.compare()
+        pair.turn(2003)
+        pair.compare()
+    finally:
+        pair.model.close()
+        O.set_threads(1)
+
+
+@pytest.mark.parametrize("name", ["1.1B-shaped-d2048-L22", "7B-shaped-d4096-L32",
+                                  "long-context-8k-d2048-L16"])
 def test_full_size_first_positions(name):
     # The model and batch width of the workload; prompts of 1 to 3 ids so
     # that the first positions generate (classifier and sampling at full
