@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <vector>
 
@@ -585,7 +586,7 @@ int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uin
   return 0;
 }
 
-// Workspace of the standalone row: a 256-byte flag word, then the digits.
+// Workspace of the standalone row: the overflow word (256 bytes kept), then the digits.
 uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
   (void)rows;
   const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
@@ -606,10 +607,21 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   uint8_t *base = reinterpret_cast<uint8_t *>(d_work);
   uint32_t *flag = reinterpret_cast<uint32_t *>(base);
   int8_t *planes = reinterpret_cast<int8_t *>(base + 256);
-  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, flag, s);
+  // Each call marks an overflow with its own number, so the flag word never
+  // needs clearing; a stale word that happens to match only sends the call
+  // down the exact path, which gives the same result.
+  static std::atomic<uint32_t> calls{0};
+  uint32_t seq = ++calls;
+  if (seq == 0) seq = ++calls;
+  // One or two inputs: plain digit rows, so the four lanes of a run read one
+  // whole 64-byte piece per block (the kernel whose waves split the
+  // contraction reads them); more: the fragment-major layout both kernels
+  // read, where the runs of a lane group share 16-byte pieces of one line.
+  const uint32_t compact = batch <= 2 ? 1u : 0u;
+  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, compact, flag, seq, s);
   if (r) return r;
   const bool aligned = cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0;
-  const RowPlan p = plan_rows(rows, cols, batch, false, aligned && cols % 128 == 0, 0);
+  const RowPlan p = plan_rows(rows, cols, batch, false, aligned && cols % 128 == 0, compact ? 1 : 0);
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
@@ -620,6 +632,8 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   a.n_runs = batch;
   a.in_sel = IN_RAW;
   a.oflag = flag;
+  a.oflag_seq = seq;
+  a.compact = compact;
   a.x_raw = d_x;
   a.y_raw = d_y;
   Seg &sg = a.seg[0];

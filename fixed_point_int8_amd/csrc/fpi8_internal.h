@@ -99,7 +99,9 @@ struct RowsArgs {
   uint32_t bp;              // planes per limb (multiple of 16)
   uint32_t n_runs;
   uint32_t in_sel;          // IN_* for the exact path
-  const uint32_t *oflag;    // nonzero: some input needs more than three limbs
+  const uint32_t *oflag;    // some input needs more than three limbs: *oflag != 0, or
+  uint32_t oflag_seq;       // when nonzero, *oflag == oflag_seq
+  uint32_t compact;         // 1: planes [3][bp][kp] plain row-major (kp-byte rows), 0: fragment-major
   // context
   uint8_t *states;          // state arena (turn) or nullptr (standalone)
   RunDesc *runs;
@@ -175,9 +177,12 @@ int launch_norm(const NormArgs &a, void *stream);
 int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_sample(const SampleArgs &a, void *stream);
+// Digits of x [n_runs][cols] into planes (compact or fragment-major); a
+// workgroup that meets a word needing more than three digits stores seq in
+// *oflag.  The word is never cleared: a call passes a seq of its own.
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
-                      uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream);
-int launch_zero_words(uint32_t *p, uint32_t n, void *stream);
+                      uint32_t kp, uint32_t bp, uint32_t compact, uint32_t *oflag, uint32_t seq,
+                      void *stream);
 size_t attention_lds_bytes(uint32_t max_npos, uint32_t head);
 int kernels_init(uint32_t max_npos, uint32_t head);
 

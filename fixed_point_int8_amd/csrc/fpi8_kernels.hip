@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "../../include/fpi8.h"
@@ -271,6 +272,14 @@ __device__ __forceinline__ bool fits32(int64_t v) { return v >= INT32_MIN && v <
 
 __device__ __forceinline__ void fail(RunDesc &rd, uint32_t layer, uint32_t phase) {
   atomicMin(&rd.errkey, (layer << 8) | phase);
+}
+
+// Whether some input word of the launch needs more than three digits, read
+// through the scalar cache so the check does not queue behind vector loads.
+__device__ __forceinline__ bool input_needs_exact(const RowsArgs &a) {
+  if (a.oflag == nullptr) return false;
+  const uint32_t f = *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag;
+  return a.oflag_seq ? f == a.oflag_seq : f != 0;
 }
 
 // The rows one wave finishes: 16 * MT rows in MT tiles of 16, from the
@@ -615,12 +624,15 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   const uint32_t live = a.n_runs > b0 ? a.n_runs - b0 : 0;
   const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
   const int8_t *dsrc[3][BT];
+  const uint32_t dstride = a.compact ? 64 : 1024;  // bytes from one 64-column block to the next
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t ie = bt * 16 + li < live ? li : 0;
 #pragma unroll
     for (int l = 0; l < 3; l++)
-      dsrc[l][bt] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
+      dsrc[l][bt] = a.compact
+          ? a.planes + ((uint64_t)l * a.bp + b0 + bt * 16 + ie) * a.kp + (uint64_t)k_lo * 64 + lg * 16
+          : a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
   }
   const uint8_t *wsrc[MT];
 #pragma unroll
@@ -635,7 +647,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
     for (int l = 0; l < 3; l++)
 #pragma unroll
       for (int bt = 0; bt < BT; bt++)
-        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * 1024);
+        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * dstride);
   };
   // Block k_lo + i into ring slot s: whole 16-byte pieces of aligned rows.
   // The scheduling fences keep each slot's loads together and in ring
@@ -689,8 +701,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 
   // The input needs more than three digits somewhere: exact path (a scalar
   // read, so it does not wait behind the loads above).
-  const bool exact =
-      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
+  const bool exact = input_needs_exact(a);
   if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
     wait_vm<0>();  // no table load may still be landing in LDS
     return;
@@ -820,8 +831,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
   EpiIn<EPI, MT, BT> in;
   epi_begin<EPI, MT, BT>(a, b0, li, in);
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
-  const bool exact =
-      a.oflag != nullptr && *(const __attribute__((address_space(4))) uint32_t *)(uintptr_t)a.oflag != 0;
+  const bool exact = input_needs_exact(a);
   if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
     wait_vm<0>();  // no table load may still be landing in LDS
     return;
@@ -952,17 +962,21 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
 }
 
 // Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
-__global__ void k_zero_words(uint32_t *p, uint32_t n) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
-__global__ void k_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
-                             uint32_t kp, uint32_t bp, uint32_t *oflag) {
-  const uint32_t b = blockIdx.y;
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= n_runs || i >= cols) return;
-  put_digits(planes, bp, kp, b, i, x[(uint64_t)b * cols + i], oflag);
+__global__ __launch_bounds__(256) void k_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols,
+                                                    int8_t *planes, uint32_t kp, uint32_t bp,
+                                                    uint32_t compact, uint32_t *oflag, uint32_t seq) {
+  const uint32_t b = blockIdx.y, k = blockIdx.x * blockDim.x + threadIdx.x;
+  bool over = false;
+  if (b < n_runs && k < cols) {
+    int8_t d0, d1, d2;
+    over = !digits3(x[(uint64_t)b * cols + k], d0, d1, d2);
+    const uint64_t limb = (uint64_t)bp * kp;
+    const uint64_t at = compact ? (uint64_t)b * kp + k : digit_at(b, k, kp);
+    planes[at] = d0;
+    planes[limb + at] = d1;
+    planes[2 * limb + at] = d2;
+  }
+  if (__syncthreads_or(over ? 1 : 0) && threadIdx.x == 0) atomicExch(oflag, seq);
 }
 
 // ---------------------------------------------------------------------------
@@ -1414,18 +1428,12 @@ int launch_sample(const SampleArgs &a, void *stream) {
   return ok(hipGetLastError());
 }
 
-int launch_zero_words(uint32_t *p, uint32_t n, void *stream) {
-  if (n == 0) return 0;
-  hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, p, n);
-  return ok(hipGetLastError());
-}
 
 int launch_digits_raw(const int64_t *x, uint32_t n_runs, uint32_t cols, int8_t *planes,
-                      uint32_t kp, uint32_t bp, uint32_t *oflag, void *stream) {
-  hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(1), 0, s, oflag, 1u);
-  hipLaunchKernelGGL(k_digits_raw, dim3((cols + 255) / 256, n_runs), dim3(256), 0, s, x, n_runs,
-                     cols, planes, kp, bp, oflag);
+                      uint32_t kp, uint32_t bp, uint32_t compact, uint32_t *oflag, uint32_t seq,
+                      void *stream) {
+  hipLaunchKernelGGL(k_digits_raw, dim3((cols + 255) / 256, n_runs), dim3(256), 0, (hipStream_t)stream,
+                     x, n_runs, cols, planes, kp, bp, compact, oflag, seq);
   return ok(hipGetLastError());
 }
 

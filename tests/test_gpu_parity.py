@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 # ---------------------------------------------------------------------------
 # The matrix row, standalone
 
-def gpu_rows(Wm, s, x):
+def gpu_rows(Wm, s, x, work=None):
     torch = require_gpu()
     rows, cols = Wm.shape
     batch = x.shape[0]
@@ -32,7 +32,7 @@ def gpu_rows(Wm, s, x):
     dX = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     dY = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
     n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
-    dWk = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dWk = work if work is not None else torch.zeros(n, dtype=torch.uint8, device="cuda")
     e = B.fpi8_matrix_rows(dW, dS, rows, cols, dX, batch, dY, dWk, n)
     assert e == 0
     torch.cuda.synchronize()
@@ -68,6 +68,21 @@ def test_matrix_rows_three_digit_edges():
     assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
     x2 = np.resize(edge[:2], (4, 128)).astype(np.int64)
     assert np.array_equal(gpu_rows(Wm, s, x2), O.rows(Wm, s, x2))
+
+
+@pytest.mark.parametrize("batch", [3, 40])
+def test_matrix_rows_reused_workspace(batch):
+    # One workspace (filled with 0xFF, not zeros) across calls whose inputs
+    # alternately need and do not need the exact path: the overflow mark of
+    # one call must not leak into the next.
+    torch = require_gpu()
+    rows, cols = 48, 320
+    Wm, s, x = W.row_operands(rows, cols, batch, 31)
+    xa = W.adversarial_row_inputs(batch, cols, 32)
+    n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
+    work = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    for xi in (x, xa, x, x, xa, xa, x):
+        assert np.array_equal(gpu_rows(Wm, s, xi, work), O.rows(Wm, s, xi))
 
 
 @pytest.mark.parametrize("batch", W.ROW_SWEEP_BATCHES)
