@@ -21,6 +21,7 @@ enum { T_ROWS = 0, T_ATTN = 1, T_NORM = 2, T_SAMPLE = 3, T_EMBED = 4 };
 
 struct Mat {
   const uint8_t *W = nullptr;
+  const uint8_t *P = nullptr;  // packed tiles (engine workspace), all but the embedding
   const uint32_t *S = nullptr;
   uint32_t rows = 0, cols = 0;
   bool vec = false;
@@ -47,6 +48,7 @@ struct fpi8_engine {
   std::vector<Mat> mats;  // [0] embedding, [1 + 7l + kind - 1], [1 + 7L] classifier
   // device workspace
   RunDesc *d_runs = nullptr;
+  uint8_t *d_packed = nullptr;  // every matrix but the embedding, in MFMA operand tiles
   int8_t *d_planes0 = nullptr, *d_planes1 = nullptr;  // per run group: [2][3][bp][kp]
   uint32_t *d_oflags = nullptr;                        // per run group: [2][n_oflags]
   uint32_t n_oflags = 0;
@@ -195,7 +197,8 @@ RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t col
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
-  a.kblocks = (cols + 63) / 64;
+  a.kblocks = ((cols + 63) / 64 + 1) / 2 * 2;  // the packed tiles' blocks per row tile
+  a.packed = 1;
   a.planes = planes;
   a.kp = e->kp;
   a.bp = e->bp;
@@ -222,6 +225,7 @@ void add_seg(RowsArgs &a, const Mat &m, uint32_t role) {
   s.rows = m.rows;
   s.role = role;
   s.pad = m.vec ? 1u : 0u;
+  s.P = m.P;
 }
 
 // Plans the launch over the segments added so far and runs it.
@@ -231,6 +235,7 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   for (uint32_t i = 0; i < a.nseg; i++) rows += a.seg[i].rows;
   bool shared_ok = a.cols % 128 == 0;
   for (uint32_t i = 0; i < a.nseg; i++) shared_ok = shared_ok && a.seg[i].pad != 0;
+  shared_ok = shared_ok || a.packed != 0;
   const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup, shared_ok,
                               e->row_kind);
   const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * (p.kind ? 4 : 1);
@@ -393,6 +398,7 @@ void release(fpi8_engine *e) {
   if (e->ev_fork) (void)hipEventDestroy(e->ev_fork);
   if (e->ev_join) (void)hipEventDestroy(e->ev_join);
   (void)hipFree(e->d_runs);
+  (void)hipFree(e->d_packed);
   (void)hipFree(e->d_planes0);
   (void)hipFree(e->d_planes1);
   (void)hipFree(e->d_oflags);
@@ -443,7 +449,7 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
   }
   // Workspace: digit planes [3][bp][kp] twice, run descriptors, flags.
   e->bp = round_up(max_runs, 64);
-  e->kp = round_up(std::max(c.dim, c.hidden), 64);
+  e->kp = round_up(std::max(c.dim, c.hidden), 128);
   e->n_oflags = 4 * c.layers + 1;
   const size_t planes = 3ull * e->bp * e->kp;
   if ((r = hip_ok(hipMalloc(&e->d_runs, sizeof(RunDesc) * max_runs))) ||
@@ -461,6 +467,28 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
       (r = hip_ok(hipEventCreateWithFlags(&e->ev_fork, hipEventDisableTiming))) ||
       (r = hip_ok(hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming))) ||
       (r = kernels_init(e->max_npos, c.head))) {
+    release(e);
+    return r;
+  }
+  // The matrices (all but the embedding, which is read one row at a time)
+  // packed once into the tiles the row kernels load whole.
+  uint64_t total = 0;
+  for (size_t i = 1; i < e->mats.size(); i++) total += packed_bytes(e->mats[i].rows, e->mats[i].cols);
+  if ((r = hip_ok(hipMalloc(&e->d_packed, total)))) {
+    release(e);
+    return r;
+  }
+  uint64_t at = 0;
+  for (size_t i = 1; i < e->mats.size(); i++) {
+    Mat &m = e->mats[i];
+    m.P = e->d_packed + at;
+    if ((r = launch_pack(m.W, m.rows, m.cols, e->d_packed + at, nullptr))) {
+      release(e);
+      return r;
+    }
+    at += packed_bytes(m.rows, m.cols);
+  }
+  if ((r = hip_ok(hipDeviceSynchronize()))) {
     release(e);
     return r;
   }

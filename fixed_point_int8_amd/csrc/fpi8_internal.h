@@ -73,6 +73,7 @@ enum : uint32_t { RUN_ACTIVE = 1u, RUN_GEN = 2u };
 // Rows of one matrix inside a row-kernel launch.
 struct Seg {
   const uint8_t *W;      // rows x cols weight bytes (weight + 128), row-major
+  const uint8_t *P;      // the same bytes packed in 16 x 64 tiles (see launch_pack), or nullptr
   const uint32_t *S;     // rows Q24 scales
   uint32_t rows;
   uint32_t tile0;        // first row tile of this matrix in the launch
@@ -102,6 +103,7 @@ struct RowsArgs {
   const uint32_t *oflag;    // some input needs more than three limbs: *oflag != 0, or
   uint32_t oflag_seq;       // when nonzero, *oflag == oflag_seq
   uint32_t compact;         // 1: planes [3][bp][kp] plain row-major (kp-byte rows), 0: fragment-major
+  uint32_t packed;          // 1: the fast path reads every segment's packed tiles (kblocks even)
   // context
   uint8_t *states;          // state arena (turn) or nullptr (standalone)
   RunDesc *runs;
@@ -176,6 +178,14 @@ int launch_norm(const NormArgs &a, void *stream);
 // (columns a multiple of 128, 16-byte aligned rows).
 int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
+// Packs a rows x cols byte matrix into tiles of 16 rows x 64 columns, tile
+// (rt, kb) at ((rt * kbp + kb) * 1024), inside it lane l = 16 g + i at
+// 16 l holding row 16 rt + i, columns 64 kb + 16 g .. + 15 (the layout of
+// one MFMA operand); kbp = ceil(cols / 64) rounded up to even.  Bytes
+// outside the matrix are 0x80 (the weight 0).  P holds
+// ceil(rows / 16) * kbp * 1024 bytes.
+int launch_pack(const uint8_t *W, uint32_t rows, uint32_t cols, uint8_t *P, void *stream);
+uint64_t packed_bytes(uint32_t rows, uint32_t cols);
 int launch_sample(const SampleArgs &a, void *stream);
 // Digits of x [n_runs][cols] into planes (compact or fragment-major); a
 // workgroup that meets a word needing more than three digits stores seq in

@@ -292,6 +292,7 @@ template <int MT>
 struct RowTile {
   uint32_t si;
   const uint8_t *Wp[MT];
+  const uint8_t *Pp[MT];
   uint32_t rbase[MT], rcount[MT];
   bool vecw[MT];
   uint32_t sc[MT][4];
@@ -309,6 +310,7 @@ __device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t tile, uint3
   for (int mt = 0; mt < MT; mt++) {
     const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[t.si];
     t.Wp[mt] = sg.W;
+    t.Pp[mt] = sg.P;
     t.rcount[mt] = sg.rows;
     t.vecw[mt] = sg.pad != 0;
     t.rbase[mt] = EPI == EPI_GATEUP ? unit * 16 * HALF + 16 * (mt % HALF)
@@ -634,11 +636,16 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
           ? a.planes + ((uint64_t)l * a.bp + b0 + bt * 16 + ie) * a.kp + (uint64_t)k_lo * 64 + lg * 16
           : a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + k_lo) * 64 + lg * 16 + ie) * 16;
   }
+  // Weights: the packed 1 KB tiles (whole cache lines per load), or the
+  // rows themselves (rows past the end of a segment re-read its last row).
   const uint8_t *wsrc[MT];
+  const uint32_t wstride = a.packed ? 1024 : 64;  // bytes from one 64-column block to the next
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
     const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
-    wsrc[mt] = t.Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
+    wsrc[mt] = a.packed
+        ? t.Pp[mt] + ((uint64_t)(t.rbase[mt] / 16) * a.kblocks + k_lo) * 1024 + lane * 16
+        : t.Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
   }
 
   v4i Wr[P][MT], Dr[P][3][BT];
@@ -655,7 +662,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   auto load = [&](int s, uint32_t i) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) Wr[s][mt] = *reinterpret_cast<const v4i *>(wsrc[mt] + (uint64_t)i * 64);
+    for (int mt = 0; mt < MT; mt++) Wr[s][mt] = *reinterpret_cast<const v4i *>(wsrc[mt] + (uint64_t)i * wstride);
     load_digits(s, i);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -686,11 +693,12 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 
   // Whole 64-column blocks of this wave, then (for the wave that owns it)
   // the partial block at the end of the rows.
-  const uint32_t nfull = a.cols / 64;
+  const uint32_t nfull = a.packed ? nkb : a.cols / 64;
   const uint32_t n_main = k_lo >= nfull ? 0 : (k_lo + n < nfull ? n : nfull - k_lo);
   bool fast = true;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) fast = fast && t.vecw[mt];
+  fast = fast || a.packed != 0;
   // The ring's first P blocks go out before anything waits.
   const uint32_t last = n_main ? n_main - 1 : 0;
   if (fast && n_main > 0) {
@@ -785,8 +793,9 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 // global-to-LDS loads (a quarter of the fragments each), P stages ahead,
 // and every wave streams its own weight rows into a register ring of the
 // same depth; one barrier per stage.  The digits then cross L2 once per
-// 64 * MT rows rather than once per 16 * MT.  For matrices whose rows are
-// 16-byte aligned and whose column count is a multiple of 64 * CD.
+// 64 * MT rows rather than once per 16 * MT.  For packed matrices (kblocks
+// even), or rows that are 16-byte aligned with a column count that is a
+// multiple of 64 * CD.
 template <int BT>
 struct SharedGeom {
   static constexpr int CD = 2;                 // 64-column blocks per stage
@@ -853,10 +862,12 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
     const uint32_t nch = a.kblocks / CD;
     const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
     const uint8_t *wsrc[MT];
+    const uint32_t wstride = a.packed ? 1024 : 64;  // bytes from one 64-column block to the next
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
       const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
-      wsrc[mt] = t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
+      wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)(t.rbase[mt] / 16) * a.kblocks * 1024 + lane * 16
+                          : t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
     }
     // This wave stages fragments f = wave + 4q of every stage; fragment f
     // is (limb l, run tile bt, block c).  Runs past the batch bring
@@ -884,7 +895,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int c = 0; c < CD; c++)
-          Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * 64);
+          Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * wstride);
 #pragma unroll
       for (int q = 0; q < FW; q++)
         __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
@@ -959,6 +970,31 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
     lds_barrier();  // every wave's share of the SiLU table has landed
   }
   rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
+}
+
+// Packing of a weight matrix into MFMA operand tiles (see launch_pack): one
+// thread per 16-byte piece of a tile.
+__global__ __launch_bounds__(256) void k_pack(const uint8_t *W, uint32_t rows, uint32_t cols,
+                                              uint32_t kbp, uint8_t *P, uint64_t pieces) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pieces) return;
+  const uint32_t lane = (uint32_t)(i % 64);
+  const uint64_t tile = i / 64;
+  const uint32_t kb = (uint32_t)(tile % kbp), rt = (uint32_t)(tile / kbp);
+  const uint32_t row = rt * 16 + lane % 16, c0 = kb * 64 + (lane / 16) * 16;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const uint32_t c = c0 + 4 * q + e;
+      const uint32_t byte = row < rows && c < cols ? W[(uint64_t)row * cols + c] : 0x80u;
+      v |= byte << (8 * e);
+    }
+    w[q] = v;
+  }
+  *reinterpret_cast<v4i *>(P + i * 16) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
 }
 
 // Digits of a plain i64 matrix [n_runs][cols] (standalone matrix rows).
@@ -1404,6 +1440,19 @@ int kernels_init(uint32_t max_npos, uint32_t head) {
     default: e = hipFuncSetAttribute((const void *)k_attention<0>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); break;
   }
   return ok(e);
+}
+
+uint64_t packed_bytes(uint32_t rows, uint32_t cols) {
+  const uint64_t kbp = ((cols + 63) / 64 + 1) / 2 * 2;
+  return (uint64_t)((rows + 15) / 16) * kbp * 1024;
+}
+
+int launch_pack(const uint8_t *W, uint32_t rows, uint32_t cols, uint8_t *P, void *stream) {
+  const uint32_t kbp = (uint32_t)(((cols + 63) / 64 + 1) / 2 * 2);
+  const uint64_t pieces = packed_bytes(rows, cols) / 16;
+  hipLaunchKernelGGL(k_pack, dim3((uint32_t)((pieces + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     W, rows, cols, kbp, P, pieces);
+  return ok(hipGetLastError());
 }
 
 int launch_attention(const AttnArgs &a, void *stream) {

@@ -122,7 +122,9 @@ typedef struct fpi8_engine fpi8_engine;
  * the whole artifact on the device, blob_len its length; max_runs bounds the
  * runs of one turn.  Errors 1, 2, 5; 101 when the context is too long for
  * the attention kernel's on-chip score buffer; 100 on a HIP failure. The
- * engine allocates its own workspace here, once. */
+ * engine allocates its own workspace here, once, with a copy of every
+ * matrix but the embedding repacked into the tiles its matrix-row kernels
+ * load (about the artifact's size in device memory). */
 int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len,
                            const uint8_t *d_blob, uint64_t blob_len, uint32_t max_runs,
                            fpi8_engine **out);
