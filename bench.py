@@ -59,9 +59,13 @@ def attention_bytes(shape, batch, npos):
 
 
 def row_sweep(torch, reps=3):
-    """GB/s of the standalone matrix row over a pool of 48 distinct
-    4096 x 4096 matrices (805 MB, over three times the 256 MB last-level
-    cache), one launch per matrix, timed with events on the launch stream."""
+    """The standalone matrix row over a pool of 48 distinct 4096 x 4096
+    matrices (805 MB, over three times the 256 MB last-level cache), one call
+    per matrix, timed with events on the launch stream: once with the
+    matrices packed beforehand (fpi8_matrix_pack, outside the timed region:
+    weights are prepared once and used many times), once row-major
+    (fpi8_matrix_rows).  A call converts the inputs to digits and runs the
+    row kernel."""
     from fixed_point_int8_amd import binding as B
     rows = cols = 4096
     pool = 48
@@ -69,6 +73,10 @@ def row_sweep(torch, reps=3):
     g.manual_seed(7)
     W = torch.randint(0, 256, (pool, rows, cols), dtype=torch.uint8, device="cuda", generator=g)
     S = torch.randint(1 << 14, 1 << 18, (pool, rows), dtype=torch.int32, device="cuda", generator=g)
+    n_p = B.fpi8_matrix_packed_size(rows, cols)
+    Pk = torch.empty((pool, n_p), dtype=torch.uint8, device="cuda")
+    for i in range(pool):
+        assert B.fpi8_matrix_pack(W[i], rows, cols, Pk[i], n_p) == 0
     out = {}
     stream = torch.cuda.current_stream()
     for batch in (1, 8, 32, 128):
@@ -76,24 +84,32 @@ def row_sweep(torch, reps=3):
         y = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
         n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
         work = torch.zeros(n, dtype=torch.uint8, device="cuda")
-        for i in range(pool):  # warm-up
-            assert B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y, work, n, stream) == 0
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for r in range(reps):
-            for i in range(pool):
-                B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y, work, n, stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / (reps * pool)
         alg = rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
+        res = {}
+        for name, call in (("packed", lambda i: B.fpi8_matrix_rows_packed(Pk[i], S[i], rows, cols, x, batch, y,
+                                                                          work, n, stream)),
+                           ("row_major", lambda i: B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y,
+                                                                      work, n, stream))):
+            for i in range(pool):  # warm-up
+                assert call(i) == 0
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for r in range(reps):
+                for i in range(pool):
+                    call(i)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = t0.elapsed_time(t1) / (reps * pool)
+        ms = res["packed"]
         out[str(batch)] = {"us_per_call": round(ms * 1e3, 3), "GB/s": round(alg / ms / 1e6, 1),
                            "frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
-                           "weight_GB/s": round(rows * cols / ms / 1e6, 1)}
+                           "weight_GB/s": round(rows * cols / ms / 1e6, 1),
+                           "row_major_us_per_call": round(res["row_major"] * 1e3, 3),
+                           "row_major_GB/s": round(alg / res["row_major"] / 1e6, 1)}
         del x, y, work
-    del W, S
+    del W, S, Pk
     torch.cuda.empty_cache()
     return out
 

@@ -32,7 +32,8 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
-           "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows")
+           "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
+           "fpi8_matrix_pack", "fpi8_matrix_rows_packed")
 
 
 class fpi8_info(C.Structure):
@@ -76,6 +77,10 @@ def lib():
             "fpi8_matrix_rows_workspace_size": (C.c_uint64, [C.c_uint32, C.c_uint32, C.c_uint32]),
             "fpi8_matrix_rows": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32, _P,
                                              _P, C.c_uint64, _P]),
+            "fpi8_matrix_packed_size": (C.c_uint64, [C.c_uint32, C.c_uint32]),
+            "fpi8_matrix_pack": (C.c_int32, [_P, C.c_uint32, C.c_uint32, _P, C.c_uint64, _P]),
+            "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
+                                                    _P, _P, C.c_uint64, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -205,3 +210,18 @@ def fpi8_matrix_rows(d_W, d_scale, rows: int, cols: int, d_x, batch: int, d_y, d
     return lib().fpi8_matrix_rows(_dev_ptr(d_W), _dev_ptr(d_scale), rows, cols, _dev_ptr(d_x),
                                   batch, _dev_ptr(d_y), _dev_ptr(d_work), work_len,
                                   _stream_ptr(stream))
+
+
+def fpi8_matrix_packed_size(rows: int, cols: int) -> int:
+    return lib().fpi8_matrix_packed_size(rows, cols)
+
+
+def fpi8_matrix_pack(d_W, rows: int, cols: int, d_P, p_len: int, stream=None) -> int:
+    return lib().fpi8_matrix_pack(_dev_ptr(d_W), rows, cols, _dev_ptr(d_P), p_len, _stream_ptr(stream))
+
+
+def fpi8_matrix_rows_packed(d_P, d_scale, rows: int, cols: int, d_x, batch: int, d_y, d_work,
+                            work_len: int, stream=None) -> int:
+    return lib().fpi8_matrix_rows_packed(_dev_ptr(d_P), _dev_ptr(d_scale), rows, cols, _dev_ptr(d_x),
+                                         batch, _dev_ptr(d_y), _dev_ptr(d_work), work_len,
+                                         _stream_ptr(stream))

@@ -617,21 +617,38 @@ int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uin
 // Workspace of the standalone row: the overflow word (256 bytes kept), then the digits.
 uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
   (void)rows;
-  const uint64_t kp = round_up(cols, 64), bp = round_up(batch, 64);
+  const uint64_t kp = round_up(cols, 128), bp = round_up(batch, 64);
   return 256 + 3 * bp * kp;
 }
 
-int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
-                         uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
-                         void *d_work, uint64_t work_len, void *stream) {
-  if (!d_W || !d_scale || !d_x || !d_y || !d_work || rows == 0 || cols == 0 || batch == 0 ||
-      cols > 65536 || batch > 65536)
+uint64_t fpi8_matrix_packed_size(uint32_t rows, uint32_t cols) {
+  if (rows == 0 || cols == 0 || cols > 65536) return UINT64_MAX;
+  return packed_bytes(rows, cols);
+}
+
+int32_t fpi8_matrix_pack(const uint8_t *d_W, uint32_t rows, uint32_t cols, uint8_t *d_P,
+                         uint64_t p_len, void *stream) {
+  if (!d_W || !d_P || rows == 0 || cols == 0 || cols > 65536 || p_len < packed_bytes(rows, cols))
+    return FPI8_ERR_ARGUMENT;
+  return launch_pack(d_W, rows, cols, d_P, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The standalone row over row-major weights (d_W) or packed tiles (d_P).
+int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
+                uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y, void *d_work,
+                uint64_t work_len, void *stream) {
+  if ((!d_W && !d_P) || !d_scale || !d_x || !d_y || !d_work || rows == 0 || cols == 0 ||
+      batch == 0 || cols > 65536 || batch > 65536)
     return FPI8_ERR_ARGUMENT;
   if (work_len < fpi8_matrix_rows_workspace_size(rows, cols, batch) ||
-      (reinterpret_cast<uintptr_t>(d_work) & 255) != 0)
+      (reinterpret_cast<uintptr_t>(d_work) & 255) != 0 || (reinterpret_cast<uintptr_t>(d_P) & 15) != 0)
     return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
-  const uint32_t kp = round_up(cols, 64), bp = round_up(batch, 64);
+  const uint32_t kp = round_up(cols, 128), bp = round_up(batch, 64);
   uint8_t *base = reinterpret_cast<uint8_t *>(d_work);
   uint32_t *flag = reinterpret_cast<uint32_t *>(base);
   int8_t *planes = reinterpret_cast<int8_t *>(base + 256);
@@ -648,12 +665,15 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   const uint32_t compact = batch <= 2 ? 1u : 0u;
   int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, compact, flag, seq, s);
   if (r) return r;
+  const bool packed = d_P != nullptr;
   const bool aligned = cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0;
-  const RowPlan p = plan_rows(rows, cols, batch, false, aligned && cols % 128 == 0, compact ? 1 : 0);
+  const bool shared_ok = packed || (aligned && cols % 128 == 0);
+  const RowPlan p = plan_rows(rows, cols, batch, false, shared_ok, compact ? 1 : 0);
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
-  a.kblocks = (cols + 63) / 64;
+  a.kblocks = packed ? ((cols + 63) / 64 + 1) / 2 * 2 : (cols + 63) / 64;
+  a.packed = packed ? 1u : 0u;
   a.planes = planes;
   a.kp = kp;
   a.bp = bp;
@@ -665,16 +685,35 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
   a.x_raw = d_x;
   a.y_raw = d_y;
   Seg &sg = a.seg[0];
-  sg.W = d_W;
+  sg.W = packed ? nullptr : d_W;
+  sg.P = d_P;
   sg.S = d_scale;
   sg.rows = rows;
   sg.tile0 = 0;
   sg.role = ROLE_PLAIN;
-  sg.pad = (cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0) ? 1u : 0u;
+  sg.pad = packed || aligned ? 1u : 0u;
   a.nseg = 1;
   a.ntiles = p.tiles;
   a.chunks = p.chunks;
   return launch_rows(EPI_RAW, p.kind, p.mt, p.bt, a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
+                         uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
+                         void *d_work, uint64_t work_len, void *stream) {
+  if (!d_W) return FPI8_ERR_ARGUMENT;
+  return matrix_rows(d_W, nullptr, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream);
+}
+
+int32_t fpi8_matrix_rows_packed(const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
+                                uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
+                                void *d_work, uint64_t work_len, void *stream) {
+  if (!d_P) return FPI8_ERR_ARGUMENT;
+  return matrix_rows(nullptr, d_P, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream);
 }
 
 }  // extern "C"

@@ -341,8 +341,18 @@ __device__ __forceinline__ void rows_exact(const RowsArgs &a, const RowTile<MT> 
         const uint32_t row = t.rbase[mt] + 4 * lg + j;
         int64_t s = 0;
         if (ok && row < t.rcount[mt]) {
-          const uint8_t *w = t.Wp[mt] + (uint64_t)row * a.cols;
-          for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+          if (t.Wp[mt] != nullptr) {
+            const uint8_t *w = t.Wp[mt] + (uint64_t)row * a.cols;
+            for (uint32_t k = c_lo; k < c_hi; k++) s = wadd(s, wmul((int64_t)w[k] - 128, x[k]));
+          } else {
+            // only the packed tiles (standalone call): byte (row, k) of tile
+            // (row / 16, k / 64), lane 16 ((k % 64) / 16) + row % 16
+            const uint8_t *P = t.Pp[mt] + (uint64_t)(row / 16) * a.kblocks * 1024 + (row % 16) * 16;
+            for (uint32_t k = c_lo; k < c_hi; k++) {
+              const uint8_t wb = P[(uint64_t)(k / 64) * 1024 + ((k % 64) / 16) * 256 + k % 16];
+              s = wadd(s, wmul((int64_t)wb - 128, x[k]));
+            }
+          }
         }
         v[mt][bt][j] = s;
       }

@@ -188,6 +188,21 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
                          uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                          void *d_work, uint64_t work_len, void *stream);
 
+/* The same matrix prepared once for many calls: its bytes packed into tiles
+ * of 16 rows x 64 columns (bytes past the last row or column are 128, the
+ * weight 0), the operand layout the matrix cores read, so that every load of
+ * the row kernel fetches whole cache lines.  fpi8_matrix_packed_size gives
+ * the bytes of the packed copy (UINT64_MAX for sizes out of range);
+ * fpi8_matrix_pack writes it from d_W into d_P (device, 16-byte aligned);
+ * fpi8_matrix_rows_packed is fpi8_matrix_rows reading d_P instead of d_W,
+ * with the same result, workspace and errors. */
+uint64_t fpi8_matrix_packed_size(uint32_t rows, uint32_t cols);
+int32_t fpi8_matrix_pack(const uint8_t *d_W, uint32_t rows, uint32_t cols, uint8_t *d_P,
+                         uint64_t p_len, void *stream);
+int32_t fpi8_matrix_rows_packed(const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
+                                uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
+                                void *d_work, uint64_t work_len, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,40 @@ pytestmark = pytest.mark.gpu
 # ---------------------------------------------------------------------------
 # The matrix row, standalone
 
+def gpu_rows_packed(Wm, s, x):
+    torch = require_gpu()
+    rows, cols = Wm.shape
+    batch = x.shape[0]
+    dW = torch.from_numpy(np.ascontiguousarray(Wm)).cuda()
+    n_p = B.fpi8_matrix_packed_size(rows, cols)
+    dP = torch.empty(n_p, dtype=torch.uint8, device="cuda")
+    assert B.fpi8_matrix_pack(dW, rows, cols, dP, n_p) == 0
+    del dW  # the packed copy alone serves the calls
+    dS = torch.from_numpy(np.ascontiguousarray(s).view(np.int32)).cuda()
+    dX = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    dY = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
+    n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
+    dWk = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    assert B.fpi8_matrix_rows_packed(dP, dS, rows, cols, dX, batch, dY, dWk, n) == 0
+    torch.cuda.synchronize()
+    return dY.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,batch", [
+    (1, 1, 1), (37, 172, 3), (100, 300, 17), (129, 4096, 64), (33, 64, 128), (48, 11008, 8),
+    (200, 2048, 65), (4096, 4096, 128)])
+def test_matrix_rows_packed(rows, cols, batch):
+    say(f"matrix_rows_packed {rows}x{cols} batch {batch}")
+    Wm, s, x = W.row_operands(rows, cols, batch, rows * 1000 + cols + batch + 5)
+    assert np.array_equal(gpu_rows_packed(Wm, s, x), O.rows(Wm, s, x))
+
+
+def test_matrix_rows_packed_exact_path():
+    Wm, s, _ = W.row_operands(40, 200, 5, 9)
+    x = W.adversarial_row_inputs(5, 200, 10)
+    assert np.array_equal(gpu_rows_packed(Wm, s, x), O.rows(Wm, s, x))
+
+
 def gpu_rows(Wm, s, x, work=None):
     torch = require_gpu()
     rows, cols = Wm.shape
