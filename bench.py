@@ -58,6 +58,27 @@ def attention_bytes(shape, batch, npos):
     return batch * (shape.kv_heads * npos * shape.head_size * 4 * 2 + shape.dim * 8 * 2)
 
 
+def measured_traffic(kernel, workload, positions):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
+    None when there are none for these launches or the kernel's source has
+    changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}-7B-decode-b64.traffic.json")
+    if workload != "7B-shaped-d4096-L32" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = open(os.path.join(ROOT, "fixed_point_int8_amd", "csrc", "fpi8_kernels.hip")).read()
+    a = src.find("// Phase 9, one workgroup per (run, head)")
+    b = src.find("// Phase 19 and the end of a position")
+    if a < 0 or b < 0 or hashlib.sha256(src[a:b].encode()).hexdigest() != t["source_sha256"]:
+        return None
+    if t["positions"] != positions:
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
 def row_sweep(torch, reps=3):
     """The standalone matrix row over a pool of 48 distinct 4096 x 4096
     matrices (805 MB, over three times the 256 MB last-level cache), one call
@@ -239,9 +260,11 @@ def main():
     }
     dom = "attention" if attn_ms > rows_ms else "rows"
     ach = kern[dom]["GB/s"]
-    roofline = {"kernel": "k_attention" if dom == "attention" else "k_rows", "bound": "hbm",
+    kname = "k_attention" if dom == "attention" else "k_rows"
+    roofline = {"kernel": kname, "bound": "hbm",
                 "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kname, w.name, [pos1, pos1 + ks - 1])}
 
     model.close()
     del batch, model

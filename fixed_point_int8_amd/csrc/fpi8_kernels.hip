@@ -1028,7 +1028,8 @@ __global__ __launch_bounds__(256) void k_digits_raw(const int64_t *x, uint32_t n
 // ---------------------------------------------------------------------------
 // Phase 9, one workgroup per (run, head) ("Attention, stage by stage").
 // Scores, exponentials and probabilities of the head's positions stay in
-// LDS with the exponential table.
+// LDS (one 64-bit slot per cached position); the exponential table is read
+// from L2, where its 16 KB stay hot.
 
 template <int HS>
 __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
