@@ -115,10 +115,10 @@ struct TimedLaunch {
 
 // Launch shape of one row-kernel call.  kind 0: 16 * mt rows and 16 * bt
 // runs per workgroup of four waves, which split the contraction; kind 1:
-// 4 * 16 * mt rows (16 * mt per wave) sharing their runs' digits through
-// LDS.
+// wr * 16 * mt rows (16 * mt for each of wr waves) and 16 * bt runs per
+// workgroup of four waves that share their runs' digits through LDS.
 struct RowPlan {
-  int kind, mt, bt;
+  int kind, mt, bt, wr;
   uint32_t chunks, tiles;
 };
 
@@ -136,27 +136,27 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
                   int force) {
   // rate: GB/s one compute unit draws for the shape; occ: workgroups of the
   // shape that fit on one compute unit (registers, LDS).
-  struct Cand { int kind, mt, bt; double gbs; int occ; };
-  static const Cand plain[] = {{0, 1, 1, 26, 1}, {0, 1, 2, 44, 2}, {0, 1, 4, 46, 1},
-                               {0, 2, 2, 37, 1}, {0, 2, 4, 42, 1}, {0, 4, 2, 28, 1},
-                               {1, 1, 2, 36, 2}, {1, 1, 4, 30, 1}, {1, 2, 2, 29, 2},
-                               {1, 2, 4, 24, 1}};
-  static const Cand pairs[] = {{0, 2, 2, 37, 1}, {0, 2, 4, 42, 1}, {0, 4, 2, 28, 1},
-                               {1, 2, 2, 29, 2}, {1, 2, 4, 24, 1}};
+  struct Cand { int kind, mt, bt, wr; double gbs; int occ; };
+  static const Cand plain[] = {{0, 1, 1, 1, 26, 1}, {0, 1, 2, 1, 44, 2}, {0, 1, 4, 1, 46, 1},
+                               {0, 2, 2, 1, 37, 1}, {0, 2, 4, 1, 42, 1}, {0, 4, 2, 1, 28, 1},
+                               {1, 1, 2, 4, 36, 2}, {1, 1, 4, 4, 30, 1}, {1, 2, 2, 4, 34, 2},
+                               {1, 2, 4, 4, 26, 1}, {1, 2, 2, 3, 33, 2}, {1, 2, 4, 3, 24, 1}};
+  static const Cand pairs[] = {{0, 2, 2, 1, 37, 1}, {0, 2, 4, 1, 42, 1}, {0, 4, 2, 1, 28, 1},
+                               {1, 2, 2, 4, 34, 2}, {1, 2, 4, 4, 26, 1}, {1, 2, 2, 3, 33, 2},
+                               {1, 2, 4, 3, 24, 1}};
   const Cand *cand = gateup ? pairs : plain;
-  const int n = gateup ? 5 : 10;
+  const int n = gateup ? 7 : 12;
   const double cus = 256, hbm_cu = 20e9;
-  RowPlan best{0, 1, 1, 1, 1};
+  RowPlan best{0, 1, 1, 1, 1, 1};
   double best_t = 1e30;
   for (int i = 0; i < n; i++) {
     const int kind = cand[i].kind;
     if (kind == 1 && !shared_ok) continue;
     if ((force == 1 && kind != 0) || (force == 2 && shared_ok && kind != 1)) continue;
-    RowPlan p{kind, cand[i].mt, cand[i].bt, 0, 0};
+    RowPlan p{kind, cand[i].mt, cand[i].bt, cand[i].wr, 0, 0};
     const uint32_t bc = 16 * p.bt;
     p.chunks = (n_runs + bc - 1) / bc;
-    const uint32_t waves_rows = kind ? 4 : 1;
-    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * waves_rows;
+    const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * p.wr;
     p.tiles = (rows + per_tile - 1) / per_tile;
     const double wgs = (double)p.tiles * p.chunks;
     const double act = wgs < cus ? wgs : cus;
@@ -164,7 +164,7 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
     // and per digit tile, whether or not all its runs exist.  Workgroups run
     // in rounds of 256 * occ; a compute unit holding k of them shares its
     // rate among them.
-    const double per_wg = 1024.0 * (waves_rows * p.mt + 3 * p.bt) * ((cols + 63) / 64);
+    const double per_wg = 1024.0 * (p.wr * p.mt + 3 * p.bt) * ((cols + 63) / 64);
     const double rounds = std::ceil(wgs / (cus * cand[i].occ));
     const double per_cu = std::min((double)cand[i].occ, std::ceil(wgs / cus));
     const double t_hbm = (double)rows * cols * (gateup ? 2 : 1) / (act * hbm_cu);
@@ -238,12 +238,17 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   shared_ok = shared_ok || a.packed != 0;
   const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup, shared_ok,
                               e->row_kind);
-  const uint32_t per_tile = 16 * (gateup ? p.mt / 2 : p.mt) * (p.kind ? 4 : 1);
-  a.ntiles = 0;
+  // Units of 16 * mt rows (of each matrix of the gate/up pair: 16 * mt / 2)
+  // over the segments in order; a workgroup finishes one (kind 0) or wr.
+  const uint32_t unit_rows = 16 * (gateup ? p.mt / 2 : p.mt);
+  uint32_t units = 0;
   for (uint32_t i = 0; i < a.nseg; i++) {
-    a.seg[i].tile0 = gateup ? 0 : a.ntiles;
-    if (!gateup || i == 0) a.ntiles += (a.seg[i].rows + per_tile - 1) / per_tile;
+    a.seg[i].unit0 = gateup ? 0 : units;
+    if (!gateup || i == 0) units += (a.seg[i].rows + unit_rows - 1) / unit_rows;
   }
+  const uint32_t per = p.kind ? (uint32_t)p.wr : 1u;
+  a.ntiles = (units + per - 1) / per;
+  a.wave_rows = per;
   a.chunks = p.chunks;
   TimedLaunch t(e, T_ROWS, s);
   return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
@@ -689,11 +694,12 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   sg.P = d_P;
   sg.S = d_scale;
   sg.rows = rows;
-  sg.tile0 = 0;
+  sg.unit0 = 0;
   sg.role = ROLE_PLAIN;
   sg.pad = packed || aligned ? 1u : 0u;
   a.nseg = 1;
   a.ntiles = p.tiles;
+  a.wave_rows = p.kind ? (uint32_t)p.wr : 1u;
   a.chunks = p.chunks;
   return launch_rows(EPI_RAW, p.kind, p.mt, p.bt, a, s);
 }

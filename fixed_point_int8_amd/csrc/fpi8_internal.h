@@ -76,7 +76,7 @@ struct Seg {
   const uint8_t *P;      // the same bytes packed in 16 x 64 tiles (see launch_pack), or nullptr
   const uint32_t *S;     // rows Q24 scales
   uint32_t rows;
-  uint32_t tile0;        // first row tile of this matrix in the launch
+  uint32_t unit0;        // first unit (16 * MT rows, or 16 * MT / 2 of the gate/up pair) of this matrix
   uint32_t role;         // epilogue role of the rows (ROLE_*)
   uint32_t pad;
 };
@@ -92,7 +92,8 @@ enum : uint32_t { IN_W1, IN_W3, IN_GATE, IN_RAW };
 struct RowsArgs {
   Seg seg[3];
   uint32_t nseg;
-  uint32_t ntiles;          // row tiles (16 * MT rows each) over all segments
+  uint32_t ntiles;          // row tiles over all segments: one unit (kind 0) or wave_rows units (kind 1)
+  uint32_t wave_rows;       // kind 1: waves of a workgroup (1..4) that own a unit of rows
   uint32_t cols;            // contraction length
   uint32_t kblocks;         // ceil(cols / 64)
   const int8_t *planes;     // [3][bp][kp] signed digits of the input, fragment-major

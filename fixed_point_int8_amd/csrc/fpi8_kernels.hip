@@ -285,27 +285,28 @@ __device__ __forceinline__ bool input_needs_exact(const RowsArgs &a) {
 // The rows one wave finishes: 16 * MT rows in MT tiles of 16, from the
 // segment (matrix) that holds them; for the gate/up pair, HALF tiles of the
 // gate matrix and the same rows of the up matrix.  unit numbers the 16*MT-row
-// units of the launch: a workgroup tile holds `per` of them, and this wave
-// finishes unit tile * per + sub.  The scales of the rows this lane
-// finishes are fetched here, long before the epilogue needs them.
+// units of the launch over all its segments in order (segment i starts at
+// unit seg[i].unit0), so one workgroup may finish rows of two matrices.
+// ptile is the packed 16-row tile the wave streams: that of rbase, or the
+// matrix's last one for rows past its end (their sums are never stored).
+// The scales of the rows this lane finishes are fetched here, long before
+// the epilogue needs them.
 template <int MT>
 struct RowTile {
   uint32_t si;
   const uint8_t *Wp[MT];
   const uint8_t *Pp[MT];
-  uint32_t rbase[MT], rcount[MT];
+  uint32_t rbase[MT], rcount[MT], ptile[MT];
   bool vecw[MT];
   uint32_t sc[MT][4];
 };
 
 template <int EPI, int MT>
-__device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t tile, uint32_t per,
-                                         uint32_t sub, int lg, RowTile<MT> &t) {
+__device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t unit, int lg, RowTile<MT> &t) {
   constexpr int HALF = MT >= 2 ? MT / 2 : 1;
   t.si = 0;
   if (EPI != EPI_GATEUP)
-    while (t.si + 1 < a.nseg && tile >= a.seg[t.si + 1].tile0) ++t.si;
-  const uint32_t unit = tile * per + sub;
+    while (t.si + 1 < a.nseg && unit >= a.seg[t.si + 1].unit0) ++t.si;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
     const Seg &sg = EPI == EPI_GATEUP ? a.seg[mt < HALF ? 0 : 1] : a.seg[t.si];
@@ -314,7 +315,9 @@ __device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t tile, uint3
     t.rcount[mt] = sg.rows;
     t.vecw[mt] = sg.pad != 0;
     t.rbase[mt] = EPI == EPI_GATEUP ? unit * 16 * HALF + 16 * (mt % HALF)
-                                    : (unit - sg.tile0 * per) * 16 * MT + 16 * mt;
+                                    : (unit - sg.unit0) * 16 * MT + 16 * mt;
+    const uint32_t last = (sg.rows - 1) / 16;
+    t.ptile[mt] = t.rbase[mt] / 16 < last ? t.rbase[mt] / 16 : last;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const uint32_t row = t.rbase[mt] + 4 * lg + j;
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
 
   RowTile<MT> t;
-  row_tile<EPI, MT>(a, tile, 1, 0, lg, t);
+  row_tile<EPI, MT>(a, tile, lg, t);
   EpiIn<EPI, MT, BT> in;
   epi_begin<EPI, MT, BT>(a, b0, li, in);
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
@@ -654,7 +657,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   for (int mt = 0; mt < MT; mt++) {
     const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
     wsrc[mt] = a.packed
-        ? t.Pp[mt] + ((uint64_t)(t.rbase[mt] / 16) * a.kblocks + k_lo) * 1024 + lane * 16
+        ? t.Pp[mt] + ((uint64_t)t.ptile[mt] * a.kblocks + k_lo) * 1024 + lane * 16
         : t.Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
   }
 
@@ -830,23 +833,29 @@ __device__ __forceinline__ v4i *ring_buf() {
 }
 
 template <int EPI, int MT, int BT>
-__global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2 : 1))) void k_rows_shared(RowsArgs a) {
   using G = SharedGeom<BT>;
   constexpr int CD = G::CD, FR = G::FR, FW = G::FW, P = G::P, NB = G::NB;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int li = lane & 15, lg = lane >> 4;
 
-  // Workgroup -> (row tile, batch chunk), chunks of a tile 8 ids apart.
+  // Workgroup -> (row tile, batch chunk), chunks of a tile 8 ids apart.  A
+  // row tile is wave_rows units of 16 * MT rows, one per wave that owns
+  // rows; the other waves only stage digits (the same rows are then
+  // covered by more workgroups, so more compute units stream weights).
   const uint32_t nchunk = a.chunks;
   const uint32_t grp = blockIdx.x / (8 * nchunk), rem = blockIdx.x % (8 * nchunk);
   const uint32_t chunk = rem / 8, tile = grp * 8 + rem % 8;
   if (tile >= a.ntiles) return;
   const uint32_t b0 = chunk * BT * 16;
+  const uint32_t wr = a.wave_rows;
+  const bool own = (uint32_t)wave < wr;
   const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
 
   __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   RowTile<MT> t;
-  row_tile<EPI, MT>(a, tile, 4, wave, lg, t);
+  row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, t);
   EpiIn<EPI, MT, BT> in;
   epi_begin<EPI, MT, BT>(a, b0, li, in);
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
@@ -859,7 +868,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
   int64_t v[MT][BT][4];
   if (exact) {
     epi_fetch<EPI, MT, BT>(a, t, lg, in);
-    rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
+    if (own) rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
   } else {
     v4i acc[MT][3][BT];
 #pragma unroll
@@ -876,7 +885,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
       const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
-      wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)(t.rbase[mt] / 16) * a.kblocks * 1024 + lane * 16
+      wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)t.ptile[mt] * a.kblocks * 1024 + lane * 16
                           : t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
     }
     // This wave stages fragments f = wave + 4q of every stage; fragment f
@@ -897,75 +906,90 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
     if constexpr (NB > 4) ring[4] = ring_buf<4, FR * 64>();
 
     v4i Wr[NB][MT][CD];
-    // Stage st into buffer s (weights into register slot s, digits into
-    // LDS buffer s).
-    auto issue = [&](int s, uint32_t st) {
-      __builtin_amdgcn_sched_barrier(0);
+    // The stage loop of a wave that owns rows (OWN) or only stages digits.
+    // Both take the same stages and barriers.
+    auto stream = [&](auto own_tag) {
+      constexpr bool OWN = decltype(own_tag)::value;
+      constexpr int NL = (OWN ? MT * CD : 0) + FW;  // loads per stage
+      // Stage st into buffer s (weights into register slot s, digits into
+      // LDS buffer s).
+      auto issue = [&](int s, uint32_t st) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (OWN) {
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++)
+          for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int c = 0; c < CD; c++)
-          Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * wstride);
-#pragma unroll
-      for (int q = 0; q < FW; q++)
-        __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
-                                         (lds_void *)(ring[s] + (wave + 4 * q) * 64), 16, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto compute = [&](int s) {
-      const int flip = (int)0x80808080u;
-      const v4i *buf = ring[s];
-#pragma unroll
-      for (int c = 0; c < CD; c++) {
-        v4i w[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-          w[mt] = Wr[s][mt][c];
-          w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+            for (int c = 0; c < CD; c++)
+              Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * wstride);
         }
 #pragma unroll
-        for (int l = 0; l < 3; l++)
+        for (int q = 0; q < FW; q++)
+          __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
+                                           (lds_void *)(ring[s] + (wave + 4 * q) * 64), 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto compute = [&](int s) {
+        if constexpr (OWN) {
+          const int flip = (int)0x80808080u;
+          const v4i *buf = ring[s];
 #pragma unroll
-          for (int bt = 0; bt < BT; bt++) {
-            const v4i Bv = buf[((l * BT + bt) * CD + c) * 64 + lane];
+          for (int c = 0; c < CD; c++) {
+            v4i w[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-              acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Bv, acc[mt][l][bt], 0, 0, 0);
+            for (int mt = 0; mt < MT; mt++) {
+              w[mt] = Wr[s][mt][c];
+              w[mt].x ^= flip; w[mt].y ^= flip; w[mt].z ^= flip; w[mt].w ^= flip;
+            }
+#pragma unroll
+            for (int l = 0; l < 3; l++)
+#pragma unroll
+              for (int bt = 0; bt < BT; bt++) {
+                const v4i Bv = buf[((l * BT + bt) * CD + c) * 64 + lane];
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+                  acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Bv, acc[mt][l][bt], 0, 0, 0);
+              }
           }
-      }
-    };
-    // Stage k lives in buffer k % NB.  Once stage k has landed and every
-    // wave has passed the barrier (so all have finished stage k - 1), a wave
-    // issues stage k + P (the last stage again when there is no further
-    // one) into buffer (k + P) % NB, the one stage k - 1 used, then computes
-    // stage k.  P - 1 younger stages are in flight at every wait.
-    const uint32_t last = nch - 1;
+        }
+      };
+      // Stage k lives in buffer k % NB.  Once stage k has landed and every
+      // wave has passed the barrier (so all have finished stage k - 1), a
+      // wave issues stage k + P (the last stage again when there is no
+      // further one) into buffer (k + P) % NB, the one stage k - 1 used,
+      // then computes stage k.  P - 1 younger stages are in flight at every
+      // wait.
+      const uint32_t last = nch - 1;
 #pragma unroll
-    for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
-    epi_fetch<EPI, MT, BT>(a, t, lg, in);
-    uint32_t ch = 0;
-    for (; ch + NB <= nch; ch += NB) {
+      for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
+      epi_fetch<EPI, MT, BT>(a, t, lg, in);
+      uint32_t ch = 0;
+      for (; ch + NB <= nch; ch += NB) {
+#pragma unroll
+        for (int s = 0; s < NB; s++) {
+          wait_vm<(P - 1) * NL>();
+          lds_barrier();
+          const uint32_t nx = ch + s + P;
+          issue((s + P) % NB, nx < nch ? nx : last);
+          compute(s);
+        }
+      }
 #pragma unroll
       for (int s = 0; s < NB; s++) {
-        wait_vm<(P - 1) * (MT * CD + FW)>();
-        lds_barrier();
-        const uint32_t nx = ch + s + P;
-        issue((s + P) % NB, nx < nch ? nx : last);
-        compute(s);
+        if (ch + s < nch) {
+          wait_vm<(P - 1) * NL>();
+          lds_barrier();
+          const uint32_t nx = ch + s + P;
+          issue((s + P) % NB, nx < nch ? nx : last);
+          compute(s);
+        }
       }
-    }
-#pragma unroll
-    for (int s = 0; s < NB; s++) {
-      if (ch + s < nch) {
-        wait_vm<(P - 1) * (MT * CD + FW)>();
-        lds_barrier();
-        const uint32_t nx = ch + s + P;
-        issue((s + P) % NB, nx < nch ? nx : last);
-        compute(s);
-      }
-    }
-    // No staging load may still be landing in LDS when the workgroup ends.
-    wait_vm<0>();
+      // No staging load may still be landing in LDS when the workgroup ends.
+      wait_vm<0>();
+    };
+    if (own)
+      stream(std::integral_constant<bool, true>{});
+    else
+      stream(std::integral_constant<bool, false>{});
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -979,7 +1003,7 @@ __global__ __launch_bounds__(256) void k_rows_shared(RowsArgs a) {
     wait_vm<0>();
     lds_barrier();  // every wave's share of the SiLU table has landed
   }
-  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
+  if (own) rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
 // Packing of a weight matrix into MFMA operand tiles (see launch_pack): one
