@@ -1079,67 +1079,115 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   for (uint32_t i = tid; i < hs; i += blockDim.x) qs[i] = q[i];
   __syncthreads();
 
-  // Stage 0, scores: s_j = (((q . K_j) >> 16) * inv) >> 24; 16 lanes per
-  // position, 16 positions at a time.
+  // Heads of a power-of-two size of at least 4 take the vector path: LPP
+  // lanes hold one position's row, 16 bytes each, so one load instruction of
+  // a wave reads 1 KB of consecutive rows; U positions per lane in flight.
+  constexpr bool VEC = HS != 0 && HS % 4 == 0;
+  constexpr int LPP = VEC ? HS / 4 : 1;  // lanes per position (<= 64)
+  constexpr int GP = 256 / LPP;          // positions per workgroup step
+  constexpr int U = 4;                   // positions per lane in one batch; two batches in flight
+  const int lp = tid % LPP, pg = tid / LPP;
+  // Batch jb holds positions jb + pg + GP u.  Positions past the end load
+  // the last row (a valid address whose line is already near) and count
+  // for nothing, so every load is unconditional and the next batch is
+  // always in flight while one is summed.
+  auto row = [&](uint32_t jb, int u) {
+    const uint32_t j = jb + pg + GP * u;
+    return j < npos ? j : npos - 1;
+  };
+
+  // Stage 0, scores: s_j = (((q . K_j) >> 16) * inv) >> 24.
   int64_t lmax = INT64_MIN;
   const int64_t inv = (int64_t)(uint64_t)a.inv;
-  if constexpr (HS != 0 && HS % 4 == 0) {
-    constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
-    constexpr int CPL = (NCH + 15) / 16;
-    constexpr int U = 4;  // positions per group in flight
-    int64_t qr[CPL][4];
+  if constexpr (VEC) {
+    int64_t qr[4];
     bool fits = true;
 #pragma unroll
-    for (int t = 0; t < CPL; t++)
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const int c = l16 + 16 * t;
-        qr[t][u] = c < NCH ? qs[4 * c + u] : 0;
-        fits = fits && qr[t][u] >= INT32_MIN && qr[t][u] <= INT32_MAX;
-      }
+    for (int u = 0; u < 4; u++) {
+      qr[u] = qs[4 * lp + u];
+      fits = fits && qr[u] >= INT32_MIN && qr[u] <= INT32_MAX;
+    }
     // Queries that fit 32 bits (the usual case) multiply as 32 x 32 -> 64.
     const bool q32 = __syncthreads_and(fits ? 1 : 0) != 0;
     auto scores = [&](auto narrow) {
-      for (uint32_t j0 = grp; j0 < npos; j0 += 16 * U) {
-        v4i kv[U][CPL];
+      auto fetch = [&](v4i (&kv)[U], uint32_t jb) {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+          kv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(K + (uint64_t)row(jb, u) * HS + 4 * lp));
+      };
+      auto dots = [&](const v4i (&kv)[U], uint32_t jb) {
+        int64_t d[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-          const uint32_t j = j0 + 16 * u < npos ? j0 + 16 * u : j0;
-          const int32_t *kr = K + (uint64_t)j * HS;
-#pragma unroll
-          for (int t = 0; t < CPL; t++) {
-            const int c = l16 + 16 * t;
-            if (c < NCH) kv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(kr + 4 * c));
+          if constexpr (decltype(narrow)::value) {
+            d[u] = (int64_t)(int32_t)qr[0] * kv[u].x;
+            d[u] = wadd(d[u], (int64_t)(int32_t)qr[1] * kv[u].y);
+            d[u] = wadd(d[u], (int64_t)(int32_t)qr[2] * kv[u].z);
+            d[u] = wadd(d[u], (int64_t)(int32_t)qr[3] * kv[u].w);
+          } else {
+            d[u] = wmul(qr[0], kv[u].x);
+            d[u] = wadd(d[u], wmul(qr[1], kv[u].y));
+            d[u] = wadd(d[u], wmul(qr[2], kv[u].z));
+            d[u] = wadd(d[u], wmul(qr[3], kv[u].w));
           }
         }
+        if constexpr (LPP >= U) {
+          // Sum the U partial dots over the LPP lanes of a position while
+          // spreading them out: each halving step keeps half of the
+          // positions (chosen by one lane bit) and adds the partner's copy,
+          // so log2(U) steps leave one position per lane; the remaining
+          // lane bits then sum as usual.  Lane lp ends with position
+          // u = its bits (LPP/2, LPP/4, ...) read as a binary number.
+          int np = U;
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-          int64_t dot = 0;
+          for (int o = LPP / 2; np > 1; o >>= 1) {
+            const int half = np / 2;
+            const bool up = (lp & o) != 0;
 #pragma unroll
-          for (int t = 0; t < CPL; t++) {
-            const int c = l16 + 16 * t;
-            if (c < NCH) {
-              if constexpr (decltype(narrow)::value) {
-                dot = wadd(dot, (int64_t)(int32_t)qr[t][0] * kv[u][t].x);
-                dot = wadd(dot, (int64_t)(int32_t)qr[t][1] * kv[u][t].y);
-                dot = wadd(dot, (int64_t)(int32_t)qr[t][2] * kv[u][t].z);
-                dot = wadd(dot, (int64_t)(int32_t)qr[t][3] * kv[u][t].w);
-              } else {
-                dot = wadd(dot, wmul(qr[t][0], kv[u][t].x));
-                dot = wadd(dot, wmul(qr[t][1], kv[u][t].y));
-                dot = wadd(dot, wmul(qr[t][2], kv[u][t].z));
-                dot = wadd(dot, wmul(qr[t][3], kv[u][t].w));
-              }
+            for (int i = 0; i < half; i++) {
+              const int64_t mine = up ? d[half + i] : d[i];
+              const int64_t other = up ? d[i] : d[half + i];
+              d[i] = wadd(mine, (int64_t)__shfl_xor((long long)other, o, LPP));
+            }
+            np = half;
+          }
+          constexpr int REST = LPP / U;  // lanes still holding parts of one position
+#pragma unroll
+          for (int o = REST / 2; o > 0; o >>= 1) d[0] = wadd(d[0], (int64_t)__shfl_xor((long long)d[0], o, LPP));
+          const uint32_t j = jb + pg + GP * (lp / REST);
+          if (lp % REST == 0 && j < npos) {
+            const int64_t sj = wmul(d[0] >> 16, inv) >> 24;
+            sc[j] = sj;
+            lmax = sj > lmax ? sj : lmax;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; u++) {
+            int64_t dot = d[u];
+#pragma unroll
+            for (int o = LPP / 2; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, LPP));
+            const uint32_t j = jb + pg + GP * u;
+            if (lp == 0 && j < npos) {
+              const int64_t sj = wmul(dot >> 16, inv) >> 24;
+              sc[j] = sj;
+              lmax = sj > lmax ? sj : lmax;
             }
           }
-          for (int o = 8; o > 0; o >>= 1) dot = wadd(dot, (int64_t)__shfl_xor((long long)dot, o, 16));
-          const uint32_t j = j0 + 16 * u;
-          if (l16 == 0 && j < npos) {
-            const int64_t s = wmul(dot >> 16, inv) >> 24;
-            sc[j] = s;
-            lmax = s > lmax ? s : lmax;
-          }
         }
+      };
+      // The scheduling fences keep each batch's loads in program order, so
+      // summing one batch waits only for that batch.
+      v4i A[U], B[U];
+      fetch(A, 0);
+      for (uint32_t jb = 0; jb < npos; jb += 2 * GP * U) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(B, jb + GP * U);
+        __builtin_amdgcn_sched_barrier(0);
+        dots(A, jb);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(A, jb + 2 * GP * U);
+        __builtin_amdgcn_sched_barrier(0);
+        dots(B, jb + GP * U);
       }
     };
     if (q32) scores(std::true_type{});
@@ -1181,55 +1229,42 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   // Stage 3, weighted values: o_i = (sum_j p_j * V_j,i) >> 24.
   int64_t *w3 = reinterpret_cast<int64_t *>(st + rd.off_w3) + (uint64_t)h * hs;
-  if constexpr (HS != 0 && HS % 4 == 0) {
-    constexpr int NCH = HS / 4 > 0 ? HS / 4 : 1;
-    constexpr int CPL = (NCH + 15) / 16;
-    constexpr int U = 4;  // positions per group in flight
-    int64_t acc[CPL][4];
+  if constexpr (VEC) {
+    int64_t acc[4] = {0, 0, 0, 0};
+    auto fetch = [&](v4i (&vv)[U], uint32_t jb) {
 #pragma unroll
-    for (int t = 0; t < CPL; t++)
-#pragma unroll
-      for (int u = 0; u < 4; u++) acc[t][u] = 0;
-    for (uint32_t j0 = grp; j0 < npos; j0 += 16 * U) {
-      v4i vv[U][CPL];
+      for (int u = 0; u < U; u++)
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(V + (uint64_t)row(jb, u) * HS + 4 * lp));
+    };
+    auto weigh = [&](const v4i (&vv)[U], uint32_t jb) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        const uint32_t j = j0 + 16 * u < npos ? j0 + 16 * u : j0;
-        const int32_t *vr = V + (uint64_t)j * HS;
-#pragma unroll
-        for (int t = 0; t < CPL; t++) {
-          const int c = l16 + 16 * t;
-          if (c < NCH) vv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(vr + 4 * c));
-        }
+        // a position past the end weighs nothing (read without a branch)
+        const int32_t p = (int32_t)sc[row(jb, u)] & -(int32_t)(jb + pg + GP * u < npos);
+        acc[0] = wadd(acc[0], (int64_t)p * vv[u].x);
+        acc[1] = wadd(acc[1], (int64_t)p * vv[u].y);
+        acc[2] = wadd(acc[2], (int64_t)p * vv[u].z);
+        acc[3] = wadd(acc[3], (int64_t)p * vv[u].w);
       }
-#pragma unroll
-      for (int u = 0; u < U; u++) {
-        const uint32_t j = j0 + 16 * u;
-        // a position past the end weighs nothing
-        const int32_t p = j < npos ? (int32_t)sc[j] : 0;
-#pragma unroll
-        for (int t = 0; t < CPL; t++) {
-          const int c = l16 + 16 * t;
-          if (c < NCH) {
-            acc[t][0] = wadd(acc[t][0], (int64_t)p * vv[u][t].x);
-            acc[t][1] = wadd(acc[t][1], (int64_t)p * vv[u][t].y);
-            acc[t][2] = wadd(acc[t][2], (int64_t)p * vv[u][t].z);
-            acc[t][3] = wadd(acc[t][3], (int64_t)p * vv[u][t].w);
-          }
-        }
-      }
+    };
+    v4i A[U], B[U];
+    fetch(A, 0);
+    for (uint32_t jb = 0; jb < npos; jb += 2 * GP * U) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(B, jb + GP * U);
+      __builtin_amdgcn_sched_barrier(0);
+      weigh(A, jb);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(A, jb + 2 * GP * U);
+      __builtin_amdgcn_sched_barrier(0);
+      weigh(B, jb + GP * U);
     }
 #pragma unroll
-    for (int t = 0; t < CPL; t++) {
-      const int c = l16 + 16 * t;
-      if (c < NCH)
-#pragma unroll
-        for (int u = 0; u < 4; u++) red[grp * HS + 4 * c + u] = acc[t][u];
-    }
+    for (int u = 0; u < 4; u++) red[pg * HS + 4 * lp + u] = acc[u];
     __syncthreads();
     for (uint32_t e = tid; e < HS; e += blockDim.x) {
       int64_t o = 0;
-      for (int g = 0; g < 16; g++) o = wadd(o, red[g * HS + e]);
+      for (int g = 0; g < GP; g++) o = wadd(o, red[g * HS + e]);
       o >>= 24;
       w3[e] = o;
       put_digits(a.planes, a.bp, a.kp, b, h * HS + e, o, a.oflag);
@@ -1455,7 +1490,8 @@ int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stre
 }
 
 size_t attention_lds_bytes(uint32_t max_npos, uint32_t head) {
-  const size_t red = (head % 4 == 0 && (head & (head - 1)) == 0) ? 16ull * head : 256ull;
+  // partial sums of stage 3: (256 / (head / 4)) position groups x head
+  const size_t red = (head % 4 == 0 && (head & (head - 1)) == 0) ? 1024ull : 256ull;
   return 8ull * max_npos + 8ull * red;
 }
 
