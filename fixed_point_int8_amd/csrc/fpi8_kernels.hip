@@ -173,6 +173,53 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   uint8_t *st = run_base(a.states, rd);
   const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
   int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
+  // y = ((x * w) / rms) >> 8 with a truncating division by rms, through
+  // its 64-bit reciprocal m = floor(2^64 / rms): q = mulhi(|p|, m) is the
+  // quotient or one less, and one remainder test fixes it (Granlund and
+  // Montgomery, "Division by invariant integers using multiplication", 1994).
+  auto finish = [&](uint32_t i, int64_t xi, int32_t wi, uint64_t r, uint64_t m) {
+    const int64_t p = wmul(xi, (int64_t)wi);
+    const uint64_t n = p < 0 ? 0ull - (uint64_t)p : (uint64_t)p;
+    uint64_t q = n;
+    if (r > 1) {
+      q = __umul64hi(n, m);
+      if (n - q * r >= r) q++;
+    }
+    const int64_t v = (p < 0 ? (int64_t)(0ull - q) : (int64_t)q) >> 8;
+    y[i] = v;
+    put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
+  };
+  auto rms_of = [&](uint64_t ss, uint64_t &m) {
+    uint64_t r = isqrt64(ss / a.dim + 42950u);
+    if (r < 1) r = 1;
+    m = ~0ull / r;
+    if (~0ull % r == r - 1) m++;
+    return r;
+  };
+  if (a.dim <= nt * U) {
+    // The whole vector fits in registers: x and the weights are read once,
+    // together.
+    int64_t xv[U];
+    int32_t wv[U];
+    uint64_t ss = 0;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = threadIdx.x + u * nt;
+      xv[u] = i < a.dim ? x[i] : 0;
+      wv[u] = i < a.dim ? a.w[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) ss += (uint64_t)wmul(xv[u], xv[u]);
+    ss = block_sum_u64(ss, scratch);
+    uint64_t m;
+    const uint64_t r = rms_of(ss, m);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = threadIdx.x + u * nt;
+      if (i < a.dim) finish(i, xv[u], wv[u], r, m);
+    }
+    return;
+  }
   uint64_t ss = 0;
   for (uint32_t base = threadIdx.x; base < a.dim; base += nt * U) {
     int64_t v[U];
@@ -185,14 +232,8 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     for (int u = 0; u < U; u++) ss += (uint64_t)wmul(v[u], v[u]);
   }
   ss = block_sum_u64(ss, scratch);
-  uint64_t r = isqrt64(ss / a.dim + 42950u);
-  if (r < 1) r = 1;
-  // Truncating division by rms through its 64-bit reciprocal
-  // m = floor(2^64 / rms): q = mulhi(|p|, m) is the quotient or one less,
-  // and one remainder test fixes it (Granlund and Montgomery, "Division by
-  // invariant integers using multiplication", 1994).
-  uint64_t m = ~0ull / r;
-  if (~0ull % r == r - 1) m++;
+  uint64_t m;
+  const uint64_t r = rms_of(ss, m);
   for (uint32_t base = threadIdx.x; base < a.dim; base += nt * U) {
     int64_t xv[U];
     int32_t wv[U];
@@ -205,17 +246,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint32_t i = base + u * nt;
-      if (i >= a.dim) continue;
-      const int64_t p = wmul(xv[u], (int64_t)wv[u]);
-      const uint64_t n = p < 0 ? 0ull - (uint64_t)p : (uint64_t)p;
-      uint64_t q = n;
-      if (r > 1) {
-        q = __umul64hi(n, m);
-        if (n - q * r >= r) q++;
-      }
-      const int64_t v = (p < 0 ? (int64_t)(0ull - q) : (int64_t)q) >> 8;
-      y[i] = v;
-      put_digits(a.planes, a.bp, a.kp, b, i, v, a.oflag);
+      if (i < a.dim) finish(i, xv[u], wv[u], r, m);
     }
   }
 }
@@ -1457,6 +1488,7 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 14: return rows_launch<EPI, 1, 4>(a, s);
       case 22: return rows_launch<EPI, 2, 2>(a, s);
       case 24: return rows_launch<EPI, 2, 4>(a, s);
+      case 41: return rows_launch<EPI, 4, 1>(a, s);
       case 42: return rows_launch<EPI, 4, 2>(a, s);
       case 112: return rows_launch_shared<EPI, 1, 2>(a, s);
       case 114: return rows_launch_shared<EPI, 1, 4>(a, s);
