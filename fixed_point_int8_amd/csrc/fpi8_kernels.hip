@@ -198,7 +198,9 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   };
   if (a.dim <= nt * U) {
     // The whole vector fits in registers: x and the weights are read once,
-    // together.
+    // together.  gridDim.y workgroups share a run: each sums all of x (a
+    // few L2 reads) and finishes its own share of the registers, so the
+    // stores spread over more compute units.
     int64_t xv[U];
     int32_t wv[U];
     uint64_t ss = 0;
@@ -213,13 +215,15 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     ss = block_sum_u64(ss, scratch);
     uint64_t m;
     const uint64_t r = rms_of(ss, m);
+    const uint32_t part = blockIdx.y, parts = gridDim.y;
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint32_t i = threadIdx.x + u * nt;
-      if (i < a.dim) finish(i, xv[u], wv[u], r, m);
+      if ((u * parts) / U == part && i < a.dim) finish(i, xv[u], wv[u], r, m);
     }
     return;
   }
+  if (blockIdx.y != 0) return;
   uint64_t ss = 0;
   for (uint32_t base = threadIdx.x; base < a.dim; base += nt * U) {
     int64_t v[U];
@@ -1456,7 +1460,10 @@ int launch_embed(const EmbedArgs &a, void *stream) {
 }
 
 int launch_norm(const NormArgs &a, void *stream) {
-  hipLaunchKernelGGL(k_norm, dim3(a.n_runs), dim3(512), 0, (hipStream_t)stream, a);
+  // Four workgroups per run share the stores when the vector fits one
+  // workgroup's registers (8 of them per thread); otherwise one workgroup.
+  const uint32_t parts = a.dim <= 512 * 8 ? 4 : 1;
+  hipLaunchKernelGGL(k_norm, dim3(a.n_runs, parts), dim3(512), 0, (hipStream_t)stream, a);
   return ok(hipGetLastError());
 }
 
