@@ -135,24 +135,30 @@ def row_sweep(torch, reps=3):
     return out
 
 
-def cpu_baseline(blob, shape, positions=3):
-    """The oracle on the host: one run of the same model from a one-id prompt
-    for `positions` generating positions (each with the classifier), on as
-    many threads as the box gives this job (at most 16)."""
+def cpu_baseline(blob, shape, name, seconds=12.0, max_positions=64):
+    """The oracle on the host: one run of the same model from a one-id prompt,
+    generating (classifier included) in turns of 4 positions until about
+    `seconds` of wall time have passed, on as many threads as the box gives
+    this job (at most 16)."""
     import oracle as O
     import workloads as Wl
     threads = min(16, os.cpu_count() or 1)
     O.set_threads(threads)
     ids = Wl.prompt_ids(shape.vocab, 1, 2003, 0)
-    e, st = O.init_state(shape.as_tuple(), ids, positions, 0, 1)
+    max_positions = min(max_positions, shape.context - 1)
+    e, st = O.init_state(shape.as_tuple(), ids, max_positions, 0, 1)
     assert e == 0
     t0 = time.perf_counter()
-    assert O.turn(blob, st, positions) == 0
+    while True:
+        assert O.turn(blob, st, 4) == 0
+        info = O.state_info(st)[1]
+        if info["complete"] or time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
-    gen = O.state_info(st)[1]["generated"]
+    gen = info["generated"]
     O.set_threads(1)
     return {"value": round(gen / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one run of the 7B-shaped model, a 1-id prompt, {gen} generating positions "
+            "sample": f"one run of the {name} model, a 1-id prompt, {gen} generating positions "
                       f"(classifier included), {dt:.1f} s wall; runs are independent, so B runs take "
                       f"B times as long"}
 
@@ -270,7 +276,7 @@ def main():
     del batch, model
     torch.cuda.empty_cache()
     sweep = None if args.no_sweep else row_sweep(torch)
-    cpu = None if args.no_cpu else cpu_baseline(blob, shape)
+    cpu = None if args.no_cpu else cpu_baseline(blob, shape, w.name)
 
     res = {
         "metric": METRIC, "value": round(tokens / dt, 2), "unit": "tokens/s", "n_gpus": 1,

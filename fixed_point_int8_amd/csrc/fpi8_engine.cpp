@@ -67,7 +67,7 @@ struct fpi8_engine {
   uint32_t graph_runs = 0;
   uint32_t graph_cap = 0;
   uint32_t score_cap = 0;  // attention's LDS score slots for the current turn
-  int row_kind = 0;  // 0 planner's choice, 1 or 2 restrict it (fpi8_engine_set_row_kernel)
+  int row_kind = 0;  // 0 planner's choice, 1 to 3 restrict it (fpi8_engine_set_row_kernel)
   // Runs split into two groups advanced on two streams, so one group's
   // row kernels overlap the other's attention (2); one stream (0, 1).
   // Measured on the 7B-shaped decode at 64 runs, two groups are slower:
@@ -153,7 +153,9 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
   for (int i = 0; i < n; i++) {
     const int kind = cand[i].kind;
     if (kind == 1 && !shared_ok) continue;
-    if ((force == 1 && kind != 0) || (force == 2 && shared_ok && kind != 1)) continue;
+    if ((force == 1 && kind != 0) || (force >= 2 && shared_ok && kind != 1) ||
+        (force == 3 && shared_ok && cand[i].wr != 3))
+      continue;
     RowPlan p{kind, cand[i].mt, cand[i].bt, cand[i].wr, 0, 0};
     const uint32_t bc = 16 * p.bt;
     p.chunks = (n_runs + bc - 1) / bc;
@@ -579,7 +581,7 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
 }
 
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
-  if (!e || kind < 0 || kind > 2) return FPI8_ERR_ARGUMENT;
+  if (!e || kind < 0 || kind > 3) return FPI8_ERR_ARGUMENT;
   if (e->row_kind != kind) {
     e->row_kind = kind;
     e->graph_states = nullptr;  // record the position again with the new shapes

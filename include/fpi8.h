@@ -149,9 +149,10 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
 /* Which matrix-row kernel the engine's launches use: 0 the planner's choice
  * (the default), 1 always the kernel whose four waves split the contraction,
  * 2 the kernel whose waves share their runs' digits through LDS wherever it
- * can run (columns a multiple of 128, 16-byte aligned rows).  Results are
- * identical under every setting; it exists for tests and tuning.  Error 102
- * for another value. */
+ * can run (columns a multiple of 128, 16-byte aligned rows), 3 that kernel
+ * with three of its four waves owning rows and the fourth only staging
+ * digits.  Results are identical under every setting; it exists for tests
+ * and tuning.  Error 102 for another value. */
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
 
 /* Whether a turn replays one position recorded as a HIP graph (nonzero, the

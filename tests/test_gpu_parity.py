@@ -44,8 +44,11 @@ def gpu_rows_packed(Wm, s, x):
 
 @pytest.mark.parametrize("rows,cols,batch", [
     (1, 1, 1), (37, 172, 3), (100, 300, 17), (129, 4096, 64), (33, 64, 128), (48, 11008, 8),
-    (200, 2048, 65), (4096, 4096, 128)])
+    (200, 2048, 65), (4096, 4096, 128), (12000, 384, 50), (12290, 128, 33)])
 def test_matrix_rows_packed(rows, cols, batch):
+    # (12000, 384, 50) takes the shared-digit kernel with three row-owning
+    # waves, its last workgroup ending inside the matrix; (12290, 128, 33)
+    # four row-owning waves with rows past the last full tile.
     say(f"matrix_rows_packed {rows}x{cols} batch {batch}")
     Wm, s, x = W.row_operands(rows, cols, batch, rows * 1000 + cols + batch + 5)
     assert np.array_equal(gpu_rows_packed(Wm, s, x), O.rows(Wm, s, x))
@@ -213,12 +216,14 @@ def test_split_contraction_whole_pass(n_runs):
     run_pair(shape, blob, runs, [2, 3])
 
 
-@pytest.mark.parametrize("row_kernel", [1, 2])
+@pytest.mark.parametrize("row_kernel", [1, 2, 3])
 @pytest.mark.parametrize("n_runs", [3, 20, 70])
 def test_row_kernels_whole_pass(n_runs, row_kernel):
     # Every matrix of the split shape has a column count that is a multiple
     # of 128, so both row kernels can run all of them: 1 forces the kernel
-    # whose waves split the contraction, 2 the one that shares digits in LDS.
+    # whose waves split the contraction, 2 the one that shares digits in LDS,
+    # 3 that one with three row-owning waves, so that workgroups end inside
+    # a matrix and span the Q/K and K/V boundaries.
     shape = W.SMALL_SHAPES["split"]
     say(f"split shape, {n_runs} runs, row kernel {row_kernel}")
     blob = Bl.build_blob(shape, 22)
@@ -238,13 +243,14 @@ def test_run_groups_on_two_streams(streams, n_runs, graph):
     run_pair(shape, blob, runs, [1, 2, 4], streams=streams, graph=graph)
 
 
-def test_shared_kernel_exact_path():
+@pytest.mark.parametrize("row_kernel", [2, 3])
+def test_shared_kernel_exact_path(row_kernel):
     shape = W.SMALL_SHAPES["split"]
-    say("exact path, shared-digit row kernel")
+    say(f"exact path, shared-digit row kernel {row_kernel}")
     norm = np.full((2 * shape.layers + 1) * shape.dim, 1 << 30, dtype=np.int32)
     blob = Bl.build_blob(shape, 23, tables={"norm": norm})
     runs = spec(shape, 5, [2, 3, 1, 4, 2], 3)
-    run_pair(shape, blob, runs, [1, 10], row_kernel=2)
+    run_pair(shape, blob, runs, [1, 10], row_kernel=row_kernel)
 
 
 def test_long_context_attention():
