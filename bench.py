@@ -257,9 +257,11 @@ def main():
         "steps": ks, "positions": [pos1, pos1 + ks - 1],
         "rows": {"launches": rows_n, "avg_us": round(rows_ms * 1e3 / max(rows_n, 1), 2),
                  "GB/s": round(rows_alg / (rows_ms * 1e6), 1),
+                 "frac": round(rows_alg / (rows_ms * 1e6) / HBM_PEAK_GBS, 4),
                  "bytes_per_launch": int(rows_alg / max(rows_n, 1))},
         "attention": {"launches": attn_n, "avg_us": round(attn_ms * 1e3 / max(attn_n, 1), 2),
                       "GB/s": round(attn_alg / (attn_ms * 1e6), 1),
+                      "frac": round(attn_alg / (attn_ms * 1e6) / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": int(attn_alg / max(attn_n, 1))},
         "share_of_step": {"rows": round(rows_ms / (dk * 1e3), 3),
                           "attention": round(attn_ms / (dk * 1e3), 3)},

@@ -851,6 +851,7 @@ struct SharedGeom {
   static constexpr int FW = FR / 4;            // fragments each wave stages
   static constexpr int P = BT >= 4 ? 3 : 4;    // stages in flight
   static constexpr int NB = P + 1;             // stage buffers (LDS and registers)
+  static_assert(FR % 4 == 0, "every wave stages the same number of fragments");
 };
 
 // A workgroup barrier that orders LDS accesses only.  __syncthreads() would
