@@ -135,6 +135,26 @@ def row_sweep(torch, reps=3):
     return out
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth of a plain device copy (bytes read plus bytes
+    written per second), measured beside the nominal peak."""
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (t0.elapsed_time(t1) * 1e6)
+    del a, b
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def cpu_baseline(blob, shape, name, seconds=12.0, max_positions=64):
     """The oracle on the host: one run of the same model from a one-id prompt,
     generating (classifier included) in turns of 4 positions until about
@@ -216,7 +236,11 @@ def main():
     assert e == 0, (e, list(errs))
     log(f"prefill {w.prompt} positions x {w.runs} runs in {prefill_s:.2f} s")
 
+    gen_prefill = sum(batch.info(i)["generated"] for i in range(w.runs))
+    t = time.perf_counter()
     e, errs = batch.turn(model, args.warmup, stream)
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t
     assert e == 0, (e, list(errs))
     gen0 = sum(batch.info(i)["generated"] for i in range(w.runs))
     pos0 = batch.info(0)["position"]
@@ -277,6 +301,7 @@ def main():
     model.close()
     del batch, model
     torch.cuda.empty_cache()
+    copy_gbs = copy_bandwidth(torch)
     sweep = None if args.no_sweep else row_sweep(torch)
     cpu = None if args.no_cpu else cpu_baseline(blob, shape, w.name)
 
@@ -289,7 +314,11 @@ def main():
                    "prompt": w.prompt, "decode_positions": [pos0, pos0 + args.steps - 1],
                    "seq_len": w.prompt + w.max_tokens - 1, "parallelism": "none (one GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
-        "prefill_s": round(prefill_s, 2), "row_sweep_4096": sweep,
+        "prefill_s": round(prefill_s, 2),
+        # every token the runs hold over prefill, warm-up and timed steps, over their wall time
+        "prefill_and_decode_tokens_per_s": round(gen1 / (prefill_s + warm_s + dt), 2),
+        "first_tokens": gen_prefill,
+        "hbm_copy_GB/s": copy_gbs, "row_sweep_4096": sweep,
     }
     print(json.dumps(res), flush=True)
 
