@@ -835,15 +835,15 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 }
 
 // The matrix row with the digits shared through LDS.  A workgroup of four
-// waves owns 4 * 16 * MT rows (each wave its own 16 * MT) and 16 * BT runs,
-// over the whole contraction.  The four waves stage each run of CD
-// 64-column blocks of digit fragments into an LDS ring with direct
-// global-to-LDS loads (a quarter of the fragments each), P stages ahead,
-// and every wave streams its own weight rows into a register ring of the
-// same depth; one barrier per stage.  The digits then cross L2 once per
-// 64 * MT rows rather than once per 16 * MT.  For packed matrices (kblocks
-// even), or rows that are 16-byte aligned with a column count that is a
-// multiple of 64 * CD.
+// waves owns wave_rows * 16 * MT rows (wave_rows = 3 or 4 waves each own
+// 16 * MT of them) and 16 * BT runs, over the whole contraction.  All four
+// waves stage each run of CD 64-column blocks of digit fragments into an
+// LDS ring with direct global-to-LDS loads (a quarter of the fragments
+// each), P stages ahead, and every row-owning wave streams its own weight
+// rows into a register ring of the same depth; one barrier per stage.  The
+// digits then cross L2 once per wave_rows * 16 * MT rows rather than once
+// per 16 * MT.  For packed matrices (kblocks even), or rows that are
+// 16-byte aligned with a column count that is a multiple of 64 * CD.
 template <int BT>
 struct SharedGeom {
   static constexpr int CD = 2;                 // 64-column blocks per stage
