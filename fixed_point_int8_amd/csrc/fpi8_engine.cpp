@@ -663,36 +663,19 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   uint8_t *base = reinterpret_cast<uint8_t *>(d_work);
   uint32_t *flag = reinterpret_cast<uint32_t *>(base);
   int8_t *planes = reinterpret_cast<int8_t *>(base + 256);
-  // Each call marks an overflow with its own number, so the flag word never
-  // needs clearing; a stale word that happens to match only sends the call
-  // down the exact path, which gives the same result.
-  static std::atomic<uint32_t> calls{0};
-  uint32_t seq = ++calls;
-  if (seq == 0) seq = ++calls;
-  // One or two inputs: plain digit rows, so the four lanes of a run read one
-  // whole 64-byte piece per block (the kernel whose waves split the
-  // contraction reads them); more: the fragment-major layout both kernels
-  // read, where the runs of a lane group share 16-byte pieces of one line.
-  const uint32_t compact = batch <= 2 ? 1u : 0u;
-  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, compact, flag, seq, s);
-  if (r) return r;
   const bool packed = d_P != nullptr;
   const bool aligned = cols % 16 == 0 && (reinterpret_cast<uintptr_t>(d_W) & 15) == 0;
   const bool shared_ok = packed || (aligned && cols % 128 == 0);
-  const RowPlan p = plan_rows(rows, cols, batch, false, shared_ok, compact ? 1 : 0);
+  const uint32_t kblocks = packed ? ((cols + 63) / 64 + 1) / 2 * 2 : (cols + 63) / 64;
   RowsArgs a;
   memset(&a, 0, sizeof a);
   a.cols = cols;
-  a.kblocks = packed ? ((cols + 63) / 64 + 1) / 2 * 2 : (cols + 63) / 64;
+  a.kblocks = kblocks;
   a.packed = packed ? 1u : 0u;
-  a.planes = planes;
   a.kp = kp;
   a.bp = bp;
   a.n_runs = batch;
   a.in_sel = IN_RAW;
-  a.oflag = flag;
-  a.oflag_seq = seq;
-  a.compact = compact;
   a.x_raw = d_x;
   a.y_raw = d_y;
   Seg &sg = a.seg[0];
@@ -704,6 +687,39 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   sg.role = ROLE_PLAIN;
   sg.pad = packed || aligned ? 1u : 0u;
   a.nseg = 1;
+
+  // One or two inputs whose digits fit a wave's LDS share: one launch, the
+  // kernel's waves split the inputs into digits themselves.
+  const uint32_t per = (kblocks + 3) / 4;
+  if (batch <= 2 && (uint64_t)3 * batch * per * 64 <= kRawInputLds) {
+    const RowPlan p = plan_rows(rows, cols, batch, false, shared_ok, 1);
+    if (p.kind == 0 && p.bt == 1 && (p.mt == 1 || p.mt == 4)) {
+      a.ntiles = p.tiles;
+      a.wave_rows = 1;
+      a.chunks = p.chunks;
+      return launch_rows_raw(p.mt, a, s);
+    }
+  }
+
+  // Otherwise the digits first.  Each call marks an overflow with its own
+  // number, so the flag word never needs clearing; a stale word that happens
+  // to match only sends the call down the exact path, which gives the same
+  // result.
+  static std::atomic<uint32_t> calls{0};
+  uint32_t seq = ++calls;
+  if (seq == 0) seq = ++calls;
+  // One or two inputs: plain digit rows, so the four lanes of a run read one
+  // whole 64-byte piece per block (the kernel whose waves split the
+  // contraction reads them); more: the fragment-major layout both kernels
+  // read, where the runs of a lane group share 16-byte pieces of one line.
+  const uint32_t compact = batch <= 2 ? 1u : 0u;
+  int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, compact, flag, seq, s);
+  if (r) return r;
+  const RowPlan p = plan_rows(rows, cols, batch, false, shared_ok, compact ? 1 : 0);
+  a.planes = planes;
+  a.oflag = flag;
+  a.oflag_seq = seq;
+  a.compact = compact;
   a.ntiles = p.tiles;
   a.wave_rows = p.kind ? (uint32_t)p.wr : 1u;
   a.chunks = p.chunks;

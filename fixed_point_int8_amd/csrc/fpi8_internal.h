@@ -178,6 +178,12 @@ int launch_norm(const NormArgs &a, void *stream);
 // rows; kind 1: they own 16 * mt rows each and share the digits through LDS
 // (columns a multiple of 128, 16-byte aligned rows).
 int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream);
+// The standalone row of one or two inputs (x_raw) on the
+// kernel whose waves split the contraction, without digit planes: each wave
+// splits its own columns of the inputs into digits in kRawInputLds bytes of
+// LDS, so 3 * n_runs * ceil(kblocks / 4) * 64 must fit that; mt 1 or 4.
+constexpr uint32_t kRawInputLds = 24576;
+int launch_rows_raw(int mt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 // Packs a rows x cols byte matrix into tiles of 16 rows x 64 columns, tile
 // (rt, kb) at ((rt * kbp + kb) * 1024), inside it lane l = 16 g + i at

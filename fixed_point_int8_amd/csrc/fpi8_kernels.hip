@@ -616,19 +616,28 @@ __device__ __forceinline__ void wait_vm() {
 
 
 // Blocks in flight per wave: the fragments of a block take 4 * (MT + 3 BT)
-// VGPRs, and about 190 of them hold the prefetch ring.
-template <int MT, int BT>
+// VGPRs (4 * MT when the digits come from LDS), and about 190 of them hold
+// the prefetch ring.
+template <int MT, int BT, bool XR = false>
 struct RowsGeom {
-  static constexpr int FRAG = MT + 3 * BT;
+  static constexpr int FRAG = MT + (XR ? 0 : 3 * BT);
   static constexpr int P0 = 48 / FRAG;
   static constexpr int P = P0 < 2 ? 2 : P0 > 12 ? 12 : P0;
 };
 
-template <int EPI, int MT, int BT>
+// XR (standalone calls of one or two inputs): no digit planes;
+// each wave reads its own columns of the raw inputs, splits them into
+// digits in LDS (kRawInputLds bytes a wave: 3 limbs x inputs x its column
+// span), and takes the exact path by itself when one of its words needs more.
+constexpr uint32_t XR_CAP = kRawInputLds;
+
+template <int EPI, int MT, int BT, bool XR = false>
 __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
-  constexpr int P = RowsGeom<MT, BT>::P;
+  static_assert(!XR || (EPI == EPI_RAW && BT == 1), "raw-input rows are standalone calls of one or two inputs");
+  constexpr int P = RowsGeom<MT, BT, XR>::P;
   __shared__ int64_t red[3][MT * BT * 4 * 64];
   __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
+  __shared__ __align__(16) int8_t xdig[XR ? 4 * XR_CAP : 16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
 
@@ -696,13 +705,21 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
         : t.Wp[mt] + (uint64_t)row * a.cols + (uint64_t)k_lo * 64 + lg * 16;
   }
 
-  v4i Wr[P][MT], Dr[P][3][BT];
+  // XR: this wave's digits, [limb][input][column of its span], in LDS.
+  const uint32_t span = per * 64;
+  int8_t *xd = xdig + (XR ? wave * XR_CAP : 0);
+  bool x_exact = false;
+  const uint32_t xrun = li < a.n_runs ? li : 0;  // XR: the input this lane's product column takes
+
+  v4i Wr[P][MT], Dr[XR ? 1 : P][3][BT];
   auto load_digits = [&](int s, uint32_t i) {
+    if constexpr (!XR) {
 #pragma unroll
-    for (int l = 0; l < 3; l++)
+      for (int l = 0; l < 3; l++)
 #pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * dstride);
+        for (int bt = 0; bt < BT; bt++)
+          Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)i * dstride);
+    }
   };
   // Block k_lo + i into ring slot s: whole 16-byte pieces of aligned rows.
   // The scheduling fences keep each slot's loads together and in ring
@@ -722,7 +739,8 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
       Wr[s][mt] = load_weights_raw(t.Wp[mt], t.rbase[mt] + li, t.rcount[mt], a.cols, (k_lo + i) * 64 + lg * 16, t.vecw[mt]);
     load_digits(s, i);
   };
-  auto compute = [&](int s) {
+  // Ring slot s, which holds block k_lo + i.
+  auto compute = [&](int s, uint32_t i) {
     const int flip = (int)0x80808080u;
     v4i w[MT];
 #pragma unroll
@@ -733,10 +751,16 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
     for (int l = 0; l < 3; l++)
 #pragma unroll
-      for (int bt = 0; bt < BT; bt++)
+      for (int bt = 0; bt < BT; bt++) {
+        v4i d;
+        if constexpr (XR)
+          d = *reinterpret_cast<const v4i *>(xd + ((uint64_t)l * a.n_runs + xrun) * span + i * 64 + lg * 16);
+        else
+          d = Dr[s][l][bt];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++)
-          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Dr[s][l][bt], acc[mt][l][bt], 0, 0, 0);
+          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], d, acc[mt][l][bt], 0, 0, 0);
+      }
   };
 
   // Whole 64-column blocks of this wave, then (for the wave that owns it)
@@ -747,6 +771,44 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) fast = fast && t.vecw[mt];
   fast = fast || a.packed != 0;
+  // XR: split this wave's columns of the inputs into digits in LDS (16
+  // columns a lane, both inputs' words requested before any is used).  It
+  // goes before the weight tiles: a wait for the inputs would otherwise
+  // wait for every tile requested before them.
+  if constexpr (XR) {
+    bool fits = true;
+    for (uint32_t c = 16 * lane; c < n * 64; c += 1024) {
+      // columns of the row left from here; none in the padding blocks past its end
+      const int64_t room = (int64_t)a.cols - (int64_t)(k_lo * 64 + c);
+      int64_t xv[2][16];
+#pragma unroll
+      for (int b = 0; b < 2; b++) {
+        const int64_t *xr = a.x_raw + (uint64_t)b * a.cols + (uint64_t)k_lo * 64 + c;
+#pragma unroll
+        for (int e = 0; e < 16; e++) xv[b][e] = (uint32_t)b < a.n_runs && e < room ? xr[e] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; b++) {
+        if ((uint32_t)b >= a.n_runs) break;
+        uint32_t w[3][4] = {};
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          int8_t d0, d1, d2;
+          fits = digits3(xv[b][e], d0, d1, d2) && fits;
+          const int sh = 8 * (e & 3);
+          w[0][e >> 2] |= (uint32_t)(uint8_t)d0 << sh;
+          w[1][e >> 2] |= (uint32_t)(uint8_t)d1 << sh;
+          w[2][e >> 2] |= (uint32_t)(uint8_t)d2 << sh;
+        }
+#pragma unroll
+        for (int l = 0; l < 3; l++)
+          *reinterpret_cast<v4i *>(xd + ((uint64_t)l * a.n_runs + b) * span + c) =
+              v4i{(int)w[l][0], (int)w[l][1], (int)w[l][2], (int)w[l][3]};
+      }
+    }
+    x_exact = __any(fits ? 0 : 1) != 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own digit stores, before its reads
+  }
   // The ring's first P blocks go out before anything waits.
   const uint32_t last = n_main ? n_main - 1 : 0;
   if (fast && n_main > 0) {
@@ -764,7 +826,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   }
 
   int64_t v[MT][BT][4];
-  if (!exact) {
+  if (!exact && !x_exact) {
     if (fast && n_main > 0) {
       // P blocks in flight; the loop body has no branches, so the compiler
       // waits only for the slot about to be used.
@@ -772,29 +834,29 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
       for (; i + 2 * P <= n_main; i += P) {
 #pragma unroll
         for (int s = 0; s < P; s++) {
-          compute(s);
+          compute(s, i + s);
           load(s, i + s + P);
         }
       }
 #pragma unroll
       for (int s = 0; s < P; s++) {
-        if (i + s < n_main) compute(s);
+        if (i + s < n_main) compute(s, i + s);
         const uint32_t nx = i + s + P;
         load(s, nx < n_main ? nx : last);
       }
       i += P;
 #pragma unroll
       for (int s = 0; s < P; s++)
-        if (i + s < n_main) compute(s);
+        if (i + s < n_main) compute(s, i + s);
     } else {
       for (uint32_t i = 0; i < n_main; i++) {
         load_checked(0, i);
-        compute(0);
+        compute(0, i);
       }
     }
     if (nfull < nkb && k_lo <= nfull && nfull < k_lo + n) {
       load_checked(0, nfull - k_lo);
-      compute(0);
+      compute(0, nfull - k_lo);
     }
 
 #pragma unroll
@@ -1513,6 +1575,21 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
     }
   }
   return FPI8_ERR_ARGUMENT;
+}
+
+int launch_rows_raw(int mt, const RowsArgs &a, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.ntiles == 0 || a.chunks == 0) return 0;
+  if (a.chunks != 1 || a.n_runs > 2) return FPI8_ERR_ARGUMENT;
+  const uint32_t per = (a.kblocks + 3) / 4;
+  if ((uint64_t)3 * a.n_runs * per * 64 > XR_CAP) return FPI8_ERR_ARGUMENT;
+  const dim3 grid((a.ntiles + 7) / 8 * 8), block(256);
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((k_rows<EPI_RAW, 1, 1, true>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rows<EPI_RAW, 4, 1, true>), grid, block, 0, s, a); break;
+    default: return FPI8_ERR_ARGUMENT;
+  }
+  return ok(hipGetLastError());
 }
 
 int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream) {

@@ -44,7 +44,8 @@ def gpu_rows_packed(Wm, s, x):
 
 @pytest.mark.parametrize("rows,cols,batch", [
     (1, 1, 1), (37, 172, 3), (100, 300, 17), (129, 4096, 64), (33, 64, 128), (48, 11008, 8),
-    (200, 2048, 65), (4096, 4096, 128), (12000, 384, 50), (12290, 128, 33)])
+    (200, 2048, 65), (4096, 4096, 128), (12000, 384, 50), (12290, 128, 33), (4096, 4096, 1),
+    (4096, 4096, 8), (100, 4096, 8), (7, 100, 2), (40, 1000, 5), (24, 2752, 2)])
 def test_matrix_rows_packed(rows, cols, batch):
     # (12000, 384, 50) takes the shared-digit kernel with three row-owning
     # waves, its last workgroup ending inside the matrix; (12290, 128, 33)
@@ -95,6 +96,19 @@ def test_matrix_rows_adversarial_inputs(rows, cols, batch):
     s[0] = 2**32 - 1
     s[2] = 0
     assert np.array_equal(gpu_rows(Wm, s, x), O.rows(Wm, s, x))
+
+
+@pytest.mark.parametrize("batch,packed", [(1, False), (2, True), (8, False), (8, True)])
+def test_matrix_rows_one_wave_exact(batch, packed):
+    # Calls of at most 8 inputs split their digits per wave; one word too
+    # wide for three digits, in the last wave's columns only, sends that wave
+    # alone down the exact path.
+    rows, cols = 64, 4096
+    Wm, s, x = W.row_operands(rows, cols, batch, 41 + batch)
+    x[batch - 1, cols - 5] = 2**40 + 12345
+    ref = O.rows(Wm, s, x)
+    got = gpu_rows_packed(Wm, s, x) if packed else gpu_rows(Wm, s, x)
+    assert np.array_equal(got, ref)
 
 
 def test_matrix_rows_three_digit_edges():
