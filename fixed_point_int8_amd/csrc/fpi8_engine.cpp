@@ -656,7 +656,8 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
       batch == 0 || cols > 65536 || batch > 65536)
     return FPI8_ERR_ARGUMENT;
   if (work_len < fpi8_matrix_rows_workspace_size(rows, cols, batch) ||
-      (reinterpret_cast<uintptr_t>(d_work) & 255) != 0 || (reinterpret_cast<uintptr_t>(d_P) & 15) != 0)
+      (reinterpret_cast<uintptr_t>(d_work) & 255) != 0 || (reinterpret_cast<uintptr_t>(d_P) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(d_x) & 7) != 0 || (reinterpret_cast<uintptr_t>(d_y) & 7) != 0)
     return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   const uint32_t kp = round_up(cols, 128), bp = round_up(batch, 64);

@@ -180,10 +180,14 @@ int32_t fpi8_engine_timing(fpi8_engine *engine, int32_t kernel, double *total_ms
  * y[b][r] = ((sum_c W[r][c] * x[b][c] - 128 * sum_c x[b][c]) * scale[r]) >> 24
  * in wrapping 64-bit arithmetic, for W rows x cols bytes (weight + 128,
  * row-major), scale u32 Q24, x [batch][cols] i64 Q16, y [batch][rows] i64.
- * The workspace (device, 256-byte aligned, at least
- * fpi8_matrix_rows_workspace_size bytes) holds the byte digits of x and an
- * overflow word; its contents need no initialization.  Calls that share a workspace must not overlap.  Errors
- * 102 (sizes, null pointers, small or misaligned workspace), 100. */
+ * x and y must be 8-byte aligned.  The workspace (device, 256-byte aligned, at
+ * least fpi8_matrix_rows_workspace_size bytes) holds the byte digits of x
+ * and an overflow word; its contents need no initialization, and a call of
+ * one or two inputs over at most 16,384 columns (32,768 for one) may leave
+ * it untouched, splitting x inside the row kernel.  Calls that share a
+ * workspace must not overlap.  Runs on `stream` (the null stream if NULL)
+ * and does not synchronize.  Errors 102 (sizes, null pointers, small or
+ * misaligned workspace), 100. */
 uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch);
 int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t rows,
                          uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,

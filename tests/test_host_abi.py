@@ -140,3 +140,23 @@ def test_oracle_turn_after_library_init():
     assert B.fpi8_init_state(cfg, st, [3, 4, 5, 6, 7], 3, 0, 0) == 0
     assert O.run_to_end(bl, st) == 0
     assert B.fpi8_state_info(st)[1]["complete"] == 1
+
+
+def test_matrix_rows_rejects_bad_arguments_before_any_launch():
+    # Sizes, null pointers and alignments are checked on the host before the
+    # call touches the GPU (the pointers here are never dereferenced).
+    need = B.fpi8_matrix_rows_workspace_size(16, 64, 2)
+    ok = dict(d_W=0x10000, d_scale=0x20000, rows=16, cols=64, d_x=0x30000, batch=2, d_y=0x40000,
+              d_work=0x50000, work_len=need)
+    bad = [dict(rows=0), dict(cols=0), dict(batch=0), dict(cols=65537), dict(d_W=0), dict(d_x=0),
+           dict(d_y=0), dict(d_work=0), dict(work_len=need - 1), dict(d_work=0x50010),
+           dict(d_x=0x30004), dict(d_y=0x40002)]
+    for change in bad:
+        args = dict(ok, **change)
+        assert B.fpi8_matrix_rows(**args) == B.ERR_ARGUMENT, change
+        pk = dict(args, d_P=args.pop("d_W"))
+        assert B.fpi8_matrix_rows_packed(**pk) == B.ERR_ARGUMENT, change
+    # a packed copy must be 16-byte aligned
+    pk = dict(ok, d_P=0x10008)
+    del pk["d_W"]
+    assert B.fpi8_matrix_rows_packed(**pk) == B.ERR_ARGUMENT
