@@ -658,7 +658,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile, lg, t);
   EpiIn<EPI, MT, BT> in;
-  epi_begin<EPI, MT, BT>(a, b0, li, in);
+  if (wave == 0) epi_begin<EPI, MT, BT>(a, b0, li, in);  // only wave 0 runs the epilogue
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
 
   // This wave's blocks [k_lo, k_lo + n).
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
     for (int s = 0; s < P; s++) load(s, (uint32_t)s < n_main ? (uint32_t)s : last);
   }
-  epi_fetch<EPI, MT, BT>(a, t, lg, in);
+  if (wave == 0) epi_fetch<EPI, MT, BT>(a, t, lg, in);
 
   // The input needs more than three digits somewhere: exact path (a scalar
   // read, so it does not wait behind the loads above).
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, t);
   EpiIn<EPI, MT, BT> in;
-  epi_begin<EPI, MT, BT>(a, b0, li, in);
+  if (own) epi_begin<EPI, MT, BT>(a, b0, li, in);  // waves that own rows run an epilogue
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
   const bool exact = input_needs_exact(a);
   if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
@@ -965,8 +965,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
 
   int64_t v[MT][BT][4];
   if (exact) {
-    epi_fetch<EPI, MT, BT>(a, t, lg, in);
-    if (own) rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
+    if (own) {
+      epi_fetch<EPI, MT, BT>(a, t, lg, in);
+      rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
+    }
   } else {
     v4i acc[MT][3][BT];
 #pragma unroll
@@ -1059,7 +1061,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
       const uint32_t last = nch - 1;
 #pragma unroll
       for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
-      epi_fetch<EPI, MT, BT>(a, t, lg, in);
+      if constexpr (OWN) epi_fetch<EPI, MT, BT>(a, t, lg, in);
       uint32_t ch = 0;
       for (; ch + NB <= nch; ch += NB) {
 #pragma unroll
