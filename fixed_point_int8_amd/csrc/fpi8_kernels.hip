@@ -324,8 +324,8 @@ __device__ __forceinline__ bool input_needs_exact(const RowsArgs &a) {
 // unit seg[i].unit0), so one workgroup may finish rows of two matrices.
 // ptile is the packed 16-row tile the wave streams: that of rbase, or the
 // matrix's last one for rows past its end (their sums are never stored).
-// The scales of the rows this lane finishes are fetched here, long before
-// the epilogue needs them.
+// A wave that runs the epilogue (scales = true) fetches the scales of the
+// rows its lanes finish here, long before the epilogue needs them.
 template <int MT>
 struct RowTile {
   uint32_t si;
@@ -337,7 +337,8 @@ struct RowTile {
 };
 
 template <int EPI, int MT>
-__device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t unit, int lg, RowTile<MT> &t) {
+__device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t unit, int lg, bool scales,
+                                         RowTile<MT> &t) {
   constexpr int HALF = MT >= 2 ? MT / 2 : 1;
   t.si = 0;
   if (EPI != EPI_GATEUP)
@@ -353,10 +354,12 @@ __device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t unit, int l
                                     : (unit - sg.unit0) * 16 * MT + 16 * mt;
     const uint32_t last = (sg.rows - 1) / 16;
     t.ptile[mt] = t.rbase[mt] / 16 < last ? t.rbase[mt] / 16 : last;
+    if (scales) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint32_t row = t.rbase[mt] + 4 * lg + j;
-      t.sc[mt][j] = sg.S[row < t.rcount[mt] ? row : t.rcount[mt] - 1];
+      for (int j = 0; j < 4; j++) {
+        const uint32_t row = t.rbase[mt] + 4 * lg + j;
+        t.sc[mt][j] = sg.S[row < t.rcount[mt] ? row : t.rcount[mt] - 1];
+      }
     }
   }
 }
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
 
   RowTile<MT> t;
-  row_tile<EPI, MT>(a, tile, lg, t);
+  row_tile<EPI, MT>(a, tile, lg, wave == 0, t);
   EpiIn<EPI, MT, BT> in;
   if (wave == 0) epi_begin<EPI, MT, BT>(a, b0, li, in);  // only wave 0 runs the epilogue
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
@@ -953,7 +956,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
 
   __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   RowTile<MT> t;
-  row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, t);
+  row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, own, t);
   EpiIn<EPI, MT, BT> in;
   if (own) epi_begin<EPI, MT, BT>(a, b0, li, in);  // waves that own rows run an epilogue
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
