@@ -45,7 +45,7 @@ def gpu_rows_packed(Wm, s, x):
 @pytest.mark.parametrize("rows,cols,batch", [
     (1, 1, 1), (37, 172, 3), (100, 300, 17), (129, 4096, 64), (33, 64, 128), (48, 11008, 8),
     (200, 2048, 65), (4096, 4096, 128), (12000, 384, 50), (12290, 128, 33), (4096, 4096, 1),
-    (4096, 4096, 8), (100, 4096, 8), (7, 100, 2), (40, 1000, 5), (24, 2752, 2)])
+    (4096, 4096, 8), (100, 4096, 8), (7, 100, 2), (40, 1000, 5), (24, 2752, 2), (20, 40000, 2)])
 def test_matrix_rows_packed(rows, cols, batch):
     # (12000, 384, 50) takes the shared-digit kernel with three row-owning
     # waves, its last workgroup ending inside the matrix; (12290, 128, 33)
@@ -79,7 +79,8 @@ def gpu_rows(Wm, s, x, work=None):
 
 @pytest.mark.parametrize("rows,cols,batch", [
     (16, 64, 1), (1, 1, 1), (37, 172, 3), (100, 300, 17), (256, 512, 32), (129, 4096, 64),
-    (64, 128, 100), (33, 64, 128), (48, 11008, 8), (200, 2048, 65), (24, 65536, 3)])
+    (64, 128, 100), (33, 64, 128), (48, 11008, 8), (200, 2048, 65), (24, 65536, 3),
+    (20, 40000, 2), (20, 40000, 1), (20, 16384, 2)])
 def test_matrix_rows_random(rows, cols, batch):
     say(f"matrix_rows {rows}x{cols} batch {batch}")
     Wm, s, x = W.row_operands(rows, cols, batch, rows * 1000 + cols + batch)
