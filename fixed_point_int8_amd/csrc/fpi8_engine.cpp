@@ -128,10 +128,11 @@ struct RowPlan {
 // a launch wants a workgroup on each of the 256 compute units.  The rate at
 // which one compute unit draws a workgroup's bytes depends on the shape
 // (registers left for loads in flight, sums per wave, one workgroup's digits
-// serving four waves' rows); the figures are measured on MI355X with the
-// 7B-shaped matrices at 64 runs.  shared_ok: the shared-digit kernel can run
-// (columns a multiple of 128, aligned rows); force 1 or 2 restricts the
-// choice to kind 0 or kind 1.
+// serving three or four waves' rows); the figures come from sweeps of every
+// shape over the 7B-, 1.1B- and long-context-shaped matrices on MI355X.
+// shared_ok: the shared-digit kernel can run (columns a multiple of 128,
+// aligned rows); force 1 or 2 restricts the choice to kind 0 or kind 1,
+// force 3 to kind 1 with three row-owning waves.
 RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bool shared_ok,
                   int force) {
   // rate: GB/s one compute unit draws for the shape; occ: workgroups of the
