@@ -19,8 +19,9 @@
 // i32 partial sums (|sum| <= 2^14 * cols < 2^31).  Recombined they are the
 // signed dot sum_c (b_c - 128) x_c exactly, which equals the page's
 // acc - 128 * sum modulo 2^64.  A launch whose inputs hold any value outside
-// the three-digit range takes an exact 64-bit path instead, so the result is
-// the page's for every input.
+// the three-digit range takes an exact 64-bit path instead (a standalone call
+// of one or two inputs decides wave by wave), so the result is the page's
+// for every input.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
