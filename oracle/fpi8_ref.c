@@ -559,50 +559,58 @@ static int store_rows(const cfg_t *c, const mat_t *M, const int64_t *in, int64_t
   return 1;
 }
 
-static int32_t position(const model_t *m, const mat_t *mats, run_t *r) {
+/* One phase of the pass ("The forward pass, in order"), the one the cursor
+ * in the state header (phase, layer) names; the cursor then names the next
+ * one, so a turn can stop between any two phases and a later turn continue
+ * from there ("The resumable state").  Every phase reads only the state's
+ * buffers and writes its results back into them.  *ended is set when the
+ * position is finished: the cursor then stands at the next position's
+ * embedding (phase 3), or at phase 20 when the run is complete.  Returns 0,
+ * or the error that froze the run. */
+static int32_t phase_step(const model_t *m, const mat_t *mats, run_t *r, int *ended) {
   const cfg_t *c = &m->c;
   uint8_t *st = r->st;
+  const uint32_t p = rd32(st + H_PHASE), l = rd32(st + H_LAYER);
   const uint32_t t = rd32(st + H_POSITION);
   const uint32_t n_ids = rd32(st + H_NIDS), cachepos = rd32(st + H_CACHEPOS);
-  const uint32_t tok = rd32(st + H_TOKEN);
   const uint32_t half = c->head / 2;
   const uint32_t group = c->heads / c->kv_heads;
-
-  /* Phase 3: embedding, ((byte - 128) * scale) >> 8 with the token row's
-   * scale. */
-  {
-    const mat_t *E = &mats[0];
-    const uint8_t *row = E->w + (uint64_t)tok * c->dim;
-    uint32_t sc = rd32(E->s_bytes + 4ull * tok);
-    for (uint32_t i = 0; i < c->dim; i++)
-      r->x[i] = asr(wmul((int64_t)row[i] - 128, (int64_t)(uint64_t)sc), 8);
-  }
-
-  for (uint32_t l = 0; l < c->layers; l++) {
-    const mat_t *Lm = &mats[1 + 7 * l];
-    const int32_t *n1 = m->norm + (uint64_t)(2 * l) * c->dim;
-    const int32_t *n2 = m->norm + (uint64_t)(2 * l + 1) * c->dim;
-    wr32(st + H_LAYER, l);
-    /* Phase 4: attention normalization into w1. */
-    fpi8_ref_rmsnorm(r->x, n1, c->dim, r->w1);
-    /* Phase 5: the query into w2. */
-    matvec(&Lm[K_Q - 1], r->w1, r->w2);
-    /* Phases 6 and 7: key and value into the cache (w3 holds the rows
-     * before the store). */
-    if (!store_rows(c, &Lm[K_K - 1], r->w1, r->w3, r->keys, cachepos, l, t))
-      return fail(r, 6, l);
-    if (!store_rows(c, &Lm[K_V - 1], r->w1, r->w3, r->values, cachepos, l, t))
-      return fail(r, 7, l);
-    /* Phase 8: rotary.  Reading: pairs are adjacent elements (2j, 2j+1) of
-     * each head, turned by the position's entry j of the tables; the
-     * query first, then this position's keys, each stored key checked. */
-    {
+  const mat_t *Lm = &mats[1 + 7 * l];
+  uint32_t np = p + 1, nl = l;
+  *ended = 0;
+  switch (p) {
+    case 3: {
+      /* Embedding, ((byte - 128) * scale) >> 8 with the token row's scale. */
+      const uint32_t tok = rd32(st + H_TOKEN);
+      const mat_t *E = &mats[0];
+      const uint8_t *row = E->w + (uint64_t)tok * c->dim;
+      uint32_t sc = rd32(E->s_bytes + 4ull * tok);
+      for (uint32_t i = 0; i < c->dim; i++)
+        r->x[i] = asr(wmul((int64_t)row[i] - 128, (int64_t)(uint64_t)sc), 8);
+      nl = 0;
+      break;
+    }
+    case 4: /* attention normalization into w1 */
+      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l) * c->dim, c->dim, r->w1);
+      break;
+    case 5: /* the query into w2 */
+      matvec(&Lm[K_Q - 1], r->w1, r->w2);
+      break;
+    case 6: /* the key into the cache (w3 holds the rows before the store) */
+      if (!store_rows(c, &Lm[K_K - 1], r->w1, r->w3, r->keys, cachepos, l, t)) return fail(r, 6, l);
+      break;
+    case 7: /* the value into the cache */
+      if (!store_rows(c, &Lm[K_V - 1], r->w1, r->w3, r->values, cachepos, l, t)) return fail(r, 7, l);
+      break;
+    case 8: {
+      /* Rotary.  Reading: pairs are adjacent elements (2j, 2j+1) of each
+       * head, turned by the position's entry j of the tables; the query
+       * first, then this position's keys, each stored key checked. */
       const int32_t *cs = m->cos_tab + (uint64_t)t * half;
       const int32_t *sn = m->sin_tab + (uint64_t)t * half;
       for (uint32_t h = 0; h < c->heads; h++)
         for (uint32_t j = 0; j < half; j++)
-          fpi8_ref_rotate(&r->w2[h * c->head + 2 * j], &r->w2[h * c->head + 2 * j + 1],
-                          cs[j], sn[j]);
+          fpi8_ref_rotate(&r->w2[h * c->head + 2 * j], &r->w2[h * c->head + 2 * j + 1], cs[j], sn[j]);
       for (uint32_t kh = 0; kh < c->kv_heads; kh++)
         for (uint32_t j = 0; j < half; j++) {
           int32_t *k0 = &r->keys[cache_index(c, cachepos, l, kh, t, 2 * j)];
@@ -612,70 +620,107 @@ static int32_t position(const model_t *m, const mat_t *mats, run_t *r) {
           k0[0] = (int32_t)a;
           k0[1] = (int32_t)b;
         }
+      break;
     }
-    /* Phase 9: attention, head by head, outputs into w3.  Head h reads key
-     * and value head h / (heads / kv_heads). */
-    for (uint32_t h = 0; h < c->heads; h++) {
-      uint32_t kh = h / group;
-      const int32_t *K = &r->keys[cache_index(c, cachepos, l, kh, 0, 0)];
-      const int32_t *V = &r->values[cache_index(c, cachepos, l, kh, 0, 0)];
-      fpi8_ref_attention_head(&r->w2[h * c->head], K, V, t + 1, c->head, c->head, m->inv,
-                              m->exp_tab, r->scores, &r->w3[h * c->head], NULL, NULL);
+    case 9: /* attention, head by head, outputs into w3; head h reads key and
+             * value head h / (heads / kv_heads) */
+      for (uint32_t h = 0; h < c->heads; h++) {
+        uint32_t kh = h / group;
+        const int32_t *K = &r->keys[cache_index(c, cachepos, l, kh, 0, 0)];
+        const int32_t *V = &r->values[cache_index(c, cachepos, l, kh, 0, 0)];
+        fpi8_ref_attention_head(&r->w2[h * c->head], K, V, t + 1, c->head, c->head, m->inv,
+                                m->exp_tab, r->scores, &r->w3[h * c->head], NULL, NULL);
+      }
+      break;
+    case 10: /* the attention output matrix into w1 */
+      matvec(&Lm[K_O - 1], r->w3, r->w1);
+      break;
+    case 11: /* residual, then the feed-forward normalization into w1 */
+      for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
+      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l + 1) * c->dim, c->dim, r->w1);
+      break;
+    case 12: /* gate */
+      matvec(&Lm[K_GATE - 1], r->w1, r->gate);
+      break;
+    case 13: /* up */
+      matvec(&Lm[K_UP - 1], r->w1, r->up);
+      break;
+    case 14: /* gate element through SiLU times the up element, >> 16, kept in gate */
+      for (uint32_t i = 0; i < c->hidden; i++)
+        r->gate[i] = asr(wmul(fpi8_ref_silu(r->gate[i], m->silu_tab), r->up[i]), 16);
+      break;
+    case 15: /* down into w1 */
+      matvec(&Lm[K_DOWN - 1], r->gate, r->w1);
+      break;
+    case 16: /* residual; then the next layer, the final phases, or the next
+              * prompt position (phases 17-19 run only where a token is
+              * generated: the last prompt position and every later one) */
+      for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
+      if (l + 1 < c->layers) {
+        np = 4;
+        nl = l + 1;
+      } else if (t + 1 >= n_ids) {
+        np = 17;
+        nl = 0;
+      } else {
+        wr32(st + H_TOKEN, r->ids[t + 1]);
+        wr32(st + H_POSITION, t + 1);
+        np = 3;
+        nl = 0;
+        *ended = 1;
+      }
+      break;
+    case 17: /* final normalization into w1 */
+      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * c->layers) * c->dim, c->dim, r->w1);
+      break;
+    case 18: /* classifier into the logits */
+      matvec(&mats[1 + 7 * c->layers], r->w1, r->logits);
+      break;
+    case 19: {
+      /* sampling; the token is appended, then phase 20 (token 1 or 2, or max
+       * tokens reached) or the next position */
+      uint64_t gen = rd64(st + H_GENERATOR);
+      const uint32_t next = fpi8_ref_sample(r->logits, c->vocab, rd32(st + H_TEMP), m->exp_tab, &gen);
+      wr64(st + H_GENERATOR, gen);
+      uint32_t g = rd32(st + H_GENERATED);
+      r->out[g] = next;
+      g++;
+      wr32(st + H_GENERATED, g);
+      const int complete = next == 1 || next == 2 || g == rd32(st + H_MAX);
+      wr32(st + H_TOKEN, next);
+      wr32(st + H_POSITION, t + 1);
+      np = complete ? 20 : 3;
+      nl = 0;
+      *ended = 1;
+      break;
     }
-    /* Phase 10: the attention output matrix into w1. */
-    matvec(&Lm[K_O - 1], r->w3, r->w1);
-    /* Phase 11: residual, then the feed-forward normalization into w1. */
-    for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
-    fpi8_ref_rmsnorm(r->x, n2, c->dim, r->w1);
-    /* Phases 12 and 13: gate and up. */
-    matvec(&Lm[K_GATE - 1], r->w1, r->gate);
-    matvec(&Lm[K_UP - 1], r->w1, r->up);
-    /* Phase 14: gate element through SiLU times the up element, >> 16,
-     * kept in the gate vector. */
-    for (uint32_t i = 0; i < c->hidden; i++)
-      r->gate[i] = asr(wmul(fpi8_ref_silu(r->gate[i], m->silu_tab), r->up[i]), 16);
-    /* Phase 15: down into w1.  Phase 16: residual. */
-    matvec(&Lm[K_DOWN - 1], r->gate, r->w1);
-    for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
+    default:
+      return FPI8_REF_INVALID_STATE;
   }
-  wr32(st + H_LAYER, 0);
-
-  uint32_t next_token;
-  int complete = 0;
-  if (t + 1 >= n_ids) {
-    /* Phases 17-19 run only where a token is generated: the last prompt
-     * position and every later one. */
-    fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * c->layers) * c->dim, c->dim, r->w1);
-    matvec(&mats[1 + 7 * c->layers], r->w1, r->logits);
-    uint64_t gen = rd64(st + H_GENERATOR);
-    next_token = fpi8_ref_sample(r->logits, c->vocab, rd32(st + H_TEMP), m->exp_tab, &gen);
-    wr64(st + H_GENERATOR, gen);
-    uint32_t g = rd32(st + H_GENERATED);
-    r->out[g] = next_token;
-    g++;
-    wr32(st + H_GENERATED, g);
-    /* Phase 20: token 1 or 2, or max tokens reached. */
-    complete = next_token == 1 || next_token == 2 || g == rd32(st + H_MAX);
-  } else {
-    next_token = r->ids[t + 1];
-  }
-  wr32(st + H_TOKEN, next_token);
-  wr32(st + H_POSITION, t + 1);
-  wr32(st + H_PHASE, complete ? 20 : 3);
+  wr32(st + H_PHASE, np);
+  wr32(st + H_LAYER, nl);
   return 0;
 }
 
 /* State checks shared by turn: tag, alignment, size for the configuration,
- * and a cursor at the start of a position ("Core errors", InvalidState). */
+ * and a cursor at a phase of a position: 3 (its start), 4 to 16 with a
+ * layer, or 17 to 19 at a position that generates ("Core errors",
+ * InvalidState).  Cursors inside a phase (row, attention stage and index,
+ * sampling pass) are not produced here and must be zero. */
 static int32_t check_state(const cfg_t *c, uint8_t *st, uint64_t len, fpi8_ref_layout *L) {
   if (((uintptr_t)st) & 7 || len < HEADER || memcmp(st, STATE_TAG, 8))
     return FPI8_REF_INVALID_STATE;
   uint32_t n_ids = rd32(st + H_NIDS), mx = rd32(st + H_MAX);
   if (!layout_ids(c, n_ids, mx, L) || L->total != len) return FPI8_REF_INVALID_STATE;
   if (rd32(st + H_CACHEPOS) != L->cache_positions) return FPI8_REF_INVALID_STATE;
-  if (rd32(st + H_ERROR) != 0 || rd32(st + H_PHASE) != 3 || rd32(st + H_LAYER) != 0)
+  const uint32_t phase = rd32(st + H_PHASE), layer = rd32(st + H_LAYER);
+  if (rd32(st + H_ERROR) != 0 || phase < 3 || phase > 19) return FPI8_REF_INVALID_STATE;
+  if ((phase >= 4 && phase <= 16) ? layer >= c->layers : layer != 0) return FPI8_REF_INVALID_STATE;
+  if (rd32(st + H_ROW) != 0 || rd32(st + H_STAGE) != 0 || rd32(st + H_INDEX) != 0 ||
+      rd32(st + H_PASS) != 0)
     return FPI8_REF_INVALID_STATE;
   uint32_t pos = rd32(st + H_POSITION), gen = rd32(st + H_GENERATED);
+  if (phase >= 17 && pos + 1 < n_ids) return FPI8_REF_INVALID_STATE;
   if (pos >= L->cache_positions) return FPI8_REF_INVALID_STATE;
   if (gen != (pos + 1 > n_ids ? pos + 1 - n_ids : 0)) return FPI8_REF_INVALID_STATE;
   if (rd32(st + H_TOKEN) >= c->vocab || rd32(st + H_TEMP) > (16u << 16))
@@ -683,8 +728,10 @@ static int32_t check_state(const cfg_t *c, uint8_t *st, uint64_t len, fpi8_ref_l
   return 0;
 }
 
-int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
-                      uint64_t state_len, uint32_t max_positions) {
+/* A turn from the cursor: whole positions (the first one finished from
+ * wherever the cursor stands) when by_phase is 0, else single phases. */
+static int32_t turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state, uint64_t state_len,
+                    uint32_t count, int by_phase) {
   model_t m;
   mat_t *mats;
   uint32_t nm;
@@ -714,11 +761,24 @@ int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
   r.ids = (uint32_t *)(state + r.L.ids);
   r.out = (uint32_t *)(state + r.L.out);
   wr64(state + H_TURNS, rd64(state + H_TURNS) + 1);
-  for (uint32_t k = 0; k < max_positions; k++) {
-    e = position(&m, mats, &r);
+  uint32_t done = 0;
+  while (done < count) {
+    int ended;
+    e = phase_step(&m, mats, &r, &ended);
     if (e) break;
+    if (by_phase || ended) done++;
     if (rd32(state + H_PHASE) == 20) break;
   }
   free(mats);
   return e;
+}
+
+int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
+                      uint64_t state_len, uint32_t max_positions) {
+  return turn(blob, blob_len, state, state_len, max_positions, 0);
+}
+
+int32_t fpi8_ref_turn_phases(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
+                             uint64_t state_len, uint32_t max_phases) {
+  return turn(blob, blob_len, state, state_len, max_phases, 1);
 }

@@ -104,9 +104,16 @@ int32_t fpi8_ref_init_state(const uint32_t cfg[7], uint8_t *state, uint64_t stat
 
 int32_t fpi8_ref_state_info(const uint8_t *state, uint64_t len, fpi8_ref_info *out);
 
-/* Runs up to max_positions whole positions of one run. */
+/* Runs up to max_positions positions of one run; the first one is
+ * finished from wherever the state's cursor stands. */
 int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
                       uint64_t state_len, uint32_t max_positions);
+
+/* Runs up to max_phases single phases of one run from the state's cursor
+ * (phase 3 to 19, with a layer for phases 4 to 16), stopping early at
+ * phase 20 or an error. */
+int32_t fpi8_ref_turn_phases(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
+                             uint64_t state_len, uint32_t max_phases);
 
 /* Byte offsets of the state's buffers (for tests that read them). */
 typedef struct {

@@ -683,6 +683,176 @@ def test_turn_cuts_do_not_change_results():
     assert np.array_equal(a, b)
 
 
+# --------------------------------------------------------------------------
+# Stopping between phases ("The resumable state")
+
+H_PHASE, H_LAYER, H_ROW = 8, 12, 16
+
+
+def set_cursor(st, phase, layer, row=0):
+    st[H_PHASE:H_PHASE + 4] = np.frombuffer(np.uint32(phase).tobytes(), np.uint8)
+    st[H_LAYER:H_LAYER + 4] = np.frombuffer(np.uint32(layer).tobytes(), np.uint8)
+    st[H_ROW:H_ROW + 4] = np.frombuffer(np.uint32(row).tobytes(), np.uint8)
+
+
+def test_each_phase_does_what_the_pages_list():
+    # One phase per turn: the cursor walks the pages' order (3, then 4-16 per
+    # layer, then 17-19 where a token is generated), and each phase writes
+    # the value of the building blocks pinned above, applied to the buffers
+    # the previous phases left, into the buffer the pages name.
+    shape = W.SMALL_SHAPES["gqa"]
+    cfg = shape.as_tuple()
+    bl = B.build_blob(shape, 41)
+    lay = B.plan(shape)
+    ids = W.prompt_ids(shape.vocab, 3, 4, 0)
+    max_tokens = 3
+    e, st = O.init_state(cfg, ids, max_tokens, 65536, 7)
+    assert e == 0
+    L = O.state_layout(cfg, len(ids), max_tokens)
+    D, Hd, hs = shape.dim, shape.hidden, shape.head_size
+    half, kvd, cp = hs // 2, shape.kv_dim, L["cache_positions"]
+
+    def view(name, n, dt=np.int64):
+        return st[L[name]: L[name] + np.dtype(dt).itemsize * n].view(dt)
+
+    def table(name, n):
+        return bl[lay.offsets[name]: lay.offsets[name] + 4 * n].view(np.int32)
+
+    norm = table("norm", (2 * shape.layers + 1) * D).reshape(-1, D)
+    cos = table("cos", shape.context * half).reshape(-1, half)
+    sin = table("sin", shape.context * half).reshape(-1, half)
+    exp_tab = table("exp", 4097).view(np.uint32)
+    silu_tab = table("silu", 4097)
+    keys = view("keys", shape.layers * shape.kv_heads * cp * hs, np.int32).reshape(
+        shape.layers, shape.kv_heads, cp, hs)
+    vals = view("values", shape.layers * shape.kv_heads * cp * hs, np.int32).reshape(
+        shape.layers, shape.kv_heads, cp, hs)
+
+    def mv(kind, layer, v):
+        return O.rows(*B.matrix_view(bl, shape, kind, layer), v).reshape(-1)
+
+    walked = []
+    gen = O.state_info(st)[1]["generator"]
+    while not O.state_info(st)[1]["complete"]:
+        info = O.state_info(st)[1]
+        p, l, t = info["phase"], info["layer"], info["position"]
+        walked.append((p, l, t))
+        x, w1, w2, w3 = (view(n, D).copy() for n in ("x", "w1", "w2", "w3"))
+        gate, up = view("gate", Hd).copy(), view("up", Hd).copy()
+        kc, vc = keys.copy(), vals.copy()
+        assert O.turn_phases(bl, st, 1) == 0
+        if p == 3:
+            E, sE = B.matrix_view(bl, shape, B.KIND_EMBED)
+            tok = info["token"]
+            want = ((E[tok].astype(np.int64) - 128) * int(sE[tok])) >> 8
+            assert np.array_equal(view("x", D), want)
+        elif p in (4, 11, 17):
+            xx = x + w1 if p == 11 else x
+            assert np.array_equal(view("x", D), xx)
+            k = 2 * shape.layers if p == 17 else 2 * l + (p == 11)
+            assert np.array_equal(view("w1", D), O.rmsnorm(xx, norm[k]))
+        elif p == 5:
+            assert np.array_equal(view("w2", D), mv(B.KIND_Q, l, w1))
+        elif p in (6, 7):
+            kind, cache, before = (B.KIND_K, keys, kc) if p == 6 else (B.KIND_V, vals, vc)
+            want = mv(kind, l, w1).reshape(shape.kv_heads, hs)
+            assert np.array_equal(cache[l, :, t], want)
+            before[l, :, t] = want
+            assert np.array_equal(cache, before)
+        elif p == 8:
+            q = w2.copy()
+            for h in range(shape.heads):
+                for j in range(half):
+                    i = h * hs + 2 * j
+                    q[i], q[i + 1] = O.rotate(int(q[i]), int(q[i + 1]), int(cos[t, j]), int(sin[t, j]))
+            assert np.array_equal(view("w2", D), q)
+            for kh in range(shape.kv_heads):
+                for j in range(half):
+                    a, b = O.rotate(int(kc[l, kh, t, 2 * j]), int(kc[l, kh, t, 2 * j + 1]),
+                                    int(cos[t, j]), int(sin[t, j]))
+                    kc[l, kh, t, 2 * j:2 * j + 2] = (a, b)
+            assert np.array_equal(keys, kc)
+        elif p == 9:
+            grp = shape.heads // shape.kv_heads
+            for h in range(shape.heads):
+                out = O.attention_head(w2[h * hs:(h + 1) * hs], keys[l, h // grp, :t + 1],
+                                       vals[l, h // grp, :t + 1], B.inv_sqrt_head(shape), exp_tab)[0]
+                assert np.array_equal(view("w3", D)[h * hs:(h + 1) * hs], out)
+        elif p == 10:
+            assert np.array_equal(view("w1", D), mv(B.KIND_O, l, w3))
+        elif p in (12, 13):
+            name, kind = ("gate", B.KIND_GATE) if p == 12 else ("up", B.KIND_UP)
+            assert np.array_equal(view(name, Hd), mv(kind, l, w1))
+        elif p == 14:
+            want = [(O.silu(int(g), silu_tab) * int(u)) >> 16 for g, u in zip(gate, up)]
+            assert np.array_equal(view("gate", Hd), np.array(want, np.int64))
+        elif p == 15:
+            assert np.array_equal(view("w1", D), mv(B.KIND_DOWN, l, gate))
+        elif p == 16:
+            assert np.array_equal(view("x", D), x + w1)
+        elif p == 18:
+            assert np.array_equal(view("logits", shape.vocab), mv(B.KIND_CLS, 0, w1))
+        elif p == 19:
+            tok, gen = O.sample(view("logits", shape.vocab), 65536, exp_tab, gen)
+            after = O.state_info(st)[1]
+            assert after["token"] == tok and after["generator"] == gen
+            assert view("out", max_tokens, np.uint32)[info["generated"]] == tok
+    per_layer = [(p, l) for l in range(shape.layers) for p in range(4, 17)]
+    want = []
+    for t in range(len(ids) + max_tokens - 1):
+        want += [(3, 0, t)] + [(p, l, t) for p, l in per_layer]
+        if t >= len(ids) - 1:
+            want += [(17, 0, t), (18, 0, t), (19, 0, t)]
+    # the run ends at the sampling of max_tokens tokens, or earlier at a
+    # closing token
+    assert walked == want[: len(walked)] and walked[-1][0] == 19
+    assert len(walked) == len(want) or O.state_info(st)[1]["generated"] < max_tokens
+
+
+def test_phase_cuts_do_not_change_results():
+    # Turns that stop after any number of phases, mixed with turns of whole
+    # positions, end in the state of one uninterrupted turn.
+    shape = W.SMALL_SHAPES["ragged"]
+    bl = B.build_blob(shape, 32)
+    ids = W.prompt_ids(shape.vocab, 5, 6, 0)
+    cfg = shape.as_tuple()
+    e, a = O.init_state(cfg, ids, 7, 3 * 65536 // 2, 5)
+    assert O.run_to_end(bl, a) == 0
+    rng = np.random.default_rng(8)
+    for trial in range(3):
+        e, b = O.init_state(cfg, ids, 7, 3 * 65536 // 2, 5)
+        while not O.state_info(b)[1]["complete"]:
+            if rng.random() < 0.2:
+                assert O.turn(bl, b, int(rng.integers(1, 3))) == 0
+            else:
+                assert O.turn_phases(bl, b, int(rng.integers(1, 40))) == 0
+        a[80:88] = 0
+        b[80:88] = 0
+        assert np.array_equal(a, b)
+
+
+def test_mid_position_cursor_checks():
+    shape, bl = tiny_setup()
+    cfg = shape.as_tuple()
+    e, st = O.init_state(cfg, [5, 6, 7], 2)
+    assert O.turn_phases(bl, st, 5) == 0
+    info = O.state_info(st)[1]
+    assert (info["phase"], info["layer"], info["position"]) == (8, 0, 0)
+    for phase, layer in ((2, 0), (20, 0), (4, shape.layers), (3, 1), (17, 0), (21, 0)):
+        bad = st.copy()
+        set_cursor(bad, phase, layer)
+        assert O.turn_phases(bl, bad, 1) == 3, (phase, layer)
+    bad = st.copy()
+    set_cursor(bad, 8, 0, row=1)                   # inside a phase
+    assert O.turn_phases(bl, bad, 1) == 3
+    assert O.turn_phases(bl, st, 0) == 0           # nothing to do
+    assert O.state_info(st)[1]["phase"] == 8
+    # a turn of positions finishes the one under way, then whole ones
+    assert O.turn(bl, st, 1) == 0
+    info = O.state_info(st)[1]
+    assert (info["phase"], info["layer"], info["position"]) == (3, 0, 1)
+
+
 def stop_token_blob(shape, seed=1000):
     """Every activation +127.0 from the embedding, no residual updates, and a
     classifier whose only nonzero row is the closing token's: token 2 wins."""
