@@ -199,7 +199,8 @@ Group group(fpi8_engine *e, int g, uint32_t r0, uint32_t n) {
 }
 
 RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t cols,
-                   const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer) {
+                   const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer,
+                   uint32_t step, uint32_t resume) {
   const uint32_t n_runs = G.n;
   RowsArgs a;
   memset(&a, 0, sizeof a);
@@ -222,6 +223,8 @@ RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t col
   a.half = e->c.head / 2;
   a.kv_heads = e->c.kv_heads;
   a.hidden = e->c.hidden;
+  a.step = step;
+  a.resume = resume;
   return a;
 }
 
@@ -261,30 +264,33 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
 }
 
-// One position of every active run of a group.
-int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s) {
+// One position of every active run of a group.  `resume`: some run's state
+// stands between two phases, so each launch checks the step each run starts
+// at (run_flags); every launch below is one step, in order.
+int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, uint32_t resume) {
   const Cfg &c = e->c;
   const uint32_t n_runs = G.n;
   int r;
   {
-    BeginArgs a{states, G.runs, n_runs, G.oflags, e->n_oflags};
+    BeginArgs a{states, G.runs, n_runs, G.oflags, e->n_oflags, c.layers};
     if ((r = launch_begin(a, s))) return r;
   }
   {
-    EmbedArgs a{states, G.runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S};
+    EmbedArgs a{states, G.runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S, resume};
     TimedLaunch t(e, T_EMBED, s);
     if ((r = launch_embed(a, s))) return r;
   }
   for (uint32_t l = 0; l < c.layers; l++) {
     uint32_t *fl = G.oflags + 4 * l;
+    const uint32_t s0 = 1 + 7 * l;
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
-                G.planes0, e->kp, e->bp, fl + 0, 0};
+                G.planes0, e->kp, e->bp, fl + 0, 0, s0, resume};
     {
       TimedLaunch t(e, T_NORM, s);
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 0, IN_W1, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 0, IN_W1, l, s0 + 1, resume);
       add_seg(a, e->layer_mat(l, M_Q), ROLE_Q);
       add_seg(a, e->layer_mat(l, M_K), ROLE_K);
       add_seg(a, e->layer_mat(l, M_V), ROLE_V);
@@ -293,23 +299,24 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s) {
     {
       AttnArgs a{states, G.runs, n_runs, l, c.heads, c.kv_heads, c.head,
                  c.heads / c.kv_heads, e->model.inv, e->exp_tab, G.planes0, e->kp, e->bp,
-                 fl + 1, e->score_cap};
+                 fl + 1, e->score_cap, s0 + 2, resume};
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l, s0 + 3, resume);
       add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_RESID, a, n_runs, s))) return r;
     }
     na.w = e->norm + (uint64_t)(2 * l + 1) * c.dim;
     na.oflag = fl + 2;
+    na.step = s0 + 4;
     {
       TimedLaunch t(e, T_NORM, s);
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 2, IN_W1, l);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 2, IN_W1, l, s0 + 5, resume);
       add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN);
       add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN);  // shares the gate's row tiles
       a.planes_out = G.planes1;
@@ -318,7 +325,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s) {
       if ((r = run_rows(e, EPI_GATEUP, a, n_runs, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.hidden, G.planes1, fl + 3, IN_GATE, l);
+      RowsArgs a = rows_base(e, G, states, c.hidden, G.planes1, fl + 3, IN_GATE, l, s0 + 6, resume);
       add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_DOWN, a, n_runs, s))) return r;
     }
@@ -326,12 +333,12 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s) {
   uint32_t *ff = G.oflags + 4 * c.layers;
   {
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
-                G.planes0, e->kp, e->bp, ff, 1};
+                G.planes0, e->kp, e->bp, ff, 1, 1 + 7 * c.layers, resume};
     TimedLaunch t(e, T_NORM, s);
     if ((r = launch_norm(na, s))) return r;
   }
   {
-    RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, ff, IN_W1, 0);
+    RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, ff, IN_W1, 0, 2 + 7 * c.layers, resume);
     add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN);
     if ((r = run_rows(e, EPI_CLS, a, n_runs, s))) return r;
   }
@@ -351,15 +358,15 @@ uint32_t n_groups(const fpi8_engine *e, uint32_t n_runs) {
 
 // One position of every active run: one group on stream s, or two, the
 // second on the engine's side stream, forked from and joined back to s.
-int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s) {
-  if (n_groups(e, n_runs) == 1) return step_group(e, group(e, 0, 0, n_runs), states, s);
+int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s, uint32_t resume) {
+  if (n_groups(e, n_runs) == 1) return step_group(e, group(e, 0, 0, n_runs), states, s, resume);
   int r;
   const uint32_t h = (n_runs / 2 + 15) / 16 * 16 < n_runs ? (n_runs / 2 + 15) / 16 * 16 : n_runs / 2;
   if ((r = hip_ok(hipEventRecord(e->ev_fork, s))) ||
       (r = hip_ok(hipStreamWaitEvent(e->side_stream, e->ev_fork, 0))))
     return r;
-  if ((r = step_group(e, group(e, 0, 0, h), states, s))) return r;
-  if ((r = step_group(e, group(e, 1, h, n_runs - h), states, e->side_stream))) return r;
+  if ((r = step_group(e, group(e, 0, 0, h), states, s, resume))) return r;
+  if ((r = step_group(e, group(e, 1, h, n_runs - h), states, e->side_stream, resume))) return r;
   if ((r = hip_ok(hipEventRecord(e->ev_join, e->side_stream))) ||
       (r = hip_ok(hipStreamWaitEvent(s, e->ev_join, 0))))
     return r;
@@ -381,7 +388,7 @@ int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   if (!e->cap_stream && (r = hip_ok(hipStreamCreateWithFlags(&e->cap_stream, hipStreamNonBlocking))))
     return r;
   if ((r = hip_ok(hipStreamBeginCapture(e->cap_stream, hipStreamCaptureModeThreadLocal)))) return r;
-  const int rs = step(e, states, n_runs, e->cap_stream);
+  const int rs = step(e, states, n_runs, e->cap_stream, 0);
   hipGraph_t g = nullptr;
   const hipError_t ec = hipStreamEndCapture(e->cap_stream, &g);
   if (rs) {
@@ -525,7 +532,7 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
                                    hipMemcpyDeviceToHost, s))) ||
       (r = hip_ok(hipStreamSynchronize(s))))
     return r;
-  uint32_t steps = 0;
+  uint32_t steps = 0, resume = 0;
   for (uint32_t b = 0; b < n_runs; b++) {
     RunDesc &rd = e->h_runs[b];
     memset(&rd, 0, sizeof rd);
@@ -546,6 +553,8 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
     rd.off_keys = L.keys; rd.off_values = L.values; rd.off_ids = L.ids; rd.off_out = L.out;
     memcpy(&v, h + ST_POSITION, 4);
     steps = std::max(steps, L.cachepos - v);
+    memcpy(&v, h + ST_PHASE, 4);
+    if (v != 3) resume = 1;
   }
   steps = std::min(steps, max_positions);
   // Attention keeps one score per cached position in LDS: size it for the
@@ -562,13 +571,21 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
   if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
   bool timing = false;
   for (const Timer &t : e->timers) timing = timing || t.on;
-  if (steps > 0 && !timing && e->use_graph) {
+  // A run that stopped between two phases finishes its position first, in
+  // launches that check where each run starts; the recorded position
+  // serves the rest.
+  uint32_t k0 = 0;
+  if (resume && steps > 0) {
+    if ((r = step(e, d_states, n_runs, s, 1))) return r;
+    k0 = 1;
+  }
+  if (steps > k0 && !timing && e->use_graph) {
     if ((r = step_graph(e, d_states, n_runs))) return r;
-    for (uint32_t k = 0; k < steps; k++)
+    for (uint32_t k = k0; k < steps; k++)
       if ((r = hip_ok(hipGraphLaunch(e->graph, s)))) return r;
   } else {
-    for (uint32_t k = 0; k < steps; k++)
-      if ((r = step(e, d_states, n_runs, s))) return r;
+    for (uint32_t k = k0; k < steps; k++)
+      if ((r = step(e, d_states, n_runs, s, 0))) return r;
   }
   if ((r = hip_ok(hipMemcpyAsync(e->h_err, e->d_run_err, 4ull * n_runs, hipMemcpyDeviceToHost, s))) ||
       (r = hip_ok(hipStreamSynchronize(s))))

@@ -69,11 +69,20 @@ int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L
   uint32_t n_ids = ld32(h + ST_NIDS), mx = ld32(h + ST_MAX);
   if (!state_layout(c, n_ids, mx, L) || L->total > stride) return FPI8_INVALID_STATE;
   if (ld32(h + ST_CACHEPOS) != L->cachepos) return FPI8_INVALID_STATE;
-  if (ld32(h + ST_ERROR) != 0 || ld32(h + ST_LAYER) != 0) return FPI8_INVALID_STATE;
-  uint32_t phase = ld32(h + ST_PHASE);
-  if (phase == 20) return -1;
-  if (phase != 3) return FPI8_INVALID_STATE;
+  if (ld32(h + ST_ERROR) != 0) return FPI8_INVALID_STATE;
+  // The cursor: a phase boundary of a position (3 its start; 4-16 with a
+  // layer; 17-19 only where the position generates), or 20 (complete).
+  // Cursors inside a phase (row, attention stage and index, sampling pass)
+  // are not taken.
+  const uint32_t phase = ld32(h + ST_PHASE), layer = ld32(h + ST_LAYER);
+  if (phase == 20 && layer == 0) return -1;
+  if (phase < 3 || phase > 19) return FPI8_INVALID_STATE;
+  if ((phase >= 4 && phase <= 16) ? layer >= c.layers : layer != 0) return FPI8_INVALID_STATE;
+  if (ld32(h + ST_ROW) != 0 || ld32(h + ST_STAGE) != 0 || ld32(h + ST_INDEX) != 0 ||
+      ld32(h + ST_PASS) != 0)
+    return FPI8_INVALID_STATE;
   uint32_t pos = ld32(h + ST_POSITION), gen = ld32(h + ST_GENERATED);
+  if (phase >= 17 && pos + 1 < n_ids) return FPI8_INVALID_STATE;
   if (pos >= L->cachepos) return FPI8_INVALID_STATE;
   if (gen != (pos + 1 > n_ids ? pos + 1 - n_ids : 0)) return FPI8_INVALID_STATE;
   if (ld32(h + ST_TOKEN) >= c.vocab || ld32(h + ST_TEMP) > (16u << 16)) return FPI8_INVALID_STATE;

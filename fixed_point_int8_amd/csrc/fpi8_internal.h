@@ -44,7 +44,8 @@ int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L
 enum : uint32_t {
   ST_PHASE = 8, ST_LAYER = 12, ST_ROW = 16, ST_POSITION = 20, ST_TOKEN = 24, ST_ERROR = 28,
   ST_NIDS = 32, ST_MAX = 36, ST_TEMP = 40, ST_GENERATED = 44, ST_CACHEPOS = 48,
-  ST_GENERATOR = 72, ST_TURNS = 80, ST_HEADER = 128
+  ST_GENERATOR = 72, ST_TURNS = 80, ST_PASS = 100, ST_STAGE = 120, ST_INDEX = 124,
+  ST_HEADER = 128
 };
 
 // Matrix kinds of the artifact.
@@ -55,7 +56,7 @@ enum : uint32_t { M_EMBED, M_Q, M_K, M_V, M_O, M_GATE, M_UP, M_DOWN, M_CLS, M_KI
 // every position.
 struct RunDesc {
   // dynamic
-  uint32_t flags;     // RUN_ACTIVE, RUN_GEN
+  uint32_t flags;     // RUN_ACTIVE, RUN_GEN, and where the position resumes (run_flags)
   uint32_t pos;       // position computed in this step
   uint32_t token;     // token embedded in this step
   uint32_t errkey;    // first failing (layer, phase) of this step, ~0 if none
@@ -69,6 +70,20 @@ struct RunDesc {
 };
 
 enum : uint32_t { RUN_ACTIVE = 1u, RUN_GEN = 2u };
+
+// A position runs as a fixed sequence of launches, numbered by step: 0 the
+// embedding; for layer l, 1 + 7l the first normalization, 2 + 7l the query,
+// key and value rows with rotary, 3 + 7l attention, 4 + 7l the output rows
+// with the residual, 5 + 7l the second normalization, 6 + 7l gate/up with
+// SiLU, 7 + 7l down with the residual; then 1 + 7L the final normalization,
+// 2 + 7L the classifier and 3 + 7L sampling.  A run whose state stands
+// between two phases of a position starts at a later step (`start`), and the
+// fused launch that holds its phase takes the results of the phases already
+// done from the state (`pick`, the state's phase; at step start + after).
+// flags bits: 0-1 RUN_ACTIVE / RUN_GEN, 2-6 pick, 7 after, 8-31 start.
+constexpr uint32_t run_flags(uint32_t active_gen, uint32_t start, uint32_t pick, uint32_t after) {
+  return active_gen | (pick << 2) | (after << 7) | (start << 8);
+}
 
 // Rows of one matrix inside a row-kernel launch.
 struct Seg {
@@ -112,6 +127,8 @@ struct RowsArgs {
   const int32_t *rope_cos, *rope_sin;   // [context][head/2]
   const int32_t *silu;                  // [4097]
   uint32_t head, half, kv_heads, hidden;
+  uint32_t step;            // this launch's step in the position (run_flags)
+  uint32_t resume;          // some run starts this position after step 0
   // gate/up epilogue: digits of the hidden vector for the down matrix
   int8_t *planes_out;
   uint32_t kp_out;
@@ -131,6 +148,7 @@ struct NormArgs {
   uint32_t kp, bp;
   uint32_t *oflag;
   uint32_t final_norm;      // 1: only generating runs (phase 17)
+  uint32_t step, resume;    // as in RowsArgs
 };
 
 struct EmbedArgs {
@@ -139,6 +157,7 @@ struct EmbedArgs {
   uint32_t n_runs, dim, vocab;
   const uint8_t *E;
   const uint32_t *S;
+  uint32_t resume;          // as in RowsArgs (the embedding is step 0)
 };
 
 struct AttnArgs {
@@ -151,6 +170,7 @@ struct AttnArgs {
   uint32_t kp, bp;
   uint32_t *oflag;
   uint32_t max_npos;        // LDS score slots: at least every run's cache positions
+  uint32_t step, resume;    // as in RowsArgs
 };
 
 struct SampleArgs {
@@ -167,6 +187,7 @@ struct BeginArgs {
   uint32_t n_runs;
   uint32_t *oflags;
   uint32_t n_oflags;
+  uint32_t layers;
 };
 
 // Launchers (defined in the .hip file).

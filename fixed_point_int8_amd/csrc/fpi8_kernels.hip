@@ -124,7 +124,12 @@ __global__ void k_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs) {
   *turns += 1;
 }
 
-// First kernel of a position: which runs compute it, which generate.
+// First kernel of a position: which runs compute it, which generate, and
+// for a run whose state stands between two phases, the step it starts at
+// and the phase its fused launch picks up at (run_flags).  A phase whose
+// inputs are still in the state and whose outputs nothing has read yet is
+// run again rather than picked up: the normalizations (5 after 4, 12 after
+// 11, 18 after 17) and attention (10 after 9) give the same words again.
 __global__ void k_begin(BeginArgs a) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < a.n_oflags) a.oflags[i] = 0;
@@ -134,23 +139,51 @@ __global__ void k_begin(BeginArgs a) {
   if (rd.valid) {
     const uint8_t *st = run_base(a.states, rd);
     const uint32_t phase = *reinterpret_cast<const uint32_t *>(st + ST_PHASE);
+    const uint32_t layer = *reinterpret_cast<const uint32_t *>(st + ST_LAYER);
     const uint32_t err = *reinterpret_cast<const uint32_t *>(st + ST_ERROR);
-    if (phase == 3 && err == 0) {
+    if (phase >= 3 && phase <= 19 && err == 0) {
       const uint32_t pos = *reinterpret_cast<const uint32_t *>(st + ST_POSITION);
       rd.pos = pos;
       rd.token = *reinterpret_cast<const uint32_t *>(st + ST_TOKEN);
-      flags = RUN_ACTIVE | (pos + 1 >= rd.n_ids ? RUN_GEN : 0u);
+      const uint32_t l7 = 7 * layer, f7 = 7 * a.layers;
+      uint32_t start = 0, pick = 0, after = 0;
+      switch (phase) {
+        case 4: case 5: start = 1 + l7; break;
+        case 6: case 7: case 8: start = 1 + l7; pick = phase; after = 1; break;
+        case 9: case 10: start = 3 + l7; break;
+        case 11: start = 4 + l7; pick = 11; break;
+        case 12: start = 5 + l7; break;
+        case 13: case 14: case 15: start = 5 + l7; pick = phase; after = 1; break;
+        case 16: start = 7 + l7; pick = 16; break;
+        case 17: case 18: start = 1 + f7; break;
+        case 19: start = 3 + f7; break;
+        default: break;
+      }
+      flags = run_flags(RUN_ACTIVE | (pos + 1 >= rd.n_ids ? RUN_GEN : 0u), start, pick, after);
     }
   }
   rd.flags = flags;
   rd.errkey = 0xFFFFFFFFu;
 }
 
+// Whether a run takes part in the launch at `step` of its position (it is
+// active, generates where `need` says so, and does not start later).
+__device__ __forceinline__ bool live_at(uint32_t flags, uint32_t need, uint32_t step,
+                                        uint32_t resume) {
+  return (flags & need) != 0 && (resume == 0 || (flags >> 8) <= step);
+}
+
+// The state's phase that the fused launch at `step` picks up at for this
+// run, or 0 when it runs the launch's phases from the start.
+__device__ __forceinline__ uint32_t pick_at(uint32_t flags, uint32_t step, uint32_t resume) {
+  return resume != 0 && (flags >> 8) + ((flags >> 7) & 1u) == step ? (flags >> 2) & 31u : 0u;
+}
+
 // Phase 3: ((byte - 128) * scale) >> 8 with the token row's scale.
 __global__ void k_embed(EmbedArgs a) {
   const uint32_t b = blockIdx.y;
   const RunDesc &rd = a.runs[b];
-  if (!(rd.flags & RUN_ACTIVE)) return;
+  if (!live_at(rd.flags, RUN_ACTIVE, 0, a.resume)) return;
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= a.dim) return;
   const uint32_t tok = rd.token;
@@ -169,8 +202,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   constexpr int U = 8;  // loads in flight per thread
   const uint32_t b = blockIdx.x, nt = blockDim.x;
   const RunDesc &rd = a.runs[b];
-  const uint32_t need = a.final_norm ? RUN_GEN : RUN_ACTIVE;
-  if (!(rd.flags & need)) return;
+  if (!live_at(rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.resume)) return;
   uint8_t *st = run_base(a.states, rd);
   const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
   int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
@@ -291,8 +323,7 @@ template <int EPI>
 __device__ __forceinline__ bool row_run_ok(const RowsArgs &a, uint32_t b) {
   if (b >= a.n_runs) return false;
   if (EPI == EPI_RAW) return true;
-  const uint32_t f = a.runs[b].flags;
-  return EPI == EPI_CLS ? (f & RUN_GEN) != 0 : (f & RUN_ACTIVE) != 0;
+  return live_at(a.runs[b].flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.resume);
 }
 
 template <int EPI>
@@ -434,8 +465,7 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
     in.flags[bt] = b < a.n_runs ? rd.flags : 0u;
     in.base[bt] = rd.base;
     if (EPI == EPI_CLS) in.o1[bt] = rd.off_logits;
-    if (EPI == EPI_RESID || EPI == EPI_DOWN) in.o1[bt] = rd.off_x;
-    if (EPI == EPI_DOWN) in.o2[bt] = rd.off_w1;
+    if (EPI == EPI_RESID || EPI == EPI_DOWN) { in.o1[bt] = rd.off_x; in.o2[bt] = rd.off_w1; }
     if (EPI == EPI_GATEUP) { in.o1[bt] = rd.off_gate; in.o2[bt] = rd.off_up; }
     if (EPI == EPI_QKV) {
       in.pos[bt] = rd.pos;
@@ -446,9 +476,9 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
 }
 
 template <int EPI>
-__device__ __forceinline__ bool epi_live(uint32_t flags) {
+__device__ __forceinline__ bool epi_live(const RowsArgs &a, uint32_t flags) {
   if (EPI == EPI_RAW) return flags != 0;
-  return EPI == EPI_CLS ? (flags & RUN_GEN) != 0 : (flags & RUN_ACTIVE) != 0;
+  return live_at(flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.resume);
 }
 
 template <int EPI, int MT, int BT>
@@ -509,7 +539,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
-    if (!epi_live<EPI>(in.flags[bt])) continue;
+    if (!epi_live<EPI>(a, in.flags[bt])) continue;
     int64_t y[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -530,6 +560,9 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
     }
     RunDesc &rd = a.runs[b];  // only for recording a fit failure
     uint8_t *st = a.states + in.base[bt];
+    // A run that stopped inside this launch's phases: the results of the
+    // phases it finished come from its state instead of the sums.
+    const uint32_t pick = pick_at(in.flags[bt], a.step, a.resume);
 #pragma unroll
     for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
       const uint32_t r0 = rbase[mt] + 4 * lg;
@@ -541,11 +574,14 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
       } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
         int64_t *x = reinterpret_cast<int64_t *>(st + in.o1[bt]);
         int64_t *w1 = reinterpret_cast<int64_t *>(st + in.o2[bt]);
+        // picked up at 11 or 16: the matrix's output is already in w1
+        const bool held = pick == (EPI == EPI_RESID ? 11u : 16u);
 #pragma unroll
         for (int j = 0; j < 4; j++)
           if (r0 + j < rcount[mt]) {
-            if (EPI == EPI_DOWN) w1[r0 + j] = y[mt][j];
-            x[r0 + j] = wadd(in.x[EPI == EPI_RESID || EPI == EPI_DOWN ? mt : 0][bt][j], y[mt][j]);
+            const int64_t yv = held ? w1[r0 + j] : y[mt][j];
+            if (EPI == EPI_DOWN) w1[r0 + j] = yv;
+            x[r0 + j] = wadd(in.x[EPI == EPI_RESID || EPI == EPI_DOWN ? mt : 0][bt][j], yv);
           }
       } else if (EPI == EPI_GATEUP) {
         // Phase 14: h = (SILU(gate) * up) >> 16, kept in the gate vector.
@@ -556,9 +592,12 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
         for (int j = 0; j < 4; j++) {
           const uint32_t row = r0 + j;
           if (row >= a.hidden) continue;
-          const int64_t g = y[mt][j], u = y[mt + HALF][j];
+          // picked up at 13: the gate is in the state; at 14 the up rows
+          // too; at 15 the product is already in the gate vector
+          const int64_t g = pick >= 13 ? gate[row] : y[mt][j];
+          const int64_t u = pick >= 14 ? up[row] : y[mt + HALF][j];
           const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)silu[(g + lim) >> 9];
-          const int64_t h = wmul(sg, u) >> 16;
+          const int64_t h = pick == 15 ? g : wmul(sg, u) >> 16;
           gate[row] = h;
           up[row] = u;
           put_digits(a.planes_out, a.bp, a.kp_out, b, row, h, a.oflag_out);
@@ -573,9 +612,11 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
           for (int j = 0; j < 4; j++) {
             const uint32_t row = r0 + j;
             if (row >= rcount[mt]) continue;
-            if (!fits32(y[mt][j])) { fail(rd, a.layer, 7); continue; }
             const uint32_t kvh = row / a.head, e = row % a.head;
-            V[(((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e] = (int32_t)y[mt][j];
+            int32_t *dst = V + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
+            const int64_t yv = pick >= 8 ? (int64_t)*dst : y[mt][j];  // stored before the cut
+            if (!fits32(yv)) { fail(rd, a.layer, 7); continue; }
+            *dst = (int32_t)yv;
           }
         } else {
           // Phase 8 on the query (kept in w2) and on the key after its
@@ -587,7 +628,14 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
           for (int j = 0; j < 4; j += 2) {
             const uint32_t row = r0 + j;
             if (row >= rcount[mt]) continue;
-            const int64_t A0 = y[mt][j], B0 = y[mt][j + 1];
+            int32_t *dst = nullptr;  // the key's cache words
+            if (role == ROLE_K)
+              dst = K + (((uint64_t)a.layer * a.kv_heads + row / a.head) * in.cache[bt] + pos) * a.head + row % a.head;
+            // picked up at 6 or later: the query (unturned) is in w2; at 7
+            // or later the key (unturned) is in the cache
+            int64_t A0 = y[mt][j], B0 = y[mt][j + 1];
+            if (role == ROLE_Q && pick >= 6) { A0 = q[row]; B0 = q[row + 1]; }
+            if (role == ROLE_K && pick >= 7) { A0 = dst[0]; B0 = dst[1]; }
             if (role == ROLE_K && (!fits32(A0) || !fits32(B0))) { fail(rd, a.layer, 6); continue; }
             const int64_t c = in.c[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
             const int64_t s = in.s[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
@@ -598,8 +646,6 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
               q[row + 1] = rb;
             } else {
               if (!fits32(ra) || !fits32(rb)) { fail(rd, a.layer, 8); continue; }
-              const uint32_t kvh = row / a.head, e = row % a.head;
-              int32_t *dst = K + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
               dst[0] = (int32_t)ra;
               dst[1] = (int32_t)rb;
             }
@@ -1169,7 +1215,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   const uint32_t h = blockIdx.x, b = blockIdx.y;
   const RunDesc &rd = a.runs[b];
-  if (!(rd.flags & RUN_ACTIVE)) return;
+  if (!live_at(rd.flags, RUN_ACTIVE, a.step, a.resume)) return;
   const uint32_t hs = HS ? HS : a.head;
   const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
   const uint32_t npos = rd.pos + 1, cachepos = rd.cachepos;
@@ -1501,6 +1547,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     *reinterpret_cast<uint32_t *>(st + ST_TOKEN) = token;
     *reinterpret_cast<uint32_t *>(st + ST_POSITION) = pos + 1;
     *reinterpret_cast<uint32_t *>(st + ST_PHASE) = complete ? 20u : 3u;
+    *reinterpret_cast<uint32_t *>(st + ST_LAYER) = 0u;
   }
 }
 

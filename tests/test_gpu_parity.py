@@ -446,6 +446,90 @@ def test_invalid_and_complete_runs_in_a_batch():
         pair.model.close()
 
 
+# ---------------------------------------------------------------------------
+# States that stand between two phases ("The resumable state")
+
+def cut_at(blob, st, position, phase, layer):
+    """Advances an oracle state one phase at a time to the cursor."""
+    while True:
+        i = O.state_info(st)[1]
+        if (i["position"], i["phase"], i["layer"]) == (position, phase, layer):
+            return
+        assert not i["complete"] and i["position"] <= position
+        assert O.turn_phases(blob, st, 1) == 0
+
+
+def phase_cuts(shape, prompt):
+    """Every cursor a position has, at a prompt position and at a generating
+    one: (position, phase, layer)."""
+    out = []
+    for t in (1, prompt + 1):
+        out.append((t, 3, 0))
+        for l in range(shape.layers):
+            out += [(t, p, l) for p in range(4, 17)]
+    for t in (prompt - 1, prompt + 1):
+        out += [(t, p, 0) for p in (17, 18, 19)]
+    return out
+
+
+@pytest.mark.parametrize("row_kernel,streams", [(0, 0), (1, 0), (2, 2)])
+def test_resume_between_phases(row_kernel, streams):
+    # Oracle runs stopped after every phase of a position, one per run, on
+    # the GPU in one batch: the first turn finishes each run's position, and
+    # every later word matches the oracle's uninterrupted arithmetic.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 51)
+    prompt = 4
+    cuts = phase_cuts(shape, prompt)
+    n = len(cuts)
+    say(f"resume between phases: {n} runs, row kernel {row_kernel}, streams {streams}")
+    temps = [0 if r % 3 else 65536 for r in range(n)]
+    runs = spec(shape, n, prompt, 5, seed=3, temps=temps)
+    pair = Pair(shape, blob, runs)
+    assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    assert B.fpi8_engine_set_streams(pair.model.engine, streams) == 0
+    try:
+        for i, (t, p, l) in enumerate(cuts):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, t, p, l)
+            pair.load(i, st)
+        for k in (1, 1, 2):
+            errs = pair.turn(k)
+            assert not any(errs), errs
+            pair.compare()
+        while not pair.complete():
+            pair.turn(1 << 20)
+        pair.compare()
+    finally:
+        pair.model.close()
+
+
+def test_resume_cursor_checks():
+    # Cursors the pages' state cannot hold get error 3, on the GPU as in the
+    # oracle; the run is left as it is.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 52)
+    runs = spec(shape, 6, 4, 3, seed=4)
+    pair = Pair(shape, blob, runs)
+    bad = [(17, 0, 0), (4, shape.layers, 0), (3, 1, 0), (2, 0, 0), (9, 0, 1), (21, 0, 0)]
+    try:
+        for i, (p, l, row) in enumerate(bad):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, 1, 5, 0)
+            st[8:12] = np.frombuffer(np.uint32(p).tobytes(), np.uint8)
+            st[12:16] = np.frombuffer(np.uint32(l).tobytes(), np.uint8)
+            st[16:20] = np.frombuffer(np.uint32(row).tobytes(), np.uint8)
+            assert O.turn(blob, st.copy(), 1) == 3
+            pair.load(i, st)
+        before = [pair.batch.state(i) for i in range(len(bad))]
+        errs = pair.turn(1, oracle_runs=[])
+        assert list(errs) == [3] * len(bad)
+        for i in range(len(bad)):
+            assert np.array_equal(before[i], pair.batch.state(i))
+    finally:
+        pair.model.close()
+
+
 def test_stop_token_completes_a_run():
     from test_oracle_pins import stop_token_blob
     shape = W.TINY.shape
