@@ -28,7 +28,7 @@ UINT64_MAX = (1 << 64) - 1
 # Symbols include/fpi8.h declares.
 EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_init_state",
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
-           "fpi8_engine_destroy", "fpi8_turn", "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
+           "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -68,6 +68,7 @@ def lib():
                                                C.POINTER(_P)]),
             "fpi8_engine_destroy": (None, [_P]),
             "fpi8_turn": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
+            "fpi8_turn_phases": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -175,6 +176,14 @@ def fpi8_turn(engine, d_states, state_stride: int, n_runs: int, max_positions: i
     errs = np.zeros(n_runs, dtype=np.int32)
     e = lib().fpi8_turn(engine, _dev_ptr(d_states), state_stride, n_runs, max_positions,
                         _stream_ptr(stream), _np_ptr(errs))
+    return e, errs
+
+
+def fpi8_turn_phases(engine, d_states, state_stride: int, n_runs: int, max_phases: int,
+                     stream=None):
+    errs = np.zeros(n_runs, dtype=np.int32)
+    e = lib().fpi8_turn_phases(engine, _dev_ptr(d_states), state_stride, n_runs, max_phases,
+                               _stream_ptr(stream), _np_ptr(errs))
     return e, errs
 
 

@@ -200,7 +200,7 @@ Group group(fpi8_engine *e, int g, uint32_t r0, uint32_t n) {
 
 RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t cols,
                    const int8_t *planes, const uint32_t *oflag, uint32_t in_sel, uint32_t layer,
-                   uint32_t step, uint32_t resume) {
+                   uint32_t step, uint32_t partial) {
   const uint32_t n_runs = G.n;
   RowsArgs a;
   memset(&a, 0, sizeof a);
@@ -224,7 +224,7 @@ RowsArgs rows_base(fpi8_engine *e, const Group &G, uint8_t *states, uint32_t col
   a.kv_heads = e->c.kv_heads;
   a.hidden = e->c.hidden;
   a.step = step;
-  a.resume = resume;
+  a.partial = partial;
   return a;
 }
 
@@ -264,10 +264,11 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
 }
 
-// One position of every active run of a group.  `resume`: some run's state
-// stands between two phases, so each launch checks the step each run starts
-// at (run_flags); every launch below is one step, in order.
-int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, uint32_t resume) {
+// One position of every active run of a group.  `partial`: some run starts
+// this position between two phases or stops before its end, so each launch
+// checks the steps each run runs (run_flags, RunDesc::end); every launch
+// below is one step, in order.
+int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, uint32_t partial) {
   const Cfg &c = e->c;
   const uint32_t n_runs = G.n;
   int r;
@@ -276,7 +277,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
     if ((r = launch_begin(a, s))) return r;
   }
   {
-    EmbedArgs a{states, G.runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S, resume};
+    EmbedArgs a{states, G.runs, n_runs, c.dim, c.vocab, e->mats[0].W, e->mats[0].S, partial};
     TimedLaunch t(e, T_EMBED, s);
     if ((r = launch_embed(a, s))) return r;
   }
@@ -284,13 +285,13 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
     uint32_t *fl = G.oflags + 4 * l;
     const uint32_t s0 = 1 + 7 * l;
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
-                G.planes0, e->kp, e->bp, fl + 0, 0, s0, resume};
+                G.planes0, e->kp, e->bp, fl + 0, 0, s0, partial};
     {
       TimedLaunch t(e, T_NORM, s);
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 0, IN_W1, l, s0 + 1, resume);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 0, IN_W1, l, s0 + 1, partial);
       add_seg(a, e->layer_mat(l, M_Q), ROLE_Q);
       add_seg(a, e->layer_mat(l, M_K), ROLE_K);
       add_seg(a, e->layer_mat(l, M_V), ROLE_V);
@@ -299,12 +300,12 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
     {
       AttnArgs a{states, G.runs, n_runs, l, c.heads, c.kv_heads, c.head,
                  c.heads / c.kv_heads, e->model.inv, e->exp_tab, G.planes0, e->kp, e->bp,
-                 fl + 1, e->score_cap, s0 + 2, resume};
+                 fl + 1, e->score_cap, s0 + 2, partial};
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l, s0 + 3, resume);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l, s0 + 3, partial);
       add_seg(a, e->layer_mat(l, M_O), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_RESID, a, n_runs, s))) return r;
     }
@@ -316,7 +317,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
       if ((r = launch_norm(na, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 2, IN_W1, l, s0 + 5, resume);
+      RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 2, IN_W1, l, s0 + 5, partial);
       add_seg(a, e->layer_mat(l, M_GATE), ROLE_PLAIN);
       add_seg(a, e->layer_mat(l, M_UP), ROLE_PLAIN);  // shares the gate's row tiles
       a.planes_out = G.planes1;
@@ -325,7 +326,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
       if ((r = run_rows(e, EPI_GATEUP, a, n_runs, s))) return r;
     }
     {
-      RowsArgs a = rows_base(e, G, states, c.hidden, G.planes1, fl + 3, IN_GATE, l, s0 + 6, resume);
+      RowsArgs a = rows_base(e, G, states, c.hidden, G.planes1, fl + 3, IN_GATE, l, s0 + 6, partial);
       add_seg(a, e->layer_mat(l, M_DOWN), ROLE_PLAIN);
       if ((r = run_rows(e, EPI_DOWN, a, n_runs, s))) return r;
     }
@@ -333,17 +334,18 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
   uint32_t *ff = G.oflags + 4 * c.layers;
   {
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
-                G.planes0, e->kp, e->bp, ff, 1, 1 + 7 * c.layers, resume};
+                G.planes0, e->kp, e->bp, ff, 1, 1 + 7 * c.layers, partial};
     TimedLaunch t(e, T_NORM, s);
     if ((r = launch_norm(na, s))) return r;
   }
   {
-    RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, ff, IN_W1, 0, 2 + 7 * c.layers, resume);
+    RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, ff, IN_W1, 0, 2 + 7 * c.layers, partial);
     add_seg(a, e->mats[1 + 7 * c.layers], ROLE_PLAIN);
     if ((r = run_rows(e, EPI_CLS, a, n_runs, s))) return r;
   }
   {
-    SampleArgs a{states, G.runs, n_runs, c.vocab, e->exp_tab, G.run_err};
+    SampleArgs a{states, G.runs, n_runs, c.vocab, e->exp_tab, G.run_err, 3 + 7 * c.layers,
+                 partial, c.layers};
     TimedLaunch t(e, T_SAMPLE, s);
     if ((r = launch_sample(a, s))) return r;
   }
@@ -358,15 +360,15 @@ uint32_t n_groups(const fpi8_engine *e, uint32_t n_runs) {
 
 // One position of every active run: one group on stream s, or two, the
 // second on the engine's side stream, forked from and joined back to s.
-int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s, uint32_t resume) {
-  if (n_groups(e, n_runs) == 1) return step_group(e, group(e, 0, 0, n_runs), states, s, resume);
+int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s, uint32_t partial) {
+  if (n_groups(e, n_runs) == 1) return step_group(e, group(e, 0, 0, n_runs), states, s, partial);
   int r;
   const uint32_t h = (n_runs / 2 + 15) / 16 * 16 < n_runs ? (n_runs / 2 + 15) / 16 * 16 : n_runs / 2;
   if ((r = hip_ok(hipEventRecord(e->ev_fork, s))) ||
       (r = hip_ok(hipStreamWaitEvent(e->side_stream, e->ev_fork, 0))))
     return r;
-  if ((r = step_group(e, group(e, 0, 0, h), states, s, resume))) return r;
-  if ((r = step_group(e, group(e, 1, h, n_runs - h), states, e->side_stream, resume))) return r;
+  if ((r = step_group(e, group(e, 0, 0, h), states, s, partial))) return r;
+  if ((r = step_group(e, group(e, 1, h, n_runs - h), states, e->side_stream, partial))) return r;
   if ((r = hip_ok(hipEventRecord(e->ev_join, e->side_stream))) ||
       (r = hip_ok(hipStreamWaitEvent(s, e->ev_join, 0))))
     return r;
@@ -517,8 +519,65 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
 
 void fpi8_engine_destroy(fpi8_engine *e) { release(e); }
 
-int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
-                  uint32_t max_positions, void *stream, int32_t *h_run_errors) {
+}  // extern "C"
+
+namespace {
+
+// Phases a position has done when the cursor stands at (phase, layer): 0 at
+// its start (phase 3), then one per phase in the order of the pass.
+uint32_t phases_done(const Cfg &c, uint32_t phase, uint32_t layer) {
+  if (phase <= 3) return 0;
+  if (phase <= 16) return 1 + 13 * layer + (phase - 4);
+  return 1 + 13 * c.layers + (phase - 17);
+}
+
+// Where a turn of at most max_phases phases stops a run whose cursor is
+// (pos, phase, layer): the position and the step (run_flags) before which it
+// stops there, at the last launch boundary the phases reach.  A launch
+// boundary is a cursor between two phases, except inside phase 11 (the
+// output rows carry its residual, the second normalization its rest).  No
+// stop when the run reaches the end of its cache positions first.
+void stop_of(const Cfg &c, uint32_t n_ids, uint32_t cachepos, uint32_t pos, uint32_t phase,
+             uint32_t layer, uint32_t max_phases, RunDesc &rd) {
+  rd.stop_pos = 0xFFFFFFFFu;
+  rd.stop_step = 0xFFFFFFFFu;
+  uint64_t k = max_phases;
+  uint32_t d = phases_done(c, phase, layer);
+  for (uint32_t t = pos; t < cachepos; t++, d = 0) {
+    const bool gen = t + 1 >= n_ids;
+    const uint64_t total = 1 + 13ull * c.layers + (gen ? 3 : 0);
+    if (k >= total - d) {
+      k -= total - d;
+      continue;
+    }
+    const uint64_t target = d + k;
+    uint32_t best = 0;
+    auto at = [&](uint64_t end, uint64_t done) {
+      if (done > d && done <= target && done < total) best = (uint32_t)end;
+    };
+    at(1, 1);
+    for (uint64_t l = 0; l < c.layers; l++) {
+      at(2 + 7 * l, 2 + 13 * l);   // after the first normalization: phase 5
+      at(3 + 7 * l, 6 + 13 * l);   // after q/k/v with rotary: phase 9
+      at(4 + 7 * l, 7 + 13 * l);   // after attention: phase 10
+      at(6 + 7 * l, 9 + 13 * l);   // after the second normalization: phase 12
+      at(7 + 7 * l, 12 + 13 * l);  // after gate/up with SiLU: phase 15
+      at(8 + 7 * l, 14 + 13 * l);  // after down: phase 4 of the next layer, or 17
+    }
+    if (gen) {
+      at(2 + 7ull * c.layers, 2 + 13ull * c.layers);  // after the final normalization: 18
+      at(3 + 7ull * c.layers, 3 + 13ull * c.layers);  // after the classifier: 19
+    }
+    rd.stop_pos = t;
+    rd.stop_step = best;
+    return;
+  }
+}
+
+// A turn over a batch: up to max_positions positions, and, when max_phases
+// is not ~0, up to max_phases phases of each run.
+int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
+             uint32_t max_positions, uint32_t max_phases, void *stream, int32_t *h_run_errors) {
   if (!e || !d_states || n_runs == 0 || n_runs > e->max_runs) return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   if ((reinterpret_cast<uintptr_t>(d_states) & 7) != 0 || (stride & 7) != 0 || stride < 128) {
@@ -532,29 +591,41 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
                                    hipMemcpyDeviceToHost, s))) ||
       (r = hip_ok(hipStreamSynchronize(s))))
     return r;
+  // Positions each run computes in this turn (its first one maybe only in
+  // part), and which positions of the turn have a run that starts or stops
+  // between two phases.
+  std::vector<uint32_t> first(n_runs, 0), count(n_runs, 0);
   uint32_t steps = 0, resume = 0;
   for (uint32_t b = 0; b < n_runs; b++) {
     RunDesc &rd = e->h_runs[b];
     memset(&rd, 0, sizeof rd);
+    rd.stop_pos = 0xFFFFFFFFu;
+    rd.stop_step = 0xFFFFFFFFu;
     const uint8_t *h = e->h_headers + 128ull * b;
     StateLayout L;
     const int chk = check_header(e->c, h, stride, &L);
     e->h_err[b] = chk > 0 ? chk : 0;
     if (chk != 0) continue;
-    uint32_t v;
+    uint32_t v, pos, phase, layer;
     memcpy(&v, h + ST_NIDS, 4); rd.n_ids = v;
     memcpy(&v, h + ST_MAX, 4); rd.max_tokens = v;
     memcpy(&v, h + ST_TEMP, 4); rd.temp = v;
+    memcpy(&pos, h + ST_POSITION, 4);
+    memcpy(&phase, h + ST_PHASE, 4);
+    memcpy(&layer, h + ST_LAYER, 4);
     rd.cachepos = L.cachepos;
     rd.valid = 1;
     rd.base = stride * b;
     rd.off_x = L.x; rd.off_w1 = L.w1; rd.off_w2 = L.w2; rd.off_w3 = L.w3;
     rd.off_gate = L.gate; rd.off_up = L.up; rd.off_logits = L.logits; rd.off_scores = L.scores;
     rd.off_keys = L.keys; rd.off_values = L.values; rd.off_ids = L.ids; rd.off_out = L.out;
-    memcpy(&v, h + ST_POSITION, 4);
-    steps = std::max(steps, L.cachepos - v);
-    memcpy(&v, h + ST_PHASE, 4);
-    if (v != 3) resume = 1;
+    if (max_phases != 0xFFFFFFFFu)
+      stop_of(e->c, rd.n_ids, L.cachepos, pos, phase, layer, max_phases, rd);
+    first[b] = pos;
+    count[b] = rd.stop_pos == 0xFFFFFFFFu ? L.cachepos - pos
+                                           : rd.stop_pos - pos + (rd.stop_step != 0 ? 1 : 0);
+    steps = std::max(steps, count[b]);
+    if (phase != 3) resume = 1;
   }
   steps = std::min(steps, max_positions);
   // Attention keeps one score per cached position in LDS: size it for the
@@ -571,31 +642,46 @@ int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n
   if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
   bool timing = false;
   for (const Timer &t : e->timers) timing = timing || t.on;
-  // A run that stopped between two phases finishes its position first, in
-  // launches that check where each run starts; the recorded position
-  // serves the rest.
-  uint32_t k0 = 0;
-  if (resume && steps > 0) {
-    if ((r = step(e, d_states, n_runs, s, 1))) return r;
-    k0 = 1;
-  }
-  if (steps > k0 && !timing && e->use_graph) {
-    if ((r = step_graph(e, d_states, n_runs))) return r;
-    for (uint32_t k = k0; k < steps; k++)
+  // A position where some run starts or stops between two phases runs in
+  // launches that check each run's steps; the recorded position serves the
+  // others.
+  for (uint32_t k = 0; k < steps; k++) {
+    uint32_t partial = k == 0 ? resume : 0;
+    for (uint32_t b = 0; b < n_runs && !partial; b++) {
+      const RunDesc &rd = e->h_runs[b];
+      if (rd.valid && rd.stop_pos == first[b] + k && rd.stop_step != 0) partial = 1;
+    }
+    if (!partial && !timing && e->use_graph) {
+      if ((r = step_graph(e, d_states, n_runs))) return r;
       if ((r = hip_ok(hipGraphLaunch(e->graph, s)))) return r;
-  } else {
-    for (uint32_t k = k0; k < steps; k++)
-      if ((r = step(e, d_states, n_runs, s, 0))) return r;
+    } else if ((r = step(e, d_states, n_runs, s, partial))) {
+      return r;
+    }
   }
   if ((r = hip_ok(hipMemcpyAsync(e->h_err, e->d_run_err, 4ull * n_runs, hipMemcpyDeviceToHost, s))) ||
       (r = hip_ok(hipStreamSynchronize(s))))
     return r;
-  int32_t first = 0;
+  int32_t first_err = 0;
   for (uint32_t b = 0; b < n_runs; b++) {
     if (h_run_errors) h_run_errors[b] = e->h_err[b];
-    if (!first && e->h_err[b]) first = e->h_err[b];
+    if (!first_err && e->h_err[b]) first_err = e->h_err[b];
   }
-  return first;
+  return first_err;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
+                  uint32_t max_positions, void *stream, int32_t *h_run_errors) {
+  return turn(e, d_states, stride, n_runs, max_positions, 0xFFFFFFFFu, stream, h_run_errors);
+}
+
+int32_t fpi8_turn_phases(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
+                         uint32_t max_phases, void *stream, int32_t *h_run_errors) {
+  if (max_phases == 0xFFFFFFFFu) max_phases--;
+  return turn(e, d_states, stride, n_runs, 0xFFFFFFFFu, max_phases, stream, h_run_errors);
 }
 
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {

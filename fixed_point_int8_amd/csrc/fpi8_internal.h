@@ -60,10 +60,12 @@ struct RunDesc {
   uint32_t pos;       // position computed in this step
   uint32_t token;     // token embedded in this step
   uint32_t errkey;    // first failing (layer, phase) of this step, ~0 if none
+  uint32_t end;       // the step this position stops before (~0: it runs to its end)
   // static
   uint32_t n_ids, max_tokens, temp, cachepos;
   uint32_t valid;     // passed the host checks at the start of the turn
-  uint32_t pad;
+  uint32_t stop_pos;  // the turn stops this run in position stop_pos before step
+  uint32_t stop_step; // stop_step (0: the position does not start); ~0: no stop
   uint64_t base;      // byte offset of the run's state in the arena
   uint64_t off_x, off_w1, off_w2, off_w3, off_gate, off_up, off_logits, off_scores;
   uint64_t off_keys, off_values, off_ids, off_out;
@@ -80,6 +82,7 @@ enum : uint32_t { RUN_ACTIVE = 1u, RUN_GEN = 2u };
 // between two phases of a position starts at a later step (`start`), and the
 // fused launch that holds its phase takes the results of the phases already
 // done from the state (`pick`, the state's phase; at step start + after).
+// A turn may also stop a run before a later step (RunDesc::end).
 // flags bits: 0-1 RUN_ACTIVE / RUN_GEN, 2-6 pick, 7 after, 8-31 start.
 constexpr uint32_t run_flags(uint32_t active_gen, uint32_t start, uint32_t pick, uint32_t after) {
   return active_gen | (pick << 2) | (after << 7) | (start << 8);
@@ -128,7 +131,7 @@ struct RowsArgs {
   const int32_t *silu;                  // [4097]
   uint32_t head, half, kv_heads, hidden;
   uint32_t step;            // this launch's step in the position (run_flags)
-  uint32_t resume;          // some run starts this position after step 0
+  uint32_t partial;         // some run starts this position after step 0 or stops before its end
   // gate/up epilogue: digits of the hidden vector for the down matrix
   int8_t *planes_out;
   uint32_t kp_out;
@@ -148,7 +151,7 @@ struct NormArgs {
   uint32_t kp, bp;
   uint32_t *oflag;
   uint32_t final_norm;      // 1: only generating runs (phase 17)
-  uint32_t step, resume;    // as in RowsArgs
+  uint32_t step, partial;   // as in RowsArgs
 };
 
 struct EmbedArgs {
@@ -157,7 +160,7 @@ struct EmbedArgs {
   uint32_t n_runs, dim, vocab;
   const uint8_t *E;
   const uint32_t *S;
-  uint32_t resume;          // as in RowsArgs (the embedding is step 0)
+  uint32_t partial;         // as in RowsArgs (the embedding is step 0)
 };
 
 struct AttnArgs {
@@ -170,7 +173,7 @@ struct AttnArgs {
   uint32_t kp, bp;
   uint32_t *oflag;
   uint32_t max_npos;        // LDS score slots: at least every run's cache positions
-  uint32_t step, resume;    // as in RowsArgs
+  uint32_t step, partial;   // as in RowsArgs
 };
 
 struct SampleArgs {
@@ -179,6 +182,7 @@ struct SampleArgs {
   uint32_t n_runs, vocab;
   const uint32_t *exp_tab;
   int32_t *run_err;
+  uint32_t step, partial, layers;  // step and partial as in RowsArgs
 };
 
 struct BeginArgs {

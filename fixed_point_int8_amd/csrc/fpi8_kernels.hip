@@ -135,14 +135,15 @@ __global__ void k_begin(BeginArgs a) {
   if (i < a.n_oflags) a.oflags[i] = 0;
   if (i >= a.n_runs) return;
   RunDesc &rd = a.runs[i];
-  uint32_t flags = 0;
+  uint32_t flags = 0, end = 0xFFFFFFFFu;
   if (rd.valid) {
     const uint8_t *st = run_base(a.states, rd);
     const uint32_t phase = *reinterpret_cast<const uint32_t *>(st + ST_PHASE);
     const uint32_t layer = *reinterpret_cast<const uint32_t *>(st + ST_LAYER);
     const uint32_t err = *reinterpret_cast<const uint32_t *>(st + ST_ERROR);
-    if (phase >= 3 && phase <= 19 && err == 0) {
-      const uint32_t pos = *reinterpret_cast<const uint32_t *>(st + ST_POSITION);
+    const uint32_t pos = *reinterpret_cast<const uint32_t *>(st + ST_POSITION);
+    if (pos == rd.stop_pos) end = rd.stop_step;
+    if (phase >= 3 && phase <= 19 && err == 0 && end != 0) {
       rd.pos = pos;
       rd.token = *reinterpret_cast<const uint32_t *>(st + ST_TOKEN);
       const uint32_t l7 = 7 * layer, f7 = 7 * a.layers;
@@ -163,27 +164,29 @@ __global__ void k_begin(BeginArgs a) {
     }
   }
   rd.flags = flags;
+  rd.end = end;
   rd.errkey = 0xFFFFFFFFu;
 }
 
-// Whether a run takes part in the launch at `step` of its position (it is
-// active, generates where `need` says so, and does not start later).
-__device__ __forceinline__ bool live_at(uint32_t flags, uint32_t need, uint32_t step,
-                                        uint32_t resume) {
-  return (flags & need) != 0 && (resume == 0 || (flags >> 8) <= step);
+// Whether a run takes part in the launch at `step` of its position: it is
+// active, generates where `need` says so, does not start later and is not
+// stopped before (flags is rd.flags, maybe read earlier).
+__device__ __forceinline__ bool live_at(const RunDesc &rd, uint32_t flags, uint32_t need,
+                                        uint32_t step, uint32_t partial) {
+  return (flags & need) != 0 && (partial == 0 || ((flags >> 8) <= step && step < rd.end));
 }
 
 // The state's phase that the fused launch at `step` picks up at for this
 // run, or 0 when it runs the launch's phases from the start.
-__device__ __forceinline__ uint32_t pick_at(uint32_t flags, uint32_t step, uint32_t resume) {
-  return resume != 0 && (flags >> 8) + ((flags >> 7) & 1u) == step ? (flags >> 2) & 31u : 0u;
+__device__ __forceinline__ uint32_t pick_at(uint32_t flags, uint32_t step, uint32_t partial) {
+  return partial != 0 && (flags >> 8) + ((flags >> 7) & 1u) == step ? (flags >> 2) & 31u : 0u;
 }
 
 // Phase 3: ((byte - 128) * scale) >> 8 with the token row's scale.
 __global__ void k_embed(EmbedArgs a) {
   const uint32_t b = blockIdx.y;
   const RunDesc &rd = a.runs[b];
-  if (!live_at(rd.flags, RUN_ACTIVE, 0, a.resume)) return;
+  if (!live_at(rd, rd.flags, RUN_ACTIVE, 0, a.partial)) return;
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= a.dim) return;
   const uint32_t tok = rd.token;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   constexpr int U = 8;  // loads in flight per thread
   const uint32_t b = blockIdx.x, nt = blockDim.x;
   const RunDesc &rd = a.runs[b];
-  if (!live_at(rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.resume)) return;
+  if (!live_at(rd, rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.partial)) return;
   uint8_t *st = run_base(a.states, rd);
   const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
   int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
@@ -323,7 +326,8 @@ template <int EPI>
 __device__ __forceinline__ bool row_run_ok(const RowsArgs &a, uint32_t b) {
   if (b >= a.n_runs) return false;
   if (EPI == EPI_RAW) return true;
-  return live_at(a.runs[b].flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.resume);
+  const RunDesc &rd = a.runs[b];
+  return live_at(rd, rd.flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.partial);
 }
 
 template <int EPI>
@@ -444,7 +448,7 @@ struct EpiIn {
   static constexpr int NX = (EPI == EPI_RESID || EPI == EPI_DOWN) ? MT : 1;
   static constexpr int NR = EPI == EPI_QKV ? MT : 1;
   uint32_t flags[BT], pos[BT], cache[BT];
-  uint64_t base[BT], o1[BT], o2[BT], o3[BT];
+  uint64_t base[BT], o1[BT], o2[BT], o3[BT], o4[EPI == EPI_QKV ? BT : 1];
   int64_t x[NX][BT][4];
   int32_t c[NR][BT][2], s[NR][BT][2];
 };
@@ -457,6 +461,7 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
     const uint32_t b = b0 + bt * 16 + li;
     in.flags[bt] = 0; in.pos[bt] = 0; in.cache[bt] = 0;
     in.base[bt] = 0; in.o1[bt] = 0; in.o2[bt] = 0; in.o3[bt] = 0;
+    if (EPI == EPI_QKV) in.o4[EPI == EPI_QKV ? bt : 0] = 0;
     if (EPI == EPI_RAW) {
       in.flags[bt] = b < a.n_runs ? 1u : 0u;
       continue;
@@ -471,14 +476,16 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
       in.pos[bt] = rd.pos;
       in.cache[bt] = rd.cachepos;
       in.o1[bt] = rd.off_w2; in.o2[bt] = rd.off_keys; in.o3[bt] = rd.off_values;
+      in.o4[EPI == EPI_QKV ? bt : 0] = rd.off_w3;
     }
   }
 }
 
 template <int EPI>
-__device__ __forceinline__ bool epi_live(const RowsArgs &a, uint32_t flags) {
+__device__ __forceinline__ bool epi_live(const RowsArgs &a, uint32_t flags, uint32_t b) {
   if (EPI == EPI_RAW) return flags != 0;
-  return live_at(flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.resume);
+  return live_at(a.runs[b < a.n_runs ? b : 0], flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step,
+                 a.partial);
 }
 
 template <int EPI, int MT, int BT>
@@ -539,7 +546,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
-    if (!epi_live<EPI>(a, in.flags[bt])) continue;
+    if (!epi_live<EPI>(a, in.flags[bt], b)) continue;
     int64_t y[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -562,7 +569,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
     uint8_t *st = a.states + in.base[bt];
     // A run that stopped inside this launch's phases: the results of the
     // phases it finished come from its state instead of the sums.
-    const uint32_t pick = pick_at(in.flags[bt], a.step, a.resume);
+    const uint32_t pick = pick_at(in.flags[bt], a.step, a.partial);
 #pragma unroll
     for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
       const uint32_t r0 = rbase[mt] + 4 * lg;
@@ -615,6 +622,10 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             const uint32_t kvh = row / a.head, e = row % a.head;
             int32_t *dst = V + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
             const int64_t yv = pick >= 8 ? (int64_t)*dst : y[mt][j];  // stored before the cut
+            // The value rows pass through the third working vector on their
+            // way to the cache; it matters only where a turn stops before
+            // attention writes that vector, so only such launches write it.
+            if (a.partial) reinterpret_cast<int64_t *>(st + in.o4[EPI == EPI_QKV ? bt : 0])[row] = yv;
             if (!fits32(yv)) { fail(rd, a.layer, 7); continue; }
             *dst = (int32_t)yv;
           }
@@ -1215,7 +1226,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   const uint32_t h = blockIdx.x, b = blockIdx.y;
   const RunDesc &rd = a.runs[b];
-  if (!live_at(rd.flags, RUN_ACTIVE, a.step, a.resume)) return;
+  if (!live_at(rd, rd.flags, RUN_ACTIVE, a.step, a.partial)) return;
   const uint32_t hs = HS ? HS : a.head;
   const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
   const uint32_t npos = rd.pos + 1, cachepos = rd.cachepos;
@@ -1465,6 +1476,27 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       *reinterpret_cast<uint32_t *>(st + ST_PHASE) = rd.errkey & 0xFFu;
       *reinterpret_cast<uint32_t *>(st + ST_LAYER) = rd.errkey >> 8;
       a.run_err[b] = FPI8_ARITHMETIC;
+    }
+    return;
+  }
+  if (a.partial && rd.end <= a.step) {
+    // The turn stops the run before step rd.end: its cursor names the
+    // phase that step starts (a boundary between two phases).
+    if (tid == 0) {
+      const uint32_t f = 1 + 7 * a.layers, end = rd.end;
+      uint32_t phase = 4, layer = 0;
+      if (end >= f) {
+        phase = 17 + (end - f);
+      } else if (end > 1) {
+        // after the first normalization, q/k/v, attention, (the output rows
+        // stop nowhere), the second normalization, gate/up, down
+        const uint32_t r = (end - 2) % 7;
+        layer = (end - 2) / 7;
+        phase = r == 0 ? 5 : r == 1 ? 9 : r == 2 ? 10 : r == 4 ? 12 : r == 5 ? 15 : 4;
+        if (r == 6) layer++;
+      }
+      *reinterpret_cast<uint32_t *>(st + ST_PHASE) = phase;
+      *reinterpret_cast<uint32_t *>(st + ST_LAYER) = layer;
     }
     return;
   }

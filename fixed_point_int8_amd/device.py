@@ -86,6 +86,10 @@ class DeviceBatch:
     def turn(self, model: DeviceModel, max_positions: int, stream=None):
         return B.fpi8_turn(model.engine, self.d_states, self.stride, self.n, max_positions, stream)
 
+    def turn_phases(self, model: DeviceModel, max_phases: int, stream=None):
+        return B.fpi8_turn_phases(model.engine, self.d_states, self.stride, self.n, max_phases,
+                                  stream)
+
     def state(self, i: int) -> np.ndarray:
         """A host copy of run i's state (8-byte aligned)."""
         size = self.sizes[i]

@@ -151,6 +151,20 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
                   uint32_t n_runs, uint32_t max_positions, void *stream,
                   int32_t *h_run_errors);
 
+/* A turn of at most max_phases phases of each run (counted as "The forward
+ * pass, in order" lists them: 3, 4-16 per layer, 17-19 where a token is
+ * generated), as many positions as they reach.  Each run stops at the last
+ * point within its budget where the engine's launches meet: a boundary
+ * between two phases, except the one inside phase 11 (so before phase 4, 5,
+ * 9, 10, 12, 15 or 17-19, or a position's start).  A run that cannot reach
+ * such a point is left as it is.  The state it stops in holds what the
+ * oracle's state holds at the same cursor, and a later turn of either
+ * continues it.  Errors, arguments and synchronization as fpi8_turn;
+ * max_phases 4294967295 counts as 4294967294. */
+int32_t fpi8_turn_phases(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
+                         uint32_t n_runs, uint32_t max_phases, void *stream,
+                         int32_t *h_run_errors);
+
 /* Which matrix-row kernel the engine's launches use: 0 the planner's choice
  * (the default), 1 always the kernel whose four waves split the contraction,
  * 2 the kernel whose waves share their runs' digits through LDS wherever it

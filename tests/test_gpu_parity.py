@@ -504,6 +504,93 @@ def test_resume_between_phases(row_kernel, streams):
         pair.model.close()
 
 
+# Cursors where the engine's launches meet, so where a turn of phases may
+# stop a run: every boundary between two phases but the one inside phase 11.
+STOPS = {3, 4, 5, 9, 10, 12, 15, 17, 18, 19}
+
+
+def cursor(st):
+    i = O.state_info(st)[1]
+    return i["position"], i["phase"], i["layer"], i["complete"]
+
+
+def same_but_turns(pair, i, turns):
+    """Run i's states agree byte for byte outside the turn counter, which
+    counts the GPU's turns (the oracle took one per phase)."""
+    g, r = pair.batch.state(i), pair.ref[i].copy()
+    assert O.state_info(g)[1]["turns"] == turns
+    g[80:88] = 0
+    r[80:88] = 0
+    if not np.array_equal(g, r):
+        from gpu_helpers import diff_report
+        raise AssertionError(f"run {i}: " + diff_report(pair.cfg, pair.runs[i], g, r))
+
+
+@pytest.mark.parametrize("row_kernel,streams", [(0, 0), (2, 2)])
+def test_stop_between_phases(row_kernel, streams):
+    # Turns of k phases on the GPU: each run stops at the last launch
+    # boundary within k phases of the oracle's count, in the state the oracle
+    # has at that cursor; runs start at every cursor, including those inside
+    # a launch, which make no progress until k reaches the next boundary.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 53)
+    prompt = 4
+    cuts = phase_cuts(shape, prompt)[::3]
+    n = len(cuts)
+    say(f"stop between phases: {n} runs, row kernel {row_kernel}, streams {streams}")
+    temps = [0 if r % 4 else 65536 for r in range(n)]
+    runs = spec(shape, n, prompt, 5, seed=5, temps=temps)
+    pair = Pair(shape, blob, runs)
+    assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    assert B.fpi8_engine_set_streams(pair.model.engine, streams) == 0
+    rng = np.random.default_rng(row_kernel * 10 + streams)
+    try:
+        turns = []
+        for i, (t, p, l) in enumerate(cuts):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, t, p, l)
+            pair.load(i, st)
+            turns.append(O.state_info(st)[1]["turns"])
+        seen = set()
+        for rounds in range(200):
+            if pair.complete():
+                break
+            live = [i for i in range(n) if not cursor(pair.ref[i])[3]]
+            if rng.random() < 0.15:
+                errs = pair.turn(1)
+                assert not any(errs), errs
+                for i in range(n):
+                    turns[i] += 1 if i in live else 0
+                    same_but_turns(pair, i, turns[i])
+                continue
+            k = int(rng.integers(1, 45))
+            e, errs = pair.batch.turn_phases(pair.model, k)
+            assert e == 0 and not any(errs), (e, errs)
+            for i in range(n):
+                want = cursor(pair.batch.state(i))
+                seen.add(want[1])
+                ref = pair.ref[i]
+                used = 0
+                while cursor(ref) != want:
+                    assert used < k and not cursor(ref)[3], (i, k, cursor(ref), want)
+                    assert O.turn_phases(blob, ref, 1) == 0
+                    used += 1
+                # the GPU stopped at the last boundary the budget reaches
+                probe = ref.copy()
+                for _ in range(k - used):
+                    if cursor(probe)[3]:
+                        break
+                    assert O.turn_phases(blob, probe, 1) == 0
+                    c = cursor(probe)
+                    assert c[1] not in STOPS or c[3], (i, k, used, want, c)
+                turns[i] += 1 if i in live else 0
+                same_but_turns(pair, i, turns[i])
+        assert pair.complete()
+        assert seen >= STOPS, seen     # every kind of stop was taken
+    finally:
+        pair.model.close()
+
+
 def test_resume_cursor_checks():
     # Cursors the pages' state cannot hold get error 3, on the GPU as in the
     # oracle; the run is left as it is.
