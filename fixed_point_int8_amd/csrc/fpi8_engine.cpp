@@ -246,8 +246,11 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   bool shared_ok = a.cols % 128 == 0;
   for (uint32_t i = 0; i < a.nseg; i++) shared_ok = shared_ok && a.seg[i].pad != 0;
   shared_ok = shared_ok || a.packed != 0;
-  const RowPlan p = plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup, shared_ok,
-                              e->row_kind);
+  // A position where some run starts or stops between two phases uses the
+  // one shape built for it (32 rows, 32 runs, kind 0).
+  const RowPlan p = a.partial ? RowPlan{0, 2, 2, 1, (n_runs + 31) / 32, 0}
+                              : plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup,
+                                          shared_ok, e->row_kind);
   // Units of 16 * mt rows (of each matrix of the gate/up pair: 16 * mt / 2)
   // over the segments in order; a workgroup finishes one (kind 0) or wr.
   const uint32_t unit_rows = 16 * (gateup ? p.mt / 2 : p.mt);

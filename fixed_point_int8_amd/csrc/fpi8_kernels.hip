@@ -322,12 +322,15 @@ __device__ __forceinline__ v4i load_weights_raw(const uint8_t *W, uint32_t row, 
   return r;
 }
 
-template <int EPI>
+// PART: the launch of a position where some run starts or stops between two
+// phases (RowsArgs::partial); only the row kernel instantiated for it checks
+// each run's steps and picks up finished phases.
+template <int EPI, bool PART>
 __device__ __forceinline__ bool row_run_ok(const RowsArgs &a, uint32_t b) {
   if (b >= a.n_runs) return false;
   if (EPI == EPI_RAW) return true;
   const RunDesc &rd = a.runs[b];
-  return live_at(rd, rd.flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, a.partial);
+  return live_at(rd, rd.flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step, PART ? 1u : 0u);
 }
 
 template <int EPI>
@@ -402,7 +405,7 @@ __device__ __forceinline__ void row_tile(const RowsArgs &a, uint32_t unit, int l
 
 // Exact 64-bit path: sum_c (b_c - 128) * x_c over columns [c_lo, c_hi) with
 // wrapping products, for the outputs this lane holds.
-template <int EPI, int MT, int BT>
+template <int EPI, int MT, int BT, bool PART>
 __device__ __forceinline__ void rows_exact(const RowsArgs &a, const RowTile<MT> &t, uint32_t b0,
                                            uint32_t c_lo, uint32_t c_hi, int li, int lg,
                                            int64_t (&v)[MT][BT][4]) {
@@ -411,7 +414,7 @@ __device__ __forceinline__ void rows_exact(const RowsArgs &a, const RowTile<MT> 
 #pragma unroll
     for (int bt = 0; bt < BT; bt++) {
       const uint32_t b = b0 + bt * 16 + li;
-      const bool ok = row_run_ok<EPI>(a, b);
+      const bool ok = row_run_ok<EPI, PART>(a, b);
       const int64_t *x = ok ? row_input<EPI>(a, b) : nullptr;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -481,11 +484,11 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
   }
 }
 
-template <int EPI>
+template <int EPI, bool PART>
 __device__ __forceinline__ bool epi_live(const RowsArgs &a, uint32_t flags, uint32_t b) {
   if (EPI == EPI_RAW) return flags != 0;
   return live_at(a.runs[b < a.n_runs ? b : 0], flags, EPI == EPI_CLS ? RUN_GEN : RUN_ACTIVE, a.step,
-                 a.partial);
+                 PART ? 1u : 0u);
 }
 
 template <int EPI, int MT, int BT>
@@ -534,7 +537,7 @@ __device__ __forceinline__ void silu_to_lds(const int32_t *silu, int32_t *lds, i
 
 // Epilogue of the outputs this lane holds: y = (v * scale) >> 24, then the
 // phase's own work.
-template <int EPI, int MT, int BT>
+template <int EPI, int MT, int BT, bool PART>
 __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<MT> &t, uint32_t b0,
                                               const int64_t (&v)[MT][BT][4], int li, int lg,
                                               const EpiIn<EPI, MT, BT> &in, const int32_t *silu) {
@@ -546,7 +549,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
 #pragma unroll
   for (int bt = 0; bt < BT; bt++) {
     const uint32_t b = b0 + bt * 16 + li;
-    if (!epi_live<EPI>(a, in.flags[bt], b)) continue;
+    if (!epi_live<EPI, PART>(a, in.flags[bt], b)) continue;
     int64_t y[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -569,7 +572,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
     uint8_t *st = a.states + in.base[bt];
     // A run that stopped inside this launch's phases: the results of the
     // phases it finished come from its state instead of the sums.
-    const uint32_t pick = pick_at(in.flags[bt], a.step, a.partial);
+    const uint32_t pick = PART ? pick_at(in.flags[bt], a.step, 1u) : 0u;
 #pragma unroll
     for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
       const uint32_t r0 = rbase[mt] + 4 * lg;
@@ -625,7 +628,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             // The value rows pass through the third working vector on their
             // way to the cache; it matters only where a turn stops before
             // attention writes that vector, so only such launches write it.
-            if (a.partial) reinterpret_cast<int64_t *>(st + in.o4[EPI == EPI_QKV ? bt : 0])[row] = yv;
+            if (PART) reinterpret_cast<int64_t *>(st + in.o4[EPI == EPI_QKV ? bt : 0])[row] = yv;
             if (!fits32(yv)) { fail(rd, a.layer, 7); continue; }
             *dst = (int32_t)yv;
           }
@@ -692,7 +695,7 @@ struct RowsGeom {
 // span), and takes the exact path by itself when one of its words needs more.
 constexpr uint32_t XR_CAP = kRawInputLds;
 
-template <int EPI, int MT, int BT, bool XR = false>
+template <int EPI, int MT, int BT, bool XR = false, bool PART = false>
 __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   static_assert(!XR || (EPI == EPI_RAW && BT == 1), "raw-input rows are standalone calls of one or two inputs");
   constexpr int P = RowsGeom<MT, BT, XR>::P;
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   // Whether this batch chunk has a run in this phase (the classifier skips
   // prompt positions and finished runs); read first, tested after the first
   // loads are on their way.
-  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
+  const bool busy = EPI == EPI_RAW || row_run_ok<EPI, PART>(a, b0 + (tid & (16 * BT - 1)));
 
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile, lg, wave == 0, t);
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   } else {
     // Exact 64-bit path over this wave's columns.
     const uint32_t c_lo = k_lo * 64, c_hi = (k_lo + n) * 64 < a.cols ? (k_lo + n) * 64 : a.cols;
-    rows_exact<EPI, MT, BT>(a, t, b0, c_lo, c_hi, li, lg, v);
+    rows_exact<EPI, MT, BT, PART>(a, t, b0, c_lo, c_hi, li, lg, v);
   }
 
   // The four waves' sums meet in wave 0 (wrapping adds).
@@ -954,7 +957,7 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; j++) v[mt][bt][j] = wadd(v[mt][bt][j], red[w][((mt * BT + bt) * 4 + j) * 64 + lane]);
 
-  rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
+  rows_epilogue<EPI, MT, BT, PART>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
 // The matrix row with the digits shared through LDS.  A workgroup of four
@@ -1010,7 +1013,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
   const uint32_t b0 = chunk * BT * 16;
   const uint32_t wr = a.wave_rows;
   const bool own = (uint32_t)wave < wr;
-  const bool busy = EPI == EPI_RAW || row_run_ok<EPI>(a, b0 + (tid & (16 * BT - 1)));
+  const bool busy = EPI == EPI_RAW || row_run_ok<EPI, false>(a, b0 + (tid & (16 * BT - 1)));
 
   __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   RowTile<MT> t;
@@ -1028,7 +1031,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
   if (exact) {
     if (own) {
       epi_fetch<EPI, MT, BT>(a, t, lg, in);
-      rows_exact<EPI, MT, BT>(a, t, b0, 0, a.cols, li, lg, v);
+      rows_exact<EPI, MT, BT, false>(a, t, b0, 0, a.cols, li, lg, v);
     }
   } else {
     v4i acc[MT][3][BT];
@@ -1164,7 +1167,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
     wait_vm<0>();
     lds_barrier();  // every wave's share of the SiLU table has landed
   }
-  if (own) rows_epilogue<EPI, MT, BT>(a, t, b0, v, li, lg, in, silu_lds);
+  if (own) rows_epilogue<EPI, MT, BT, false>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
 // Packing of a weight matrix into MFMA operand tiles (see launch_pack): one
@@ -1677,9 +1680,30 @@ int launch_rows_raw(int mt, const RowsArgs &a, void *stream) {
   return ok(hipGetLastError());
 }
 
+// The one shape of a position where some run starts or stops between two
+// phases (kind 0, 32 rows, 32 runs).
+template <int EPI>
+static int rows_launch_partial(const RowsArgs &a, hipStream_t s) {
+  const uint32_t groups = (a.ntiles + 7) / 8;
+  const dim3 grid(groups * 8 * a.chunks), block(256);
+  hipLaunchKernelGGL((k_rows<EPI, 2, 2, false, true>), grid, block, 0, s, a);
+  return ok(hipGetLastError());
+}
+
 int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.ntiles == 0 || a.chunks == 0) return 0;
+  if (a.partial) {
+    if (kind != 0 || mt != 2 || bt != 2) return FPI8_ERR_ARGUMENT;
+    switch (epi) {
+      case EPI_QKV: return rows_launch_partial<EPI_QKV>(a, s);
+      case EPI_RESID: return rows_launch_partial<EPI_RESID>(a, s);
+      case EPI_DOWN: return rows_launch_partial<EPI_DOWN>(a, s);
+      case EPI_CLS: return rows_launch_partial<EPI_CLS>(a, s);
+      case EPI_GATEUP: return rows_launch_partial<EPI_GATEUP>(a, s);
+    }
+    return FPI8_ERR_ARGUMENT;
+  }
   switch (epi) {
     case EPI_RAW: return rows_shape<EPI_RAW>(kind, mt, bt, a, s);
     case EPI_QKV: return rows_shape<EPI_QKV>(kind, mt, bt, a, s);

@@ -551,7 +551,6 @@ def test_stop_between_phases(row_kernel, streams):
             cut_at(blob, st, t, p, l)
             pair.load(i, st)
             turns.append(O.state_info(st)[1]["turns"])
-        seen = set()
         for rounds in range(200):
             if pair.complete():
                 break
@@ -563,12 +562,12 @@ def test_stop_between_phases(row_kernel, streams):
                     turns[i] += 1 if i in live else 0
                     same_but_turns(pair, i, turns[i])
                 continue
-            k = int(rng.integers(1, 45))
+            # small budgets first (every boundary gets its turn), then any
+            k = 1 + rounds % 8 if rounds < 40 else int(rng.integers(1, 45))
             e, errs = pair.batch.turn_phases(pair.model, k)
             assert e == 0 and not any(errs), (e, errs)
             for i in range(n):
                 want = cursor(pair.batch.state(i))
-                seen.add(want[1])
                 ref = pair.ref[i]
                 used = 0
                 while cursor(ref) != want:
@@ -586,7 +585,46 @@ def test_stop_between_phases(row_kernel, streams):
                 turns[i] += 1 if i in live else 0
                 same_but_turns(pair, i, turns[i])
         assert pair.complete()
-        assert seen >= STOPS, seen     # every kind of stop was taken
+    finally:
+        pair.model.close()
+
+
+def test_stop_at_each_boundary():
+    # From the start of a prompt position and of a generating one, a turn
+    # of k phases for every k up to a position and a half: the cursor is the
+    # last boundary within k phases, the state the oracle's at that cursor.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 54)
+    prompt = 4
+    runs = spec(shape, 2, prompt, 4, seed=6, temps=[0, 65536])
+    starts = [(1, 3, 0), (prompt - 1, 3, 0)]
+    pair = Pair(shape, blob, runs)
+    try:
+        cut = []
+        for i, (t, p, l) in enumerate(starts):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, t, p, l)
+            cut.append(st)
+        per_position = 1 + 13 * shape.layers + 3
+        seen = set()
+        for k in range(1, per_position * 3 // 2 + 1):
+            for i in range(2):
+                pair.load(i, cut[i])
+            e, errs = pair.batch.turn_phases(pair.model, k)
+            assert e == 0 and not any(errs), (k, e, errs)
+            for i in range(2):
+                ref = cut[i].copy()
+                last = ref.copy()
+                for _ in range(k):
+                    assert O.turn_phases(blob, ref, 1) == 0
+                    if cursor(ref)[1] in STOPS:
+                        last = ref.copy()
+                turns = O.state_info(cut[i])[1]["turns"] + 1
+                pair.ref[i][:] = last
+                assert cursor(pair.batch.state(i)) == cursor(last), (k, i)
+                same_but_turns(pair, i, turns)
+                seen.add(cursor(last)[1])
+        assert seen == STOPS, seen
     finally:
         pair.model.close()
 
