@@ -88,6 +88,7 @@ def lib():
             "fpi8_ref_state_layout": (C.c_int32, [_P, C.c_uint32, C.c_uint32, C.POINTER(Layout)]),
             "fpi8_ref_turn": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint32]),
             "fpi8_ref_turn_phases": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint32]),
+            "fpi8_ref_turn_units": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint64]),
             "fpi8_ref_set_threads": (C.c_int32, [C.c_int32]),
         }
         for name, (res, args) in sig.items():
@@ -245,6 +246,11 @@ def turn(blob: np.ndarray, state: np.ndarray, max_positions: int) -> int:
 def turn_phases(blob: np.ndarray, state: np.ndarray, max_phases: int) -> int:
     """Runs up to max_phases single phases from the state's cursor."""
     return lib().fpi8_ref_turn_phases(_ptr(blob), blob.size, _ptr(state), state.size, max_phases)
+
+
+def turn_units(blob: np.ndarray, state: np.ndarray, max_units: int) -> int:
+    """Runs up to max_units units of work from the state's cursor."""
+    return lib().fpi8_ref_turn_units(_ptr(blob), blob.size, _ptr(state), state.size, max_units)
 
 
 def run_to_end(blob, state, chunk=1 << 30):

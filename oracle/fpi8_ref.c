@@ -138,38 +138,69 @@ int64_t fpi8_ref_silu(int64_t x, const int32_t *tab) {
  *   normalization: p_j = (e_j << 24) / sum;
  *   weighted values: o_i = (sum_j p_j * V_j,i) >> 24.
  * The one scores buffer carries s, then e, then p, as the state has one.
- * inv enters zero-extended; cached words are sign-extended. */
+ * inv enters zero-extended; cached words are sign-extended.
+ *
+ * A head can stop after any unit of a stage ("The resumable state"): one
+ * position in stages 0 to 2, one output element in stage 3.  The cursor is
+ * the stage, the index of the next unit, the largest score and the sum of
+ * exponentials; the scores buffer and the outputs hold the rest. */
+typedef struct {
+  uint32_t stage, index;
+  int64_t max;
+  uint64_t sum;
+} attn_cursor;
+
+/* One unit at the cursor; returns 1 when it was the head's last. */
+static int attention_unit(const int64_t *q, const int32_t *K, const int32_t *V, uint32_t npos,
+                          uint32_t head, uint64_t stride, uint32_t inv_sqrt_head,
+                          const uint32_t *exp_tab, int64_t *scores, int64_t *out,
+                          attn_cursor *c) {
+  const uint32_t j = c->index;
+  switch (c->stage) {
+    case 0: {
+      const int32_t *k = K + (uint64_t)j * stride;
+      int64_t dot = 0;
+      for (uint32_t i = 0; i < head; i++) dot = wadd(dot, wmul(q[i], (int64_t)k[i]));
+      int64_t s = asr(wmul(asr(dot, 16), (int64_t)(uint64_t)inv_sqrt_head), 24);
+      scores[j] = s;
+      if (j == 0 || s > c->max) c->max = s;
+      break;
+    }
+    case 1: {
+      if (j == 0) c->sum = 0;
+      uint64_t d = (uint64_t)c->max - (uint64_t)scores[j];
+      uint32_t e = exp_tab[fpi8_ref_exp_index(d)];
+      scores[j] = (int64_t)e;
+      c->sum += e;
+      break;
+    }
+    case 2:
+      scores[j] = (int64_t)(((uint64_t)scores[j] << 24) / c->sum);
+      break;
+    default: {
+      int64_t acc = 0;
+      for (uint32_t t = 0; t < npos; t++)
+        acc = wadd(acc, wmul(scores[t], (int64_t)V[(uint64_t)t * stride + j]));
+      out[j] = asr(acc, 24);
+      break;
+    }
+  }
+  c->index = j + 1;
+  if (c->index < (c->stage < 3 ? npos : head)) return 0;
+  c->index = 0;
+  return c->stage++ == 3;
+}
+
 void fpi8_ref_attention_head(const int64_t *q, const int32_t *K, const int32_t *V,
                              uint32_t npos, uint32_t head, uint64_t stride,
                              uint32_t inv_sqrt_head, const uint32_t *exp_tab,
                              int64_t *scores, int64_t *out,
                              int64_t *max_out, uint64_t *sum_out) {
-  int64_t m = 0;
-  for (uint32_t j = 0; j < npos; j++) {
-    const int32_t *k = K + (uint64_t)j * stride;
-    int64_t dot = 0;
-    for (uint32_t i = 0; i < head; i++) dot = wadd(dot, wmul(q[i], (int64_t)k[i]));
-    int64_t s = asr(wmul(asr(dot, 16), (int64_t)(uint64_t)inv_sqrt_head), 24);
-    scores[j] = s;
-    if (j == 0 || s > m) m = s;
+  attn_cursor c = {0, 0, 0, 0};
+  while (!attention_unit(q, K, V, npos, head, stride, inv_sqrt_head, exp_tab, scores, out, &c)) {
   }
-  uint64_t sum = 0;
-  for (uint32_t j = 0; j < npos; j++) {
-    uint64_t d = (uint64_t)m - (uint64_t)scores[j];
-    uint32_t e = exp_tab[fpi8_ref_exp_index(d)];
-    scores[j] = (int64_t)e;
-    sum += e;
-  }
-  for (uint32_t j = 0; j < npos; j++)
-    scores[j] = (int64_t)(((uint64_t)scores[j] << 24) / sum);
-  for (uint32_t i = 0; i < head; i++) {
-    int64_t acc = 0;
-    for (uint32_t j = 0; j < npos; j++)
-      acc = wadd(acc, wmul(scores[j], (int64_t)V[(uint64_t)j * stride + i]));
-    out[i] = asr(acc, 24);
-  }
-  if (max_out) *max_out = m;
-  if (sum_out) *sum_out = sum;
+  if (max_out) *max_out = c.max;
+  if (sum_out) *sum_out = c.sum;
 }
 
 /* "Sampling": xorshift64* with the run's seed as its first state. */
@@ -195,24 +226,55 @@ static uint32_t temp_index(uint64_t d, uint32_t t) {
 /* "Sampling": the maximum pass (the lowest index wins a tie, the first
  * found in a forward scan); at temperature zero its index is the token.
  * Above zero: the sum pass, one advance of the generator, the draw modulo
- * the sum, and the walk that subtracts each entry's exponential. */
+ * the sum, and the walk that subtracts each entry's exponential.
+ *
+ * A pass can stop after any vocabulary entry ("The resumable state"): the
+ * cursor is the pass, the next entry, the largest logit, the entry chosen so
+ * far, the sum of exponentials and what is left of the draw.  The generator
+ * advances when the sum pass ends. */
+typedef struct {
+  uint32_t pass, row, chosen;
+  int64_t max;
+  uint64_t sum, rem;
+} sample_cursor;
+
+/* One entry at the cursor; returns 1 when the token is chosen (c->chosen). */
+static int sample_unit(const int64_t *logits, uint32_t vocab, uint32_t temperature_q16,
+                       const uint32_t *exp_tab, uint64_t *generator, sample_cursor *c) {
+  const uint32_t i = c->row;
+  c->row = i + 1;
+  if (c->pass == 0) {
+    if (i == 0 || logits[i] > c->max) { c->max = logits[i]; c->chosen = i; }
+    if (c->row < vocab) return 0;
+    if (temperature_q16 == 0) return 1;
+    c->pass = 1;
+    c->row = 0;
+    return 0;
+  }
+  const uint64_t e = exp_tab[temp_index((uint64_t)c->max - (uint64_t)logits[i], temperature_q16)];
+  if (c->pass == 1) {
+    if (i == 0) c->sum = 0;
+    c->sum += e;
+    if (c->row < vocab) return 0;
+    c->rem = fpi8_ref_xorshift64s(generator) % c->sum;
+    c->pass = 2;
+    c->row = 0;
+    return 0;
+  }
+  if (c->rem < e || c->row == vocab) { /* the second is not reached: rem < sum */
+    c->chosen = i;
+    return 1;
+  }
+  c->rem -= e;
+  return 0;
+}
+
 uint32_t fpi8_ref_sample(const int64_t *logits, uint32_t vocab, uint32_t temperature_q16,
                          const uint32_t *exp_tab, uint64_t *generator) {
-  uint32_t best = 0;
-  int64_t m = logits[0];
-  for (uint32_t i = 1; i < vocab; i++)
-    if (logits[i] > m) { m = logits[i]; best = i; }
-  if (temperature_q16 == 0) return best;
-  uint64_t sum = 0;
-  for (uint32_t i = 0; i < vocab; i++)
-    sum += exp_tab[temp_index((uint64_t)m - (uint64_t)logits[i], temperature_q16)];
-  uint64_t r = fpi8_ref_xorshift64s(generator) % sum;
-  for (uint32_t i = 0; i < vocab; i++) {
-    uint64_t e = exp_tab[temp_index((uint64_t)m - (uint64_t)logits[i], temperature_q16)];
-    if (r < e) return i;
-    r -= e;
+  sample_cursor c = {0, 0, 0, 0, 0, 0};
+  while (!sample_unit(logits, vocab, temperature_q16, exp_tab, generator, &c)) {
   }
-  return vocab - 1; /* not reached: r < sum */
+  return c.chosen;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -525,12 +587,8 @@ typedef struct {
   int64_t *x, *w1, *w2, *w3, *gate, *up, *logits, *scores;
   int32_t *keys, *values;
   uint32_t *ids, *out;
+  int64_t *tmp; /* key or value rows on their way to the cache (not state) */
 } run_t;
-
-/* Matrix times vector with the weights' own scales. */
-static void matvec(const mat_t *M, const int64_t *in, int64_t *out) {
-  fpi8_ref_rows(M->w, M->s, M->rows, M->cols, in, 1, out);
-}
 
 /* Index of a cache word: [layer][kv head][position][element]. */
 static uint64_t cache_index(const cfg_t *c, uint32_t cachepos, uint32_t l, uint32_t kvh,
@@ -547,27 +605,37 @@ static int32_t fail(run_t *r, uint32_t phase, uint32_t layer) {
   return FPI8_REF_ARITHMETIC;
 }
 
-/* Phases 6 and 7: a key or value matrix, each row stored into the cache
- * with the 32-bit fit check ("The attention cache"). */
+/* Phases 6 and 7, rows [row, row + n) of a key or value matrix: each row
+ * goes straight into the cache after the 32-bit fit check ("The attention
+ * cache"; the planner's charge is per row stored).  Returns 0 at the first
+ * row that does not fit (the rows before it are stored). */
 static int store_rows(const cfg_t *c, const mat_t *M, const int64_t *in, int64_t *tmp,
-                      int32_t *cache, uint32_t cachepos, uint32_t l, uint32_t pos) {
-  matvec(M, in, tmp);
-  for (uint32_t r = 0; r < c->kvd; r++) {
-    if (!fits32(tmp[r])) return 0;
-    cache[cache_index(c, cachepos, l, r / c->head, pos, r % c->head)] = (int32_t)tmp[r];
+                      uint32_t row, uint32_t n, int32_t *cache, uint32_t cachepos, uint32_t l,
+                      uint32_t pos) {
+  fpi8_ref_rows(M->w + (uint64_t)row * M->cols, M->s + row, n, M->cols, in, 1, tmp);
+  for (uint32_t k = 0; k < n; k++) {
+    const uint32_t r = row + k;
+    if (!fits32(tmp[k])) return 0;
+    cache[cache_index(c, cachepos, l, r / c->head, pos, r % c->head)] = (int32_t)tmp[k];
   }
   return 1;
 }
 
-/* One phase of the pass ("The forward pass, in order"), the one the cursor
- * in the state header (phase, layer) names; the cursor then names the next
- * one, so a turn can stop between any two phases and a later turn continue
- * from there ("The resumable state").  Every phase reads only the state's
- * buffers and writes its results back into them.  *ended is set when the
- * position is finished: the cursor then stands at the next position's
- * embedding (phase 3), or at phase 20 when the run is complete.  Returns 0,
- * or the error that froze the run. */
-static int32_t phase_step(const model_t *m, const mat_t *mats, run_t *r, int *ended) {
+/* Runs the phase the state's cursor names ("The forward pass, in order"),
+ * from wherever inside it the cursor stands, for at most *budget units of
+ * work ("The resumable state": a row of a matrix, a position or an output
+ * element of an attention stage, a vocabulary entry of a sampling pass, or
+ * one whole vector operation), which it takes off *budget.  Every phase
+ * reads only the state's buffers and writes its results back into them.
+ * When the budget ends inside the phase the cursor records where (row,
+ * attention stage and index, sampling pass, and the running maximum, sum,
+ * choice and remainder) and *done stays 0.  Otherwise *done is set and the
+ * cursor names the next phase; *ended is set when that ends the position:
+ * the cursor then stands at the next position's embedding (phase 3), or at
+ * phase 20 when the run is complete.  Returns 0, or the error that froze
+ * the run. */
+static int32_t run_phase(const model_t *m, const mat_t *mats, run_t *r, uint64_t *budget,
+                         int *done, int *ended) {
   const cfg_t *c = &m->c;
   uint8_t *st = r->st;
   const uint32_t p = rd32(st + H_PHASE), l = rd32(st + H_LAYER);
@@ -577,136 +645,202 @@ static int32_t phase_step(const model_t *m, const mat_t *mats, run_t *r, int *en
   const uint32_t group = c->heads / c->kv_heads;
   const mat_t *Lm = &mats[1 + 7 * l];
   uint32_t np = p + 1, nl = l;
+  *done = 0;
   *ended = 0;
+  if (*budget == 0) return 0;
+  /* the matrix of a row phase, its input and its output */
+  const mat_t *M = NULL;
+  const int64_t *in = r->w1;
+  int64_t *out = NULL;
   switch (p) {
-    case 3: {
-      /* Embedding, ((byte - 128) * scale) >> 8 with the token row's scale. */
-      const uint32_t tok = rd32(st + H_TOKEN);
-      const mat_t *E = &mats[0];
-      const uint8_t *row = E->w + (uint64_t)tok * c->dim;
-      uint32_t sc = rd32(E->s_bytes + 4ull * tok);
-      for (uint32_t i = 0; i < c->dim; i++)
-        r->x[i] = asr(wmul((int64_t)row[i] - 128, (int64_t)(uint64_t)sc), 8);
-      nl = 0;
-      break;
+    case 5: M = &Lm[K_Q - 1]; out = r->w2; break;
+    case 6: M = &Lm[K_K - 1]; break;
+    case 7: M = &Lm[K_V - 1]; break;
+    case 10: M = &Lm[K_O - 1]; in = r->w3; out = r->w1; break;
+    case 12: M = &Lm[K_GATE - 1]; out = r->gate; break;
+    case 13: M = &Lm[K_UP - 1]; out = r->up; break;
+    case 15: M = &Lm[K_DOWN - 1]; in = r->gate; out = r->w1; break;
+    case 18: M = &mats[1 + 7 * c->layers]; out = r->logits; break;
+    default: break;
+  }
+  if (M) {
+    /* Phases 5, 6, 7 (query, key, value), 10 (attention output matrix), 12
+     * and 13 (gate, up), 15 (down), 18 (classifier): rows from the cursor's
+     * row on, as many as the budget allows. */
+    const uint32_t row = rd32(st + H_ROW);
+    const uint64_t left = M->rows - row;
+    const uint32_t n = (uint32_t)(left < *budget ? left : *budget);
+    if (out) {
+      fpi8_ref_rows(M->w + (uint64_t)row * M->cols, M->s + row, n, M->cols, in, 1, out + row);
+    } else if (!store_rows(c, M, in, r->tmp, row, n, p == 6 ? r->keys : r->values, cachepos, l, t)) {
+      return fail(r, p, l);
     }
-    case 4: /* attention normalization into w1 */
-      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l) * c->dim, c->dim, r->w1);
-      break;
-    case 5: /* the query into w2 */
-      matvec(&Lm[K_Q - 1], r->w1, r->w2);
-      break;
-    case 6: /* the key into the cache (w3 holds the rows before the store) */
-      if (!store_rows(c, &Lm[K_K - 1], r->w1, r->w3, r->keys, cachepos, l, t)) return fail(r, 6, l);
-      break;
-    case 7: /* the value into the cache */
-      if (!store_rows(c, &Lm[K_V - 1], r->w1, r->w3, r->values, cachepos, l, t)) return fail(r, 7, l);
-      break;
-    case 8: {
-      /* Rotary.  Reading: pairs are adjacent elements (2j, 2j+1) of each
-       * head, turned by the position's entry j of the tables; the query
-       * first, then this position's keys, each stored key checked. */
-      const int32_t *cs = m->cos_tab + (uint64_t)t * half;
-      const int32_t *sn = m->sin_tab + (uint64_t)t * half;
-      for (uint32_t h = 0; h < c->heads; h++)
-        for (uint32_t j = 0; j < half; j++)
-          fpi8_ref_rotate(&r->w2[h * c->head + 2 * j], &r->w2[h * c->head + 2 * j + 1], cs[j], sn[j]);
-      for (uint32_t kh = 0; kh < c->kv_heads; kh++)
-        for (uint32_t j = 0; j < half; j++) {
-          int32_t *k0 = &r->keys[cache_index(c, cachepos, l, kh, t, 2 * j)];
-          int64_t a = k0[0], b = k0[1];
-          fpi8_ref_rotate(&a, &b, cs[j], sn[j]);
-          if (!fits32(a) || !fits32(b)) return fail(r, 8, l);
-          k0[0] = (int32_t)a;
-          k0[1] = (int32_t)b;
+    *budget -= n;
+    if (row + n < M->rows) {
+      wr32(st + H_ROW, row + n);
+      return 0;
+    }
+    wr32(st + H_ROW, 0);
+  } else if (p == 9) {
+    /* Attention, head by head (the cursor's row is the head), stage by
+     * stage, outputs into w3; head h reads key and value head
+     * h / (heads / kv_heads). */
+    uint32_t h = rd32(st + H_ROW);
+    attn_cursor ac = {rd32(st + H_STAGE), rd32(st + H_INDEX), (int64_t)rd64(st + H_MAXSCORE),
+                      rd64(st + H_SUM)};
+    while (h < c->heads && *budget > 0) {
+      const uint32_t kh = h / group;
+      const int32_t *K = &r->keys[cache_index(c, cachepos, l, kh, 0, 0)];
+      const int32_t *V = &r->values[cache_index(c, cachepos, l, kh, 0, 0)];
+      const int last = attention_unit(&r->w2[h * c->head], K, V, t + 1, c->head, c->head, m->inv,
+                                      m->exp_tab, r->scores, &r->w3[h * c->head], &ac);
+      (*budget)--;
+      if (last) {
+        h++;
+        ac.stage = 0;
+        ac.index = 0;
+      }
+    }
+    wr64(st + H_MAXSCORE, (uint64_t)ac.max);
+    wr64(st + H_SUM, ac.sum);
+    wr32(st + H_STAGE, ac.stage);
+    wr32(st + H_INDEX, ac.index);
+    if (h < c->heads) {
+      wr32(st + H_ROW, h);
+      return 0;
+    }
+    wr32(st + H_ROW, 0);
+  } else if (p == 19) {
+    /* Sampling, entry by entry; the token is appended, then phase 20
+     * (token 1 or 2, or max tokens reached) or the next position. */
+    sample_cursor sc = {rd32(st + H_PASS), rd32(st + H_ROW), rd32(st + H_CHOSEN),
+                        (int64_t)rd64(st + H_MAXSCORE), rd64(st + H_SUM), rd64(st + H_REMAINDER)};
+    uint64_t gen = rd64(st + H_GENERATOR);
+    int chosen = 0;
+    while (!chosen && *budget > 0) {
+      chosen = sample_unit(r->logits, c->vocab, rd32(st + H_TEMP), m->exp_tab, &gen, &sc);
+      (*budget)--;
+    }
+    wr64(st + H_GENERATOR, gen);
+    wr32(st + H_CHOSEN, sc.chosen);
+    wr64(st + H_MAXSCORE, (uint64_t)sc.max);
+    wr64(st + H_SUM, sc.sum);
+    wr64(st + H_REMAINDER, sc.rem);
+    if (!chosen) {
+      wr32(st + H_PASS, sc.pass);
+      wr32(st + H_ROW, sc.row);
+      return 0;
+    }
+    wr32(st + H_PASS, 0);
+    wr32(st + H_ROW, 0);
+    const uint32_t next = sc.chosen;
+    uint32_t g = rd32(st + H_GENERATED);
+    r->out[g] = next;
+    g++;
+    wr32(st + H_GENERATED, g);
+    const int complete = next == 1 || next == 2 || g == rd32(st + H_MAX);
+    wr32(st + H_TOKEN, next);
+    wr32(st + H_POSITION, t + 1);
+    np = complete ? 20 : 3;
+    nl = 0;
+    *ended = 1;
+  } else {
+    /* the phases that are one whole vector operation */
+    (*budget)--;
+    switch (p) {
+      case 3: {
+        /* Embedding, ((byte - 128) * scale) >> 8 with the token row's scale. */
+        const uint32_t tok = rd32(st + H_TOKEN);
+        const mat_t *E = &mats[0];
+        const uint8_t *row = E->w + (uint64_t)tok * c->dim;
+        uint32_t sc = rd32(E->s_bytes + 4ull * tok);
+        for (uint32_t i = 0; i < c->dim; i++)
+          r->x[i] = asr(wmul((int64_t)row[i] - 128, (int64_t)(uint64_t)sc), 8);
+        nl = 0;
+        break;
+      }
+      case 4: /* attention normalization into w1 */
+        fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l) * c->dim, c->dim, r->w1);
+        break;
+      case 8: {
+        /* Rotary.  Reading: pairs are adjacent elements (2j, 2j+1) of each
+         * head, turned by the position's entry j of the tables; the query
+         * first, then this position's keys, each stored key checked. */
+        const int32_t *cs = m->cos_tab + (uint64_t)t * half;
+        const int32_t *sn = m->sin_tab + (uint64_t)t * half;
+        for (uint32_t h = 0; h < c->heads; h++)
+          for (uint32_t j = 0; j < half; j++)
+            fpi8_ref_rotate(&r->w2[h * c->head + 2 * j], &r->w2[h * c->head + 2 * j + 1], cs[j], sn[j]);
+        for (uint32_t kh = 0; kh < c->kv_heads; kh++)
+          for (uint32_t j = 0; j < half; j++) {
+            int32_t *k0 = &r->keys[cache_index(c, cachepos, l, kh, t, 2 * j)];
+            int64_t a = k0[0], b = k0[1];
+            fpi8_ref_rotate(&a, &b, cs[j], sn[j]);
+            if (!fits32(a) || !fits32(b)) return fail(r, 8, l);
+            k0[0] = (int32_t)a;
+            k0[1] = (int32_t)b;
+          }
+        break;
+      }
+      case 11: /* residual, then the feed-forward normalization into w1 */
+        for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
+        fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l + 1) * c->dim, c->dim, r->w1);
+        break;
+      case 14: /* gate element through SiLU times the up element, >> 16, kept in gate */
+        for (uint32_t i = 0; i < c->hidden; i++)
+          r->gate[i] = asr(wmul(fpi8_ref_silu(r->gate[i], m->silu_tab), r->up[i]), 16);
+        break;
+      case 16: /* residual; then the next layer, the final phases, or the next
+                * prompt position (phases 17-19 run only where a token is
+                * generated: the last prompt position and every later one) */
+        for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
+        if (l + 1 < c->layers) {
+          np = 4;
+          nl = l + 1;
+        } else if (t + 1 >= n_ids) {
+          np = 17;
+          nl = 0;
+        } else {
+          wr32(st + H_TOKEN, r->ids[t + 1]);
+          wr32(st + H_POSITION, t + 1);
+          np = 3;
+          nl = 0;
+          *ended = 1;
         }
-      break;
+        break;
+      case 17: /* final normalization into w1 */
+        fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * c->layers) * c->dim, c->dim, r->w1);
+        break;
+      default:
+        return FPI8_REF_INVALID_STATE;
     }
-    case 9: /* attention, head by head, outputs into w3; head h reads key and
-             * value head h / (heads / kv_heads) */
-      for (uint32_t h = 0; h < c->heads; h++) {
-        uint32_t kh = h / group;
-        const int32_t *K = &r->keys[cache_index(c, cachepos, l, kh, 0, 0)];
-        const int32_t *V = &r->values[cache_index(c, cachepos, l, kh, 0, 0)];
-        fpi8_ref_attention_head(&r->w2[h * c->head], K, V, t + 1, c->head, c->head, m->inv,
-                                m->exp_tab, r->scores, &r->w3[h * c->head], NULL, NULL);
-      }
-      break;
-    case 10: /* the attention output matrix into w1 */
-      matvec(&Lm[K_O - 1], r->w3, r->w1);
-      break;
-    case 11: /* residual, then the feed-forward normalization into w1 */
-      for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
-      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * l + 1) * c->dim, c->dim, r->w1);
-      break;
-    case 12: /* gate */
-      matvec(&Lm[K_GATE - 1], r->w1, r->gate);
-      break;
-    case 13: /* up */
-      matvec(&Lm[K_UP - 1], r->w1, r->up);
-      break;
-    case 14: /* gate element through SiLU times the up element, >> 16, kept in gate */
-      for (uint32_t i = 0; i < c->hidden; i++)
-        r->gate[i] = asr(wmul(fpi8_ref_silu(r->gate[i], m->silu_tab), r->up[i]), 16);
-      break;
-    case 15: /* down into w1 */
-      matvec(&Lm[K_DOWN - 1], r->gate, r->w1);
-      break;
-    case 16: /* residual; then the next layer, the final phases, or the next
-              * prompt position (phases 17-19 run only where a token is
-              * generated: the last prompt position and every later one) */
-      for (uint32_t i = 0; i < c->dim; i++) r->x[i] = wadd(r->x[i], r->w1[i]);
-      if (l + 1 < c->layers) {
-        np = 4;
-        nl = l + 1;
-      } else if (t + 1 >= n_ids) {
-        np = 17;
-        nl = 0;
-      } else {
-        wr32(st + H_TOKEN, r->ids[t + 1]);
-        wr32(st + H_POSITION, t + 1);
-        np = 3;
-        nl = 0;
-        *ended = 1;
-      }
-      break;
-    case 17: /* final normalization into w1 */
-      fpi8_ref_rmsnorm(r->x, m->norm + (uint64_t)(2 * c->layers) * c->dim, c->dim, r->w1);
-      break;
-    case 18: /* classifier into the logits */
-      matvec(&mats[1 + 7 * c->layers], r->w1, r->logits);
-      break;
-    case 19: {
-      /* sampling; the token is appended, then phase 20 (token 1 or 2, or max
-       * tokens reached) or the next position */
-      uint64_t gen = rd64(st + H_GENERATOR);
-      const uint32_t next = fpi8_ref_sample(r->logits, c->vocab, rd32(st + H_TEMP), m->exp_tab, &gen);
-      wr64(st + H_GENERATOR, gen);
-      uint32_t g = rd32(st + H_GENERATED);
-      r->out[g] = next;
-      g++;
-      wr32(st + H_GENERATED, g);
-      const int complete = next == 1 || next == 2 || g == rd32(st + H_MAX);
-      wr32(st + H_TOKEN, next);
-      wr32(st + H_POSITION, t + 1);
-      np = complete ? 20 : 3;
-      nl = 0;
-      *ended = 1;
-      break;
-    }
-    default:
-      return FPI8_REF_INVALID_STATE;
   }
   wr32(st + H_PHASE, np);
   wr32(st + H_LAYER, nl);
+  *done = 1;
   return 0;
 }
 
+/* Rows of the matrix phase p works through, 0 for the other phases. */
+static uint32_t phase_rows(const cfg_t *c, uint32_t p) {
+  switch (p) {
+    case 5: case 10: case 15: return c->dim;
+    case 6: case 7: return c->kvd;
+    case 12: case 13: return c->hidden;
+    case 18: return c->vocab;
+    default: return 0;
+  }
+}
+
 /* State checks shared by turn: tag, alignment, size for the configuration,
- * and a cursor at a phase of a position: 3 (its start), 4 to 16 with a
- * layer, or 17 to 19 at a position that generates ("Core errors",
- * InvalidState).  Cursors inside a phase (row, attention stage and index,
- * sampling pass) are not produced here and must be zero. */
+ * and a cursor the pass can stand at ("Core errors", InvalidState): phase 3
+ * (a position's start), 4 to 16 with a layer, or 17 to 19 at a position
+ * that generates; inside a matrix phase a row below its rows, inside
+ * attention a head, a stage 0 to 3 and an index below the stage's units
+ * (with a sum of exponentials once stage 1 has ended), inside sampling a
+ * pass 0 to 2 (1 and 2 above temperature zero) and an entry below the
+ * vocabulary (in the draw pass a remainder below the sum).  Every other
+ * sub-phase field is zero. */
 static int32_t check_state(const cfg_t *c, uint8_t *st, uint64_t len, fpi8_ref_layout *L) {
   if (((uintptr_t)st) & 7 || len < HEADER || memcmp(st, STATE_TAG, 8))
     return FPI8_REF_INVALID_STATE;
@@ -716,22 +850,36 @@ static int32_t check_state(const cfg_t *c, uint8_t *st, uint64_t len, fpi8_ref_l
   const uint32_t phase = rd32(st + H_PHASE), layer = rd32(st + H_LAYER);
   if (rd32(st + H_ERROR) != 0 || phase < 3 || phase > 19) return FPI8_REF_INVALID_STATE;
   if ((phase >= 4 && phase <= 16) ? layer >= c->layers : layer != 0) return FPI8_REF_INVALID_STATE;
-  if (rd32(st + H_ROW) != 0 || rd32(st + H_STAGE) != 0 || rd32(st + H_INDEX) != 0 ||
-      rd32(st + H_PASS) != 0)
-    return FPI8_REF_INVALID_STATE;
   uint32_t pos = rd32(st + H_POSITION), gen = rd32(st + H_GENERATED);
   if (phase >= 17 && pos + 1 < n_ids) return FPI8_REF_INVALID_STATE;
   if (pos >= L->cache_positions) return FPI8_REF_INVALID_STATE;
   if (gen != (pos + 1 > n_ids ? pos + 1 - n_ids : 0)) return FPI8_REF_INVALID_STATE;
   if (rd32(st + H_TOKEN) >= c->vocab || rd32(st + H_TEMP) > (16u << 16))
     return FPI8_REF_INVALID_STATE;
+  const uint32_t row = rd32(st + H_ROW), stage = rd32(st + H_STAGE), index = rd32(st + H_INDEX);
+  const uint32_t pass = rd32(st + H_PASS);
+  if (phase == 9) {
+    if (row >= c->heads || stage > 3 || index >= (stage < 3 ? pos + 1 : c->head) || pass != 0)
+      return FPI8_REF_INVALID_STATE;
+    if (stage >= 2 && rd64(st + H_SUM) == 0) return FPI8_REF_INVALID_STATE;
+  } else if (phase == 19) {
+    if (pass > 2 || (pass > 0 && rd32(st + H_TEMP) == 0) || row >= c->vocab || stage != 0 ||
+        index != 0)
+      return FPI8_REF_INVALID_STATE;
+    if (pass == 2 && rd64(st + H_REMAINDER) >= rd64(st + H_SUM)) return FPI8_REF_INVALID_STATE;
+  } else {
+    if (row >= (phase_rows(c, phase) ? phase_rows(c, phase) : 1) || stage != 0 || index != 0 ||
+        pass != 0)
+      return FPI8_REF_INVALID_STATE;
+  }
   return 0;
 }
 
-/* A turn from the cursor: whole positions (the first one finished from
- * wherever the cursor stands) when by_phase is 0, else single phases. */
+/* A turn from the cursor (mode 0: up to count positions, the first one
+ * finished from wherever the cursor stands; 1: up to count phases, the
+ * first one likewise; 2: up to count units of work). */
 static int32_t turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state, uint64_t state_len,
-                    uint32_t count, int by_phase) {
+                    uint64_t count, int mode) {
   model_t m;
   mat_t *mats;
   uint32_t nm;
@@ -747,6 +895,8 @@ static int32_t turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state, uint
   run_t r;
   int32_t e = check_state(&m.c, state, state_len, &r.L);
   if (e) { free(mats); return e; }
+  r.tmp = (int64_t *)malloc(8ull * m.c.kvd);
+  if (!r.tmp) { free(mats); return FPI8_REF_BUFFER_TOO_SMALL; }
   r.st = state;
   r.x = (int64_t *)(state + r.L.x);
   r.w1 = (int64_t *)(state + r.L.w1);
@@ -761,14 +911,16 @@ static int32_t turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state, uint
   r.ids = (uint32_t *)(state + r.L.ids);
   r.out = (uint32_t *)(state + r.L.out);
   wr64(state + H_TURNS, rd64(state + H_TURNS) + 1);
-  uint32_t done = 0;
-  while (done < count) {
-    int ended;
-    e = phase_step(&m, mats, &r, &ended);
-    if (e) break;
-    if (by_phase || ended) done++;
+  uint64_t units = mode == 2 ? count : UINT64_MAX;
+  uint64_t n = 0;
+  while (mode == 2 ? units > 0 : n < count) {
+    int done, ended;
+    e = run_phase(&m, mats, &r, &units, &done, &ended);
+    if (e || !done) break;
+    if ((mode == 0 && ended) || mode == 1) n++;
     if (rd32(state + H_PHASE) == 20) break;
   }
+  free(r.tmp);
   free(mats);
   return e;
 }
@@ -781,4 +933,9 @@ int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
 int32_t fpi8_ref_turn_phases(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
                              uint64_t state_len, uint32_t max_phases) {
   return turn(blob, blob_len, state, state_len, max_phases, 1);
+}
+
+int32_t fpi8_ref_turn_units(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
+                            uint64_t state_len, uint64_t max_units) {
+  return turn(blob, blob_len, state, state_len, max_units, 2);
 }

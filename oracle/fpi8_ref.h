@@ -109,11 +109,18 @@ int32_t fpi8_ref_state_info(const uint8_t *state, uint64_t len, fpi8_ref_info *o
 int32_t fpi8_ref_turn(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
                       uint64_t state_len, uint32_t max_positions);
 
-/* Runs up to max_phases single phases of one run from the state's cursor
- * (phase 3 to 19, with a layer for phases 4 to 16), stopping early at
- * phase 20 or an error. */
+/* Runs up to max_phases phases of one run from the state's cursor (the
+ * first one finished from wherever inside it the cursor stands), stopping
+ * early at phase 20 or an error. */
 int32_t fpi8_ref_turn_phases(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
                              uint64_t state_len, uint32_t max_phases);
+
+/* Runs up to max_units units of work of one run from the state's cursor: a
+ * row of a matrix, a position or output element of an attention stage, a
+ * vocabulary entry of a sampling pass, or a phase that is one whole vector
+ * operation.  It may stop inside a phase; the cursor then records where. */
+int32_t fpi8_ref_turn_units(const uint8_t *blob, uint64_t blob_len, uint8_t *state,
+                            uint64_t state_len, uint64_t max_units);
 
 /* Byte offsets of the state's buffers (for tests that read them). */
 typedef struct {

@@ -853,6 +853,213 @@ def test_mid_position_cursor_checks():
     assert (info["phase"], info["layer"], info["position"]) == (3, 0, 1)
 
 
+H_STAGE, H_INDEX, H_PASS = 120, 124, 100
+H_MAXSCORE, H_CHOSEN, H_SUM, H_REMAINDER, H_GENERATOR = 88, 96, 104, 112, 72
+
+
+def u32(st, off):
+    return int(st[off:off + 4].view(np.uint32)[0])
+
+
+def u64(st, off):
+    return int(st[off:off + 8].view(np.uint64)[0])
+
+
+def i64(st, off):
+    return int(st[off:off + 8].view(np.int64)[0])
+
+
+def test_unit_cuts_do_not_change_results():
+    # Turns that stop after any number of units of work (inside matrices,
+    # attention stages and sampling passes), mixed with turns of phases and
+    # of positions, end in the state of one uninterrupted turn.
+    shape = W.SMALL_SHAPES["gqa"]
+    bl = B.build_blob(shape, 33)
+    ids = W.prompt_ids(shape.vocab, 5, 7, 0)
+    cfg = shape.as_tuple()
+    e, a = O.init_state(cfg, ids, 6, 65536, 9)
+    assert O.run_to_end(bl, a) == 0
+    rng = np.random.default_rng(10)
+    for trial in range(3):
+        e, b = O.init_state(cfg, ids, 6, 65536, 9)
+        while not O.state_info(b)[1]["complete"]:
+            u = rng.random()
+            if u < 0.1:
+                assert O.turn(bl, b, 1) == 0
+            elif u < 0.2:
+                assert O.turn_phases(bl, b, int(rng.integers(1, 5))) == 0
+            else:
+                assert O.turn_units(bl, b, int(rng.integers(1, [3, 40, 400][trial]))) == 0
+        a[80:88] = 0
+        b[80:88] = 0
+        assert np.array_equal(a, b)
+
+
+def test_attention_cursor_holds_each_stage():
+    # One unit at a time through phase 9: the cursor's head, stage and index
+    # walk heads, stages 0-3 and their units in order; the scores buffer and
+    # the header hold each stage's values (scores and their maximum,
+    # exponentials and their sum, probabilities), and the outputs so far are
+    # those of the pinned whole-head routine.
+    shape = W.SMALL_SHAPES["gqa"]
+    cfg = shape.as_tuple()
+    bl = B.build_blob(shape, 34)
+    lay = B.plan(shape)
+    ids = W.prompt_ids(shape.vocab, 6, 8, 0)
+    e, st = O.init_state(cfg, ids, 2)
+    L = O.state_layout(cfg, len(ids), 2)
+    while True:                       # position 4, layer 1, phase 9
+        i = O.state_info(st)[1]
+        if (i["position"], i["layer"], i["phase"]) == (4, 1, 9):
+            break
+        assert O.turn_phases(bl, st, 1) == 0
+    hs, cp, npos = shape.head_size, L["cache_positions"], 5
+    exp_tab = bl[lay.offsets["exp"]: lay.offsets["exp"] + 4 * 4097].view(np.uint32)
+    keys = st[L["keys"]: L["keys"] + 4 * shape.layers * shape.kv_heads * cp * hs].view(
+        np.int32).reshape(shape.layers, shape.kv_heads, cp, hs)
+    vals = st[L["values"]: L["values"] + 4 * shape.layers * shape.kv_heads * cp * hs].view(
+        np.int32).reshape(shape.layers, shape.kv_heads, cp, hs)
+    q = st[L["w2"]: L["w2"] + 8 * shape.dim].view(np.int64).copy()
+    grp = shape.heads // shape.kv_heads
+    want = [O.attention_head(q[h * hs:(h + 1) * hs], keys[1, h // grp, :npos].copy(),
+                             vals[1, h // grp, :npos].copy(), B.inv_sqrt_head(shape), exp_tab)
+            for h in range(shape.heads)]
+    scores = lambda: st[L["scores"]: L["scores"] + 8 * npos].view(np.int64)
+    w3 = lambda: st[L["w3"]: L["w3"] + 8 * shape.dim].view(np.int64)
+    walk = []
+    while O.state_info(st)[1]["phase"] == 9:
+        h, sg, ix = u32(st, H_ROW), u32(st, H_STAGE), u32(st, H_INDEX)
+        walk.append((h, sg, ix))
+        out, p, m, ssum = want[h]
+        if sg == 1 and ix > 0:
+            assert u64(st, H_SUM) == int(scores()[:ix].sum())
+        if sg >= 1:
+            assert i64(st, H_MAXSCORE) == m
+        if sg >= 2:
+            assert u64(st, H_SUM) == ssum
+        if sg == 3:
+            assert np.array_equal(scores(), p)
+            assert np.array_equal(w3()[h * hs: h * hs + ix], out[:ix])
+        assert O.turn_units(bl, st, 1) == 0
+    assert walk == [(h, sg, ix) for h in range(shape.heads) for sg in range(4)
+                    for ix in range(npos if sg < 3 else hs)]
+    # the phase's end: every head's output; the last head's maximum and sum
+    for h in range(shape.heads):
+        assert np.array_equal(w3()[h * hs:(h + 1) * hs], want[h][0])
+    assert (i64(st, H_MAXSCORE), u64(st, H_SUM)) == (want[-1][2], want[-1][3])
+    assert (u32(st, H_ROW), u32(st, H_STAGE), u32(st, H_INDEX)) == (0, 0, 0)
+
+
+@pytest.mark.parametrize("temp", [0, 65536 * 3 // 4])
+def test_sampling_cursor_holds_each_pass(temp):
+    # One vocabulary entry at a time through phase 19: the maximum pass keeps
+    # the running maximum and the first index that reached it; above
+    # temperature zero the sum pass follows, the generator advances once
+    # when it ends and the draw starts from xorshift64* modulo the sum; the
+    # token is the pinned sampler's.
+    shape = W.SMALL_SHAPES["gqa"]
+    cfg = shape.as_tuple()
+    bl = B.build_blob(shape, 35)
+    lay = B.plan(shape)
+    exp_tab = bl[lay.offsets["exp"]: lay.offsets["exp"] + 4 * 4097].view(np.uint32)
+    ids = W.prompt_ids(shape.vocab, 3, 9, 0)
+    e, st = O.init_state(cfg, ids, 3, temp, 77)
+    L = O.state_layout(cfg, len(ids), 3)
+    while O.state_info(st)[1]["phase"] != 19:
+        assert O.turn_phases(bl, st, 1) == 0
+    logits = st[L["logits"]: L["logits"] + 8 * shape.vocab].view(np.int64).copy()
+    gen0 = u64(st, H_GENERATOR)
+    want_tok, want_gen = O.sample(logits, temp, exp_tab, gen0)
+    V = shape.vocab
+    seen = []
+    while O.state_info(st)[1]["phase"] == 19:
+        ps, row = u32(st, H_PASS), u32(st, H_ROW)
+        seen.append((ps, row))
+        if ps == 0 and row > 0:
+            assert i64(st, H_MAXSCORE) == logits[:row].max()
+            assert u32(st, H_CHOSEN) == int(np.argmax(logits[:row]))
+        if ps >= 1:
+            assert u32(st, H_CHOSEN) == int(np.argmax(logits))
+        if ps == 2 and row == 0:
+            g, x = O.xorshift64s(gen0)
+            assert u64(st, H_GENERATOR) == g
+            assert u64(st, H_REMAINDER) == x % u64(st, H_SUM)
+        assert O.turn_units(bl, st, 1) == 0
+    passes = [(0, r) for r in range(V)]
+    if temp:
+        passes += [(1, r) for r in range(V)] + [(2, r) for r in range(want_tok + 1)]
+    assert seen == passes
+    assert u32(st, H_CHOSEN) == want_tok and O.state_info(st)[1]["token"] == want_tok
+    assert u64(st, H_GENERATOR) == want_gen
+    assert (u32(st, H_PASS), u32(st, H_ROW)) == (0, 0)
+
+
+def test_matrix_cursor_holds_rows_done():
+    # Inside a matrix phase the cursor's row counts the rows done; those rows
+    # of the output hold the pinned row routine's values and the rest are
+    # untouched; key and value rows go straight into the cache.
+    shape = W.SMALL_SHAPES["ragged"]
+    cfg = shape.as_tuple()
+    bl = B.build_blob(shape, 36)
+    ids = W.prompt_ids(shape.vocab, 3, 10, 0)
+    e, st = O.init_state(cfg, ids, 2)
+    L = O.state_layout(cfg, len(ids), 2)
+    cp, hs = L["cache_positions"], shape.head_size
+    for phase, kind, name, n in ((5, B.KIND_Q, "w2", shape.dim), (6, B.KIND_K, None, shape.kv_dim),
+                                 (12, B.KIND_GATE, "gate", shape.hidden)):
+        while O.state_info(st)[1]["phase"] != phase:
+            assert O.turn_phases(bl, st, 1) == 0
+        w1 = st[L["w1"]: L["w1"] + 8 * shape.dim].view(np.int64).copy()
+        want = O.rows(*B.matrix_view(bl, shape, kind, 0), w1).reshape(-1)
+        w3 = st[L["w3"]: L["w3"] + 8 * shape.dim].copy()
+        before = st.copy()
+        k = n // 3 + 1
+        assert O.turn_units(bl, st, k) == 0
+        assert O.state_info(st)[1]["phase"] == phase and u32(st, H_ROW) == k
+        if name:
+            buf = st[L[name]: L[name] + 8 * n].view(np.int64)
+            old = before[L[name]: L[name] + 8 * n].view(np.int64)
+            assert np.array_equal(buf[:k], want[:k]) and np.array_equal(buf[k:], old[k:])
+        else:
+            t = O.state_info(st)[1]["position"]
+            keys = st[L["keys"]: L["keys"] + 4 * shape.layers * shape.kv_heads * cp * hs].view(
+                np.int32).reshape(shape.layers, shape.kv_heads, cp, hs)
+            assert np.array_equal(keys[0, :, t].reshape(-1)[:k], want[:k])
+            assert np.array_equal(st[L["w3"]: L["w3"] + 8 * shape.dim], w3)
+        assert O.turn_units(bl, st, n - k) == 0
+        assert O.state_info(st)[1]["phase"] == phase + 1 and u32(st, H_ROW) == 0
+
+
+def test_sub_phase_cursor_checks():
+    shape, bl = tiny_setup()
+    cfg = shape.as_tuple()
+
+    def at(phase, **f):
+        e, st = O.init_state(cfg, [5, 6, 7], 2, f.pop("temp", 0))
+        while O.state_info(st)[1]["phase"] != phase:
+            assert O.turn_phases(bl, st, 1) == 0
+        for off, v in f.items():
+            o = {"row": H_ROW, "stage": H_STAGE, "index": H_INDEX, "pass_": H_PASS,
+                 "sum": H_SUM}[off]
+            w = np.uint64(v) if off == "sum" else np.uint32(v)
+            st[o:o + w.nbytes] = np.frombuffer(w.tobytes(), np.uint8)
+        return st
+    assert O.turn_units(bl, at(5, row=63), 1) == 0                 # a row inside the matrix
+    assert O.turn_units(bl, at(5, row=64), 1) == 3                 # past the rows
+    assert O.turn_units(bl, at(4, row=1), 1) == 3                  # a vector phase has no rows
+    assert O.turn_units(bl, at(9, row=3), 1) == 0
+    assert O.turn_units(bl, at(9, row=4), 1) == 3                  # no head 4
+    assert O.turn_units(bl, at(9, stage=4), 1) == 3
+    assert O.turn_units(bl, at(9, stage=0, index=1), 1) == 3       # position 0: one unit
+    assert O.turn_units(bl, at(9, stage=3, index=15, sum=1 << 30), 1) == 0   # a head's elements
+    assert O.turn_units(bl, at(9, stage=2, sum=0), 1) == 3         # no sum to divide by
+    assert O.turn_units(bl, at(9, stage=1, pass_=1), 1) == 3
+    assert O.turn_units(bl, at(19, pass_=1), 1) == 3               # temperature zero
+    assert O.turn_units(bl, at(19, pass_=1, temp=65536), 1) == 0
+    assert O.turn_units(bl, at(19, pass_=3, temp=65536), 1) == 3
+    assert O.turn_units(bl, at(19, row=512), 1) == 3               # past the vocabulary
+
+
 def stop_token_blob(shape, seed=1000):
     """Every activation +127.0 from the embedding, no residual updates, and a
     classifier whose only nonzero row is the closing token's: token 2 wins."""
