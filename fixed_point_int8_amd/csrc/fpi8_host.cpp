@@ -70,22 +70,47 @@ int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L
   if (!state_layout(c, n_ids, mx, L) || L->total > stride) return FPI8_INVALID_STATE;
   if (ld32(h + ST_CACHEPOS) != L->cachepos) return FPI8_INVALID_STATE;
   if (ld32(h + ST_ERROR) != 0) return FPI8_INVALID_STATE;
-  // The cursor: a phase boundary of a position (3 its start; 4-16 with a
-  // layer; 17-19 only where the position generates), or 20 (complete).
-  // Cursors inside a phase (row, attention stage and index, sampling pass)
-  // are not taken.
+  // The cursor: phase 3 (a position's start), 4-16 with a layer, 17-19
+  // only where the position generates, or 20 (complete); inside a matrix
+  // phase a row below its rows, inside attention a head, a stage 0-3 and an
+  // index below the stage's units (with a sum of exponentials once stage 1
+  // has ended), inside sampling a pass 0-2 (1 and 2 above temperature zero)
+  // and an entry below the vocabulary (in the draw pass a remainder below
+  // the sum).  Every other sub-phase field is zero.
   const uint32_t phase = ld32(h + ST_PHASE), layer = ld32(h + ST_LAYER);
   if (phase == 20 && layer == 0) return -1;
   if (phase < 3 || phase > 19) return FPI8_INVALID_STATE;
   if ((phase >= 4 && phase <= 16) ? layer >= c.layers : layer != 0) return FPI8_INVALID_STATE;
-  if (ld32(h + ST_ROW) != 0 || ld32(h + ST_STAGE) != 0 || ld32(h + ST_INDEX) != 0 ||
-      ld32(h + ST_PASS) != 0)
-    return FPI8_INVALID_STATE;
   uint32_t pos = ld32(h + ST_POSITION), gen = ld32(h + ST_GENERATED);
   if (phase >= 17 && pos + 1 < n_ids) return FPI8_INVALID_STATE;
   if (pos >= L->cachepos) return FPI8_INVALID_STATE;
   if (gen != (pos + 1 > n_ids ? pos + 1 - n_ids : 0)) return FPI8_INVALID_STATE;
-  if (ld32(h + ST_TOKEN) >= c.vocab || ld32(h + ST_TEMP) > (16u << 16)) return FPI8_INVALID_STATE;
+  const uint32_t temp = ld32(h + ST_TEMP);
+  if (ld32(h + ST_TOKEN) >= c.vocab || temp > (16u << 16)) return FPI8_INVALID_STATE;
+  const uint32_t row = ld32(h + ST_ROW), stage = ld32(h + ST_STAGE), index = ld32(h + ST_INDEX);
+  const uint32_t pass = ld32(h + ST_PASS);
+  uint64_t sum, rem;
+  memcpy(&sum, h + ST_SUM, 8);
+  memcpy(&rem, h + ST_REMAINDER, 8);
+  if (phase == 9) {
+    if (row >= c.heads || stage > 3 || index >= (stage < 3 ? pos + 1 : c.head) || pass != 0)
+      return FPI8_INVALID_STATE;
+    if (stage >= 2 && sum == 0) return FPI8_INVALID_STATE;
+  } else if (phase == 19) {
+    if (pass > 2 || (pass > 0 && temp == 0) || row >= c.vocab || stage != 0 || index != 0)
+      return FPI8_INVALID_STATE;
+    if (pass == 2 && rem >= sum) return FPI8_INVALID_STATE;
+  } else {
+    uint32_t rows = 1;  // a phase that is one vector operation has no rows
+    switch (phase) {
+      case 5: case 10: case 15: rows = c.dim; break;
+      case 6: case 7: rows = c.kvd; break;
+      case 12: case 13: rows = c.hidden; break;
+      case 18: rows = c.vocab; break;
+      default: break;
+    }
+    if (row >= rows || stage != 0 || index != 0 || pass != 0) return FPI8_INVALID_STATE;
+  }
   return 0;
 }
 

@@ -44,8 +44,8 @@ int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L
 enum : uint32_t {
   ST_PHASE = 8, ST_LAYER = 12, ST_ROW = 16, ST_POSITION = 20, ST_TOKEN = 24, ST_ERROR = 28,
   ST_NIDS = 32, ST_MAX = 36, ST_TEMP = 40, ST_GENERATED = 44, ST_CACHEPOS = 48,
-  ST_GENERATOR = 72, ST_TURNS = 80, ST_PASS = 100, ST_STAGE = 120, ST_INDEX = 124,
-  ST_HEADER = 128
+  ST_GENERATOR = 72, ST_TURNS = 80, ST_MAXSCORE = 88, ST_CHOSEN = 96, ST_PASS = 100, ST_SUM = 104,
+  ST_REMAINDER = 112, ST_STAGE = 120, ST_INDEX = 124, ST_HEADER = 128
 };
 
 // Matrix kinds of the artifact.

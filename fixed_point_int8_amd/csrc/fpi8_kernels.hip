@@ -451,7 +451,7 @@ struct EpiIn {
   static constexpr int NX = (EPI == EPI_RESID || EPI == EPI_DOWN) ? MT : 1;
   static constexpr int NR = EPI == EPI_QKV ? MT : 1;
   uint32_t flags[BT], pos[BT], cache[BT];
-  uint64_t base[BT], o1[BT], o2[BT], o3[BT], o4[EPI == EPI_QKV ? BT : 1];
+  uint64_t base[BT], o1[BT], o2[BT], o3[BT];
   int64_t x[NX][BT][4];
   int32_t c[NR][BT][2], s[NR][BT][2];
 };
@@ -464,7 +464,6 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
     const uint32_t b = b0 + bt * 16 + li;
     in.flags[bt] = 0; in.pos[bt] = 0; in.cache[bt] = 0;
     in.base[bt] = 0; in.o1[bt] = 0; in.o2[bt] = 0; in.o3[bt] = 0;
-    if (EPI == EPI_QKV) in.o4[EPI == EPI_QKV ? bt : 0] = 0;
     if (EPI == EPI_RAW) {
       in.flags[bt] = b < a.n_runs ? 1u : 0u;
       continue;
@@ -479,7 +478,6 @@ __device__ __forceinline__ void epi_begin(const RowsArgs &a, uint32_t b0, int li
       in.pos[bt] = rd.pos;
       in.cache[bt] = rd.cachepos;
       in.o1[bt] = rd.off_w2; in.o2[bt] = rd.off_keys; in.o3[bt] = rd.off_values;
-      in.o4[EPI == EPI_QKV ? bt : 0] = rd.off_w3;
     }
   }
 }
@@ -625,10 +623,6 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             const uint32_t kvh = row / a.head, e = row % a.head;
             int32_t *dst = V + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
             const int64_t yv = pick >= 8 ? (int64_t)*dst : y[mt][j];  // stored before the cut
-            // The value rows pass through the third working vector on their
-            // way to the cache; it matters only where a turn stops before
-            // attention writes that vector, so only such launches write it.
-            if (PART) reinterpret_cast<int64_t *>(st + in.o4[EPI == EPI_QKV ? bt : 0])[row] = yv;
             if (!fits32(yv)) { fail(rd, a.layer, 7); continue; }
             *dst = (int32_t)yv;
           }
@@ -1382,8 +1376,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   }
   const uint64_t S = block_sum_u64(lsum, scratch);
 
-  // Stage 2, normalization: (e << 24) / S, at most 2^24.
+  // Stage 2, normalization: (e << 24) / S, at most 2^24.  The state keeps
+  // the last head's probabilities, largest score and sum.
   int64_t *scores_out = (h + 1 == a.heads) ? reinterpret_cast<int64_t *>(st + rd.off_scores) : nullptr;
+  if (scores_out && tid == 0) {
+    *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+    *reinterpret_cast<uint64_t *>(st + ST_SUM) = S;
+  }
   for (uint32_t j = tid; j < npos; j += blockDim.x) {
     const int64_t p = (int64_t)(((uint64_t)sc[j] << 24) / S);
     sc[j] = p;
@@ -1462,6 +1461,15 @@ __device__ __forceinline__ uint32_t temp_index(uint64_t d, uint32_t t) {
   return i > 4096 ? 4096u : (uint32_t)i;
 }
 
+// A cursor between two phases: no row, attention stage or index, or
+// sampling pass of its own.
+__device__ __forceinline__ void clear_sub_phase(uint8_t *st) {
+  *reinterpret_cast<uint32_t *>(st + ST_ROW) = 0u;
+  *reinterpret_cast<uint32_t *>(st + ST_PASS) = 0u;
+  *reinterpret_cast<uint32_t *>(st + ST_STAGE) = 0u;
+  *reinterpret_cast<uint32_t *>(st + ST_INDEX) = 0u;
+}
+
 __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   __shared__ int64_t best_v[256];
   __shared__ uint32_t best_i[256];
@@ -1500,6 +1508,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       }
       *reinterpret_cast<uint32_t *>(st + ST_PHASE) = phase;
       *reinterpret_cast<uint32_t *>(st + ST_LAYER) = layer;
+      clear_sub_phase(st);
     }
     return;
   }
@@ -1543,29 +1552,41 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       if (tid == 0) {
         uint64_t total = 0;
         for (int i = 0; i < 256; i++) total += part[i];
+        // The generator advances when the sum pass ends; a state stopped in
+        // the draw pass has advanced it already.
         uint64_t *gen = reinterpret_cast<uint64_t *>(st + ST_GENERATOR);
         uint64_t x = *gen;
-        x ^= x >> 12;
-        x ^= x << 25;
-        x ^= x >> 27;
-        *gen = x;
+        if (*reinterpret_cast<const uint32_t *>(st + ST_PASS) != 2) {
+          x ^= x >> 12;
+          x ^= x << 25;
+          x ^= x >> 27;
+          *gen = x;
+        }
         uint64_t r = (x * 0x2545F4914F6CDD1Dull) % total;
         uint32_t c = 0;
         while (c < 255 && r >= part[c]) { r -= part[c]; c++; }
         bcast[0] = c;
         bcast[1] = r;
+        *reinterpret_cast<uint64_t *>(st + ST_SUM) = total;
       }
       __syncthreads();
       if ((uint64_t)tid == bcast[0]) {
         uint64_t r = bcast[1];
         for (uint32_t i = c0; i < c1; i++) {
           const uint64_t e = a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
-          if (r < e) { bcast[2] = i; break; }
+          if (r < e) { bcast[2] = i; bcast[3] = r; break; }
           r -= e;
         }
       }
       __syncthreads();
       token = (uint32_t)bcast[2];
+      if (tid == 0) *reinterpret_cast<uint64_t *>(st + ST_REMAINDER) = bcast[3];
+    }
+    if (tid == 0) {
+      // what the passes leave in the header: the largest logit, the chosen
+      // entry (and above, the sum and what was left of the draw)
+      *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+      *reinterpret_cast<uint32_t *>(st + ST_CHOSEN) = token;
     }
     if (tid == 0) {
       uint32_t *gen_count = reinterpret_cast<uint32_t *>(st + ST_GENERATED);
@@ -1583,6 +1604,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     *reinterpret_cast<uint32_t *>(st + ST_POSITION) = pos + 1;
     *reinterpret_cast<uint32_t *>(st + ST_PHASE) = complete ? 20u : 3u;
     *reinterpret_cast<uint32_t *>(st + ST_LAYER) = 0u;
+    clear_sub_phase(st);
   }
 }
 

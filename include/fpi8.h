@@ -135,12 +135,15 @@ void fpi8_engine_destroy(fpi8_engine *engine);
  * (phases 3-16 per layer, then 17-19 where a token is generated; "The forward
  * pass, in order").  d_states holds n_runs states at a fixed byte stride
  * (multiple of 8; each state no larger than the stride), written by
- * fpi8_init_state and copied to the device.  A state may also stand between
- * two phases of a position ("The resumable state": the header's phase 3-19
- * and, for phases 4-16, its layer; the cursors inside a phase must be zero),
- * as a turn of the oracle that stops after any phase leaves it: the first
- * position then finishes from there, counted as one of max_positions, and
- * the run's words end as they would have without the stop.  Runs are
+ * fpi8_init_state and copied to the device.  A state may also stand inside a
+ * position ("The resumable state": the header's phase 3-19 and, for phases
+ * 4-16, its layer), between two phases or inside one (the next row of a
+ * matrix; the head, stage and index of attention; the pass and next entry of
+ * sampling, with the largest score, chosen entry, sum and remainder), as a
+ * turn that stops after any unit of work leaves it: the first position then
+ * finishes from there, counted as one of max_positions, and the run's words
+ * end as they would have without the stop.  A cursor no such turn can leave
+ * is an invalid state (error 3).  Runs are
  * independent: a run that completes stops, others go on.  A run that is already complete is left
  * as it is (error 0); an invalid or frozen state gets error 3; a key or
  * value that does not fit 32 bits freezes the run with error 8, its cursor at

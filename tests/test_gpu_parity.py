@@ -629,14 +629,86 @@ def test_stop_at_each_boundary():
         pair.model.close()
 
 
+@pytest.mark.parametrize("row_kernel", [0, 2])
+def test_resume_inside_phases(row_kernel):
+    # Oracle runs stopped inside a phase (a row of a matrix, a unit of an
+    # attention stage, an entry of a sampling pass), from every phase of a
+    # prompt and of a generating position: the GPU finishes each position
+    # and every later word matches the oracle's.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 55)
+    prompt = 4
+    cuts = phase_cuts(shape, prompt)
+    n = len(cuts)
+    say(f"resume inside phases: {n} runs, row kernel {row_kernel}")
+    temps = [65536 if r % 2 else 0 for r in range(n)]
+    runs = spec(shape, n, prompt, 5, seed=7, temps=temps)
+    pair = Pair(shape, blob, runs)
+    assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    rng = np.random.default_rng(row_kernel + 1)
+    try:
+        inside = 0
+        for i, (t, p, l) in enumerate(cuts):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, t, p, l)
+            # into the phase: up to a few hundred units (a sampling pass is
+            # one unit per vocabulary entry, attention one per position or
+            # element)
+            assert O.turn_units(blob, st, int(rng.integers(1, 320 if p == 19 else 40))) == 0
+            h = st[:128]
+            inside += bool(h[16:20].view(np.uint32)[0] or h[100:104].view(np.uint32)[0]
+                           or h[120:128].view(np.uint32).any())
+            pair.load(i, st)
+        assert inside >= n // 3, inside
+        for k in (1, 1, 3):
+            errs = pair.turn(k)
+            assert not any(errs), errs
+            pair.compare()
+        while not pair.complete():
+            pair.turn(1 << 20)
+        pair.compare()
+    finally:
+        pair.model.close()
+
+
+def test_resume_inside_sampling():
+    # Above temperature zero, runs stopped in each sampling pass: in the
+    # maximum pass, the sum pass, and the draw pass before and after its
+    # first entry (the generator has advanced there; the GPU must not again).
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 56)
+    V = shape.vocab
+    units = [1, V + 1, 2 * V, 2 * V + 1]
+    runs = spec(shape, len(units), 4, 3, seed=8, temps=[65536 * 3 // 2] * len(units))
+    pair = Pair(shape, blob, runs)
+    try:
+        for i, u in enumerate(units):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, 3, 19, 0)
+            assert O.turn_units(blob, st, u) == 0
+            assert O.state_info(st)[1]["phase"] == 19, (i, u)
+            pair.load(i, st)
+        passes = [int(pair.ref[i][100:104].view(np.uint32)[0]) for i in range(len(units))]
+        assert passes == [0, 1, 2, 2], passes
+        errs = pair.turn(1)
+        assert not any(errs), errs
+        pair.compare()
+        while not pair.complete():
+            pair.turn(1 << 20)
+        pair.compare()
+    finally:
+        pair.model.close()
+
+
 def test_resume_cursor_checks():
     # Cursors the pages' state cannot hold get error 3, on the GPU as in the
     # oracle; the run is left as it is.
     shape = W.SMALL_SHAPES["gqa"]
     blob = Bl.build_blob(shape, 52)
-    runs = spec(shape, 6, 4, 3, seed=4)
+    bad = [(17, 0, 0), (4, shape.layers, 0), (3, 1, 0), (2, 0, 0), (9, 0, shape.heads),
+           (21, 0, 0), (5, 0, shape.dim), (4, 0, 1)]
+    runs = spec(shape, len(bad), 4, 3, seed=4)
     pair = Pair(shape, blob, runs)
-    bad = [(17, 0, 0), (4, shape.layers, 0), (3, 1, 0), (2, 0, 0), (9, 0, 1), (21, 0, 0)]
     try:
         for i, (p, l, row) in enumerate(bad):
             st = pair.ref[i].copy()
