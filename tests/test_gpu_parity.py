@@ -701,8 +701,8 @@ def test_resume_inside_sampling():
 
 
 def test_resume_cursor_checks():
-    # Cursors the pages' state cannot hold get error 3, on the GPU as in the
-    # oracle; the run is left as it is.
+    # Cursors no turn can leave in the state ("The resumable state") get
+    # error 3, on the GPU as in the oracle; the run is left as it is.
     shape = W.SMALL_SHAPES["gqa"]
     blob = Bl.build_blob(shape, 52)
     bad = [(17, 0, 0), (4, shape.layers, 0), (3, 1, 0), (2, 0, 0), (9, 0, shape.heads),

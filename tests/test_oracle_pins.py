@@ -696,8 +696,9 @@ def set_cursor(st, phase, layer, row=0):
 
 
 def test_each_phase_does_what_the_pages_list():
-    # One phase per turn: the cursor walks the pages' order (3, then 4-16 per
-    # layer, then 17-19 where a token is generated), and each phase writes
+    # One phase per turn: the cursor walks the order of "The forward pass,
+    # in order" (3, then 4-16 per layer, then 17-19 where a token is
+    # generated), and each phase writes
     # the value of the building blocks pinned above, applied to the buffers
     # the previous phases left, into the buffer the pages name.
     shape = W.SMALL_SHAPES["gqa"]
