@@ -28,7 +28,8 @@ UINT64_MAX = (1 << 64) - 1
 # Symbols include/fpi8.h declares.
 EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_init_state",
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
-           "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
+           "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
+           "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -69,6 +70,7 @@ def lib():
             "fpi8_engine_destroy": (None, [_P]),
             "fpi8_turn": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
             "fpi8_turn_phases": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
+            "fpi8_turn_units": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint64, _P, _P]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -184,6 +186,14 @@ def fpi8_turn_phases(engine, d_states, state_stride: int, n_runs: int, max_phase
     errs = np.zeros(n_runs, dtype=np.int32)
     e = lib().fpi8_turn_phases(engine, _dev_ptr(d_states), state_stride, n_runs, max_phases,
                                _stream_ptr(stream), _np_ptr(errs))
+    return e, errs
+
+
+def fpi8_turn_units(engine, d_states, state_stride: int, n_runs: int, max_units: int,
+                    stream=None):
+    errs = np.zeros(n_runs, dtype=np.int32)
+    e = lib().fpi8_turn_units(engine, _dev_ptr(d_states), state_stride, n_runs, max_units,
+                              _stream_ptr(stream), _np_ptr(errs))
     return e, errs
 
 

@@ -276,7 +276,8 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
   const uint32_t n_runs = G.n;
   int r;
   {
-    BeginArgs a{states, G.runs, n_runs, G.oflags, e->n_oflags, c.layers};
+    BeginArgs a{states, G.runs, n_runs, G.oflags, e->n_oflags, c.layers,
+                c.dim, c.hidden, c.kvd, c.heads, c.head, c.vocab};
     if ((r = launch_begin(a, s))) return r;
   }
   {
@@ -306,6 +307,12 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
                  fl + 1, e->score_cap, s0 + 2, partial};
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
+    }
+    if (partial) {
+      // the head a turn of units stops inside, for the runs it stops
+      AttnTailArgs ta{states, G.runs, n_runs, l, c.kv_heads, c.head, c.heads / c.kv_heads, s0 + 2,
+                      e->model.inv, e->exp_tab};
+      if ((r = launch_attention_tail(ta, s))) return r;
     }
     {
       RowsArgs a = rows_base(e, G, states, c.dim, G.planes0, fl + 1, IN_W3, l, s0 + 3, partial);
@@ -578,9 +585,12 @@ void stop_of(const Cfg &c, uint32_t n_ids, uint32_t cachepos, uint32_t pos, uint
 }
 
 // A turn over a batch: up to max_positions positions, and, when max_phases
-// is not ~0, up to max_phases phases of each run.
+// is not ~0, up to max_phases phases of each run, or, when max_units is not
+// ~0, up to max_units units of work of each run (counted on the device,
+// where the draw pass shows its length).
 int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
-             uint32_t max_positions, uint32_t max_phases, void *stream, int32_t *h_run_errors) {
+             uint32_t max_positions, uint32_t max_phases, uint64_t max_units, void *stream,
+             int32_t *h_run_errors) {
   if (!e || !d_states || n_runs == 0 || n_runs > e->max_runs) return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
   if ((reinterpret_cast<uintptr_t>(d_states) & 7) != 0 || (stride & 7) != 0 || stride < 128) {
@@ -627,6 +637,17 @@ int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs
     first[b] = pos;
     count[b] = rd.stop_pos == 0xFFFFFFFFu ? L.cachepos - pos
                                            : rd.stop_pos - pos + (rd.stop_step != 0 ? 1 : 0);
+    if (max_units != ~0ull) {
+      // Every position has at least the units of a prompt position at its
+      // first place: a bound on the positions the budget reaches.
+      const Cfg &c = e->c;
+      const uint64_t per_layer = 5 + 3ull * c.dim + 2ull * c.kvd + 2ull * c.hidden +
+                                 (uint64_t)c.heads * (3 + c.head);
+      const uint64_t least = 1 + per_layer * c.layers;
+      rd.units = 1;
+      rd.budget = max_units;
+      count[b] = (uint32_t)std::min<uint64_t>(count[b], max_units / least + 2);
+    }
     steps = std::max(steps, count[b]);
     if (phase != 3) resume = 1;
   }
@@ -650,6 +671,7 @@ int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs
   // others.
   for (uint32_t k = 0; k < steps; k++) {
     uint32_t partial = k == 0 ? resume : 0;
+    if (max_units != ~0ull) partial = 1;
     for (uint32_t b = 0; b < n_runs && !partial; b++) {
       const RunDesc &rd = e->h_runs[b];
       if (rd.valid && rd.stop_pos == first[b] + k && rd.stop_step != 0) partial = 1;
@@ -678,13 +700,20 @@ extern "C" {
 
 int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
                   uint32_t max_positions, void *stream, int32_t *h_run_errors) {
-  return turn(e, d_states, stride, n_runs, max_positions, 0xFFFFFFFFu, stream, h_run_errors);
+  return turn(e, d_states, stride, n_runs, max_positions, 0xFFFFFFFFu, ~0ull, stream, h_run_errors);
 }
 
 int32_t fpi8_turn_phases(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
                          uint32_t max_phases, void *stream, int32_t *h_run_errors) {
   if (max_phases == 0xFFFFFFFFu) max_phases--;
-  return turn(e, d_states, stride, n_runs, 0xFFFFFFFFu, max_phases, stream, h_run_errors);
+  return turn(e, d_states, stride, n_runs, 0xFFFFFFFFu, max_phases, ~0ull, stream, h_run_errors);
+}
+
+int32_t fpi8_turn_units(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
+                        uint64_t max_units, void *stream, int32_t *h_run_errors) {
+  if (max_units == ~0ull) max_units--;
+  return turn(e, d_states, stride, n_runs, 0xFFFFFFFFu, 0xFFFFFFFFu, max_units, stream,
+              h_run_errors);
 }
 
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {

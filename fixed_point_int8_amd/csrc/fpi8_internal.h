@@ -54,18 +54,27 @@ enum : uint32_t { M_EMBED, M_Q, M_K, M_V, M_O, M_GATE, M_UP, M_DOWN, M_CLS, M_KI
 // What one launch needs to know about a run.  The static part is filled on
 // the host at the start of a turn, the dynamic part by the first kernel of
 // every position.
-struct RunDesc {
+struct RunDesc {  // u32 fields (an even count), then 8-byte fields
   // dynamic
   uint32_t flags;     // RUN_ACTIVE, RUN_GEN, and where the position resumes (run_flags)
   uint32_t pos;       // position computed in this step
   uint32_t token;     // token embedded in this step
   uint32_t errkey;    // first failing (layer, phase) of this step, ~0 if none
   uint32_t end;       // the step this position stops before (~0: it runs to its end)
+  // a turn of units that stops the run inside this position: the cursor it
+  // stops at (phase, 0 for none; layer; row, stage, index and pass as the
+  // state's header has them), and whether the run has stopped
+  uint32_t stop_ph, stop_layer, stop_row, stop_stage, stop_index, stop_pass;
+  uint32_t stop_in;   // the step of the launch the stop falls inside (~0: between launches)
+  uint32_t halted;
   // static
   uint32_t n_ids, max_tokens, temp, cachepos;
   uint32_t valid;     // passed the host checks at the start of the turn
   uint32_t stop_pos;  // the turn stops this run in position stop_pos before step
   uint32_t stop_step; // stop_step (0: the position does not start); ~0: no stop
+  uint32_t units;     // a turn of units of work: the budget below counts them
+  uint32_t pad;
+  uint64_t budget;    // units of work left (dynamic; a turn of units only)
   uint64_t base;      // byte offset of the run's state in the arena
   uint64_t off_x, off_w1, off_w2, off_w3, off_gate, off_up, off_logits, off_scores;
   uint64_t off_keys, off_values, off_ids, off_out;
@@ -176,6 +185,16 @@ struct AttnArgs {
   uint32_t step, partial;   // as in RowsArgs
 };
 
+// The head of attention a turn of units stops inside: its stages up to the
+// cursor (one workgroup per run).
+struct AttnTailArgs {
+  uint8_t *states;
+  RunDesc *runs;
+  uint32_t n_runs, layer, kv_heads, head, group, step;
+  uint32_t inv;
+  const uint32_t *exp_tab;
+};
+
 struct SampleArgs {
   uint8_t *states;
   RunDesc *runs;
@@ -192,6 +211,8 @@ struct BeginArgs {
   uint32_t *oflags;
   uint32_t n_oflags;
   uint32_t layers;
+  // the sizes a turn of units counts its units by
+  uint32_t dim, hidden, kvd, heads, head, vocab;
 };
 
 // Launchers (defined in the .hip file).
@@ -210,6 +231,7 @@ int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stre
 constexpr uint32_t kRawInputLds = 24576;
 int launch_rows_raw(int mt, const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
+int launch_attention_tail(const AttnTailArgs &a, void *stream);
 // Packs a rows x cols byte matrix into tiles of 16 rows x 64 columns, tile
 // (rt, kb) at ((rt * kbp + kb) * 1024), inside it lane l = 16 g + i at
 // 16 l holding row 16 rt + i, columns 64 kb + 16 g .. + 15 (the layout of

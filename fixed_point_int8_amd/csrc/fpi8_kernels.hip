@@ -130,13 +130,111 @@ __global__ void k_turn_start(uint8_t *states, RunDesc *runs, uint32_t n_runs) {
 // inputs are still in the state and whose outputs nothing has read yet is
 // run again rather than picked up: the normalizations (5 after 4, 12 after
 // 11, 18 after 17) and attention (10 after 9) give the same words again.
+// A turn of units of work ("The resumable state": a row of a matrix, a
+// position or output element of an attention stage, a vocabulary entry of a
+// sampling pass, or a phase that is one vector operation).  Units of phase p
+// in a position of npos positions; sampling counts its maximum and sum
+// passes here (the draw pass ends where the draw falls).
+__device__ __forceinline__ uint64_t phase_units(const BeginArgs &a, uint32_t p, uint32_t npos,
+                                                uint32_t temp) {
+  switch (p) {
+    case 5: case 10: case 15: return a.dim;
+    case 6: case 7: return a.kvd;
+    case 9: return (uint64_t)a.heads * (3ull * npos + a.head);
+    case 12: case 13: return a.hidden;
+    case 18: return a.vocab;
+    case 19: return (uint64_t)a.vocab * (temp ? 2u : 1u);
+    default: return 1;
+  }
+}
+
+// The step of the launch that holds phase p of layer l.
+__device__ __forceinline__ uint32_t phase_step(const BeginArgs &a, uint32_t p, uint32_t l) {
+  const uint32_t l7 = 7 * l, f7 = 7 * a.layers;
+  switch (p) {
+    case 3: return 0;
+    case 4: return 1 + l7;
+    case 5: case 6: case 7: case 8: return 2 + l7;
+    case 9: return 3 + l7;
+    case 10: case 11: return 4 + l7;
+    case 12: case 13: case 14: return 6 + l7;
+    case 15: case 16: return 7 + l7;
+    case 17: return 1 + f7;
+    case 18: return 2 + f7;
+    default: return 3 + f7;
+  }
+}
+
+// Where a turn of units stops a run inside the position its cursor (p, l,
+// and d units of phase p done) stands in: walks the phases in order,
+// taking each one's units off the budget, and records the cursor where
+// the budget ends (rd.stop_*), or leaves rd.stop_ph 0 when the position's
+// phases fit (rd.budget then holds what is left, for the draw pass or the
+// next position).  Returns the step the run stops before, ~0 if none.
+__device__ uint32_t units_stop(const BeginArgs &a, RunDesc &rd, uint32_t p, uint32_t l, uint64_t d,
+                               uint32_t pos) {
+  const uint32_t npos = pos + 1, temp = rd.temp;
+  const bool gen = pos + 1 >= rd.n_ids;
+  uint64_t B = rd.budget;
+  rd.stop_ph = 0;
+  bool stop = false;
+  for (;;) {
+    if (p == 19 && temp != 0 && d >= 2ull * a.vocab) break;  // inside the draw pass
+    const uint64_t u = phase_units(a, p, npos, temp);
+    if (B < u - d) {
+      d += B;
+      B = 0;
+      stop = true;
+      break;
+    }
+    B -= u - d;
+    d = 0;
+    if (p == 19) break;  // the maximum (and sum) pass done; the draw is the sampler's
+    if (p == 16) {
+      if (l + 1 < a.layers) { p = 4; l++; }
+      else if (gen) { p = 17; l = 0; }
+      else break;  // the position's phases fit
+    } else {
+      p++;
+    }
+  }
+  rd.budget = B;
+  rd.stop_in = 0xFFFFFFFFu;
+  if (!stop) return 0xFFFFFFFFu;
+  // The budget ends inside phase p after d of its units.
+  rd.stop_ph = p;
+  rd.stop_layer = l;
+  rd.stop_row = 0; rd.stop_stage = 0; rd.stop_index = 0; rd.stop_pass = 0;
+  if (p == 9) {
+    const uint64_t per = 3ull * npos + a.head, r = d % per;
+    rd.stop_row = (uint32_t)(d / per);
+    rd.stop_stage = r < 3ull * npos ? (uint32_t)(r / npos) : 3u;
+    rd.stop_index = (uint32_t)(rd.stop_stage < 3 ? r % npos : r - 3ull * npos);
+  } else if (p == 19) {
+    rd.stop_pass = (uint32_t)(d / a.vocab);
+    rd.stop_row = (uint32_t)(d % a.vocab);
+  } else {
+    rd.stop_row = (uint32_t)d;
+  }
+  // At the start of a launch's first phase the run stops before that
+  // launch; anywhere else the launch runs for it in part.
+  const uint32_t L = phase_step(a, p, l);
+  const bool first = p == 3 || p == 4 || p == 5 || p == 9 || p == 10 || p == 12 || p == 15 ||
+                     p == 17 || p == 18 || p == 19;
+  if (d == 0 && first) return L;
+  rd.stop_in = L;
+  return L + 1;
+}
+
 __global__ void k_begin(BeginArgs a) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < a.n_oflags) a.oflags[i] = 0;
   if (i >= a.n_runs) return;
   RunDesc &rd = a.runs[i];
   uint32_t flags = 0, end = 0xFFFFFFFFu;
-  if (rd.valid) {
+  if (rd.valid && rd.units && rd.halted) {
+    // stopped by the budget in an earlier position of this turn
+  } else if (rd.valid) {
     const uint8_t *st = run_base(a.states, rd);
     const uint32_t phase = *reinterpret_cast<const uint32_t *>(st + ST_PHASE);
     const uint32_t layer = *reinterpret_cast<const uint32_t *>(st + ST_LAYER);
@@ -161,6 +259,26 @@ __global__ void k_begin(BeginArgs a) {
         default: break;
       }
       flags = run_flags(RUN_ACTIVE | (pos + 1 >= rd.n_ids ? RUN_GEN : 0u), start, pick, after);
+      if (rd.units) {
+        if (rd.budget == 0) {
+          flags = 0;  // nothing to do: the state stays as it is
+          rd.halted = 1;
+        } else {
+          // units of the current phase already done, from the cursor
+          const uint32_t row = *reinterpret_cast<const uint32_t *>(st + ST_ROW);
+          const uint32_t npos = pos + 1;
+          uint64_t d = row;
+          if (phase == 9) {
+            const uint32_t stage = *reinterpret_cast<const uint32_t *>(st + ST_STAGE);
+            const uint32_t index = *reinterpret_cast<const uint32_t *>(st + ST_INDEX);
+            d = (uint64_t)row * (3ull * npos + a.head) + (stage < 3 ? (uint64_t)stage * npos : 3ull * npos) + index;
+          } else if (phase == 19) {
+            d = (uint64_t)*reinterpret_cast<const uint32_t *>(st + ST_PASS) * a.vocab + row;
+          }
+          end = units_stop(a, rd, phase, layer, d, pos);
+          if (rd.stop_ph != 0) rd.halted = 1;
+        }
+      }
     }
   }
   rd.flags = flags;
@@ -571,6 +689,15 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
     // A run that stopped inside this launch's phases: the results of the
     // phases it finished come from its state instead of the sums.
     const uint32_t pick = PART ? pick_at(in.flags[bt], a.step, 1u) : 0u;
+    // A turn of units that stops the run inside this launch: the phase and
+    // row of the stop.  The launch writes what the phases before the stop
+    // leave in the state (matrix rows below the row, nothing turned, no
+    // residual or SiLU yet) and nothing after it.
+    uint32_t sp = 0, sr = 0;
+    if (PART) {
+      const RunDesc &rs = a.runs[b];
+      if (rs.stop_ph != 0 && a.step == rs.stop_in) { sp = rs.stop_ph; sr = rs.stop_row; }
+    }
 #pragma unroll
     for (int mt = 0; mt < (EPI == EPI_GATEUP ? HALF : MT); mt++) {
       const uint32_t r0 = rbase[mt] + 4 * lg;
@@ -578,16 +705,23 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
         int64_t *lg_out = reinterpret_cast<int64_t *>(st + in.o1[bt]);
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          if (r0 + j < rcount[mt]) lg_out[r0 + j] = y[mt][j];
+          if (r0 + j < rcount[mt] && (sp == 0 || r0 + j < sr)) lg_out[r0 + j] = y[mt][j];
       } else if (EPI == EPI_RESID || EPI == EPI_DOWN) {
         int64_t *x = reinterpret_cast<int64_t *>(st + in.o1[bt]);
         int64_t *w1 = reinterpret_cast<int64_t *>(st + in.o2[bt]);
         // picked up at 11 or 16: the matrix's output is already in w1
         const bool held = pick == (EPI == EPI_RESID ? 11u : 16u);
+        // stopped at 10 or 15 (a row of the matrix) or 11 or 16 (before the
+        // residual): the rows so far in w1, x as it was
+        const uint32_t lim = (sp == 10 || sp == 15) ? sr : rcount[mt];
 #pragma unroll
         for (int j = 0; j < 4; j++)
           if (r0 + j < rcount[mt]) {
             const int64_t yv = held ? w1[r0 + j] : y[mt][j];
+            if (sp != 0) {
+              if (r0 + j < lim) w1[r0 + j] = yv;
+              continue;
+            }
             if (EPI == EPI_DOWN) w1[r0 + j] = yv;
             x[r0 + j] = wadd(in.x[EPI == EPI_RESID || EPI == EPI_DOWN ? mt : 0][bt][j], yv);
           }
@@ -604,6 +738,13 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
           // too; at 15 the product is already in the gate vector
           const int64_t g = pick >= 13 ? gate[row] : y[mt][j];
           const int64_t u = pick >= 14 ? up[row] : y[mt + HALF][j];
+          if (sp != 0) {
+            // stopped at 12 or 13 (a row of the gate or up rows) or 14
+            // (before SiLU): the rows so far, as they come from the matrices
+            if (sp > 12 || row < sr) gate[row] = g;
+            if (sp == 14 || (sp == 13 && row < sr)) up[row] = u;
+            continue;
+          }
           const int64_t sg = g >= lim ? g : g <= -lim ? 0 : (int64_t)silu[(g + lim) >> 9];
           const int64_t h = pick == 15 ? g : wmul(sg, u) >> 16;
           gate[row] = h;
@@ -623,6 +764,7 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             const uint32_t kvh = row / a.head, e = row % a.head;
             int32_t *dst = V + (((uint64_t)a.layer * a.kv_heads + kvh) * in.cache[bt] + pos) * a.head + e;
             const int64_t yv = pick >= 8 ? (int64_t)*dst : y[mt][j];  // stored before the cut
+            if (sp != 0 && (sp < 7 || (sp == 7 && row >= sr))) continue;  // not reached by the stop
             if (!fits32(yv)) { fail(rd, a.layer, 7); continue; }
             *dst = (int32_t)yv;
           }
@@ -644,6 +786,24 @@ __device__ __forceinline__ void rows_epilogue(const RowsArgs &a, const RowTile<M
             int64_t A0 = y[mt][j], B0 = y[mt][j + 1];
             if (role == ROLE_Q && pick >= 6) { A0 = q[row]; B0 = q[row + 1]; }
             if (role == ROLE_K && pick >= 7) { A0 = dst[0]; B0 = dst[1]; }
+            if (sp != 0) {
+              // stopped at 5 (a query row), 6 (a key row), 7 or 8 (before
+              // rotary): the rows so far, unturned
+              const uint32_t lim = role == ROLE_Q ? (sp == 5 ? sr : rcount[mt])
+                                                  : (sp < 6 ? 0u : sp == 6 ? sr : rcount[mt]);
+              for (int e = 0; e < 2; e++) {
+                if (row + e >= lim) continue;
+                const int64_t val = e ? B0 : A0;
+                if (role == ROLE_Q) {
+                  q[row + e] = val;
+                } else if (!fits32(val)) {
+                  fail(rd, a.layer, 6);
+                } else {
+                  dst[e] = (int32_t)val;
+                }
+              }
+              continue;
+            }
             if (role == ROLE_K && (!fits32(A0) || !fits32(B0))) { fail(rd, a.layer, 6); continue; }
             const int64_t c = in.c[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
             const int64_t s = in.s[EPI == EPI_QKV ? mt : 0][bt][j >> 1];
@@ -1224,6 +1384,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   const uint32_t h = blockIdx.x, b = blockIdx.y;
   const RunDesc &rd = a.runs[b];
   if (!live_at(rd, rd.flags, RUN_ACTIVE, a.step, a.partial)) return;
+  // A turn of units that stops the run inside this phase: the heads before
+  // the stop's head are whole, the rest is the tail's (k_attention_tail).
+  uint32_t last = a.heads - 1;
+  if (a.partial && rd.stop_ph == 9 && a.step == rd.stop_in) {
+    if (h >= rd.stop_row) return;
+    last = rd.stop_row - 1;
+  }
   const uint32_t hs = HS ? HS : a.head;
   const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
   const uint32_t npos = rd.pos + 1, cachepos = rd.cachepos;
@@ -1378,7 +1545,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   // Stage 2, normalization: (e << 24) / S, at most 2^24.  The state keeps
   // the last head's probabilities, largest score and sum.
-  int64_t *scores_out = (h + 1 == a.heads) ? reinterpret_cast<int64_t *>(st + rd.off_scores) : nullptr;
+  int64_t *scores_out = h == last ? reinterpret_cast<int64_t *>(st + rd.off_scores) : nullptr;
   if (scores_out && tid == 0) {
     *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
     *reinterpret_cast<uint64_t *>(st + ST_SUM) = S;
@@ -1461,6 +1628,69 @@ __device__ __forceinline__ uint32_t temp_index(uint64_t d, uint32_t t) {
   return i > 4096 ? 4096u : (uint32_t)i;
 }
 
+// The head a turn of units stops inside ("Attention, stage by stage", unit
+// by unit as "The resumable state" counts them): its stages up to the
+// stop's stage and index, in the state's scores buffer, with the largest
+// score and the sum of exponentials in the header as far as the stages
+// reached.  One workgroup of 256 per run; runs without such a stop leave.
+__global__ __launch_bounds__(256) void k_attention_tail(AttnTailArgs a) {
+  __shared__ uint64_t scratch[8];
+  const RunDesc &rd = a.runs[blockIdx.x];
+  if (!(rd.flags & RUN_ACTIVE) || rd.stop_ph != 9 || a.step != rd.stop_in) return;
+  const uint32_t h = rd.stop_row, S = rd.stop_stage, I = rd.stop_index;
+  const uint32_t npos = rd.pos + 1, hs = a.head, tid = threadIdx.x;
+  uint8_t *st = a.states + rd.base;
+  const int64_t *q = reinterpret_cast<const int64_t *>(st + rd.off_w2) + (uint64_t)h * hs;
+  const uint64_t head_base = ((uint64_t)a.layer * a.kv_heads + h / a.group) * rd.cachepos * hs;
+  const int32_t *K = reinterpret_cast<const int32_t *>(st + rd.off_keys) + head_base;
+  const int32_t *V = reinterpret_cast<const int32_t *>(st + rd.off_values) + head_base;
+  int64_t *sc = reinterpret_cast<int64_t *>(st + rd.off_scores);
+  int64_t *out = reinterpret_cast<int64_t *>(st + rd.off_w3) + (uint64_t)h * hs;
+  const int64_t inv = (int64_t)(uint64_t)a.inv;
+  // stage 0: scores of the positions reached, and their maximum
+  const uint32_t n0 = S == 0 ? I : npos;
+  int64_t lmax = INT64_MIN;
+  for (uint32_t j = tid; j < n0; j += 256) {
+    int64_t dot = 0;
+    for (uint32_t i = 0; i < hs; i++) dot = wadd(dot, wmul(q[i], (int64_t)K[(uint64_t)j * hs + i]));
+    const int64_t s = wmul(dot >> 16, inv) >> 24;
+    sc[j] = s;
+    lmax = s > lmax ? s : lmax;
+  }
+  const int64_t m = block_max_i64(lmax, reinterpret_cast<int64_t *>(scratch));
+  if (n0 > 0 && tid == 0) *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+  if (S == 0) return;
+  __threadfence_block();
+  __syncthreads();
+  // stage 1: exponentials and their sum (started from zero by its first unit)
+  const uint32_t n1 = S == 1 ? I : npos;
+  uint64_t lsum = 0;
+  for (uint32_t j = tid; j < n1; j += 256) {
+    const uint64_t d = (uint64_t)m - (uint64_t)sc[j];
+    const uint64_t idx = d >> 8;
+    const uint32_t e = a.exp_tab[idx > 4096 ? 4096 : idx];
+    sc[j] = e;
+    lsum += e;
+  }
+  const uint64_t sum = block_sum_u64(lsum, scratch);
+  if (n1 > 0 && tid == 0) *reinterpret_cast<uint64_t *>(st + ST_SUM) = sum;
+  if (S == 1) return;
+  __threadfence_block();
+  __syncthreads();
+  // stage 2: normalization
+  const uint32_t n2 = S == 2 ? I : npos;
+  for (uint32_t j = tid; j < n2; j += 256) sc[j] = (int64_t)(((uint64_t)sc[j] << 24) / sum);
+  if (S == 2) return;
+  __threadfence_block();
+  __syncthreads();
+  // stage 3: the output elements reached
+  for (uint32_t e = tid; e < I; e += 256) {
+    int64_t acc = 0;
+    for (uint32_t j = 0; j < npos; j++) acc = wadd(acc, wmul(sc[j], (int64_t)V[(uint64_t)j * hs + e]));
+    out[e] = acc >> 24;
+  }
+}
+
 // A cursor between two phases: no row, attention stage or index, or
 // sampling pass of its own.
 __device__ __forceinline__ void clear_sub_phase(uint8_t *st) {
@@ -1490,7 +1720,27 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     }
     return;
   }
-  if (a.partial && rd.end <= a.step) {
+  // The cursor's sampling pass and entry as the position started (a turn
+  // may resume inside sampling).
+  const uint32_t pass_start = *reinterpret_cast<const uint32_t *>(st + ST_PASS);
+  const uint32_t row_start = *reinterpret_cast<const uint32_t *>(st + ST_ROW);
+  const uint64_t budget = rd.budget;  // read once: thread 0 updates it below
+  // A turn of units that stops the run in this position (rd.stop_*).
+  const bool ustop = a.partial && rd.stop_ph != 0;
+  auto write_stop = [&]() {
+    *reinterpret_cast<uint32_t *>(st + ST_PHASE) = rd.stop_ph;
+    *reinterpret_cast<uint32_t *>(st + ST_LAYER) = rd.stop_layer;
+    *reinterpret_cast<uint32_t *>(st + ST_ROW) = rd.stop_row;
+    *reinterpret_cast<uint32_t *>(st + ST_STAGE) = rd.stop_stage;
+    *reinterpret_cast<uint32_t *>(st + ST_INDEX) = rd.stop_index;
+    *reinterpret_cast<uint32_t *>(st + ST_PASS) = rd.stop_pass;
+  };
+  if (ustop && rd.stop_ph != 19) {
+    __syncthreads();  // every thread has read the cursor above
+    if (tid == 0) write_stop();
+    return;
+  }
+  if (!ustop && a.partial && rd.end <= a.step) {
     // The turn stops the run before step rd.end: its cursor names the
     // phase that step starts (a boundary between two phases).
     if (tid == 0) {
@@ -1520,10 +1770,12 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     const uint32_t V = a.vocab;
     const uint32_t chunk = (V + blockDim.x - 1) / blockDim.x;
     const uint32_t c0 = tid * chunk, c1 = min(V, c0 + chunk);
+    // a stop inside the maximum pass: the entries before its row
+    const uint32_t lim0 = (ustop && rd.stop_pass == 0) ? rd.stop_row : V;
     // Maximum pass: the largest logit, the lowest index on a tie.
     int64_t bv = INT64_MIN;
     uint32_t bi = 0xFFFFFFFFu;
-    for (uint32_t i = c0; i < c1; i++)
+    for (uint32_t i = c0; i < min(c1, lim0); i++)
       if (bi == 0xFFFFFFFFu || lgt[i] > bv) { bv = lgt[i]; bi = i; }
     best_v[tid] = bv;
     best_i[tid] = bi;
@@ -1543,12 +1795,36 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     const int64_t m = best_v[0];
     token = best_i[0];
     const uint32_t T = rd.temp;
+    if (ustop && rd.stop_pass == 0) {
+      // stopped inside the maximum pass
+      if (tid == 0) {
+        if (lim0 > 0) {
+          *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+          *reinterpret_cast<uint32_t *>(st + ST_CHOSEN) = token;
+        }
+        write_stop();
+      }
+      return;
+    }
     if (T != 0) {
       // Sum pass over each thread's slice, then the draw and the walk.
+      const uint32_t lim1 = ustop ? rd.stop_row : V;  // a stop inside the sum pass
       uint64_t s = 0;
-      for (uint32_t i = c0; i < c1; i++) s += a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
+      for (uint32_t i = c0; i < min(c1, lim1); i++) s += a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
       part[tid] = s;
       __syncthreads();
+      if (ustop) {
+        // stopped inside the sum pass (the generator has not advanced)
+        if (tid == 0) {
+          uint64_t total = 0;
+          for (int i = 0; i < 256; i++) total += part[i];
+          *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+          *reinterpret_cast<uint32_t *>(st + ST_CHOSEN) = token;
+          if (lim1 > 0) *reinterpret_cast<uint64_t *>(st + ST_SUM) = total;
+          write_stop();
+        }
+        return;
+      }
       if (tid == 0) {
         uint64_t total = 0;
         for (int i = 0; i < 256; i++) total += part[i];
@@ -1556,30 +1832,59 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
         // the draw pass has advanced it already.
         uint64_t *gen = reinterpret_cast<uint64_t *>(st + ST_GENERATOR);
         uint64_t x = *gen;
-        if (*reinterpret_cast<const uint32_t *>(st + ST_PASS) != 2) {
+        if (pass_start != 2) {
           x ^= x >> 12;
           x ^= x << 25;
           x ^= x >> 27;
           *gen = x;
         }
         uint64_t r = (x * 0x2545F4914F6CDD1Dull) % total;
+        bcast[1] = r;  // the draw, for a stop inside the walk
         uint32_t c = 0;
         while (c < 255 && r >= part[c]) { r -= part[c]; c++; }
         bcast[0] = c;
-        bcast[1] = r;
+        bcast[2] = r;
         *reinterpret_cast<uint64_t *>(st + ST_SUM) = total;
       }
       __syncthreads();
       if ((uint64_t)tid == bcast[0]) {
-        uint64_t r = bcast[1];
+        uint64_t r = bcast[2];
         for (uint32_t i = c0; i < c1; i++) {
           const uint64_t e = a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
-          if (r < e) { bcast[2] = i; bcast[3] = r; break; }
+          if (r < e) { best_i[0] = i; bcast[3] = r; break; }
           r -= e;
         }
       }
       __syncthreads();
-      token = (uint32_t)bcast[2];
+      const uint32_t drawn = best_i[0];
+      // A turn of units walks at most rd.budget entries of the draw pass
+      // from where this position's walk started.
+      const uint32_t walk0 = pass_start == 2 ? row_start : 0u;
+      if (a.partial && rd.units && (uint64_t)(drawn + 1 - walk0) > budget) {
+        const uint32_t R = walk0 + (uint32_t)budget;  // entries walked by the stop
+        uint64_t w = 0;
+        for (uint32_t i = c0; i < min(c1, R); i++) w += a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
+        __syncthreads();
+        part[tid] = w;
+        __syncthreads();
+        if (tid == 0) {
+          uint64_t walked = 0;
+          for (int i = 0; i < 256; i++) walked += part[i];
+          *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
+          *reinterpret_cast<uint32_t *>(st + ST_CHOSEN) = token;
+          *reinterpret_cast<uint64_t *>(st + ST_REMAINDER) = bcast[1] - walked;
+          *reinterpret_cast<uint32_t *>(st + ST_PHASE) = 19u;
+          *reinterpret_cast<uint32_t *>(st + ST_LAYER) = 0u;
+          *reinterpret_cast<uint32_t *>(st + ST_ROW) = R;
+          *reinterpret_cast<uint32_t *>(st + ST_STAGE) = 0u;
+          *reinterpret_cast<uint32_t *>(st + ST_INDEX) = 0u;
+          *reinterpret_cast<uint32_t *>(st + ST_PASS) = 2u;
+          rd.halted = 1;
+        }
+        return;
+      }
+      if (tid == 0 && a.partial && rd.units) rd.budget = budget - (drawn + 1 - walk0);
+      token = drawn;
       if (tid == 0) *reinterpret_cast<uint64_t *>(st + ST_REMAINDER) = bcast[3];
     }
     if (tid == 0) {
@@ -1771,6 +2076,12 @@ int launch_pack(const uint8_t *W, uint32_t rows, uint32_t cols, uint8_t *P, void
   const uint64_t pieces = packed_bytes(rows, cols) / 16;
   hipLaunchKernelGGL(k_pack, dim3((uint32_t)((pieces + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                      W, rows, cols, kbp, P, pieces);
+  return ok(hipGetLastError());
+}
+
+int launch_attention_tail(const AttnTailArgs &a, void *stream) {
+  if (!a.n_runs) return 0;
+  hipLaunchKernelGGL(k_attention_tail, dim3(a.n_runs), dim3(256), 0, (hipStream_t)stream, a);
   return ok(hipGetLastError());
 }
 

@@ -90,6 +90,10 @@ class DeviceBatch:
         return B.fpi8_turn_phases(model.engine, self.d_states, self.stride, self.n, max_phases,
                                   stream)
 
+    def turn_units(self, model: DeviceModel, max_units: int, stream=None):
+        return B.fpi8_turn_units(model.engine, self.d_states, self.stride, self.n, max_units,
+                                 stream)
+
     def state(self, i: int) -> np.ndarray:
         """A host copy of run i's state (8-byte aligned)."""
         size = self.sizes[i]

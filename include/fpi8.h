@@ -168,6 +168,20 @@ int32_t fpi8_turn_phases(fpi8_engine *engine, uint8_t *d_states, uint64_t state_
                          uint32_t n_runs, uint32_t max_phases, void *stream,
                          int32_t *h_run_errors);
 
+/* A turn of at most max_units units of work of each run, counted as "The
+ * resumable state" cuts the pass: a row of a matrix, a position or output
+ * element of an attention stage, a vocabulary entry of a sampling pass, or a
+ * phase that is one vector operation.  Each run stops exactly where its
+ * budget ends, inside a phase if it ends there, and its state holds what
+ * the oracle's turn of the same units leaves: the rows done, the attention
+ * head's stage values, the sampling pass's running maximum, choice, sum and
+ * remainder, and the cursor.  Positions where a run starts or stops inside
+ * run their launches one by one.  Errors, arguments and synchronization as
+ * fpi8_turn; max_units 2^64 - 1 counts as 2^64 - 2. */
+int32_t fpi8_turn_units(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
+                        uint32_t n_runs, uint64_t max_units, void *stream,
+                        int32_t *h_run_errors);
+
 /* Which matrix-row kernel the engine's launches use: 0 the planner's choice
  * (the default), 1 always the kernel whose four waves split the contraction,
  * 2 the kernel whose waves share their runs' digits through LDS wherever it

@@ -700,6 +700,82 @@ def test_resume_inside_sampling():
         pair.model.close()
 
 
+def units_pair_turn(pair, k, blob):
+    """A turn of k units on both sides; every run's state must agree."""
+    e, errs = pair.batch.turn_units(pair.model, k)
+    assert e == 0 and not any(errs), (k, e, errs)
+    for i in range(len(pair.runs)):
+        if not (O.state_info(pair.ref[i])[1]["complete"]):
+            assert O.turn_units(blob, pair.ref[i], k) == 0
+    pair.compare()
+
+
+def test_units_one_at_a_time():
+    # Turns of one unit of work each, through a generating position and on,
+    # at temperature zero and above: the GPU stops after every row of every
+    # matrix, every unit of every attention stage and every vocabulary entry
+    # of every sampling pass, in the state the oracle's turn leaves.
+    shape = W.TINY.shape
+    blob = Bl.build_blob(shape, 57)
+    runs = spec(shape, 2, 3, 3, seed=9, temps=[0, 65536])
+    pair = Pair(shape, blob, runs)
+    try:
+        for i in range(2):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, 2, 3, 0)        # the last prompt position, which generates
+            pair.load(i, st)
+        seen = set()
+        n = 0
+        while cursor(pair.ref[0])[0] < 4 or cursor(pair.ref[1])[0] < 4:
+            units_pair_turn(pair, 1, blob)
+            n += 1
+            h = pair.ref[1][:128]
+            seen.add((int(h[8:12].view(np.uint32)[0]), int(h[120:124].view(np.uint32)[0]),
+                      int(h[100:104].view(np.uint32)[0])))
+            assert n < 6000
+        say(f"{n} one-unit turns")
+        # every phase, every attention stage and every sampling pass stopped in
+        assert {p for p, _, _ in seen} >= set(range(3, 20)), seen
+        assert {(9, sg) for sg in range(4)} <= {(p, sg) for p, sg, _ in seen}
+        assert {(19, ps) for ps in range(3)} <= {(p, ps) for p, _, ps in seen}
+        while not pair.complete():
+            units_pair_turn(pair, 997, blob)
+    finally:
+        pair.model.close()
+
+
+@pytest.mark.parametrize("row_kernel", [0, 2])
+def test_units_random_budgets(row_kernel):
+    # Random budgets over a batch of runs that start at every cursor of a
+    # position (between phases and inside them), grouped heads, temperature
+    # zero and above.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 58)
+    prompt = 4
+    cuts = phase_cuts(shape, prompt)[::2]
+    n = len(cuts)
+    temps = [65536 if r % 2 else 0 for r in range(n)]
+    runs = spec(shape, n, prompt, 4, seed=10, temps=temps)
+    pair = Pair(shape, blob, runs)
+    assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    rng = np.random.default_rng(20 + row_kernel)
+    try:
+        for i, (t, p, l) in enumerate(cuts):
+            st = pair.ref[i].copy()
+            cut_at(blob, st, t, p, l)
+            assert O.turn_units(blob, st, int(rng.integers(0, 60))) == 0
+            pair.load(i, st)
+        turns = 0
+        while not pair.complete():
+            turns += 1
+            assert turns < 400
+            units_pair_turn(pair, int(rng.choice([rng.integers(1, 50), rng.integers(1, 900),
+                                                  rng.integers(1, 5000)])), blob)
+        say(f"{turns} turns of units")
+    finally:
+        pair.model.close()
+
+
 def test_resume_cursor_checks():
     # Cursors no turn can leave in the state ("The resumable state") get
     # error 3, on the GPU as in the oracle; the run is left as it is.
