@@ -29,7 +29,8 @@ UINT64_MAX = (1 << 64) - 1
 EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_init_state",
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
            "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
-           "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph",
+           "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph", "fpi8_tokenize",
+           "fpi8_token_text",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -71,6 +72,10 @@ def lib():
             "fpi8_turn": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
             "fpi8_turn_phases": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint32, _P, _P]),
             "fpi8_turn_units": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, C.c_uint64, _P, _P]),
+            "fpi8_tokenize": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint32, C.c_uint32, _P,
+                                          C.c_uint32, C.POINTER(C.c_uint32)]),
+            "fpi8_token_text": (C.c_int32, [_P, C.c_uint64, C.c_uint32, C.c_uint32, _P,
+                                            C.c_uint32, C.POINTER(C.c_uint32)]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -195,6 +200,27 @@ def fpi8_turn_units(engine, d_states, state_stride: int, n_runs: int, max_units:
     e = lib().fpi8_turn_units(engine, _dev_ptr(d_states), state_stride, n_runs, max_units,
                               _stream_ptr(stream), _np_ptr(errs))
     return e, errs
+
+
+def fpi8_tokenize(section0: np.ndarray, prompt: bytes, max_tokens: int):
+    """(error, ids) of phases 0 to 2 for a prompt of bytes."""
+    s0 = np.ascontiguousarray(section0, dtype=np.uint8)
+    p = np.frombuffer(bytes(prompt), dtype=np.uint8).copy()
+    n = C.c_uint32(0)
+    ids = np.zeros(len(prompt) + 2, dtype=np.uint32)
+    e = lib().fpi8_tokenize(_np_ptr(s0), s0.size, _np_ptr(p) if p.size else None, p.size,
+                            max_tokens, _np_ptr(ids), ids.size, C.byref(n))
+    return e, (ids[: n.value].copy() if e == 0 else None)
+
+
+def fpi8_token_text(section0: np.ndarray, prev: int, token: int):
+    """(error, bytes) a generated token adds after prev."""
+    s0 = np.ascontiguousarray(section0, dtype=np.uint8)
+    out = np.zeros(128, dtype=np.uint8)
+    n = C.c_uint32(0)
+    e = lib().fpi8_token_text(_np_ptr(s0), s0.size, prev, token, _np_ptr(out), out.size,
+                              C.byref(n))
+    return e, (out[: n.value].tobytes() if e == 0 else None)
 
 
 def fpi8_engine_set_row_kernel(engine, kind: int) -> int:

@@ -154,6 +154,8 @@ int parse_section0(const uint8_t *s0, uint64_t s0_len, uint64_t blob_len, Model 
     if ((offs[i] & 7) != 0 || !fits(offs[i], sizes[i], zero_len)) return FPI8_INVALID_FORMAT;
   uint64_t tok = ld64(s0 + 88), tok_len = ld64(s0 + 96);
   if ((tok & 7) != 0 || !fits(tok, tok_len, zero_len)) return FPI8_INVALID_FORMAT;
+  Vocab v;
+  if (tok_len != 0 && !vocab_parse(s0 + tok, tok_len, c.vocab, &v)) return FPI8_INVALID_FORMAT;
   m->off_exp = offs[0]; m->off_silu = offs[1]; m->off_cos = offs[2]; m->off_sin = offs[3];
   m->off_norm = offs[4];
   if (ld32(s0 + offs[0]) == 0) return FPI8_INVALID_FORMAT;  // EXP[0] = 0: a zero sum is possible

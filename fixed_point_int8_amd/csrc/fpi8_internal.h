@@ -32,6 +32,21 @@ struct Model {
 
 int parse_section0(const uint8_t *s0, uint64_t s0_len, uint64_t blob_len, Model *m);
 
+// The tokenizer block of section zero (layout in fpi8_tokenizer.cpp).
+struct Vocab {
+  uint32_t n = 0, longest = 0;
+  const uint8_t *score = nullptr, *start = nullptr, *sorted = nullptr, *pool = nullptr;
+  uint32_t at(const uint8_t *p, uint32_t i) const {
+    uint32_t v;
+    __builtin_memcpy(&v, p + 4ull * i, 4);
+    return v;
+  }
+  const uint8_t *piece(uint32_t id) const { return pool + at(start, id); }
+  uint32_t piece_len(uint32_t id) const { return at(start, id + 1) - at(start, id); }
+};
+bool vocab_parse(const uint8_t *blk, uint64_t len, uint32_t vocab, Vocab *v);
+int64_t vocab_lookup(const Vocab &v, const uint8_t *s, uint32_t n);
+
 // Byte offsets of a run's buffers inside its state.
 struct StateLayout {
   uint64_t ids, out, x, w1, w2, w3, gate, up, logits, scores, keys, values, total;

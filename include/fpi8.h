@@ -77,6 +77,39 @@ typedef struct {
  * 4 attention output [dim][dim], 5 gate [hidden][dim], 6 up, 7 down
  * [dim][hidden], 8 classifier [vocab][dim].                                */
 
+/* ---- The tokenizer (host) --------------------------------------------------
+ * Section zero may hold a tokenizer block at the header's offset 88, of the
+ * length at 96 (0: none): u32 n (the vocabulary size, at least 259), u32 the
+ * longest token in bytes, u32 score[n] (the higher merges first), u32
+ * start[n + 1] (token i is pool[start[i], start[i + 1]), 1 to 128 bytes),
+ * u32 sorted_ids[n] (ids in increasing byte order of their strings, a prefix
+ * first, no string twice), then the pool.  Ids 0, 1, 2 are the unknown,
+ * opening and closing tokens and 3 + b the byte b, written <0xXX>.  A block
+ * that breaks these rules makes the artifact invalid (error 2). */
+
+/* Phases 0 to 2 ("The forward pass, in order"): the token ids of a prompt of
+ * prompt_len bytes (UTF-8, no zero byte, at most 1,024): token 1, then the
+ * token of a single space when the prompt has text; then each character (a
+ * lead byte and up to three continuation bytes) looked up whole, else one
+ * token per byte, id byte + 3; then, until no adjacent pair's joined string
+ * is a token, the pair whose token scores highest (the leftmost among
+ * equals) replaced by that token.  h_section0 is section zero of the
+ * artifact in host memory (or the whole artifact).  Writes *n_ids (also
+ * when ids is too small: error 4) and the ids.  Errors: 2 (no tokenizer or
+ * an invalid artifact), 6 (the prompt or max_tokens out of range), 7 (the
+ * ids and max_tokens do not fit the context), 4. */
+int32_t fpi8_tokenize(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *prompt,
+                      uint32_t prompt_len, uint32_t max_tokens, uint32_t *ids, uint32_t capacity,
+                      uint32_t *n_ids);
+
+/* The text a generated token adds after the token prev ("Sampling", last
+ * paragraph): its bytes, a leading space dropped right after the opening
+ * token, a byte token <0xXX> (two hexadecimal digits) written as that byte,
+ * and nothing for tokens 1 and 2.  Writes *len (also when out is too small:
+ * error 4).  Errors: 2, 6 (an id out of the vocabulary), 4. */
+int32_t fpi8_token_text(const uint8_t *h_section0, uint64_t section0_len, uint32_t prev,
+                        uint32_t token, uint8_t *out, uint32_t capacity, uint32_t *len);
+
 /* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
  * (may be NULL) receives the configuration. */
 int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);

@@ -491,6 +491,50 @@ static int in_range(uint64_t off, uint64_t size, uint64_t limit) {
   return off <= limit && size <= limit - off;
 }
 
+/* The tokenizer block of section zero, when the artifact has one (its
+ * layout is this artifact format's: u32 n, u32 longest, u32 score[n], u32
+ * start[n+1], u32 sorted_ids[n], pool): n is the vocabulary and holds the
+ * 3 special and 256 byte tokens, every token has 1 to 128 bytes inside the
+ * pool (a generated token's text has 128 bytes of output text), longest is
+ * the longest, and sorted_ids lists every id once in increasing byte order
+ * of the strings (a prefix first), so no two tokens share a string. */
+static int piece_cmp(const uint8_t *pool, const uint8_t *start, uint32_t a, uint32_t b) {
+  uint32_t a0 = rd32(start + 4ull * a), a1 = rd32(start + 4ull * a + 4);
+  uint32_t b0 = rd32(start + 4ull * b), b1 = rd32(start + 4ull * b + 4);
+  uint32_t la = a1 - a0, lb = b1 - b0;
+  for (uint32_t i = 0; i < la && i < lb; i++)
+    if (pool[a0 + i] != pool[b0 + i]) return pool[a0 + i] < pool[b0 + i] ? -1 : 1;
+  return la < lb ? -1 : la > lb ? 1 : 0;
+}
+
+static int tokenizer_ok(const uint8_t *t, uint64_t len, uint32_t vocab) {
+  if (len < 8) return 0;
+  uint32_t n = rd32(t), longest = rd32(t + 4);
+  if (n != vocab || n < 259) return 0;
+  uint64_t head = 8 + 12ull * n + 4;
+  if (head > len) return 0;
+  const uint8_t *start = t + 8 + 4ull * n, *sorted = start + 4ull * (n + 1), *pool = t + head;
+  uint32_t most = 0;
+  for (uint32_t i = 0; i < n; i++) {
+    uint32_t a = rd32(start + 4ull * i), b = rd32(start + 4ull * i + 4);
+    if (b <= a || b - a > 128 || b > len - head) return 0;
+    if (b - a > most) most = b - a;
+  }
+  if (rd32(start) != 0 && rd32(start) > len - head) return 0;
+  if (most != longest) return 0;
+  uint8_t *seen = (uint8_t *)calloc(n, 1);
+  if (!seen) return 0;
+  int ok = 1;
+  for (uint32_t k = 0; k < n && ok; k++) {
+    uint32_t id = rd32(sorted + 4ull * k);
+    if (id >= n || seen[id]) { ok = 0; break; }
+    seen[id] = 1;
+    if (k > 0 && piece_cmp(pool, start, rd32(sorted + 4ull * (k - 1)), id) >= 0) ok = 0;
+  }
+  free(seen);
+  return ok;
+}
+
 /* Parses and checks an artifact.  mats (if not NULL) receives the matrix
  * table: [0] embedding, [1 + 7*l + (kind-1)] layer matrices, [1 + 7L]
  * classifier. */
@@ -517,6 +561,7 @@ static int32_t parse(const uint8_t *blob, uint64_t len, model_t *m, mat_t *mats)
   for (int i = 0; i < 6; i++)
     if ((offs[i] & 7) || !in_range(offs[i], sizes[i], s0)) return FPI8_REF_INVALID_FORMAT;
   if ((o_tok & 7) || !in_range(o_tok, n_tok, s0)) return FPI8_REF_INVALID_FORMAT;
+  if (n_tok && !tokenizer_ok(blob + o_tok, n_tok, c->vocab)) return FPI8_REF_INVALID_FORMAT;
   m->exp_tab = (const uint32_t *)(blob + o_exp);
   m->silu_tab = (const int32_t *)(blob + o_silu);
   m->cos_tab = (const int32_t *)(blob + o_cos);

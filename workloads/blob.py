@@ -22,8 +22,8 @@ Header (section zero starts at offset 0)::
     80   u64       offset of the normalization weights, i32 Q24:
                    [layers][2][dim] (before attention, before the
                    feed-forward), then the final [dim]
-    88   u64       offset of the tokenizer block
-    96   u64       length of the tokenizer block (0 here: ids are fed in)
+    88   u64       offset of the tokenizer block (layout in workloads/vocab.py)
+    96   u64       length of the tokenizer block (0 for a vocabulary below 260)
     104  u64       offset of the matrix descriptors
     112  16 bytes  zero
     128  section table: S entries of {u64 offset, u64 length};
@@ -59,6 +59,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .configs import Shape
+from . import vocab as _vocab
 
 TAG = b"CURTAW01"
 SECTION_TABLE = 128
@@ -208,7 +209,7 @@ class BlobLayout:
     offsets: dict           # name -> offset inside section zero
 
 
-def plan(shape: Shape) -> BlobLayout:
+def plan(shape: Shape, tok_len: int | None = None) -> BlobLayout:
     n_mat = 2 + 7 * shape.layers
     n_sec = 1 + n_mat
     half = shape.head_size // 2
@@ -220,6 +221,7 @@ def plan(shape: Shape) -> BlobLayout:
     o = _a8(o); offs["sin"] = o; o += 4 * shape.context * half
     o = _a8(o); offs["norm"] = o; o += 4 * (2 * shape.layers + 1) * shape.dim
     o = _a8(o); offs["tok"] = o
+    o += _vocab.block_len(shape.vocab) if tok_len is None else tok_len
     o = _a8(o); offs["desc"] = o; o += DESCRIPTOR_BYTES * n_mat
     s0 = _a8(o)
     sections = [(0, s0)]
@@ -235,13 +237,15 @@ def plan(shape: Shape) -> BlobLayout:
 
 
 def build_blob(shape: Shape, seed: int, dist: str = "normal20",
-               tables: dict | None = None) -> np.ndarray:
+               tables: dict | None = None, tok: bytes | None = None) -> np.ndarray:
     """The whole artifact as one uint8 array.
 
     `tables` may override "exp", "silu", "cos", "sin", "norm" or "inv" (used
-    by tests that need special tables, for instance an identity table).
+    by tests that need special tables, for instance an identity table), and
+    `tok` the tokenizer block (bytes; empty for none).
     """
-    lay = plan(shape)
+    tok = _vocab.block_bytes(shape.vocab) if tok is None else bytes(tok)
+    lay = plan(shape, len(tok))
     blob = np.zeros(lay.total, dtype=np.uint8)
     hdr = blob[:SECTION_TABLE]
     hdr[:8] = np.frombuffer(TAG, dtype=np.uint8)
@@ -255,8 +259,8 @@ def build_blob(shape: Shape, seed: int, dist: str = "normal20",
     put(8, np.array(shape.as_tuple(), dtype=np.uint32))
     put(36, np.array([len(lay.sections), len(lay.matrices), inv], dtype=np.uint32))
     put(48, np.array([lay.offsets["exp"], lay.offsets["silu"], lay.offsets["cos"],
-                      lay.offsets["sin"], lay.offsets["norm"], lay.offsets["tok"], 0,
-                      lay.offsets["desc"]], dtype=np.uint64))
+                      lay.offsets["sin"], lay.offsets["norm"], lay.offsets["tok"],
+                      len(tok), lay.offsets["desc"]], dtype=np.uint64))
     put(SECTION_TABLE, np.array(lay.sections, dtype=np.uint64).reshape(-1))
 
     cos, sin = rope_tables(shape)
@@ -271,6 +275,8 @@ def build_blob(shape: Shape, seed: int, dist: str = "normal20",
         norm = np.rint((1.0 + 0.02 * g.standard_normal((2 * shape.layers + 1) * shape.dim))
                        * 2.0 ** 24).astype(np.int32)
     put(lay.offsets["norm"], norm)
+    if tok:
+        put(lay.offsets["tok"], np.frombuffer(tok, dtype=np.uint8))
 
     desc = np.zeros((len(lay.matrices), 8), dtype=np.uint32)
     for i, (kind, layer, rows, cols, sec, off) in enumerate(lay.matrices):
@@ -300,7 +306,7 @@ def section_zero(blob: np.ndarray) -> np.ndarray:
 
 def matrix_view(blob: np.ndarray, shape: Shape, kind: int, layer: int = 0):
     """(weights [rows][cols] uint8, scales [rows] uint32) views into a blob."""
-    lay = plan(shape)
+    lay = plan(shape, int(blob[96:104].view(np.uint64)[0]))
     for (k, l, rows, cols, sec, off) in lay.matrices:
         if k == kind and l == layer:
             base = lay.sections[sec][0] + off
