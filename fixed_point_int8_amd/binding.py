@@ -30,7 +30,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
            "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
            "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph", "fpi8_tokenize",
-           "fpi8_token_text",
+           "fpi8_token_text", "fpi8_output_text",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -76,6 +76,8 @@ def lib():
                                           C.c_uint32, C.POINTER(C.c_uint32)]),
             "fpi8_token_text": (C.c_int32, [_P, C.c_uint64, C.c_uint32, C.c_uint32, _P,
                                             C.c_uint32, C.POINTER(C.c_uint32)]),
+            "fpi8_output_text": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64,
+                                             C.POINTER(C.c_uint64)]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -220,6 +222,20 @@ def fpi8_token_text(section0: np.ndarray, prev: int, token: int):
     n = C.c_uint32(0)
     e = lib().fpi8_token_text(_np_ptr(s0), s0.size, prev, token, _np_ptr(out), out.size,
                               C.byref(n))
+    return e, (out[: n.value].tobytes() if e == 0 else None)
+
+
+def fpi8_output_text(section0: np.ndarray, state: np.ndarray):
+    """(error, bytes) of a host state's generated tokens."""
+    s0 = np.ascontiguousarray(section0, dtype=np.uint8)
+    n = C.c_uint64(0)
+    e = lib().fpi8_output_text(_np_ptr(s0), s0.size, _np_ptr(state), state.size, None, 0,
+                               C.byref(n))
+    if e not in (0, 4):
+        return e, None
+    out = np.zeros(max(n.value, 1), dtype=np.uint8)
+    e = lib().fpi8_output_text(_np_ptr(s0), s0.size, _np_ptr(state), state.size, _np_ptr(out),
+                               out.size, C.byref(n))
     return e, (out[: n.value].tobytes() if e == 0 else None)
 
 

@@ -207,4 +207,32 @@ int32_t fpi8_token_text(const uint8_t *h_section0, uint64_t section0_len, uint32
   return 0;
 }
 
+int32_t fpi8_output_text(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *state,
+                         uint64_t state_len, uint8_t *out, uint64_t capacity, uint64_t *len) {
+  uint32_t count = 0;
+  const uint32_t *toks = fpi8_output_tokens(state, state_len, &count);
+  if (!toks) return FPI8_INVALID_STATE;
+  fpi8_info info;
+  fpi8_state_info(state, state_len, &info);
+  if (info.n_ids == 0) return FPI8_INVALID_STATE;
+  // the first generated token follows the prompt's last id
+  uint32_t ids_last;
+  memcpy(&ids_last, state + ST_HEADER + 4ull * (info.n_ids - 1), 4);
+  uint64_t n = 0;
+  uint8_t piece[128];
+  uint32_t prev = ids_last;
+  for (uint32_t i = 0; i < count; i++) {
+    uint32_t tok;
+    memcpy(&tok, toks + i, 4);
+    uint32_t k = 0;
+    const int32_t e = fpi8_token_text(h_section0, section0_len, prev, tok, piece, sizeof piece, &k);
+    if (e) return e;
+    if (out && n + k <= capacity) memcpy(out + n, piece, k);
+    n += k;
+    prev = tok;
+  }
+  if (len) *len = n;
+  return n > capacity || (n > 0 && !out) ? FPI8_BUFFER_TOO_SMALL : 0;
+}
+
 }  // extern "C"

@@ -110,6 +110,13 @@ int32_t fpi8_tokenize(const uint8_t *h_section0, uint64_t section0_len, const ui
 int32_t fpi8_token_text(const uint8_t *h_section0, uint64_t section0_len, uint32_t prev,
                         uint32_t token, uint8_t *out, uint32_t capacity, uint32_t *len);
 
+/* The text of a state's generated tokens ("The Rust API", output_text): each
+ * token's text as fpi8_token_text gives it, the first one after the
+ * prompt's last id.  state is a host copy of a run's state.  Writes *len
+ * (also when out is too small: error 4).  Errors: 2, 3 (not a state), 6, 4. */
+int32_t fpi8_output_text(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *state,
+                         uint64_t state_len, uint8_t *out, uint64_t capacity, uint64_t *len);
+
 /* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
  * (may be NULL) receives the configuration. */
 int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);

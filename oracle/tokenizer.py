@@ -117,3 +117,12 @@ def token_text(v: Vocab, prev: int, token: int) -> bytes:
             and piece[3] in hexd and piece[4] in hexd):
         return bytes([int(piece[3:5].decode(), 16)])
     return piece
+
+
+def output_text(v: Vocab, prompt_ids, generated) -> bytes:
+    """The text of generated tokens, the first one after the prompt's last id."""
+    out, prev = [], int(prompt_ids[-1])
+    for t in generated:
+        out.append(token_text(v, prev, int(t)))
+        prev = int(t)
+    return b"".join(out)

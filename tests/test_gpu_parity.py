@@ -776,6 +776,30 @@ def test_units_random_budgets(row_kernel):
         pair.model.close()
 
 
+def test_text_prompt_end_to_end():
+    # Text in, text out: prompts tokenized by the library's host tokenizer,
+    # the pass on the GPU, the generated tokens' text read back from the
+    # device states; against the oracle's tokenizer, turns and text.
+    from oracle import tokenizer as T
+    from workloads import vocab as V
+    shape = W.SMALL_SHAPES["ragged"]
+    blob = Bl.build_blob(shape, 67)
+    s0 = Bl.section_zero(blob)
+    v = T.Vocab(s0)
+    runs = []
+    for r in range(6):
+        prompt = V.sample_text(5 + 3 * r, 80 + r)
+        e, ids = B.fpi8_tokenize(s0, prompt, 6)
+        assert e == 0 and list(ids) == T.encode(v, prompt, 6)[1]
+        runs.append((np.asarray(ids, np.uint32), 6, 0 if r % 2 else 65536, 90 + r))
+    say("text prompts end to end")
+    pair = run_pair(shape, blob, runs, [2, 3])
+    for i, (ids, mx, t, sd) in enumerate(runs):
+        g = pair.batch.state(i)
+        gen = B.fpi8_output_tokens(g)
+        assert B.fpi8_output_text(s0, g) == (0, T.output_text(v, ids, gen))
+
+
 def test_resume_cursor_checks():
     # Cursors no turn can leave in the state ("The resumable state") get
     # error 3, on the GPU as in the oracle; the run is left as it is.

@@ -163,3 +163,22 @@ def test_blob_check_rejects_bad_tokenizer_blocks():
     a, b = bytes(blk[o:o + 4]), bytes(blk[o + 4:o + 8])
     blk[o:o + 4], blk[o + 4:o + 8] = b, a
     check(bytes(blk))
+
+
+def test_output_text_matches_oracle():
+    # A text prompt through the whole pass on the CPU: the library's text of
+    # the generated tokens equals the oracle's.
+    shape = W.TINY.shape
+    blob = Bl.build_blob(shape, 66)
+    s0 = Bl.section_zero(blob)
+    v = T.Vocab(s0)
+    for temp, seed in ((0, 1), (65536, 2), (3 * 65536, 3)):
+        prompt = V.sample_text(12, 70 + seed)
+        e, ids = T.encode(v, prompt, 8)
+        assert e == 0
+        e, st = O.init_state(shape.as_tuple(), ids, 8, temp, seed)
+        assert e == 0 and O.run_to_end(blob, st) == 0
+        toks = O.state_info(st)[1]["generated"]
+        L = O.state_layout(shape.as_tuple(), len(ids), 8)
+        gen = st[L["out"]: L["out"] + 4 * toks].view(np.uint32)
+        assert B.fpi8_output_text(s0, st) == (0, T.output_text(v, ids, gen))
