@@ -330,6 +330,35 @@ def test_full_size_first_positions(name):
         O.set_threads(1)
 
 
+def test_full_size_units():
+    # Turns of unit budgets at the 1.1B shape and its batch width: the
+    # budgets stop runs inside matrices, attention stages and sampling
+    # passes at full size, and a sample of runs is checked against the
+    # oracle, state for state.
+    w = W.by_name("1.1B-shaped-d2048-L22")
+    shape = w.shape
+    say("full size units: artifact")
+    blob = Bl.build_blob(shape, w.blob_seed)
+    runs = [(W.prompt_ids(shape.vocab, 1 + (r % 2), w.ids_seed, r), 3, 65536 * (r % 2),
+             w.run_seed + r) for r in range(w.runs)]
+    sample = [0, 1, 5, w.runs - 1]
+    O.set_threads(16)
+    pair = Pair(shape, blob, runs)
+    try:
+        # about a third of a layer, a whole position and a few layers, into
+        # the classifier, into sampling
+        for k in (7_001, 300_000, 223_400, 30_000, 60_000, 100_000):
+            say(f"full size units: turn of {k}")
+            e, errs = pair.batch.turn_units(pair.model, k)
+            assert e == 0 and not any(errs), (e, errs)
+            for i in sample:
+                assert O.turn_units(blob, pair.ref[i], k) == 0
+            pair.compare(sample)
+    finally:
+        pair.model.close()
+        O.set_threads(1)
+
+
 def test_generic_head_size():
     shape = Shape(120, 200, 2, 6, 3, 300, 24)  # head 20: the generic attention path
     say("generic head size 20")
