@@ -30,7 +30,8 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_state_info", "fpi8_output_tokens", "fpi8_engine_create",
            "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
            "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph", "fpi8_tokenize",
-           "fpi8_token_text", "fpi8_output_text",
+           "fpi8_token_text", "fpi8_output_text", "fpi8_pages_state_size", "fpi8_state_export",
+           "fpi8_state_import",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -78,6 +79,10 @@ def lib():
                                             C.c_uint32, C.POINTER(C.c_uint32)]),
             "fpi8_output_text": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint64,
                                              C.POINTER(C.c_uint64)]),
+            "fpi8_pages_state_size": (C.c_uint64, [_P, C.c_uint32, C.c_uint32]),
+            "fpi8_state_export": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint32, _P,
+                                              C.c_uint64]),
+            "fpi8_state_import": (C.c_int32, [_P, _P, C.c_uint64, _P, C.c_uint64]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -237,6 +242,38 @@ def fpi8_output_text(section0: np.ndarray, state: np.ndarray):
     e = lib().fpi8_output_text(_np_ptr(s0), s0.size, _np_ptr(state), state.size, _np_ptr(out),
                                out.size, C.byref(n))
     return e, (out[: n.value].tobytes() if e == 0 else None)
+
+
+def fpi8_pages_state_size(cfg, prompt_bytes: int, max_tokens: int) -> int:
+    return lib().fpi8_pages_state_size(_np_ptr(_cfg(cfg)), prompt_bytes, max_tokens)
+
+
+def fpi8_state_export(section0: np.ndarray, state: np.ndarray, prompt: bytes, cfg):
+    """(error, bytes of the state in the page's format)."""
+    s0 = np.ascontiguousarray(section0, dtype=np.uint8)
+    info = fpi8_state_info(state)[1]
+    n = fpi8_pages_state_size(cfg, len(prompt), info["max_tokens"])
+    if n == UINT64_MAX:
+        return 6, None
+    out = np.zeros(n, dtype=np.uint8)
+    p = np.frombuffer(bytes(prompt), dtype=np.uint8).copy()
+    e = lib().fpi8_state_export(_np_ptr(s0), s0.size, _np_ptr(state), state.size,
+                                _np_ptr(p) if p.size else None, p.size, _np_ptr(out), out.size)
+    return e, (out if e == 0 else None)
+
+
+def fpi8_state_import(cfg, pages: np.ndarray):
+    """(error, state in this library's format, 8-byte aligned)."""
+    n_ids = int(pages[32:36].view(np.uint32)[0])
+    mx = int(pages[36:40].view(np.uint32)[0])
+    size = fpi8_state_size(cfg, n_ids, mx)
+    if size == UINT64_MAX:
+        return 3, None
+    raw = np.zeros(size + 64, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 64
+    st = raw[off: off + size]
+    e = lib().fpi8_state_import(_np_ptr(_cfg(cfg)), _np_ptr(pages), pages.size, _np_ptr(st), size)
+    return e, (st if e == 0 else None)
 
 
 def fpi8_engine_set_row_kernel(engine, kind: int) -> int:

@@ -19,7 +19,7 @@ static inline uint64_t ld64(const uint8_t *p) { uint64_t v; memcpy(&v, p, 8); re
 static inline void st32(uint8_t *p, uint32_t v) { memcpy(p, &v, 4); }
 static inline void st64(uint8_t *p, uint64_t v) { memcpy(p, &v, 8); }
 
-static const char kStateTag[8] = {'F', 'P', 'I', '8', 'S', 'T', '0', '1'};
+const char kStateTag[8] = {'F', 'P', 'I', '8', 'S', 'T', '0', '1'};
 
 // Ranges of the seven configuration values (the page states none): all at
 // least one, dim and hidden at most 65,536, layers at most 1,024, vocab at

@@ -55,6 +55,9 @@ struct StateLayout {
 bool state_layout(const Cfg &c, uint32_t n_ids, uint32_t max_tokens, StateLayout *L);
 int check_header(const Cfg &c, const uint8_t *h, uint64_t stride, StateLayout *L);
 
+// The state's tag, FPI8ST01.
+extern const char kStateTag[8];
+
 // State header field offsets.
 enum : uint32_t {
   ST_PHASE = 8, ST_LAYER = 12, ST_ROW = 16, ST_POSITION = 20, ST_TOKEN = 24, ST_ERROR = 28,

@@ -117,6 +117,37 @@ int32_t fpi8_token_text(const uint8_t *h_section0, uint64_t section0_len, uint32
 int32_t fpi8_output_text(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *state,
                          uint64_t state_len, uint8_t *out, uint64_t capacity, uint64_t *len);
 
+/* ---- The page's own state format (host) ------------------------------------
+ * "The resumable state" lays a run's state out as a header tagged CURTAST2
+ * and the buffers prompt bytes, prompt tokens (prompt bytes + 2), output
+ * tokens, output text (max tokens x 128), x and three working vectors, gate
+ * and up, logits, scores and the key and value caches, with cache positions
+ * min(prompt bytes + max tokens + 1, context).  Readings: its caches are
+ * [layer][position][kv head * head + element]; after tokenizing, its
+ * tokenizer's next byte is the prompt's length and the other tokenizer
+ * fields are zero. */
+
+/* The size of a state in the page's format (UINT64_MAX out of range; the
+ * page's run account adds a 256-byte header to it). */
+uint64_t fpi8_pages_state_size(const uint32_t cfg[7], uint32_t prompt_bytes, uint32_t max_tokens);
+
+/* Writes a host copy of a run's state in the page's format: the prompt's
+ * bytes (those its ids came from) and the generated tokens' text (the
+ * artifact's tokenizer, as fpi8_output_text) are added, the cache reordered
+ * and widened.  out_len must be fpi8_pages_state_size.  Errors: 2 (no
+ * tokenizer), 3 (not a state, or a frozen run: the page's state has no
+ * error field), 6 (prompt too long or fewer bytes than the ids need), 4. */
+int32_t fpi8_state_export(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *state,
+                          uint64_t state_len, const uint8_t *prompt, uint32_t prompt_len,
+                          uint8_t *out, uint64_t out_len);
+
+/* Reads a state in the page's format (after tokenizing: phase 3 to 20)
+ * into this library's format; state_len must be fpi8_state_size for the
+ * prompt-token count and max tokens in its header (offsets 32 and 36), and
+ * state 8-byte aligned.  Errors: 1, 3, 4. */
+int32_t fpi8_state_import(const uint32_t cfg[7], const uint8_t *pages, uint64_t pages_len,
+                          uint8_t *state, uint64_t state_len);
+
 /* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
  * (may be NULL) receives the configuration. */
 int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);

@@ -829,6 +829,37 @@ def test_text_prompt_end_to_end():
         assert B.fpi8_output_text(s0, g) == (0, T.output_text(v, ids, gen))
 
 
+def test_page_format_round_trip_on_the_gpu():
+    # Runs stopped by unit budgets on the GPU, written out in the page's
+    # state format and read back (host), then continued on the GPU: every
+    # word as the oracle's uninterrupted runs have it.
+    from oracle import tokenizer as T
+    shape = W.SMALL_SHAPES["ragged"]
+    blob = Bl.build_blob(shape, 68)
+    s0 = Bl.section_zero(blob)
+    cfg = shape.as_tuple()
+    prompt = b"Once upon a time"
+    e, ids = T.encode(T.Vocab(s0), prompt, 5)
+    assert e == 0
+    runs = [(np.asarray(ids, np.uint32), 5, 65536 * (r % 2), 100 + r) for r in range(4)]
+    pair = Pair(shape, blob, runs)
+    try:
+        for k in (9_001, 2_500, 17_777):
+            units_pair_turn(pair, k, blob)
+            for i in range(len(runs)):
+                g = pair.batch.state(i)
+                e, pg = B.fpi8_state_export(s0, g, prompt, cfg)
+                assert e == 0
+                e, back = B.fpi8_state_import(cfg, pg)
+                assert e == 0 and np.array_equal(back, g)
+                pair.load(i, back)
+        while not pair.complete():
+            pair.turn(1 << 20)
+        pair.compare()
+    finally:
+        pair.model.close()
+
+
 def test_resume_cursor_checks():
     # Cursors no turn can leave in the state ("The resumable state") get
     # error 3, on the GPU as in the oracle; the run is left as it is.
