@@ -106,6 +106,27 @@ int vocab_of(const uint8_t *s0, uint64_t s0_len, Model *m, Vocab *v) {
   return 0;
 }
 
+// The text token adds after prev into out (at most 128 bytes); its length.
+uint32_t piece_text(const Vocab &v, uint32_t prev, uint32_t token, uint8_t *out) {
+  const uint8_t *p = v.piece(token);
+  uint32_t n = v.piece_len(token);
+  if (token == 1 || token == 2) return 0;              // no text
+  if (n > 0 && prev == 1 && p[0] == ' ') { p++; n--; }  // after the opening token
+  auto hex = [](uint8_t c, uint8_t *d) {
+    if (c >= '0' && c <= '9') { *d = c - '0'; return true; }
+    if (c >= 'A' && c <= 'F') { *d = c - 'A' + 10; return true; }
+    if (c >= 'a' && c <= 'f') { *d = c - 'a' + 10; return true; }
+    return false;
+  };
+  uint8_t hi, lo;
+  if (n == 6 && memcmp(p, "<0x", 3) == 0 && p[5] == '>' && hex(p[3], &hi) && hex(p[4], &lo)) {
+    out[0] = (uint8_t)(hi * 16 + lo);  // a byte token: that one byte
+    return 1;
+  }
+  memcpy(out, p, n);
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,31 +205,20 @@ int32_t fpi8_token_text(const uint8_t *h_section0, uint64_t section0_len, uint32
   int e = vocab_of(h_section0, section0_len, &m, &v);
   if (e) return e;
   if (token >= v.n || prev >= v.n) return FPI8_INVALID_PROMPT;
-  const uint8_t *p = v.piece(token);
-  uint32_t n = v.piece_len(token);
-  if (token == 1 || token == 2) n = 0;  // no text
-  if (n > 0 && prev == 1 && p[0] == ' ') { p++; n--; }  // after the opening token
-  uint8_t byte;
-  auto hex = [](uint8_t c, uint8_t *d) {
-    if (c >= '0' && c <= '9') { *d = c - '0'; return true; }
-    if (c >= 'A' && c <= 'F') { *d = c - 'A' + 10; return true; }
-    if (c >= 'a' && c <= 'f') { *d = c - 'a' + 10; return true; }
-    return false;
-  };
-  uint8_t hi, lo;
-  if (n == 6 && memcmp(p, "<0x", 3) == 0 && p[5] == '>' && hex(p[3], &hi) && hex(p[4], &lo)) {
-    byte = (uint8_t)(hi * 16 + lo);  // a byte token: that one byte
-    p = &byte;
-    n = 1;
-  }
+  uint8_t piece[128];
+  const uint32_t n = piece_text(v, prev, token, piece);
   if (len) *len = n;
   if (n > 0 && (!out || capacity < n)) return FPI8_BUFFER_TOO_SMALL;
-  if (n > 0) memcpy(out, p, n);
+  if (n > 0) memcpy(out, piece, n);
   return 0;
 }
 
 int32_t fpi8_output_text(const uint8_t *h_section0, uint64_t section0_len, const uint8_t *state,
                          uint64_t state_len, uint8_t *out, uint64_t capacity, uint64_t *len) {
+  Model m;
+  Vocab v;
+  int32_t e = vocab_of(h_section0, section0_len, &m, &v);
+  if (e) return e;
   uint32_t count = 0;
   const uint32_t *toks = fpi8_output_tokens(state, state_len, &count);
   if (!toks) return FPI8_INVALID_STATE;
@@ -224,9 +234,8 @@ int32_t fpi8_output_text(const uint8_t *h_section0, uint64_t section0_len, const
   for (uint32_t i = 0; i < count; i++) {
     uint32_t tok;
     memcpy(&tok, toks + i, 4);
-    uint32_t k = 0;
-    const int32_t e = fpi8_token_text(h_section0, section0_len, prev, tok, piece, sizeof piece, &k);
-    if (e) return e;
+    if (tok >= v.n || prev >= v.n) return FPI8_INVALID_PROMPT;
+    const uint32_t k = piece_text(v, prev, tok, piece);
     if (out && n + k <= capacity) memcpy(out + n, piece, k);
     n += k;
     prev = tok;
