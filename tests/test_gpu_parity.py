@@ -773,8 +773,8 @@ def test_units_one_at_a_time():
         pair.model.close()
 
 
-@pytest.mark.parametrize("row_kernel", [0, 2])
-def test_units_random_budgets(row_kernel):
+@pytest.mark.parametrize("row_kernel,streams", [(0, 0), (2, 0), (0, 2)])
+def test_units_random_budgets(row_kernel, streams):
     # Random budgets over a batch of runs that start at every cursor of a
     # position (between phases and inside them), grouped heads, temperature
     # zero and above.
@@ -787,6 +787,7 @@ def test_units_random_budgets(row_kernel):
     runs = spec(shape, n, prompt, 4, seed=10, temps=temps)
     pair = Pair(shape, blob, runs)
     assert B.fpi8_engine_set_row_kernel(pair.model.engine, row_kernel) == 0
+    assert B.fpi8_engine_set_streams(pair.model.engine, streams) == 0
     rng = np.random.default_rng(20 + row_kernel)
     try:
         for i, (t, p, l) in enumerate(cuts):
