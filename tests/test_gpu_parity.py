@@ -861,6 +861,35 @@ def test_page_format_round_trip_on_the_gpu():
         pair.model.close()
 
 
+def test_units_budget_edges():
+    # A budget of 0 changes nothing but the turn count; a budget past the
+    # end completes a run as a turn of positions does; a complete run is
+    # left as it is; a broken state gets error 3 beside runs that go on.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 69)
+    runs = spec(shape, 3, 3, 3, seed=11, temps=[0, 65536, 0])
+    pair = Pair(shape, blob, runs)
+    try:
+        before = [pair.batch.state(i) for i in range(3)]
+        units_pair_turn(pair, 0, blob)
+        for i in range(3):
+            g = pair.batch.state(i)
+            assert np.array_equal(g[88:], before[i][88:]) and np.array_equal(g[:80], before[i][:80])
+        units_pair_turn(pair, 700, blob)
+        pair.batch.d_states[2 * pair.batch.stride] = 0          # break run 2's tag
+        e, errs = pair.batch.turn_units(pair.model, (1 << 64) - 1)
+        assert list(errs) == [0, 0, 3]
+        for i in (0, 1):
+            assert O.turn_units(blob, pair.ref[i], (1 << 64) - 2) == 0
+            assert O.state_info(pair.ref[i])[1]["complete"]
+        pair.compare(runs=[0, 1])
+        done = pair.batch.state(0)
+        e, errs = pair.batch.turn_units(pair.model, 5)
+        assert errs[0] == 0 and np.array_equal(done, pair.batch.state(0))
+    finally:
+        pair.model.close()
+
+
 def test_resume_cursor_checks():
     # Cursors no turn can leave in the state ("The resumable state") get
     # error 3, on the GPU as in the oracle; the run is left as it is.
