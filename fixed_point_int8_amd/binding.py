@@ -31,7 +31,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
            "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph", "fpi8_tokenize",
            "fpi8_token_text", "fpi8_output_text", "fpi8_pages_state_size", "fpi8_state_export",
-           "fpi8_state_import",
+           "fpi8_state_import", "fpi8_pages_init", "fpi8_pages_tokenize",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -83,6 +83,9 @@ def lib():
             "fpi8_state_export": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, _P, C.c_uint32, _P,
                                               C.c_uint64]),
             "fpi8_state_import": (C.c_int32, [_P, _P, C.c_uint64, _P, C.c_uint64]),
+            "fpi8_pages_init": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, C.c_uint32,
+                                            C.c_uint64, _P, C.c_uint64]),
+            "fpi8_pages_tokenize": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint64, _P]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -274,6 +277,25 @@ def fpi8_state_import(cfg, pages: np.ndarray):
     st = raw[off: off + size]
     e = lib().fpi8_state_import(_np_ptr(_cfg(cfg)), _np_ptr(pages), pages.size, _np_ptr(st), size)
     return e, (st if e == 0 else None)
+
+
+def fpi8_pages_init(cfg, prompt: bytes, max_tokens: int, temperature_q16: int = 0, seed: int = 0):
+    """(error, a fresh state in the page's format, before tokenizing)."""
+    n = fpi8_pages_state_size(cfg, len(prompt), max_tokens)
+    out = np.zeros(0 if n == UINT64_MAX else n, dtype=np.uint8)
+    buf = C.create_string_buffer(bytes(prompt), max(len(prompt), 1))
+    e = lib().fpi8_pages_init(_np_ptr(_cfg(cfg)), buf, len(prompt), max_tokens, temperature_q16,
+                              C.c_uint64(seed), _np_ptr(out), out.size)
+    return e, (out if e == 0 else None)
+
+
+def fpi8_pages_tokenize(section0: np.ndarray, pages: np.ndarray, max_units: int):
+    """Runs up to max_units units of phases 0 to 2 in place: (error, units run)."""
+    s0 = np.ascontiguousarray(section0, dtype=np.uint8)
+    done = C.c_uint64(0)
+    e = lib().fpi8_pages_tokenize(_np_ptr(s0), s0.size, _np_ptr(pages), pages.size,
+                                  C.c_uint64(max_units), C.byref(done))
+    return e, done.value
 
 
 def fpi8_engine_set_row_kernel(engine, kind: int) -> int:

@@ -46,6 +46,7 @@ struct Vocab {
 };
 bool vocab_parse(const uint8_t *blk, uint64_t len, uint32_t vocab, Vocab *v);
 int64_t vocab_lookup(const Vocab &v, const uint8_t *s, uint32_t n);
+int32_t vocab_of(const uint8_t *s0, uint64_t s0_len, Model *m, Vocab *v);
 
 // Byte offsets of a run's buffers inside its state.
 struct StateLayout {

@@ -17,6 +17,16 @@
 // the tokenizer's next byte is the prompt's length and its other fields are
 // zero; the page's state has no error field, so a frozen run has no page
 // form.
+//
+// A state in the page's format can also start before tokenizing
+// (fpi8_pages_init) and run phases 0 to 2 in units (fpi8_pages_tokenize),
+// with the header's five tokenizer fields as the cursor.  Readings: a unit
+// is phase 0 whole; one character of phase 1, or the step that ends it;
+// one pair looked up in a merge scan, or the scan's end, which applies the
+// best merge found or, with none, checks the context and moves to phase 3.
+// The fields hold the next prompt byte, the pair being looked up, and the
+// position (0xFFFFFFFF before any), score key and id of the scan's best
+// merge; a higher score replaces it, so the leftmost of equals merges.
 #include <stdint.h>
 #include <string.h>
 
@@ -79,9 +89,156 @@ void copy_cache(const Cfg &c, const uint8_t *src, uint32_t src_cp, bool src_page
       }
 }
 
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+
+// Header words of the page's state used here.
+enum : uint32_t {
+  PG_PHASE = 8, PG_POSITION = 20, PG_TOKEN = 24, PG_PROMPT = 28, PG_NIDS = 32, PG_MAX = 36,
+  PG_TEMP = 40, PG_NEXT_BYTE = 52, PG_PAIR = 56, PG_BEST_AT = 60, PG_BEST_SCORE = 64,
+  PG_BEST_ID = 68, PG_SEED = 72
+};
+
 }  // namespace
 
 extern "C" {
+
+int32_t fpi8_pages_init(const uint32_t cfg[7], const uint8_t *prompt, uint32_t prompt_len,
+                        uint32_t max_tokens, uint32_t temperature_q16, uint64_t seed, uint8_t *out,
+                        uint64_t out_len) {
+  Cfg c;
+  PagesLayout P;
+  if (!cfg || !cfg_from_words(cfg, &c)) return FPI8_INVALID_CONFIG;
+  if ((prompt_len > 0 && !prompt) || !pages_layout(c, prompt_len, max_tokens, &P) ||
+      temperature_q16 > (16u << 16))
+    return FPI8_INVALID_PROMPT;
+  for (uint32_t i = 0; i < prompt_len; i++)
+    if (prompt[i] == 0) return FPI8_INVALID_PROMPT;
+  if (!out || out_len != P.total) return FPI8_BUFFER_TOO_SMALL;
+  memset(out, 0, out_len);
+  memcpy(out, kPagesTag, 8);
+  wr32(out + PG_PROMPT, prompt_len);
+  wr32(out + PG_MAX, max_tokens);
+  wr32(out + PG_TEMP, temperature_q16);
+  // a zero seed starts the generator at 0x9E3779B97F4A7C15 ("Sampling")
+  const uint64_t g = seed ? seed : 0x9E3779B97F4A7C15ull;
+  memcpy(out + PG_SEED, &g, 8);
+  if (prompt_len) memcpy(out + P.prompt, prompt, prompt_len);
+  return 0;
+}
+
+int32_t fpi8_pages_tokenize(const uint8_t *h_section0, uint64_t section0_len, uint8_t *pages,
+                            uint64_t pages_len, uint64_t max_units, uint64_t *units_done) {
+  if (units_done) *units_done = 0;
+  Model m;
+  Vocab v;
+  int32_t e = vocab_of(h_section0, section0_len, &m, &v);
+  if (e) return e;
+  const Cfg &c = m.cfg;
+  if (!pages || pages_len < ST_HEADER || memcmp(pages, kPagesTag, 8) != 0) return FPI8_INVALID_STATE;
+  const uint32_t pb = rd32(pages + PG_PROMPT), mx = rd32(pages + PG_MAX);
+  PagesLayout P;
+  if (!pages_layout(c, pb, mx, &P) || P.total != pages_len) return FPI8_INVALID_STATE;
+  const uint8_t *prompt = pages + P.prompt;
+  uint8_t *ids = pages + P.ids;  // u32[prompt bytes + 2], unaligned-safe access
+  auto id_at = [&](uint32_t i) { return rd32(ids + 4ull * i); };
+  auto set_id = [&](uint32_t i, uint32_t t) { wr32(ids + 4ull * i, t); };
+  // the cursor must lie where phases 0 to 2 can leave it
+  uint32_t phase = rd32(pages + PG_PHASE), n = rd32(pages + PG_NIDS);
+  if (phase > 2) return FPI8_INVALID_STATE;
+  const uint32_t cap = pb + 2;
+  if (phase > 0 && (n < 1 || n > cap)) return FPI8_INVALID_STATE;
+  if (phase == 1 && rd32(pages + PG_NEXT_BYTE) > pb) return FPI8_INVALID_STATE;
+  if (phase == 2) {
+    const uint32_t at = rd32(pages + PG_BEST_AT);
+    if (rd32(pages + PG_PAIR) >= n || (at != kNone && at + 1 >= n) ||
+        (at != kNone && rd32(pages + PG_BEST_ID) >= v.n))
+      return FPI8_INVALID_STATE;
+  }
+  for (uint32_t i = 0; phase > 0 && i < n; i++)
+    if (id_at(i) >= v.n) return FPI8_INVALID_STATE;
+  uint8_t joined[256];
+  uint64_t done = 0;
+  e = 0;
+  while (done < max_units) {
+    if (phase == 0) {
+      // the opening token, then a single space's token when there is text
+      set_id(0, 1);
+      n = 1;
+      if (pb > 0) {
+        const uint8_t space = ' ';
+        const int64_t s = vocab_lookup(v, &space, 1);
+        set_id(n++, s >= 0 ? (uint32_t)s : space + 3u);
+      }
+      wr32(pages + PG_NIDS, n);
+      wr32(pages + PG_NEXT_BYTE, 0);
+      phase = 1;
+    } else if (phase == 1) {
+      const uint32_t i = rd32(pages + PG_NEXT_BYTE);
+      if (i >= pb) {
+        phase = 2;
+        wr32(pages + PG_PAIR, 0);
+        wr32(pages + PG_BEST_AT, kNone);
+        wr32(pages + PG_BEST_SCORE, 0);
+        wr32(pages + PG_BEST_ID, 0);
+      } else {
+        // one UTF-8 character: a lead byte and up to three continuation bytes
+        uint32_t j = i + 1;
+        while (j < pb && j - i < 4 && (prompt[j] & 0xC0) == 0x80) j++;
+        const int64_t t = vocab_lookup(v, prompt + i, j - i);
+        if (t >= 0) {
+          set_id(n++, (uint32_t)t);
+        } else {
+          for (uint32_t k = i; k < j; k++) set_id(n++, prompt[k] + 3u);
+        }
+        wr32(pages + PG_NIDS, n);
+        wr32(pages + PG_NEXT_BYTE, j);
+      }
+    } else {
+      const uint32_t k = rd32(pages + PG_PAIR);
+      if (k + 1 < n) {
+        // one pair of the scan
+        const uint32_t a = id_at(k), b = id_at(k + 1);
+        const uint32_t na = v.piece_len(a), nb = v.piece_len(b);
+        memcpy(joined, v.piece(a), na);
+        memcpy(joined + na, v.piece(b), nb);
+        const int64_t t = vocab_lookup(v, joined, na + nb);
+        if (t >= 0) {
+          const uint32_t sc = v.at(v.score, (uint32_t)t);
+          if (rd32(pages + PG_BEST_AT) == kNone || sc > rd32(pages + PG_BEST_SCORE)) {
+            wr32(pages + PG_BEST_AT, k);
+            wr32(pages + PG_BEST_SCORE, sc);
+            wr32(pages + PG_BEST_ID, (uint32_t)t);
+          }
+        }
+        wr32(pages + PG_PAIR, k + 1);
+      } else if (rd32(pages + PG_BEST_AT) != kNone) {
+        // the scan's end: its best pair becomes one token
+        const uint32_t at = rd32(pages + PG_BEST_AT);
+        set_id(at, rd32(pages + PG_BEST_ID));
+        memmove(ids + 4ull * (at + 1), ids + 4ull * (at + 2), 4ull * (n - at - 2));
+        set_id(n - 1, 0);
+        wr32(pages + PG_NIDS, --n);
+        wr32(pages + PG_PAIR, 0);
+        wr32(pages + PG_BEST_AT, kNone);
+        wr32(pages + PG_BEST_SCORE, 0);
+        wr32(pages + PG_BEST_ID, 0);
+      } else {
+        // no pair merges: the prompt's tokens and max tokens must fit
+        if ((uint64_t)n + mx - 1 > c.context) { e = FPI8_CONTEXT_EXCEEDED; break; }
+        wr32(pages + PG_PAIR, 0);
+        wr32(pages + PG_BEST_AT, 0);
+        wr32(pages + PG_POSITION, 0);
+        wr32(pages + PG_TOKEN, id_at(0));
+        phase = 3;
+      }
+    }
+    wr32(pages + PG_PHASE, phase);
+    done++;
+    if (phase == 3) break;
+  }
+  if (units_done) *units_done = done;
+  return e;
+}
 
 uint64_t fpi8_pages_state_size(const uint32_t cfg[7], uint32_t prompt_bytes, uint32_t max_tokens) {
   Cfg c;

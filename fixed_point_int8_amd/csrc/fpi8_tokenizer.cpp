@@ -90,13 +90,8 @@ int64_t vocab_lookup(const Vocab &v, const uint8_t *s, uint32_t n) {
   return -1;
 }
 
-}  // namespace fpi8
-
-using namespace fpi8;
-
-namespace {
-
-int vocab_of(const uint8_t *s0, uint64_t s0_len, Model *m, Vocab *v) {
+// Section zero's configuration and its tokenizer block, checked: 0 or 2.
+int32_t vocab_of(const uint8_t *s0, uint64_t s0_len, Model *m, Vocab *v) {
   if (!s0) return FPI8_INVALID_FORMAT;
   int e = parse_section0(s0, s0_len, UINT64_MAX, m);  // section zero alone
   if (e) return e;
@@ -105,6 +100,12 @@ int vocab_of(const uint8_t *s0, uint64_t s0_len, Model *m, Vocab *v) {
   if (len == 0 || !vocab_parse(s0 + tok, len, m->cfg.vocab, v)) return FPI8_INVALID_FORMAT;
   return 0;
 }
+
+}  // namespace fpi8
+
+using namespace fpi8;
+
+namespace {
 
 // The text token adds after prev into out (at most 128 bytes); its length.
 uint32_t piece_text(const Vocab &v, uint32_t prev, uint32_t token, uint8_t *out) {

@@ -148,6 +148,30 @@ int32_t fpi8_state_export(const uint8_t *h_section0, uint64_t section0_len, cons
 int32_t fpi8_state_import(const uint32_t cfg[7], const uint8_t *pages, uint64_t pages_len,
                           uint8_t *state, uint64_t state_len);
 
+/* Writes a fresh state in the page's format before tokenizing (phase 0;
+ * "The Rust API", init_state): the prompt's bytes, max tokens, the
+ * temperature and the seed (zero becomes 0x9E3779B97F4A7C15) in a host
+ * buffer of exactly fpi8_pages_state_size bytes.  The prompt has at most
+ * 1,024 bytes and no zero byte; max tokens lies in 1 to the context; the
+ * temperature is at most 16 (Q16).  Errors 1, 6, 4 in that order. */
+int32_t fpi8_pages_init(const uint32_t cfg[7], const uint8_t *prompt, uint32_t prompt_len,
+                        uint32_t max_tokens, uint32_t temperature_q16, uint64_t seed, uint8_t *out,
+                        uint64_t out_len);
+
+/* Runs up to max_units units of phases 0 to 2 ("The forward pass, in
+ * order") on a host state in the page's format, in place, with the
+ * header's tokenizer fields (offsets 52 to 68) as the cursor, so it can
+ * stop after any unit and go on in a later call.  A unit is phase 0; one
+ * prompt character, or the step that ends phase 1; one pair looked up in a
+ * merge scan, or the scan's end (apply its best merge, or check the context
+ * and move to phase 3 at position 0).  It stops at phase 3; the state then
+ * goes to fpi8_state_import.  *units_done (may be NULL) receives the units
+ * run.  Errors: 2 (no tokenizer), 3 (not a page state, past tokenizing, or
+ * a cursor out of range), 7 (the prompt's tokens and max tokens, less one,
+ * exceed the context: the state is left at the scan's end). */
+int32_t fpi8_pages_tokenize(const uint8_t *h_section0, uint64_t section0_len, uint8_t *pages,
+                            uint64_t pages_len, uint64_t max_units, uint64_t *units_done);
+
 /* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
  * (may be NULL) receives the configuration. */
 int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);

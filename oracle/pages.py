@@ -113,3 +113,98 @@ def import_(cfg, pages: np.ndarray) -> np.ndarray:
         mine = st[S[name]: S[name] + 4 * layers * kv_heads * cs * hd].view(np.int32)
         mine.reshape(layers, kv_heads, cs, hd)[:] = theirs[:, :cs].transpose(0, 2, 1, 3)
     return st
+
+
+# ---------------------------------------------------------------------------
+# Phases 0 to 2 in the page's state, resumable ("The forward pass, in order",
+# phases 0-2, with the header's tokenizer fields of "The resumable state").
+#
+# Readings (the library takes the same): a unit of tokenizing is phase 0
+# whole; one character of phase 1, or the step that ends phase 1; one pair
+# looked up in a merge scan, or the end of a scan, which applies the best
+# merge or, when there is none, checks the context and ends phase 2.  The
+# fields at 52-68 hold the next prompt byte (phase 1), the pair being looked
+# up, the position, score key and token id of the best merge found in this
+# scan (position 0xFFFFFFFF for none).  A prompt that does not fit is error
+# 7 at the end of phase 2, the state left as it stood.
+
+NONE = 0xFFFFFFFF
+
+
+def init(cfg, prompt: bytes, max_tokens: int, temperature_q16: int, seed: int):
+    """(error, a fresh state in the page's format at phase 0)."""
+    context = cfg[6]
+    if len(prompt) > 1024 or 0 in prompt or not 1 <= max_tokens <= context or \
+            temperature_q16 > 16 * 65536:
+        return 6, None
+    P = layout(cfg, len(prompt), max_tokens)
+    st = np.zeros(P["total"], dtype=np.uint8)
+    hdr = bytearray(128)
+    hdr[0:8] = TAG
+    struct.pack_into("<I", hdr, 28, len(prompt))
+    struct.pack_into("<I", hdr, 36, max_tokens)
+    struct.pack_into("<I", hdr, 40, temperature_q16)
+    struct.pack_into("<Q", hdr, 72, seed if seed else 0x9E3779B97F4A7C15)
+    st[:128] = np.frombuffer(bytes(hdr), np.uint8)
+    st[P["prompt"]: P["prompt"] + len(prompt)] = np.frombuffer(prompt, np.uint8)
+    return 0, st
+
+
+def tokenize_units(section0, cfg, st: np.ndarray, budget: int) -> int:
+    """Runs up to `budget` units of phases 0-2; 0, or 7 (no fit), 3 (past them)."""
+    v = T.Vocab(section0)
+    pb, mx = _u32(st, 28), _u32(st, 36)
+    P = layout(cfg, pb, mx)
+    prompt = bytes(st[P["prompt"]: P["prompt"] + pb])
+    ids = st[P["ids"]: P["ids"] + 4 * (pb + 2)].view(np.uint32)
+
+    def get(off):
+        return _u32(st, off)
+
+    def put(off, val):
+        st[off: off + 4] = np.frombuffer(struct.pack("<I", val), np.uint8)
+    if get(8) > 2:
+        return 3
+    while budget > 0:
+        budget -= 1
+        phase, n = get(8), get(32)
+        if phase == 0:
+            ids[0] = 1
+            n = 1
+            if pb:
+                sp = v.lookup(b" ")
+                ids[1] = sp if sp >= 0 else ord(" ") + 3
+                n = 2
+            put(32, n); put(8, 1); put(52, 0)
+        elif phase == 1:
+            i = get(52)
+            if i >= pb:
+                put(8, 2); put(56, 0); put(60, NONE); put(64, 0); put(68, 0)
+                continue
+            ch = T.characters(prompt[i:])[0]
+            t = v.lookup(ch)
+            for tok in ([t] if t >= 0 else [b + 3 for b in ch]):
+                ids[n] = tok
+                n += 1
+            put(32, n); put(52, i + len(ch))
+        else:
+            k = get(56)
+            if k + 1 < n:
+                t = v.lookup(v.pieces[ids[k]] + v.pieces[ids[k + 1]])
+                if t >= 0 and (get(60) == NONE or v.score[t] > get(64)):
+                    put(60, k); put(64, v.score[t]); put(68, t)
+                put(56, k + 1)
+                continue
+            best = get(60)
+            if best != NONE:
+                ids[best] = get(68)
+                ids[best + 1: n - 1] = ids[best + 2: n].copy()
+                ids[n - 1] = 0
+                put(32, n - 1); put(56, 0); put(60, NONE); put(64, 0); put(68, 0)
+                continue
+            if n + mx - 1 > cfg[6]:
+                return 7
+            put(56, 0); put(60, 0)
+            put(8, 3); put(20, 0); put(24, int(ids[0]))
+            return 0
+    return 0

@@ -15,6 +15,7 @@ import workloads as W
 from workloads import blob as Bl
 from fixed_point_int8_amd import binding as B
 from conftest import read_table
+from workloads import vocab as V
 
 PROMPT = b"Once upon a time"
 
@@ -120,3 +121,126 @@ def test_export_errors():
     pg2 = pg.copy()
     pg2[0] = ord("X")
     assert B.fpi8_state_import(cfg, pg2)[0] == 3
+
+
+# ---- Tokenizing inside the page's state (phases 0 to 2, resumable) --------
+
+def _tok_shape(vocab=2048, context=2048):
+    return W.Shape(64, 96, 1, 4, 4, vocab, context)
+
+
+def _scan_units(v, prompt, ids_after):
+    """Units the reading gives: phase 0, each character, the end of phase 1,
+    and for each scan over t tokens its t - 1 pairs and its end."""
+    n0 = 1 + (1 if prompt else 0) + sum(1 if v.lookup(ch) >= 0 else len(ch)
+                                        for ch in T.characters(prompt))
+    return 1 + len(T.characters(prompt)) + 1 + sum(range(len(ids_after), n0 + 1))
+
+
+def test_oracle_resumable_tokenizing_matches_one_shot():
+    # Cut anywhere, the page-state tokenizer ends with the one-shot ids
+    # (themselves pinned by the hand-worked example), in the number of units
+    # the unit reading gives, with the cursor fields cleared as after export.
+    shape = _tok_shape()
+    cfg = shape.as_tuple()
+    s0 = Bl.section_zero(Bl.build_blob(shape, 75))
+    v = T.Vocab(s0)
+    rng = np.random.default_rng(3)
+    for trial in range(30):
+        prompt = V.sample_text(int(rng.integers(0, 80)), 500 + trial)
+        e, want = T.encode(v, prompt, 5)
+        assert e == 0
+        e, st = OP.init(cfg, prompt, 5, 0, 7)
+        assert e == 0
+        units = 0
+        while OP._u32(st, 8) < 3:
+            b = int(rng.integers(1, 9))
+            before = st.copy()
+            assert OP.tokenize_units(s0, cfg, st, b) == 0
+            units += b if OP._u32(st, 8) < 3 else 0
+            assert not np.array_equal(before, st)
+        n = OP._u32(st, 32)
+        P = OP.layout(cfg, len(prompt), 5)
+        assert list(st[P["ids"]: P["ids"] + 4 * n].view(np.uint32)) == want
+        assert [OP._u32(st, o) for o in (20, 24, 52, 56, 60, 64, 68)] == \
+            [0, 1, len(prompt), 0, 0, 0, 0]
+        # one unit at a time counts them
+        e, st1 = OP.init(cfg, prompt, 5, 0, 7)
+        k = 0
+        while OP._u32(st1, 8) < 3:
+            assert OP.tokenize_units(s0, cfg, st1, 1) == 0
+            k += 1
+        assert k == _scan_units(v, prompt, want)
+        assert np.array_equal(st1, st)
+
+
+def test_library_tokenizing_matches_oracle_at_every_cut():
+    # The library's page-state tokenizer against the oracle's, byte for
+    # byte after every call, over random budgets; then the state imports
+    # into this library's format as the state init_state makes from the
+    # one-shot ids, and the pass goes on to the same end.
+    shape = W.TINY.shape
+    cfg = shape.as_tuple()
+    blob = Bl.build_blob(shape, 76)
+    s0 = Bl.section_zero(blob)
+    v = T.Vocab(s0)
+    rng = np.random.default_rng(4)
+    for trial in range(12):
+        prompt = V.sample_text(int(rng.integers(0, 17)), 600 + trial)
+        temp, seed = (0, 0) if trial % 3 == 0 else (65536, 900 + trial)
+        e, mine = B.fpi8_pages_init(cfg, prompt, 6, temp, seed)
+        e2, ref = OP.init(cfg, prompt, 6, temp, seed)
+        assert e == e2 == 0 and np.array_equal(mine, ref)
+        while OP._u32(ref, 8) < 3:
+            b = int(rng.integers(0, 6))
+            e, done = B.fpi8_pages_tokenize(s0, mine, b)
+            assert e == 0 and OP.tokenize_units(s0, cfg, ref, b) == 0
+            assert np.array_equal(mine, ref)
+            assert done <= b
+        assert B.fpi8_pages_tokenize(s0, mine, 1) == (3, 0)
+        e, ids = T.encode(v, prompt, 6)
+        e, want = O.init_state(cfg, ids, 6, temp, seed)
+        e, got = B.fpi8_state_import(cfg, mine)
+        assert e == 0 and np.array_equal(got, want)
+        assert np.array_equal(OP.import_(cfg, mine), want)
+        assert O.run_to_end(blob, got) == 0 and O.run_to_end(blob, want) == 0
+        assert np.array_equal(got, want)
+
+
+def test_tokenizing_errors():
+    shape = W.Shape(64, 96, 1, 4, 4, 512, 40)
+    cfg = shape.as_tuple()
+    s0 = Bl.section_zero(Bl.build_blob(shape, 77))
+    # a prompt whose tokens and max tokens do not fit: 7 at the last scan's
+    # end, the state as it stood, on both sides
+    prompt = b"a b c d e f g h i j k l m n o"
+    e, mine = B.fpi8_pages_init(cfg, prompt, 30)
+    e2, ref = OP.init(cfg, prompt, 30, 0, 0)
+    assert e == e2 == 0
+    e, done = B.fpi8_pages_tokenize(s0, mine, 10**9)
+    assert e == 7 and OP.tokenize_units(s0, cfg, ref, 10**9) == 7
+    assert np.array_equal(mine, ref) and OP._u32(mine, 8) == 2
+    assert B.fpi8_pages_tokenize(s0, mine, 1)[0] == 7
+    # init: prompt and range errors, and the buffer's size
+    assert B.fpi8_pages_init(cfg, b"a\x00b", 3)[0] == 6
+    assert B.fpi8_pages_init(cfg, b"a" * 1025, 3)[0] == 6
+    assert B.fpi8_pages_init(cfg, b"ab", 0)[0] == 6
+    assert B.fpi8_pages_init(cfg, b"ab", 41)[0] == 6
+    assert B.fpi8_pages_init(cfg, b"ab", 3, 16 * 65536 + 1)[0] == 6
+    assert OP.init(cfg, b"a\x00b", 3, 0, 0)[0] == 6
+    # a cursor out of range, a wrong tag, a vocabulary without a tokenizer
+    e, st = B.fpi8_pages_init(cfg, b"hello", 3)
+    assert B.fpi8_pages_tokenize(s0, st, 3) == (0, 3)
+    bad = st.copy()
+    bad[52:56] = np.frombuffer(np.uint32(6).tobytes(), np.uint8)
+    assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
+    bad = st.copy()
+    bad[32:36] = np.frombuffer(np.uint32(8).tobytes(), np.uint8)
+    assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
+    bad = st.copy()
+    bad[0] = ord("X")
+    assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
+    small = Bl.section_zero(Bl.build_blob(W.SMALL_SHAPES["h8"], 64))
+    assert B.fpi8_pages_tokenize(small, st, 1)[0] == 2
+    # a state still tokenizing does not import
+    assert B.fpi8_state_import(cfg, st)[0] == 3
