@@ -861,6 +861,56 @@ def test_page_format_round_trip_on_the_gpu():
         pair.model.close()
 
 
+def test_page_state_from_text_on_the_gpu():
+    # Text to text through the page's state format: a fresh page state
+    # (library), phases 0-2 in random unit budgets (library, against the
+    # oracle's page tokenizer after every call), imported to the GPU and
+    # run there to the end, then exported in the page's format: byte for
+    # byte the oracle's export of the oracle's run.
+    from oracle import pages as OP
+    from workloads import vocab as V
+    shape = W.SMALL_SHAPES["ragged"]
+    blob = Bl.build_blob(shape, 70)
+    s0 = Bl.section_zero(blob)
+    cfg = shape.as_tuple()
+    rng = np.random.default_rng(12)
+    prompts = [V.sample_text(int(n), 120 + r) for r, n in enumerate(rng.integers(0, 14, 5))]
+    prompts[0] = b""
+    runs, imported = [], []
+    for r, prompt in enumerate(prompts):
+        temp, seed = 65536 * (r % 2), 130 + r
+        e, pg = B.fpi8_pages_init(cfg, prompt, 5, temp, seed)
+        e2, ref = OP.init(cfg, prompt, 5, temp, seed)
+        assert e == e2 == 0 and np.array_equal(pg, ref)
+        while OP._u32(ref, 8) < 3:
+            b = int(rng.integers(1, 12))
+            assert B.fpi8_pages_tokenize(s0, pg, b)[0] == 0
+            assert OP.tokenize_units(s0, cfg, ref, b) == 0
+            assert np.array_equal(pg, ref)
+        e, st = B.fpi8_state_import(cfg, pg)
+        assert e == 0
+        n = OP._u32(pg, 32)
+        L = O.state_layout(cfg, n, 5)
+        ids = st[L["ids"]: L["ids"] + 4 * n].view(np.uint32).copy()
+        runs.append((ids, 5, temp, seed))
+        imported.append(st)
+    say("page states from text, on the GPU")
+    pair = Pair(shape, blob, runs)
+    try:
+        for i, st in enumerate(imported):
+            assert np.array_equal(st, pair.ref[i])
+            pair.load(i, st)
+        while not pair.complete():
+            pair.turn(3)
+        pair.compare()
+        for i, prompt in enumerate(prompts):
+            e, pg = B.fpi8_state_export(s0, pair.batch.state(i), prompt, cfg)
+            assert e == 0
+            assert np.array_equal(pg, OP.export(s0, cfg, pair.ref[i], prompt))
+    finally:
+        pair.model.close()
+
+
 def test_units_budget_edges():
     # A budget of 0 changes nothing but the turn count; a budget past the
     # end completes a run as a turn of positions does; a complete run is
