@@ -147,7 +147,11 @@ int32_t fpi8_pages_tokenize(const uint8_t *h_section0, uint64_t section0_len, ui
   if (phase > 2) return FPI8_INVALID_STATE;
   const uint32_t cap = pb + 2;
   if (phase > 0 && (n < 1 || n > cap)) return FPI8_INVALID_STATE;
-  if (phase == 1 && rd32(pages + PG_NEXT_BYTE) > pb) return FPI8_INVALID_STATE;
+  // in phase 1 the tokens so far are at most the opening and space tokens
+  // and one per byte read, so the rest of the prompt still fits the buffer
+  if (phase == 1 && (rd32(pages + PG_NEXT_BYTE) > pb ||
+                     n > (pb > 0 ? 2u : 1u) + rd32(pages + PG_NEXT_BYTE)))
+    return FPI8_INVALID_STATE;
   if (phase == 2) {
     const uint32_t at = rd32(pages + PG_BEST_AT);
     if (rd32(pages + PG_PAIR) >= n || (at != kNone && at + 1 >= n) ||

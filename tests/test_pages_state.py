@@ -237,6 +237,10 @@ def test_tokenizing_errors():
     bad = st.copy()
     bad[32:36] = np.frombuffer(np.uint32(8).tobytes(), np.uint8)
     assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
+    bad = st.copy()                                               # more tokens than bytes read
+    bad[32:36] = np.frombuffer(np.uint32(5).tobytes(), np.uint8)
+    assert OP._u32(bad, 8) == 1 and OP._u32(bad, 52) == 2
+    assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
     bad = st.copy()
     bad[0] = ord("X")
     assert B.fpi8_pages_tokenize(s0, bad, 1)[0] == 3
