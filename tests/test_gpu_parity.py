@@ -330,6 +330,29 @@ def test_full_size_first_positions(name):
         O.set_threads(1)
 
 
+def test_full_size_7b_longer_prompts():
+    # The benchmark's model and batch width (64 runs, graph replay) with
+    # prompts of 66 to 70 ids, so attention at head size 128 loops over
+    # several batches of cached positions before sampling; two runs are
+    # checked against the oracle, state for state, at the end.
+    w = W.by_name("7B-shaped-d4096-L32")
+    shape = w.shape
+    say("full size 7B, longer prompts: artifact")
+    blob = Bl.build_blob(shape, w.blob_seed)
+    runs = [(W.prompt_ids(shape.vocab, 66 + (r % 5), w.ids_seed, 200 + r), 2, 0, w.run_seed + r)
+            for r in range(w.runs)]
+    sample = [4, w.runs - 2]
+    O.set_threads(16)
+    pair = Pair(shape, blob, runs)
+    try:
+        say("full size 7B, longer prompts: 71 positions")
+        pair.turn(71, oracle_runs=sample)
+        pair.compare(sample)
+    finally:
+        pair.model.close()
+        O.set_threads(1)
+
+
 def test_full_size_units():
     # Turns of unit budgets at the 1.1B shape and its batch width: the
     # budgets stop runs inside matrices, attention stages and sampling
