@@ -1014,3 +1014,29 @@ def test_engine_rejects_bad_artifacts():
     e, h = B.fpi8_engine_create(s0, d, bl.size, 4)
     assert e == 0
     B.fpi8_engine_destroy(h)
+
+
+def test_turn_rejects_bad_batches():
+    # An empty batch and one wider than the engine are argument errors
+    # before anything is read; a misaligned stride, or one shorter than a
+    # state, fails every run with error 3 and leaves the states unchanged.
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 18)
+    runs = spec(shape, 3, 4, 3, seed=12)
+    say("turn argument checks")
+    pair = Pair(shape, blob, runs, max_runs=3)
+    try:
+        b, eng = pair.batch, pair.model.engine
+        before = [b.state(i).copy() for i in range(3)]
+        assert B.fpi8_turn(eng, b.d_states, b.stride, 0, 1)[0] == B.ERR_ARGUMENT
+        assert B.fpi8_turn(eng, b.d_states, b.stride, 4, 1)[0] == B.ERR_ARGUMENT
+        for stride in (b.stride - 4, 128, b.sizes[0] - 8):
+            e, errs = B.fpi8_turn(eng, b.d_states, stride, 3, 1)
+            assert e == 3 and list(errs) == [3, 3, 3], (stride, e, list(errs))
+        for i in range(3):
+            assert np.array_equal(b.state(i), before[i])
+        # the same batch with its own stride goes on as the oracle does
+        pair.turn(2)
+        pair.compare()
+    finally:
+        pair.model.close()
