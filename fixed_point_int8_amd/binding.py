@@ -31,7 +31,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_destroy", "fpi8_turn", "fpi8_turn_phases", "fpi8_turn_units",
            "fpi8_engine_set_row_kernel", "fpi8_engine_set_graph", "fpi8_tokenize",
            "fpi8_token_text", "fpi8_output_text", "fpi8_pages_state_size", "fpi8_state_export",
-           "fpi8_state_import", "fpi8_pages_init", "fpi8_pages_tokenize",
+           "fpi8_state_import", "fpi8_pages_init", "fpi8_pages_tokenize", "fpi8_position_charges",
            "fpi8_engine_set_streams",
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
@@ -86,6 +86,7 @@ def lib():
             "fpi8_pages_init": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, C.c_uint32,
                                             C.c_uint64, _P, C.c_uint64]),
             "fpi8_pages_tokenize": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.c_uint64, _P]),
+            "fpi8_position_charges": (C.c_int32, [_P, C.c_uint32, C.c_int32, C.c_uint32, _P]),
             "fpi8_engine_set_row_kernel": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_streams": (C.c_int32, [_P, C.c_int32]),
             "fpi8_engine_set_graph": (C.c_int32, [_P, C.c_int32]),
@@ -287,6 +288,14 @@ def fpi8_pages_init(cfg, prompt: bytes, max_tokens: int, temperature_q16: int = 
     e = lib().fpi8_pages_init(_np_ptr(_cfg(cfg)), buf, len(prompt), max_tokens, temperature_q16,
                               C.c_uint64(seed), _np_ptr(out), out.size)
     return e, (out if e == 0 else None)
+
+
+def fpi8_position_charges(cfg, position: int, generating: bool, temperature_q16: int = 0):
+    """(error, compute units of phases 3 to 19 of one position, uint64[17])."""
+    out = np.zeros(17, dtype=np.uint64)
+    e = lib().fpi8_position_charges(_np_ptr(_cfg(cfg)), position, 1 if generating else 0,
+                                    temperature_q16, _np_ptr(out))
+    return e, out
 
 
 def fpi8_pages_tokenize(section0: np.ndarray, pages: np.ndarray, max_units: int):

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libfpi8.so")
 SOURCES = ["csrc/fpi8_host.cpp", "csrc/fpi8_engine.cpp", "csrc/fpi8_tokenizer.cpp",
-           "csrc/fpi8_pages.cpp", "csrc/fpi8_kernels.hip"]
+           "csrc/fpi8_pages.cpp", "csrc/fpi8_charges.cpp", "csrc/fpi8_kernels.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17", "-Wall",
          # no packed-FP32 instructions in any kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

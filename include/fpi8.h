@@ -172,6 +172,18 @@ int32_t fpi8_pages_init(const uint32_t cfg[7], const uint8_t *prompt, uint32_t p
 int32_t fpi8_pages_tokenize(const uint8_t *h_section0, uint64_t section0_len, uint8_t *pages,
                             uint64_t pages_len, uint64_t max_units, uint64_t *units_done);
 
+/* The compute units the page's turn planner charges for the phases of one
+ * position ("The turn planner", "Compute costs"), summed over layers, with
+ * every chunk whole and its 160 units included: out[phase - 3] for phases 3
+ * to 19.  position counts from 0 (the attention stages see position + 1
+ * positions); generating selects phases 17 to 19; above temperature zero
+ * sampling is three passes.  Not included: the 18,000 units of each turn,
+ * and the setup and 160 units charged again where a turn boundary splits a
+ * chunk.  Errors: 1, 6 (position at or past the context, temperature above
+ * 16), 4 (out NULL). */
+int32_t fpi8_position_charges(const uint32_t cfg[7], uint32_t position, int32_t generating,
+                              uint32_t temperature_q16, uint64_t out[17]);
+
 /* Checks a whole artifact held in host memory: 0, 1, 2 or 5.  cfg_out
  * (may be NULL) receives the configuration. */
 int32_t fpi8_blob_check(const uint8_t *blob, uint64_t len, uint32_t cfg_out[7]);
