@@ -199,7 +199,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the runs of a batch are "
-              f"independent, and this build has no multi-GPU path.", file=sys.stderr)
+              f"independent, and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
