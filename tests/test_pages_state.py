@@ -248,3 +248,29 @@ def test_tokenizing_errors():
     assert B.fpi8_pages_tokenize(small, st, 1)[0] == 2
     # a state still tokenizing does not import
     assert B.fpi8_state_import(cfg, st)[0] == 3
+
+
+def test_tokenizing_the_longest_prompt():
+    # A prompt of the largest allowed length (1,024 bytes) over a 32,000-token
+    # vocabulary: the page-state tokenizer, cut into a few large budgets,
+    # ends with the one-shot tokenizer's ids, in the library and the oracle.
+    shape = W.Shape(64, 96, 1, 4, 4, 32000, 4096)
+    cfg = shape.as_tuple()
+    s0 = Bl.section_zero(Bl.build_blob(shape, 78))
+    v = T.Vocab(s0)
+    prompt = V.sample_text(1024, 901)[:1024]
+    while len(prompt) < 1024:
+        prompt += b"a"
+    e, want = B.fpi8_tokenize(s0, prompt, 8)
+    assert e == 0 and list(want) == T.encode(v, prompt, 8)[1]
+    e, pg = B.fpi8_pages_init(cfg, prompt, 8)
+    assert e == 0
+    total = 0
+    while OP._u32(pg, 8) < 3:
+        e, done = B.fpi8_pages_tokenize(s0, pg, 50_000)
+        assert e == 0 and done > 0
+        total += done
+    n = OP._u32(pg, 32)
+    P = OP.layout(cfg, 1024, 8)
+    assert list(pg[P["ids"]: P["ids"] + 4 * n].view(np.uint32)) == list(want)
+    assert total == _scan_units(v, prompt, list(want))
