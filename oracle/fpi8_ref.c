@@ -116,7 +116,8 @@ void fpi8_ref_rotate(int64_t *a, int64_t *b, int32_t c, int32_t s) {
   *b = asr(wadd(wmul(A, s), wmul(B, c)), 24);
 }
 
-/* "Lookup tables", exponential: the index is d >> 8, capped at 4,096.
+/* "Lookup tables", exponential: a difference selects entry d >> 8, and
+ * every difference past the table's end selects its last entry, 4,096.
  * Reading: d is a non-negative difference, taken as an unsigned word. */
 uint32_t fpi8_ref_exp_index(uint64_t d) {
   uint64_t i = d >> 8;
@@ -380,10 +381,11 @@ int32_t fpi8_ref_state_layout(const uint32_t cfg[7], uint32_t n_ids, uint32_t ma
   return 0;
 }
 
-/* The page's own account: 256-byte account header, the 128-byte state
- * header, prompt bytes, prompt tokens (bytes + 2), output tokens, output
- * text (max * 128), then the shared tail; cache positions are the prompt's
- * bytes plus max tokens plus one, up to the context. */
+/* Size of a run account in the page's own layout ("The resumable state"):
+ * 256 bytes of account header, the 128-byte state header, the prompt bytes,
+ * room for bytes + 2 prompt tokens, the output tokens, 128 text bytes per
+ * output token, then the buffers both layouts share.  The cache holds
+ * prompt bytes + max tokens + 1 positions, never more than the context. */
 uint64_t fpi8_ref_pages_state_size(const uint32_t cfg[7], uint32_t prompt_bytes,
                                    uint32_t max_tokens) {
   cfg_t c;
@@ -422,8 +424,9 @@ int32_t fpi8_ref_init_state(const uint32_t cfg[7], uint8_t *state, uint64_t stat
   wr32(state + H_MAX, max_tokens);
   wr32(state + H_TEMP, temperature_q16);
   wr32(state + H_CACHEPOS, L.cache_positions);
-  /* "Sampling": a seed of zero starts the generator at 0x9E3779B97F4A7C15.
-   * Reading: the replacement is made when the state is opened. */
+  /* "Sampling": seed 0 is replaced by the golden-ratio constant
+   * 0x9E3779B97F4A7C15.  Reading: the replacement is made when the state
+   * is opened. */
   wr64(state + H_GENERATOR, seed ? seed : 0x9E3779B97F4A7C15ull);
   memcpy(state + L.ids, ids, 4ull * n_ids);
   return 0;

@@ -5,16 +5,17 @@ __graft_entry__.smoke() and bench.py's CPU baseline use it; the library
 never does.  Plain Python loops over small inputs (prompts of at most 1,024
 bytes), written from "The inference core" page:
 
-* "The forward pass, in order", phase 0: token 1 (the opening token), then
-  the token of a single space when the prompt has text;
-* phase 1: the prompt one UTF-8 character at a time, each looked up whole;
-  a character with no token becomes one token per byte, id byte + 3;
-* phase 2: every adjacent pair looked up as one string; the pair whose
-  merged token scores highest is replaced by it, until no pair merges; then
-  the prompt's tokens and max tokens must fit the context;
-* "Sampling", last paragraph: a token's text is its bytes, a leading space
-  dropped right after the opening token, <0xXX> written as that byte, and
-  tokens 1 and 2 add none (XX: two hexadecimal digits, either case).
+* "The forward pass, in order", phase 0: the ids start with the opening
+  token (1), followed by the space token if the prompt is not empty;
+* phase 1: each UTF-8 character is looked up as one string; one that is not
+  in the vocabulary falls back to its bytes, each as id byte + 3;
+* phase 2: repeatedly, among all neighbouring pairs whose joined string is a
+  token, the best-scoring one is merged; when none is left, the ids plus max
+  tokens have to fit in the context;
+* "Sampling", its closing rules for text: a token contributes its bytes,
+  except that a space at its start is dropped when it directly follows the
+  opening token, a <0xXX> token stands for the single byte XX (two hex
+  digits, either case), and tokens 1 and 2 contribute nothing.
 
 Readings where the page is silent (the same ones the library takes):
 

@@ -447,6 +447,68 @@ def test_temperature_sampling_frequencies():
     assert np.all(np.abs(counts / n - want) < 0.015)
 
 
+def test_xorshift_worked_steps_from_seed_one():
+    # States and the first draw worked by hand from the three printed shift
+    # steps ("Sampling"); the mirrored order of the shifts is also a
+    # full-period map, so only worked values tell the two apart.
+    g = {r[0]: int(r[1], 0) for r in read_table("xorshift_seed1.txt")}
+    s1, d1 = O.xorshift64s(1)
+    assert s1 == g["state_after_1"] and d1 == g["draw_1"]
+    assert s1 != g["mirrored_state_after_1"]
+    s2, _ = O.xorshift64s(s1)
+    assert s2 == g["state_after_2"]
+    # the sampler advances the generator by exactly this map at T > 0
+    tok, gen = O.sample(np.array([0, -1], dtype=np.int64), 65536, B.exp_table(), 1)
+    assert gen == g["state_after_1"]
+
+
+def _one_hot_exp_table():
+    # Entry 0 is 1 and every other entry 0: a logit whose difference indexes
+    # entry 0 can be drawn, any other never.
+    t = np.zeros(4097, dtype=np.uint32)
+    t[0] = 1
+    return t
+
+
+@pytest.mark.parametrize("temp_q16, d_last0, d_first1", [
+    (131072, 511, 512),    # T = 2.0: floor(d / 2) >> 8 is 0 up to d = 511
+    (32768, 127, 128),     # T = 0.5: (2 d) >> 8 is 0 up to d = 127
+    (65536, 255, 256),     # T = 1.0: the score-difference rule itself
+    (1048576, 4095, 4096), # T = 16 (the largest): floor(d / 16) >> 8
+])
+def test_temperature_divides_the_difference(temp_q16, d_last0, d_first1):
+    # "Sampling": the sum and draw passes take the largest logit minus each
+    # logit, divide it by the temperature (both at 16 fractional bits) and
+    # index the exponential table like a score difference.  With a table of
+    # a single nonzero entry, the lower logit is drawn (about half the
+    # seeds) exactly when its quotient indexes entry 0, and never otherwise.
+    tab = _one_hot_exp_table()
+    seeds = [(s * 0x9E3779B97F4A7C15) % (1 << 64) or 1 for s in range(1, 65)]
+    for d, drawn in ((d_last0, True), (d_first1, False)):
+        lg = np.array([0, -d], dtype=np.int64)
+        toks = [O.sample(lg, temp_q16, tab, s)[0] for s in seeds]
+        assert (1 in toks) == drawn, (temp_q16, d)
+        if drawn:
+            assert 16 < sum(toks) < 48  # the two weights are equal
+
+
+@pytest.mark.parametrize("temp_q16", [131072, 32768])
+def test_temperature_sampling_frequencies_away_from_one(temp_q16):
+    # Away from T = 1 the draw follows exp(-d / T): logits one unit apart
+    # give weights exp(-i / T) (entry round(256 i / T) of the table).
+    exp_tab = B.exp_table()
+    T = temp_q16 / 65536.0
+    lg = np.array([0, -65536, -2 * 65536, -3 * 65536], dtype=np.int64)
+    counts = np.zeros(4)
+    n = 20000
+    for s in range(1, n + 1):
+        tok, _ = O.sample(lg, temp_q16, exp_tab, s * 0x9E3779B97F4A7C15 % (1 << 64))
+        counts[tok] += 1
+    want = np.exp(-np.arange(4.0) / T)
+    want /= want.sum()
+    assert np.all(np.abs(counts / n - want) < 0.015), (counts / n, want)
+
+
 # --------------------------------------------------------------------------
 # The artifact, the state and "Core errors"
 
