@@ -38,15 +38,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def rows_bytes(shape, batch, generating=True):
-    """Algorithmic bytes of every row-kernel launch of one step: weight bytes,
-    Q24 scales, i64 inputs and i64 outputs of each matrix."""
+def step_matrices(shape, generating=True):
+    """(rows, cols) of every matrix one step multiplies."""
     d, f, kvd, v, L = shape.dim, shape.hidden, shape.kv_dim, shape.vocab, shape.layers
     mats = [(d, d), (kvd, d), (kvd, d), (d, d), (f, d), (f, d), (d, f)] * L
     if generating:
         mats.append((v, d))
+    return mats
+
+
+def rows_bytes(shape, batch, generating=True):
+    """Algorithmic bytes of every row-kernel launch of one step: weight bytes,
+    Q24 scales, i64 inputs and i64 outputs of each matrix."""
     total = 0
-    for rows, cols in mats:
+    for rows, cols in step_matrices(shape, generating):
         total += rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
     return total
 
@@ -59,10 +64,12 @@ def attention_bytes(shape, batch, npos):
 
 
 def measured_traffic(kernel, workload, positions):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    runs (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
-    None when there are none for these launches or the kernel's source has
-    changed since they were taken."""
+    """HBM bytes per launch of attention over `positions` (one launch per layer
+    and step), from the committed rocprofv3 counter runs (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings): their ratio to the
+    algorithmic bytes of the launches they counted, times the algorithmic
+    bytes of these launches.  None when there are none for this workload or
+    the kernel's source has changed since they were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}-7B-decode-b64.traffic.json")
     if workload != "7B-shaped-d4096-L32" or not os.path.exists(path):
@@ -74,30 +81,79 @@ def measured_traffic(kernel, workload, positions):
     b = src.find("// Phase 19 and the end of a position")
     if a < 0 or b < 0 or hashlib.sha256(src[a:b].encode()).hexdigest() != t["source_sha256"]:
         return None
-    if t["positions"] != positions:
+    import workloads as Wl
+    shape = Wl.by_name(workload).shape
+
+    def mean_alg(pr):
+        ps = range(pr[0], pr[1] + 1)
+        return sum(attention_bytes(shape, 64, p + 1) for p in ps) / len(ps)
+
+    ratio = t["traffic_bytes_per_launch"] / mean_alg(t["positions"])
+    return int(ratio * mean_alg(positions))
+
+
+STREAM_SRC = os.path.join(ROOT, "fixed_point_int8_amd", "csrc", "fpi8_rows_stream.hip")
+MFMA_I8_PEAK_OPS = 5.0e15  # MI355X dense int8 matrix-core peak, ops/s
+
+
+def mfma_ops(rows, cols, batch):
+    """Int8 matrix-core operations the row kernels issue for one matrix: three
+    digit passes of 16x16x64 MFMAs over 16-run tiles (a partial run tile is
+    issued whole)."""
+    return 2 * 3 * 16 * ((batch + 15) // 16) * rows * 64 * ((cols + 63) // 64)
+
+
+def source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pool_traffic(batch):
+    """HBM bytes per launch of the pooled row kernel at this batch, from the
+    committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy's readings), or None when there are none or the kernel source
+    has changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "k_rows_stream-4096-pool.traffic.json")
+    if not os.path.exists(path):
         return None
-    return t["traffic_bytes_per_launch"]
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_sha(STREAM_SRC):
+        return None
+    b = t.get("batches", {}).get(str(batch))
+    return None if b is None else b["traffic_bytes_per_launch"]
 
 
-def row_sweep(torch, reps=3):
-    """The standalone matrix row over a pool of 48 distinct 4096 x 4096
-    matrices (805 MB, over three times the 256 MB last-level cache), one call
-    per matrix, timed with events on the launch stream: once with the
-    matrices packed beforehand (fpi8_matrix_pack, outside the timed region:
-    weights are prepared once and used many times), once row-major
-    (fpi8_matrix_rows).  A call converts the inputs to digits and runs the
-    row kernel."""
+def row_sweep(torch, reps=5):
+    """The standalone matrix row at 4096 columns over a pool of 48 distinct
+    4096 x 4096 matrices (805 MB, over three times the 256 MB last-level
+    cache), packed beforehand (fpi8_matrix_pack, outside the timed region:
+    weights are prepared once and used many times).
+
+    pool: the 48 matrices are one stacked matrix of 196,608 rows of 4096
+      columns, and one call streams them all: a launch that splits the
+      inputs into digits, then one launch of the persistent row kernel.  The
+      row kernel's own duration comes from HIP events the library records
+      around its launch on the call's stream (fpi8_matrix_rows_timing).
+    per_matrix: one call per 4096 x 4096 matrix, 48 calls back to back
+      (each a short launch, bound by its ramp rather than by bandwidth)."""
     from fixed_point_int8_amd import binding as B
-    rows = cols = 4096
+    rows1 = cols = 4096
     pool = 48
+    rows = rows1 * pool
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
-    W = torch.randint(0, 256, (pool, rows, cols), dtype=torch.uint8, device="cuda", generator=g)
-    S = torch.randint(1 << 14, 1 << 18, (pool, rows), dtype=torch.int32, device="cuda", generator=g)
-    n_p = B.fpi8_matrix_packed_size(rows, cols)
-    Pk = torch.empty((pool, n_p), dtype=torch.uint8, device="cuda")
+    n_p1 = B.fpi8_matrix_packed_size(rows1, cols)
+    Pk = torch.empty((pool, n_p1), dtype=torch.uint8, device="cuda")
     for i in range(pool):
-        assert B.fpi8_matrix_pack(W[i], rows, cols, Pk[i], n_p) == 0
+        Wi = torch.randint(0, 256, (rows1, cols), dtype=torch.uint8, device="cuda", generator=g)
+        assert B.fpi8_matrix_pack(Wi, rows1, cols, Pk[i], n_p1) == 0
+        del Wi
+    S = torch.randint(1 << 14, (1 << 18) + 1, (pool, rows1), dtype=torch.int64, device="cuda",
+                      generator=g).to(torch.int32)
+    # 16-row tiles stack: the packed pool is the packed stacked matrix
+    assert B.fpi8_matrix_packed_size(rows, cols) == pool * n_p1
     out = {}
     stream = torch.cuda.current_stream()
     for batch in (1, 8, 32, 128):
@@ -105,32 +161,62 @@ def row_sweep(torch, reps=3):
         y = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
         n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
         work = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        alg1 = rows1 * cols + 4 * rows1 + 8 * batch * cols + 8 * batch * rows1
         alg = rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
-        res = {}
-        for name, call in (("packed", lambda i: B.fpi8_matrix_rows_packed(Pk[i], S[i], rows, cols, x, batch, y,
-                                                                          work, n, stream)),
-                           ("row_major", lambda i: B.fpi8_matrix_rows(W[i], S[i], rows, cols, x, batch, y,
-                                                                      work, n, stream))):
-            for i in range(pool):  # warm-up
-                assert call(i) == 0
-            torch.cuda.synchronize()
-            t0 = torch.cuda.Event(enable_timing=True)
-            t1 = torch.cuda.Event(enable_timing=True)
-            t0.record(stream)
-            for r in range(reps):
-                for i in range(pool):
-                    call(i)
-            t1.record(stream)
-            torch.cuda.synchronize()
-            res[name] = t0.elapsed_time(t1) / (reps * pool)
-        ms = res["packed"]
-        out[str(batch)] = {"us_per_call": round(ms * 1e3, 3), "GB/s": round(alg / ms / 1e6, 1),
-                           "frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
-                           "weight_GB/s": round(rows * cols / ms / 1e6, 1),
-                           "row_major_us_per_call": round(res["row_major"] * 1e3, 3),
-                           "row_major_GB/s": round(alg / res["row_major"] / 1e6, 1)}
-        del x, y, work
-    del W, S, Pk
+        ops = mfma_ops(rows, cols, batch)
+
+        def pooled():
+            return B.fpi8_matrix_rows_packed(Pk, S, rows, cols, x, batch, y, work, n, stream)
+
+        assert pooled() == 0
+        torch.cuda.synchronize()
+        B.fpi8_matrix_rows_set_timing(True)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            pooled()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        call_ms = t0.elapsed_time(t1) / reps
+        e, kern_ms, launches = B.fpi8_matrix_rows_timing()
+        B.fpi8_matrix_rows_set_timing(False)
+        assert e == 0 and launches == reps
+        kern_ms /= launches
+
+        yp = y[:, (pool - 1) * rows1:].clone()
+        y1 = torch.zeros((batch, rows1), dtype=torch.int64, device="cuda")
+
+        def single(i):
+            return B.fpi8_matrix_rows_packed(Pk[i], S[i], rows1, cols, x, batch, y1, work, n, stream)
+
+        for i in range(pool):
+            assert single(i) == 0
+        torch.cuda.synchronize()
+        # the pooled call's last matrix equals the last single call's
+        assert torch.equal(yp, y1), "pooled and single calls disagree"
+        t0.record(stream)
+        for _ in range(3):
+            for i in range(pool):
+                single(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        single_ms = t0.elapsed_time(t1) / (3 * pool)
+        out[str(batch)] = {
+            "pool": {"rows": rows, "kernel_us": round(kern_ms * 1e3, 2),
+                     "GB/s": round(alg / kern_ms / 1e6, 1),
+                     "frac": round(alg / kern_ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "weight_GB/s": round(rows * cols / kern_ms / 1e6, 1),
+                     "call_us": round(call_ms * 1e3, 2),
+                     "call_GB/s": round(alg / call_ms / 1e6, 1),
+                     "mfma_util": round(ops / (kern_ms * 1e-3) / MFMA_I8_PEAK_OPS, 4),
+                     "bytes_per_launch": alg, "traffic": pool_traffic(batch)},
+            "per_matrix": {"us_per_call": round(single_ms * 1e3, 3),
+                           "GB/s": round(alg1 / single_ms / 1e6, 1),
+                           "frac": round(alg1 / single_ms / 1e6 / HBM_PEAK_GBS, 4)},
+        }
+        del x, y, y1, yp, work
+    del Pk, S
     torch.cuda.empty_cache()
     return out
 
@@ -237,13 +323,21 @@ def main():
     log(f"prefill {w.prompt} positions x {w.runs} runs in {prefill_s:.2f} s")
 
     gen_prefill = sum(batch.info(i)["generated"] for i in range(w.runs))
+    # The timed steps sit around the middle of the decode window (positions
+    # prompt .. prompt + max_tokens - 2), where a step reads the window's mean
+    # cache length; the steps before them are untimed (warm-up included).
+    first_dec, last_dec = w.prompt, w.prompt + w.max_tokens - 2
+    mid = (first_dec + last_dec) // 2
+    start = max(first_dec + args.warmup, mid - args.steps // 2)
+    start = min(start, last_dec + 1 - args.steps - args.kernel_steps)
     t = time.perf_counter()
-    e, errs = batch.turn(model, args.warmup, stream)
+    e, errs = batch.turn(model, start - first_dec, stream)
     torch.cuda.synchronize()
     warm_s = time.perf_counter() - t
     assert e == 0, (e, list(errs))
     gen0 = sum(batch.info(i)["generated"] for i in range(w.runs))
     pos0 = batch.info(0)["position"]
+    assert pos0 == start, (pos0, start)
 
     # The timed steps: nothing but the launches of the path.
     torch.cuda.synchronize()
@@ -261,8 +355,8 @@ def main():
     ks = args.kernel_steps
     # One stream here, so that no other kernel runs beside the one timed.
     B.fpi8_engine_set_streams(model.engine, 1)
-    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, True)
-    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, True)
+    for k in (B.T_ROWS, B.T_ATTN, B.T_NORM):
+        B.fpi8_engine_set_timing(model.engine, k, True)
     torch.cuda.synchronize()
     tk = time.perf_counter()
     e, errs = batch.turn(model, ks, stream)
@@ -271,32 +365,34 @@ def main():
     assert e == 0, (e, list(errs))
     _, rows_ms, rows_n = B.fpi8_engine_timing(model.engine, B.T_ROWS)
     _, attn_ms, attn_n = B.fpi8_engine_timing(model.engine, B.T_ATTN)
-    B.fpi8_engine_set_timing(model.engine, B.T_ROWS, False)
-    B.fpi8_engine_set_timing(model.engine, B.T_ATTN, False)
+    _, norm_ms, norm_n = B.fpi8_engine_timing(model.engine, B.T_NORM)
+    for k in (B.T_ROWS, B.T_ATTN, B.T_NORM):
+        B.fpi8_engine_set_timing(model.engine, k, False)
 
     # Algorithmic bytes over the kernel-timed steps (positions pos1 .. pos1+ks-1).
     rows_alg = rows_bytes(shape, w.runs) * ks
+    rows_ops = sum(mfma_ops(r, c, w.runs) for r, c in step_matrices(shape)) * ks
     attn_alg = sum(attention_bytes(shape, w.runs, pos1 + k + 1) * shape.layers for k in range(ks))
     kern = {
         "steps": ks, "positions": [pos1, pos1 + ks - 1],
         "rows": {"launches": rows_n, "avg_us": round(rows_ms * 1e3 / max(rows_n, 1), 2),
                  "GB/s": round(rows_alg / (rows_ms * 1e6), 1),
                  "frac": round(rows_alg / (rows_ms * 1e6) / HBM_PEAK_GBS, 4),
+                 "mfma_util": round(rows_ops / (rows_ms * 1e-3) / MFMA_I8_PEAK_OPS, 4),
                  "bytes_per_launch": int(rows_alg / max(rows_n, 1))},
         "attention": {"launches": attn_n, "avg_us": round(attn_ms * 1e3 / max(attn_n, 1), 2),
                       "GB/s": round(attn_alg / (attn_ms * 1e6), 1),
                       "frac": round(attn_alg / (attn_ms * 1e6) / HBM_PEAK_GBS, 4),
                       "bytes_per_launch": int(attn_alg / max(attn_n, 1))},
+        "norm": {"launches": norm_n, "avg_us": round(norm_ms * 1e3 / max(norm_n, 1), 2)},
         "share_of_step": {"rows": round(rows_ms / (dk * 1e3), 3),
-                          "attention": round(attn_ms / (dk * 1e3), 3)},
+                          "attention": round(attn_ms / (dk * 1e3), 3),
+                          "norm": round(norm_ms / (dk * 1e3), 3)},
     }
-    dom = "attention" if attn_ms > rows_ms else "rows"
-    ach = kern[dom]["GB/s"]
-    kname = "k_attention" if dom == "attention" else "k_rows"
-    roofline = {"kernel": kname, "bound": "hbm",
-                "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kname, w.name, [pos1, pos1 + ks - 1])}
+    roofline_attention = {"kernel": "k_attention", "bound": "hbm",
+                          "achieved": kern["attention"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": kern["attention"]["frac"],
+                          "traffic": measured_traffic("k_attention", w.name, [pos1, pos1 + ks - 1])}
 
     model.close()
     del batch, model
@@ -305,6 +401,20 @@ def main():
     sweep = None if args.no_sweep else row_sweep(torch)
     cpu = None if args.no_cpu else cpu_baseline(blob, shape, w.name)
 
+    # The int8 row kernel's roofline: one launch over the pooled 4096-column
+    # sweep, at the HBM-bound batch (1, 8 or 32) where it is furthest from
+    # peak.  (At 128 inputs the three digit passes make it matrix-core bound;
+    # that batch reports its int8 MFMA utilization in the sweep.)
+    roofline = None
+    if sweep:
+        bsel = min(("1", "8", "32"), key=lambda b: sweep[b]["pool"]["frac"])
+        pl = sweep[bsel]["pool"]
+        roofline = {"kernel": "k_rows_stream" if int(bsel) <= 16 else "k_rows_stream_shared",
+                    "bound": "hbm", "achieved": pl["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": pl["frac"], "traffic": pl["traffic"],
+                    "workload": f"4096-column rows, 48 stacked 4096x4096 matrices, batch {bsel}",
+                    "bytes_per_launch": pl["bytes_per_launch"]}
+
     res = {
         "metric": METRIC, "value": round(tokens / dt, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
@@ -312,10 +422,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name} decode", "global_batch": w.runs,
                    "prompt": w.prompt, "decode_positions": [pos0, pos0 + args.steps - 1],
+                   "decode_window": [first_dec, last_dec],
                    "seq_len": w.prompt + w.max_tokens - 1, "parallelism": "none (one GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
+        "roofline": roofline, "roofline_attention": roofline_attention,
+        "cpu_baseline": cpu, "kernels": kern,
         "prefill_s": round(prefill_s, 2),
-        # every token the runs hold over prefill, warm-up and timed steps, over their wall time
+        # every token the runs hold over prefill, the untimed and the timed steps, over their wall time
         "prefill_and_decode_tokens_per_s": round(gen1 / (prefill_s + warm_s + dt), 2),
         "first_tokens": gen_prefill,
         "hbm_copy_GB/s": copy_gbs, "row_sweep_4096": sweep,

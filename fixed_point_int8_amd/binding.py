@@ -36,7 +36,8 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_set_timing",
            "fpi8_engine_timing",
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
-           "fpi8_matrix_pack", "fpi8_matrix_rows_packed")
+           "fpi8_matrix_pack", "fpi8_matrix_rows_packed", "fpi8_matrix_rows_set_timing",
+           "fpi8_matrix_rows_timing")
 
 
 class fpi8_info(C.Structure):
@@ -100,6 +101,8 @@ def lib():
             "fpi8_matrix_pack": (C.c_int32, [_P, C.c_uint32, C.c_uint32, _P, C.c_uint64, _P]),
             "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
                                                     _P, _P, C.c_uint64, _P]),
+            "fpi8_matrix_rows_set_timing": (C.c_int32, [C.c_int32]),
+            "fpi8_matrix_rows_timing": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_uint64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -327,6 +330,17 @@ def fpi8_engine_timing(engine, kernel: int):
     ms = C.c_double(0)
     n = C.c_uint64(0)
     e = lib().fpi8_engine_timing(engine, kernel, C.byref(ms), C.byref(n))
+    return e, ms.value, n.value
+
+
+def fpi8_matrix_rows_set_timing(enable: bool) -> int:
+    return lib().fpi8_matrix_rows_set_timing(1 if enable else 0)
+
+
+def fpi8_matrix_rows_timing():
+    ms = C.c_double(0)
+    n = C.c_uint64(0)
+    e = lib().fpi8_matrix_rows_timing(C.byref(ms), C.byref(n))
     return e, ms.value, n.value
 
 

@@ -87,12 +87,10 @@ int hip_ok(hipError_t e) { return e == hipSuccess ? 0 : FPI8_ERR_HIP; }
 
 // Brackets a launch with events when its class is being timed.
 struct TimedLaunch {
-  fpi8_engine *e;
-  int cls;
+  Timer &t;
   hipStream_t s;
   bool on;
-  TimedLaunch(fpi8_engine *eng, int c, hipStream_t st) : e(eng), cls(c), s(st) {
-    Timer &t = e->timers[cls];
+  TimedLaunch(Timer &timer, hipStream_t st) : t(timer), s(st) {
     on = t.on;
     if (!on) return;
     if (t.used == t.starts.size()) {
@@ -104,14 +102,29 @@ struct TimedLaunch {
     }
     (void)hipEventRecord(t.starts[t.used], s);
   }
+  TimedLaunch(fpi8_engine *eng, int c, hipStream_t st) : TimedLaunch(eng->timers[c], st) {}
   ~TimedLaunch() {
     if (!on) return;
-    Timer &t = e->timers[cls];
     (void)hipEventRecord(t.stops[t.used], s);
     t.used++;
   }
 };
 
+int timer_sum(Timer &t, double *total_ms, uint64_t *launches) {
+  double sum = 0;
+  for (size_t i = 0; i < t.used; i++) {
+    if (hipEventSynchronize(t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, t.starts[i], t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = t.used;
+  return 0;
+}
+
+// Timing of the standalone row's row-kernel launches (measurement only).
+Timer g_rows_timer;
 
 // Launch shape of one row-kernel call.  kind 0: 16 * mt rows and 16 * bt
 // runs per workgroup of four waves, which split the contraction; kind 1:
@@ -748,17 +761,17 @@ int32_t fpi8_engine_set_timing(fpi8_engine *e, int32_t kernel, int32_t enable) {
 
 int32_t fpi8_engine_timing(fpi8_engine *e, int32_t kernel, double *total_ms, uint64_t *launches) {
   if (!e || kernel < 0 || kernel >= kTimingClasses) return FPI8_ERR_ARGUMENT;
-  Timer &t = e->timers[kernel];
-  double sum = 0;
-  for (size_t i = 0; i < t.used; i++) {
-    if (hipEventSynchronize(t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
-    float ms = 0;
-    if (hipEventElapsedTime(&ms, t.starts[i], t.stops[i]) != hipSuccess) return FPI8_ERR_HIP;
-    sum += ms;
-  }
-  if (total_ms) *total_ms = sum;
-  if (launches) *launches = t.used;
+  return timer_sum(e->timers[kernel], total_ms, launches);
+}
+
+int32_t fpi8_matrix_rows_set_timing(int32_t enable) {
+  g_rows_timer.on = enable != 0;
+  g_rows_timer.used = 0;
   return 0;
+}
+
+int32_t fpi8_matrix_rows_timing(double *total_ms, uint64_t *launches) {
+  return timer_sum(g_rows_timer, total_ms, launches);
 }
 
 // Workspace of the standalone row: the overflow word (256 bytes kept), then the digits.
@@ -825,6 +838,24 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   sg.pad = packed || aligned ? 1u : 0u;
   a.nseg = 1;
 
+  static std::atomic<uint32_t> calls{0};
+
+  // Many rows of a packed matrix: the persistent streaming kernel over
+  // fragment-major digit planes (one launch for the digits, one for the rows).
+  if (packed && batch <= 128 && kblocks % kStreamBlockMultiple == 0 && rows >= stream_min_rows()) {
+    uint32_t seq = ++calls;
+    if (seq == 0) seq = ++calls;
+    int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, 0, flag, seq, s);
+    if (r) return r;
+    a.planes = planes;
+    a.oflag = flag;
+    a.oflag_seq = seq;
+    a.compact = 0;
+    a.chunks = 1;
+    TimedLaunch t(g_rows_timer, s);
+    return launch_rows_stream(a, s);
+  }
+
   // One or two inputs whose digits fit a wave's LDS share: one launch, the
   // kernel's waves split the inputs into digits themselves.
   const uint32_t per = (kblocks + 3) / 4;
@@ -834,6 +865,7 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
       a.ntiles = p.tiles;
       a.wave_rows = 1;
       a.chunks = p.chunks;
+      TimedLaunch t(g_rows_timer, s);
       return launch_rows_raw(p.mt, a, s);
     }
   }
@@ -842,7 +874,6 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   // number, so the flag word never needs clearing; a stale word that happens
   // to match only sends the call down the exact path, which gives the same
   // result.
-  static std::atomic<uint32_t> calls{0};
   uint32_t seq = ++calls;
   if (seq == 0) seq = ++calls;
   // One or two inputs: plain digit rows, so the four lanes of a run read one
@@ -860,6 +891,7 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   a.ntiles = p.tiles;
   a.wave_rows = p.kind ? (uint32_t)p.wr : 1u;
   a.chunks = p.chunks;
+  TimedLaunch t(g_rows_timer, s);
   return launch_rows(EPI_RAW, p.kind, p.mt, p.bt, a, s);
 }
 

@@ -249,6 +249,13 @@ int launch_rows(int epi, int kind, int mt, int bt, const RowsArgs &a, void *stre
 // LDS, so 3 * n_runs * ceil(kblocks / 4) * 64 must fit that; mt 1 or 4.
 constexpr uint32_t kRawInputLds = 24576;
 int launch_rows_raw(int mt, const RowsArgs &a, void *stream);
+// The standalone row over a packed matrix with many rows (one segment,
+// fragment-major digit planes of at most 128 runs, kblocks a multiple of
+// kStreamBlockMultiple): persistent workgroups, see fpi8_rows_stream.hip.
+// Worth it from stream_min_rows() rows on (every wave gets a 64-row tile).
+constexpr uint32_t kStreamBlockMultiple = 8;
+uint32_t stream_min_rows();
+int launch_rows_stream(const RowsArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_attention_tail(const AttnTailArgs &a, void *stream);
 // Packs a rows x cols byte matrix into tiles of 16 rows x 64 columns, tile

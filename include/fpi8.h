@@ -336,6 +336,16 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
                          uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                          void *d_work, uint64_t work_len, void *stream);
 
+/* Timing of the standalone row for measurement: while enabled, the
+ * row-kernel launch of every fpi8_matrix_rows / fpi8_matrix_rows_packed call
+ * (not the launch that splits the inputs into digits) is bracketed by HIP
+ * events on the call's stream.  fpi8_matrix_rows_timing returns the summed
+ * milliseconds and the launch count since the last enable (it synchronizes
+ * on the recorded events).  Not for calls made from several threads at
+ * once while enabled. */
+int32_t fpi8_matrix_rows_set_timing(int32_t enable);
+int32_t fpi8_matrix_rows_timing(double *total_ms, uint64_t *launches);
+
 /* The same matrix prepared once for many calls: its bytes packed into tiles
  * of 16 rows x 64 columns (bytes past the last row or column are 128, the
  * weight 0), the operand layout the matrix cores read, so that every load of
