@@ -736,6 +736,49 @@ static int32_t run_phase(const model_t *m, const mat_t *mats, run_t *r, uint64_t
     uint32_t h = rd32(st + H_ROW);
     attn_cursor ac = {rd32(st + H_STAGE), rd32(st + H_INDEX), (int64_t)rd64(st + H_MAXSCORE),
                       rd64(st + H_SUM)};
+    /* When the budget covers every remaining head whole, the heads may run
+     * on several threads: each head's scores, exponentials, probabilities
+     * and outputs are its own (the shared scores buffer is only scratch
+     * between them), so every word is still computed whole, in the same
+     * order.  Heads other than the last use a scratch buffer of their own;
+     * the last one leaves its probabilities, largest score and sum in the
+     * state, as the head-by-head walk does. */
+    const uint64_t per_head = 3ull * (t + 1) + c->head;
+    if (g_threads > 1 && ac.stage == 0 && ac.index == 0 && h + 1 < c->heads &&
+        *budget >= (uint64_t)(c->heads - h) * per_head) {
+      int64_t *scratch = (int64_t *)malloc(sizeof(int64_t) * (uint64_t)(t + 1) * (uint64_t)g_threads);
+      if (scratch) {
+        int64_t last_max = 0;
+        uint64_t last_sum = 0;
+        const uint32_t h0 = h;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
+        for (uint32_t hh = h0; hh < c->heads; hh++) {
+#ifdef _OPENMP
+          const int tid = omp_get_thread_num();
+#else
+          const int tid = 0;
+#endif
+          const uint32_t kh = hh / group;
+          int64_t *sc = hh + 1 == c->heads ? r->scores : scratch + (uint64_t)tid * (t + 1);
+          attn_cursor hc = {0, 0, 0, 0};
+          while (!attention_unit(&r->w2[hh * c->head], &r->keys[cache_index(c, cachepos, l, kh, 0, 0)],
+                                 &r->values[cache_index(c, cachepos, l, kh, 0, 0)], t + 1, c->head,
+                                 c->head, m->inv, m->exp_tab, sc, &r->w3[hh * c->head], &hc)) {
+          }
+          if (hh + 1 == c->heads) {
+            last_max = hc.max;
+            last_sum = hc.sum;
+          }
+        }
+        free(scratch);
+        *budget -= (uint64_t)(c->heads - h) * per_head;
+        h = c->heads;
+        ac.stage = 0;
+        ac.index = 0;
+        ac.max = last_max;
+        ac.sum = last_sum;
+      }
+    }
     while (h < c->heads && *budget > 0) {
       const uint32_t kh = h / group;
       const int32_t *K = &r->keys[cache_index(c, cachepos, l, kh, 0, 0)];

@@ -324,23 +324,55 @@ def test_long_context_attention():
 
 def test_full_context_score_buffer():
     # A run whose cache spans the whole 8192-entry context (the long-context
-    # workload's): attention keeps 8192 scores in LDS, the largest buffer.
-    # The first 4003 positions (4000 prompt ids, 3 generated) are checked.
+    # workload's): 8192 prompt ids and one generated token, so the last
+    # position attends over all 8192 cached positions and attention keeps
+    # 8192 scores in LDS, the largest buffer.  Checked halfway and at the end.
     shape = Shape(128, 256, 1, 1, 1, 300, 8192)
     say("full 8192 context")
     blob = Bl.build_blob(shape, 26)
-    runs = [(W.prompt_ids(shape.vocab, 4000, 126, 0), 4193, 0, 1),
+    runs = [(W.prompt_ids(shape.vocab, 8192, 126, 0), 1, 0, 1),
             (W.prompt_ids(shape.vocab, 100, 126, 1), 3, 0, 2)]
     O.set_threads(16)
     pair = Pair(shape, blob, runs)
     try:
-        pair.turn(2000)
+        pair.turn(4096)
         pair.compare()
-        pair.turn(2003)
+        pair.turn(4096)
         pair.compare()
+        info = O.state_info(pair.ref[0])[1]
+        assert info["position"] == 8192 and info["generated"] == 1 and info["complete"]
     finally:
         pair.model.close()
         O.set_threads(1)
+
+
+def test_argmax_ties_across_sampling_chunks():
+    # Classifier rows repeat with period 7 (weights and scales), so every
+    # logit value occurs at indices k, k + 7, k + 14, ... spread over all of
+    # the sampler's per-thread chunks: at temperature zero the lowest index
+    # of the largest value must win ("Sampling": lowest index on ties), and
+    # above zero the draw walks the tied entries in index order.  A second
+    # model repeats its rows with period 300, so tied maxima sit in chunks
+    # far apart.
+    for period, vocab in ((7, 1000), (300, 32000)):
+        shape = Shape(64, 172, 1, 4, 4, vocab, 32)
+        say(f"argmax ties, period {period}, vocab {vocab}")
+        blob = Bl.build_blob(shape, 40 + period)
+        Wc, Sc = Bl.matrix_view(blob, shape, Bl.KIND_CLS)
+        for r in range(period, vocab):
+            Wc[r] = Wc[r % period]
+            Sc[r] = Sc[r % period]
+        runs = [(W.prompt_ids(vocab, 3 + r % 4, 50 + period, r), 6, (0, 0, 65536, 45000)[r % 4],
+                 r + 1) for r in range(8)]
+        pair = run_pair(shape, blob, runs, [1, 2, 100])
+        for r, (ids, mx, t, _) in enumerate(runs):
+            st = pair.ref[r]
+            lay = O.state_layout(shape.as_tuple(), len(ids), mx)
+            n = O.state_info(st)[1]["generated"]
+            toks = st[lay["out"]: lay["out"] + 4 * n].view(np.uint32)
+            assert n > 0
+            if t == 0:  # every greedy token is the first of its tied maxima
+                assert np.all(toks < period), (period, toks)
 
 
 @pytest.mark.parametrize("name", ["1.1B-shaped-d2048-L22", "7B-shaped-d4096-L32",

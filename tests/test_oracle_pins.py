@@ -182,6 +182,32 @@ def test_rows_threads_do_not_change_results():
     assert np.array_equal(y1, y4)
 
 
+def test_attention_threads_do_not_change_results():
+    # The heads of a layer run on several threads when a turn covers them
+    # whole; every state word (outputs, the scores buffer, the cursor's
+    # largest score and sum) is the one-thread walk's, with grouped heads,
+    # after cuts inside attention and at T > 0.
+    shape = Shape(96, 160, 2, 8, 2, 300, 64)
+    blob = B.build_blob(shape, 31)
+    cfg = shape.as_tuple()
+    for ids_n, mx, temp, seed in ((40, 6, 0, 3), (9, 20, 65536, 5)):
+        ids = W.prompt_ids(shape.vocab, ids_n, 77, seed)
+        outs = []
+        for threads in (1, 6):
+            O.set_threads(threads)
+            e, st = O.init_state(cfg, ids, mx, temp, seed)
+            assert e == 0
+            # a turn of units that stops inside the first layer's attention
+            # (sequential from there), then whole positions
+            assert O.turn_units(blob, st, 4 + 96 * 3 + 3 * 4) == 0
+            assert O.turn(blob, st, 3) == 0
+            outs.append(st.copy())
+            assert O.run_to_end(blob, st) == 0
+            outs.append(st.copy())
+        O.set_threads(1)
+        assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+
+
 # --------------------------------------------------------------------------
 # Phase 8, rotary
 
