@@ -37,7 +37,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_timing",
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
            "fpi8_matrix_pack", "fpi8_matrix_rows_packed", "fpi8_matrix_rows_set_timing",
-           "fpi8_matrix_rows_timing")
+           "fpi8_matrix_rows_timing", "fpi8_matrix_rows_packed_noalloc")
 
 
 class fpi8_info(C.Structure):
@@ -102,6 +102,8 @@ def lib():
             "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
                                                     _P, _P, C.c_uint64, _P]),
             "fpi8_matrix_rows_set_timing": (C.c_int32, [C.c_int32]),
+            "fpi8_matrix_rows_packed_noalloc": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P,
+                                                            C.c_uint32, _P, _P]),
             "fpi8_matrix_rows_timing": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_uint64)]),
         }
         for name, (res, args) in sig.items():
@@ -331,6 +333,17 @@ def fpi8_engine_timing(engine, kernel: int):
     n = C.c_uint64(0)
     e = lib().fpi8_engine_timing(engine, kernel, C.byref(ms), C.byref(n))
     return e, ms.value, n.value
+
+
+NOALLOC_MAX_BATCH = 128
+NOALLOC_MAX_COLS = 16384
+
+
+def fpi8_matrix_rows_packed_noalloc(d_P, d_scale, rows: int, cols: int, d_x, batch: int, d_y,
+                                    stream=None) -> int:
+    return lib().fpi8_matrix_rows_packed_noalloc(_dev_ptr(d_P), _dev_ptr(d_scale), rows, cols,
+                                                 _dev_ptr(d_x), batch, _dev_ptr(d_y),
+                                                 _stream_ptr(stream))
 
 
 def fpi8_matrix_rows_set_timing(enable: bool) -> int:

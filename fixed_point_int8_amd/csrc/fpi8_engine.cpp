@@ -795,12 +795,14 @@ int32_t fpi8_matrix_pack(const uint8_t *d_W, uint32_t rows, uint32_t cols, uint8
 
 }  // extern "C"
 
-namespace {
+namespace fpi8 {
 
 // The standalone row over row-major weights (d_W) or packed tiles (d_P).
 int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
                 uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y, void *d_work,
-                uint64_t work_len, void *stream) {
+                uint64_t work_len, void *stream, bool timed) {
+  Timer untimed;  // no events: an empty timer that is off
+  Timer &tm = timed ? g_rows_timer : untimed;
   if ((!d_W && !d_P) || !d_scale || !d_x || !d_y || !d_work || rows == 0 || cols == 0 ||
       batch == 0 || cols > 65536 || batch > 65536)
     return FPI8_ERR_ARGUMENT;
@@ -852,7 +854,7 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
     a.oflag_seq = seq;
     a.compact = 0;
     a.chunks = 1;
-    TimedLaunch t(g_rows_timer, s);
+    TimedLaunch t(tm, s);
     return launch_rows_stream(a, s);
   }
 
@@ -865,7 +867,7 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
       a.ntiles = p.tiles;
       a.wave_rows = 1;
       a.chunks = p.chunks;
-      TimedLaunch t(g_rows_timer, s);
+      TimedLaunch t(tm, s);
       return launch_rows_raw(p.mt, a, s);
     }
   }
@@ -891,11 +893,11 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
   a.ntiles = p.tiles;
   a.wave_rows = p.kind ? (uint32_t)p.wr : 1u;
   a.chunks = p.chunks;
-  TimedLaunch t(g_rows_timer, s);
+  TimedLaunch t(tm, s);
   return launch_rows(EPI_RAW, p.kind, p.mt, p.bt, a, s);
 }
 
-}  // namespace
+}  // namespace fpi8
 
 extern "C" {
 
@@ -903,14 +905,16 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
                          uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                          void *d_work, uint64_t work_len, void *stream) {
   if (!d_W) return FPI8_ERR_ARGUMENT;
-  return matrix_rows(d_W, nullptr, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream);
+  return fpi8::matrix_rows(d_W, nullptr, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream,
+                           true);
 }
 
 int32_t fpi8_matrix_rows_packed(const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
                                 uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                                 void *d_work, uint64_t work_len, void *stream) {
   if (!d_P) return FPI8_ERR_ARGUMENT;
-  return matrix_rows(nullptr, d_P, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream);
+  return fpi8::matrix_rows(nullptr, d_P, d_scale, rows, cols, d_x, batch, d_y, d_work, work_len, stream,
+                           true);
 }
 
 }  // extern "C"

@@ -256,6 +256,12 @@ int launch_rows_raw(int mt, const RowsArgs &a, void *stream);
 constexpr uint32_t kStreamBlockMultiple = 8;
 uint32_t stream_min_rows();
 int launch_rows_stream(const RowsArgs &a, void *stream);
+// The standalone row (fpi8_matrix_rows / fpi8_matrix_rows_packed) over a
+// caller's workspace; `timed` lets fpi8_matrix_rows_set_timing bracket its
+// row-kernel launch with events.  Allocates nothing.
+int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
+                uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y, void *d_work,
+                uint64_t work_len, void *stream, bool timed);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_attention_tail(const AttnTailArgs &a, void *stream);
 // Packs a rows x cols byte matrix into tiles of 16 rows x 64 columns, tile

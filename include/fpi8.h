@@ -361,6 +361,25 @@ int32_t fpi8_matrix_rows_packed(const uint8_t *d_P, const uint32_t *d_scale, uin
                                 uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                                 void *d_work, uint64_t work_len, void *stream);
 
+/* ---- The standalone row for callers that cannot allocate ---------------
+ * For code that may not call hipMalloc: work under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The same call as
+ * fpi8_matrix_rows_packed, with the same result and errors, but its
+ * workspace is a device array the library holds for each GPU (taken the
+ * first time the call runs with that GPU current, kept until the process
+ * ends), so the call allocates nothing.  Limits: at most
+ * FPI8_NOALLOC_MAX_BATCH inputs of at most FPI8_NOALLOC_MAX_COLS columns
+ * (the array is FPI8_NOALLOC_WORKSPACE_BYTES); beyond them error 102.  All
+ * calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be made.
+ * Runs on `stream` (the null stream if NULL) and does not synchronize. */
+#define FPI8_NOALLOC_MAX_BATCH 128u
+#define FPI8_NOALLOC_MAX_COLS 16384u
+#define FPI8_NOALLOC_WORKSPACE_BYTES (256u + 3u * 128u * 16384u)
+int32_t fpi8_matrix_rows_packed_noalloc(const uint8_t *d_P, const uint32_t *d_scale, uint32_t rows,
+                                        uint32_t cols, const int64_t *d_x, uint32_t batch,
+                                        int64_t *d_y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
