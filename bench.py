@@ -279,6 +279,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--workload", default="7B-shaped-d4096-L32")
+    ap.add_argument("--only-sweep", action="store_true",
+                    help="only the standalone 4096-column row sweep and the device copy (for "
+                         "profiler runs of the row kernel); prints their JSON")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel itself instead of replaying a recorded position "
                          "(for profilers that cannot follow graph launches)")
@@ -289,6 +292,11 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.only_sweep:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        print(json.dumps({"hbm_copy_GB/s": copy_bandwidth(torch, 1 << 28),
+                          "row_sweep_4096": row_sweep(torch)}), flush=True)
+        return
     import workloads as Wl
     from workloads import blob as Bl
     from fixed_point_int8_amd import binding as B

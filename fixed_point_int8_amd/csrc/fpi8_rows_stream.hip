@@ -39,10 +39,12 @@ namespace fpi8 {
 
 namespace {
 
-// The exact path (a cold path, kept out of line so its registers do not
-// add to the streaming loop's): y of every row and run this lane holds in
-// the tile, from 64-bit sums over the packed bytes.
-__device__ __attribute__((noinline)) void stream_exact(const RowsArgs &a, uint32_t ptile0, int mt_n, int bt_n,
+// The exact path (a cold path; written as one output at a time, so that its
+// registers stay below the streaming loop's): y of every row and run this
+// lane holds in the tile, from 64-bit sums over the packed bytes.  Inlined:
+// a call would give the kernel a stack, whose scratch setup cost about 5%
+// of a launch over the stacked 4096-column pool.
+__device__ __forceinline__ void stream_exact(const RowsArgs &a, uint32_t ptile0, int mt_n, int bt_n,
                                                        int li, int lg) {
   const Seg &sg = a.seg[0];
   for (int mt = 0; mt < mt_n; mt++)
