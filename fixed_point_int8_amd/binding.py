@@ -37,7 +37,8 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_engine_timing",
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
            "fpi8_matrix_pack", "fpi8_matrix_rows_packed", "fpi8_matrix_rows_set_timing",
-           "fpi8_matrix_rows_timing", "fpi8_matrix_rows_packed_noalloc")
+           "fpi8_matrix_rows_timing", "fpi8_matrix_rows_packed_noalloc", "fpi8_plan_turn",
+           "fpi8_quote_turns")
 
 
 class fpi8_info(C.Structure):
@@ -48,6 +49,12 @@ class fpi8_info(C.Structure):
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+class fpi8_turn_plan(C.Structure):
+    _fields_ = [("sections", C.c_uint32 * 2), ("section_count", C.c_uint32),
+                ("estimated_cu", C.c_uint32), ("max_generated", C.c_uint32),
+                ("ends_with_draw", C.c_uint32), ("units", C.c_uint64)]
 
 
 _P = C.c_void_p
@@ -102,6 +109,8 @@ def lib():
             "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
                                                     _P, _P, C.c_uint64, _P]),
             "fpi8_matrix_rows_set_timing": (C.c_int32, [C.c_int32]),
+            "fpi8_plan_turn": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.POINTER(fpi8_turn_plan)]),
+            "fpi8_quote_turns": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.POINTER(C.c_uint64)]),
             "fpi8_matrix_rows_packed_noalloc": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P,
                                                             C.c_uint32, _P, _P]),
             "fpi8_matrix_rows_timing": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_uint64)]),
@@ -333,6 +342,23 @@ def fpi8_engine_timing(engine, kernel: int):
     n = C.c_uint64(0)
     e = lib().fpi8_engine_timing(engine, kernel, C.byref(ms), C.byref(n))
     return e, ms.value, n.value
+
+
+def fpi8_plan_turn(section_zero: np.ndarray, state: np.ndarray):
+    """(error, plan dict) of the next turn of the run in a host state."""
+    p = fpi8_turn_plan()
+    e = lib().fpi8_plan_turn(_np_ptr(section_zero), section_zero.size, _np_ptr(state), state.size,
+                             C.byref(p))
+    return e, {"sections": list(p.sections)[:p.section_count], "estimated_cu": p.estimated_cu,
+               "max_generated": p.max_generated, "units": p.units,
+               "ends_with_draw": p.ends_with_draw}
+
+
+def fpi8_quote_turns(section_zero: np.ndarray, state: np.ndarray):
+    n = C.c_uint64(0)
+    e = lib().fpi8_quote_turns(_np_ptr(section_zero), section_zero.size, _np_ptr(state), state.size,
+                               C.byref(n))
+    return e, n.value
 
 
 NOALLOC_MAX_BATCH = 128

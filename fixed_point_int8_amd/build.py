@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libfpi8.so")
 OBJ_DIR = os.path.join(os.path.dirname(HERE), "_build", "fpi8")
 SOURCES = ["csrc/fpi8_host.cpp", "csrc/fpi8_engine.cpp", "csrc/fpi8_tokenizer.cpp",
-           "csrc/fpi8_pages.cpp", "csrc/fpi8_charges.cpp", "csrc/fpi8_kernels.hip",
+           "csrc/fpi8_pages.cpp", "csrc/fpi8_charges.cpp", "csrc/fpi8_planner.cpp",
+           "csrc/fpi8_kernels.hip",
            "csrc/fpi8_rows_stream.hip", "csrc/fpi8_noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          # No packed-FP32 instructions in device code.  Only the device pass

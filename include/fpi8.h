@@ -336,6 +336,48 @@ int32_t fpi8_matrix_rows(const uint8_t *d_W, const uint32_t *d_scale, uint32_t r
                          uint32_t cols, const int64_t *d_x, uint32_t batch, int64_t *d_y,
                          void *d_work, uint64_t work_len, void *stream);
 
+/* ---- The turn planner ("The turn planner", "Compute costs") -----------
+ * A turn is charged 18,000 compute units, then chunks of work (each 160 plus
+ * its own charges from "Compute costs"), until the next chunk does not fit
+ * what is left of 1,350,000, or needs a third matrix section, or the run is
+ * complete (max tokens; a stop token ends a run sooner than planned).  A
+ * chunk is a run of rows of one matrix, of units of one attention stage of
+ * one head, of vocabulary entries of one sampling pass, or one whole vector
+ * operation; it takes as many units as fit.  Units are those of
+ * fpi8_turn_units, so the planned turn of a state runs as
+ * fpi8_turn_units(..., plan.units, ...).  Readings where the page is
+ * silent: the 18,000 count against the 1,350,000; a chunk continuing an
+ * item from an earlier turn pays its setup and 160 again; the chunk that
+ * ends a sampling pass carries its 4,000; matrix chunks and the embedding
+ * need their matrix's section (the artifact's matrix descriptors), all else
+ * section zero alone; above temperature zero three passes, each ending with
+ * the 4,000, and a turn ends with the chunk that ends a draw pass: the draw
+ * stops at the entry its remainder falls inside, known only when it runs,
+ * so the plan charges every entry left (an upper bound), counts them in
+ * units and sets ends_with_draw; such a turn runs as fpi8_turn(..., 1, ...)
+ * (which finishes the position), every other one as a turn of its units.
+ *
+ * fpi8_plan_turn plans the next turn of the run in h_state (host copy of a
+ * state, 8-byte aligned) over an artifact whose section zero is
+ * h_section_zero: the compute units charged, the matrix sections read in
+ * the order reached (section zero left out), the most tokens it completes
+ * and the units of work it runs.  A complete run gives an all-zero plan.
+ * fpi8_quote_turns counts the turns the run takes from its cursor to max
+ * tokens.  Errors: 2 (section zero unreadable), 3 (bad state), 4 (a null
+ * pointer), 1 (a single unit of work larger than a turn). */
+typedef struct {
+  uint32_t sections[2];
+  uint32_t section_count;
+  uint32_t estimated_cu;
+  uint32_t max_generated;
+  uint32_t ends_with_draw;  /* 1: the turn ends with a draw pass (see above) */
+  uint64_t units;
+} fpi8_turn_plan;
+int32_t fpi8_plan_turn(const uint8_t *h_section_zero, uint64_t section_zero_len, const uint8_t *h_state,
+                       uint64_t state_len, fpi8_turn_plan *out);
+int32_t fpi8_quote_turns(const uint8_t *h_section_zero, uint64_t section_zero_len, const uint8_t *h_state,
+                         uint64_t state_len, uint64_t *turns);
+
 /* Timing of the standalone row for measurement: while enabled, the
  * row-kernel launch of every fpi8_matrix_rows / fpi8_matrix_rows_packed call
  * (not the launch that splits the inputs into digits) is bracketed by HIP

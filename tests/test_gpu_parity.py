@@ -424,6 +424,45 @@ def test_full_size_7b_longer_prompts():
         O.set_threads(1)
 
 
+def test_planned_turns():
+    # Turns as the planner plans them ("The turn planner"): each turn runs
+    # the planned units of work (or finishes the position when it ends with
+    # a draw), the GPU state equals the oracle's after every turn, and the
+    # run takes the quoted number of turns when it reaches max tokens.
+    from oracle import planner as PL
+    shape = Shape(96, 160, 3, 8, 2, 300, 64)
+    blob = Bl.build_blob(shape, 61)
+    s0 = np.ascontiguousarray(Bl.section_zero(blob))
+    for temp in (0, 45000):
+        say(f"planned turns, temperature {temp}")
+        runs = [(W.prompt_ids(shape.vocab, 9, 62, temp), 7, temp, 5)]
+        pair = Pair(shape, blob, runs)
+        try:
+            quote = PL.quote_turns(s0, pair.ref[0])
+            e, q = B.fpi8_quote_turns(s0, pair.ref[0])
+            assert e == 0 and q == quote
+            turns = 0
+            while True:
+                e, plan = B.fpi8_plan_turn(s0, pair.ref[0])
+                assert e == 0
+                if plan["units"] == 0:
+                    break
+                if plan["ends_with_draw"]:
+                    pair.turn(1)
+                else:
+                    e, errs = pair.batch.turn_units(pair.model, plan["units"])
+                    assert e == 0 and not any(errs), (e, errs)
+                    assert O.turn_units(blob, pair.ref[0], plan["units"]) == 0
+                pair.compare()
+                turns += 1
+            info = O.state_info(pair.ref[0])[1]
+            assert info["complete"]
+            if info["generated"] == 7:
+                assert turns == quote
+        finally:
+            pair.model.close()
+
+
 def test_full_size_units():
     # Turns of unit budgets at the 1.1B shape and its batch width: the
     # budgets stop runs inside matrices, attention stages and sampling
