@@ -38,7 +38,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
            "fpi8_matrix_pack", "fpi8_matrix_rows_packed", "fpi8_matrix_rows_set_timing",
            "fpi8_matrix_rows_timing", "fpi8_matrix_rows_packed_noalloc", "fpi8_plan_turn",
-           "fpi8_quote_turns")
+           "fpi8_quote_turns", "fpi8_turn_bind", "fpi8_turn_async")
 
 
 class fpi8_info(C.Structure):
@@ -109,6 +109,8 @@ def lib():
             "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
                                                     _P, _P, C.c_uint64, _P]),
             "fpi8_matrix_rows_set_timing": (C.c_int32, [C.c_int32]),
+            "fpi8_turn_bind": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, _P, _P]),
+            "fpi8_turn_async": (C.c_int32, [_P, C.c_uint32, _P, _P]),
             "fpi8_plan_turn": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.POINTER(fpi8_turn_plan)]),
             "fpi8_quote_turns": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.POINTER(C.c_uint64)]),
             "fpi8_matrix_rows_packed_noalloc": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P,
@@ -209,6 +211,18 @@ def fpi8_turn(engine, d_states, state_stride: int, n_runs: int, max_positions: i
     e = lib().fpi8_turn(engine, _dev_ptr(d_states), state_stride, n_runs, max_positions,
                         _stream_ptr(stream), _np_ptr(errs))
     return e, errs
+
+
+def fpi8_turn_bind(engine, d_states, state_stride: int, n_runs: int, stream=None):
+    errs = np.zeros(n_runs, dtype=np.int32)
+    e = lib().fpi8_turn_bind(engine, _dev_ptr(d_states), state_stride, n_runs, _stream_ptr(stream),
+                             _np_ptr(errs))
+    return e, errs
+
+
+def fpi8_turn_async(engine, max_positions: int, stream=None, d_run_errors=None) -> int:
+    return lib().fpi8_turn_async(engine, max_positions, _stream_ptr(stream),
+                                 None if d_run_errors is None else _dev_ptr(d_run_errors))
 
 
 def fpi8_turn_phases(engine, d_states, state_stride: int, n_runs: int, max_phases: int,

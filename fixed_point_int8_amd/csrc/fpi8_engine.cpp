@@ -77,6 +77,11 @@ struct fpi8_engine {
   uint32_t graph_groups = 0;
   hipStream_t side_stream = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // The arena bound for queued turns (fpi8_turn_bind / fpi8_turn_async):
+  // its run descriptors are on the device; `left` bounds the positions any
+  // run still has; `resume`: some run stood inside a position at the bind.
+  uint8_t *bound_states = nullptr;
+  uint32_t bound_runs = 0, bound_left = 0, bound_resume = 0;
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -603,9 +608,10 @@ void stop_of(const Cfg &c, uint32_t n_ids, uint32_t cachepos, uint32_t pos, uint
 // where the draw pass shows its length).
 int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
              uint32_t max_positions, uint32_t max_phases, uint64_t max_units, void *stream,
-             int32_t *h_run_errors) {
+             int32_t *h_run_errors, bool bind_only = false) {
   if (!e || !d_states || n_runs == 0 || n_runs > e->max_runs) return FPI8_ERR_ARGUMENT;
   hipStream_t s = (hipStream_t)stream;
+  e->bound_states = nullptr;  // this turn replaces the device run descriptors
   if ((reinterpret_cast<uintptr_t>(d_states) & 7) != 0 || (stride & 7) != 0 || stride < 128) {
     if (h_run_errors)
       for (uint32_t b = 0; b < n_runs; b++) h_run_errors[b] = FPI8_INVALID_STATE;
@@ -676,6 +682,23 @@ int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs
                                  hipMemcpyHostToDevice, s))) ||
       (r = hip_ok(hipMemcpyAsync(e->d_run_err, e->h_err, 4ull * n_runs, hipMemcpyHostToDevice, s))))
     return r;
+  if (bind_only) {
+    // Queued turns advance whole positions: bound the positions any run has left.
+    uint32_t left = 0;
+    for (uint32_t b = 0; b < n_runs; b++)
+      if (e->h_runs[b].valid) left = std::max(left, count[b]);
+    if ((r = hip_ok(hipStreamSynchronize(s)))) return r;  // the pinned descriptors are copied
+    e->bound_states = d_states;
+    e->bound_runs = n_runs;
+    e->bound_left = left;
+    e->bound_resume = resume;
+    int32_t first_err = 0;
+    for (uint32_t b = 0; b < n_runs; b++) {
+      if (h_run_errors) h_run_errors[b] = e->h_err[b];
+      if (!first_err && e->h_err[b]) first_err = e->h_err[b];
+    }
+    return first_err;
+  }
   if ((r = launch_turn_start(d_states, e->d_runs, n_runs, s))) return r;
   bool timing = false;
   for (const Timer &t : e->timers) timing = timing || t.on;
@@ -714,6 +737,38 @@ extern "C" {
 int32_t fpi8_turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,
                   uint32_t max_positions, void *stream, int32_t *h_run_errors) {
   return turn(e, d_states, stride, n_runs, max_positions, 0xFFFFFFFFu, ~0ull, stream, h_run_errors);
+}
+
+int32_t fpi8_turn_bind(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs, void *stream,
+                       int32_t *h_run_errors) {
+  return turn(e, d_states, stride, n_runs, 0xFFFFFFFFu, 0xFFFFFFFFu, ~0ull, stream, h_run_errors, true);
+}
+
+int32_t fpi8_turn_async(fpi8_engine *e, uint32_t max_positions, void *stream, int32_t *d_run_errors) {
+  if (!e || !e->bound_states) return FPI8_ERR_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *states = e->bound_states;
+  const uint32_t n_runs = e->bound_runs;
+  const uint32_t steps = std::min(max_positions, e->bound_left);
+  e->bound_left -= steps;
+  int r;
+  if ((r = launch_turn_start(states, e->d_runs, n_runs, s))) return r;
+  bool timing = false;
+  for (const Timer &t : e->timers) timing = timing || t.on;
+  for (uint32_t k = 0; k < steps; k++) {
+    const uint32_t partial = k == 0 ? e->bound_resume : 0;
+    if (!partial && !timing && e->use_graph) {
+      if ((r = step_graph(e, states, n_runs))) return r;
+      if ((r = hip_ok(hipGraphLaunch(e->graph, s)))) return r;
+    } else if ((r = step(e, states, n_runs, s, partial))) {
+      return r;
+    }
+    e->bound_resume = 0;
+  }
+  if (d_run_errors &&
+      (r = hip_ok(hipMemcpyAsync(d_run_errors, e->d_run_err, 4ull * n_runs, hipMemcpyDeviceToDevice, s))))
+    return r;
+  return 0;
 }
 
 int32_t fpi8_turn_phases(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs,

@@ -261,6 +261,25 @@ int32_t fpi8_turn(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride,
                   uint32_t n_runs, uint32_t max_positions, void *stream,
                   int32_t *h_run_errors);
 
+/* Queued turns: turns that a caller can issue back to back on a stream
+ * without waiting ("The Rust API", turn, over a batch of runs).
+ * fpi8_turn_bind reads every run's header once (it synchronizes the
+ * stream), checks it as fpi8_turn does (per-run errors into h_run_errors,
+ * may be NULL; returns the first) and keeps the batch's run descriptors on
+ * the device.  Each fpi8_turn_async then advances every run of the bound
+ * batch by up to max_positions whole positions (the first one, after a
+ * bind at a cursor inside a position, finished from there) with launches
+ * only: no host transfer and no synchronization.  When d_run_errors
+ * (device, n_runs int32) is not NULL, the per-run error numbers as they
+ * stand after the turn's launches are copied there, on the stream.  Returns
+ * 102 when no batch is bound, 100 on a launch failure, else 0.  A batch
+ * stays bound until the next fpi8_turn_bind or a turn of any other kind on
+ * this engine; the states must not be changed in between except by queued
+ * turns. */
+int32_t fpi8_turn_bind(fpi8_engine *engine, uint8_t *d_states, uint64_t state_stride, uint32_t n_runs,
+                       void *stream, int32_t *h_run_errors);
+int32_t fpi8_turn_async(fpi8_engine *engine, uint32_t max_positions, void *stream, int32_t *d_run_errors);
+
 /* A turn of at most max_phases phases of each run (counted as "The forward
  * pass, in order" lists them: 3, 4-16 per layer, 17-19 where a token is
  * generated), as many positions as they reach.  Each run stops at the last

@@ -463,6 +463,46 @@ def test_planned_turns():
             pair.model.close()
 
 
+def test_queued_turns():
+    # Turns queued back to back on a stream (fpi8_turn_bind, then
+    # fpi8_turn_async with no synchronization in between), from a cursor
+    # inside a position: the states equal the oracle's, and the per-run
+    # errors land in a device array (a run with a broken header keeps its
+    # error 3 and is not advanced).
+    torch = require_gpu()
+    shape = W.SMALL_SHAPES["gqa"]
+    blob = Bl.build_blob(shape, 71)
+    runs = [(W.prompt_ids(shape.vocab, 3 + r, 72, r), 6, (0, 65536)[r % 2], r + 1) for r in range(5)]
+    pair = Pair(shape, blob, runs)
+    try:
+        # stop every run inside a position first
+        e, errs = pair.batch.turn_units(pair.model, 777)
+        assert e == 0
+        for i in range(len(runs)):
+            assert O.turn_units(blob, pair.ref[i], 777) == 0
+        pair.compare()
+        bad = pair.batch.d_states[4 * pair.batch.stride: 4 * pair.batch.stride + 8]
+        bad.fill_(0)  # run 4: not a state
+        stream = torch.cuda.Stream()
+        e, herrs = B.fpi8_turn_bind(pair.model.engine, pair.batch.d_states, pair.batch.stride,
+                                    len(runs), stream)
+        assert e == 3 and list(herrs) == [0, 0, 0, 0, 3]
+        derr = torch.full((len(runs),), -1, dtype=torch.int32, device="cuda")
+        for k in (1, 2, 1, 3):
+            assert B.fpi8_turn_async(pair.model.engine, k, stream, derr) == 0
+        stream.synchronize()
+        assert derr.cpu().tolist() == [0, 0, 0, 0, 3]
+        for i in range(4):
+            for k in (1, 2, 1, 3):  # one turn each, as on the GPU
+                assert O.turn(blob, pair.ref[i], k) == 0
+        pair.compare(range(4))
+        # a turn of another kind unbinds the batch
+        pair.batch.turn(pair.model, 1)
+        assert B.fpi8_turn_async(pair.model.engine, 1, stream, derr) == 102
+    finally:
+        pair.model.close()
+
+
 def test_full_size_units():
     # Turns of unit budgets at the 1.1B shape and its batch width: the
     # budgets stop runs inside matrices, attention stages and sampling
