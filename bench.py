@@ -137,7 +137,9 @@ def row_sweep(torch, reps=5):
       row kernel's own duration comes from HIP events the library records
       around its launch on the call's stream (fpi8_matrix_rows_timing).
     per_matrix: one call per 4096 x 4096 matrix, 48 calls back to back
-      (each a short launch, bound by its ramp rather than by bandwidth)."""
+      (each a short launch, bound by its ramp rather than by bandwidth).
+    valu_vs_mfma: the pooled call at 1, 2 and 4 inputs with the digits on
+      the vector ALU (v_dot4) and on the matrix cores, kernel time of each."""
     from fixed_point_int8_amd import binding as B
     rows1 = cols = 4096
     pool = 48
@@ -216,6 +218,37 @@ def row_sweep(torch, reps=5):
                            "frac": round(alg1 / single_ms / 1e6 / HBM_PEAK_GBS, 4)},
         }
         del x, y, y1, yp, work
+
+    # The same pooled call on the vector ALU (v_dot4 over the same digits,
+    # held in LDS) beside the matrix cores, at the batches the vector-ALU
+    # kernel takes: the arithmetic closer to the HBM roof is the default.
+    cmp = {}
+    for batch in (1, 2, 4):
+        x = (torch.randn((batch, cols), device="cuda", generator=g) * 2.0 * 65536).round().to(torch.int64)
+        n = B.fpi8_matrix_rows_workspace_size(rows, cols, batch)
+        work = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        alg = rows * cols + 4 * rows + 8 * batch * cols + 8 * batch * rows
+        ys, row = [], {}
+        for name, path in (("mfma", B.PATH_MFMA), ("valu", B.PATH_VALU)):
+            y = torch.zeros((batch, rows), dtype=torch.int64, device="cuda")
+            assert B.fpi8_matrix_rows_set_path(path) == 0
+            assert B.fpi8_matrix_rows_packed(Pk, S, rows, cols, x, batch, y, work, n, stream) == 0
+            torch.cuda.synchronize()
+            B.fpi8_matrix_rows_set_timing(True)
+            for _ in range(reps):
+                B.fpi8_matrix_rows_packed(Pk, S, rows, cols, x, batch, y, work, n, stream)
+            e, kern_ms, launches = B.fpi8_matrix_rows_timing()
+            B.fpi8_matrix_rows_set_timing(False)
+            assert e == 0 and launches == reps
+            kern_ms /= launches
+            row[name + "_us"] = round(kern_ms * 1e3, 2)
+            row[name + "_frac"] = round(alg / kern_ms / 1e6 / HBM_PEAK_GBS, 4)
+            ys.append(y)
+        B.fpi8_matrix_rows_set_path(B.PATH_AUTO)
+        assert torch.equal(ys[0], ys[1]), "vector-ALU and matrix-core rows disagree"
+        cmp[str(batch)] = row
+        del x, work, ys
+    out["valu_vs_mfma"] = cmp
     del Pk, S
     torch.cuda.empty_cache()
     return out

@@ -38,7 +38,7 @@ EXPORTS = ("fpi8_blob_check", "fpi8_state_size", "fpi8_state_offsets", "fpi8_ini
            "fpi8_matrix_rows_workspace_size", "fpi8_matrix_rows", "fpi8_matrix_packed_size",
            "fpi8_matrix_pack", "fpi8_matrix_rows_packed", "fpi8_matrix_rows_set_timing",
            "fpi8_matrix_rows_timing", "fpi8_matrix_rows_packed_noalloc", "fpi8_plan_turn",
-           "fpi8_quote_turns", "fpi8_turn_bind", "fpi8_turn_async")
+           "fpi8_quote_turns", "fpi8_turn_bind", "fpi8_turn_async", "fpi8_matrix_rows_set_path")
 
 
 class fpi8_info(C.Structure):
@@ -109,6 +109,7 @@ def lib():
             "fpi8_matrix_rows_packed": (C.c_int32, [_P, _P, C.c_uint32, C.c_uint32, _P, C.c_uint32,
                                                     _P, _P, C.c_uint64, _P]),
             "fpi8_matrix_rows_set_timing": (C.c_int32, [C.c_int32]),
+            "fpi8_matrix_rows_set_path": (C.c_int32, [C.c_int32]),
             "fpi8_turn_bind": (C.c_int32, [_P, _P, C.c_uint64, C.c_uint32, _P, _P]),
             "fpi8_turn_async": (C.c_int32, [_P, C.c_uint32, _P, _P]),
             "fpi8_plan_turn": (C.c_int32, [_P, C.c_uint64, _P, C.c_uint64, C.POINTER(fpi8_turn_plan)]),
@@ -388,6 +389,14 @@ def fpi8_matrix_rows_packed_noalloc(d_P, d_scale, rows: int, cols: int, d_x, bat
 
 def fpi8_matrix_rows_set_timing(enable: bool) -> int:
     return lib().fpi8_matrix_rows_set_timing(1 if enable else 0)
+
+
+# fpi8_matrix_rows_set_path values
+PATH_AUTO, PATH_MFMA, PATH_VALU = 0, 1, 2
+
+
+def fpi8_matrix_rows_set_path(path: int) -> int:
+    return lib().fpi8_matrix_rows_set_path(path)
 
 
 def fpi8_matrix_rows_timing():

@@ -131,6 +131,10 @@ int timer_sum(Timer &t, double *total_ms, uint64_t *launches) {
 // Timing of the standalone row's row-kernel launches (measurement only).
 Timer g_rows_timer;
 
+// Which arithmetic the standalone streaming row uses: 0 automatic (the
+// matrix cores), 1 the matrix cores, 2 the vector ALU where it applies.
+std::atomic<int> g_rows_path{0};
+
 // Launch shape of one row-kernel call.  kind 0: 16 * mt rows and 16 * bt
 // runs per workgroup of four waves, which split the contraction; kind 1:
 // wr * 16 * mt rows (16 * mt for each of wr waves) and 16 * bt runs per
@@ -829,6 +833,12 @@ int32_t fpi8_matrix_rows_timing(double *total_ms, uint64_t *launches) {
   return timer_sum(g_rows_timer, total_ms, launches);
 }
 
+int32_t fpi8_matrix_rows_set_path(int32_t path) {
+  if (path < 0 || path > 2) return FPI8_ERR_ARGUMENT;
+  g_rows_path.store(path);
+  return 0;
+}
+
 // Workspace of the standalone row: the overflow word (256 bytes kept), then the digits.
 uint64_t fpi8_matrix_rows_workspace_size(uint32_t rows, uint32_t cols, uint32_t batch) {
   (void)rows;
@@ -899,7 +909,13 @@ int matrix_rows(const uint8_t *d_W, const uint8_t *d_P, const uint32_t *d_scale,
 
   // Many rows of a packed matrix: the persistent streaming kernel over
   // fragment-major digit planes (one launch for the digits, one for the rows).
+  // On request, up to four inputs take the vector-ALU variant instead (one
+  // launch: its workgroups split the inputs into digits in LDS).
   if (packed && batch <= 128 && kblocks % kStreamBlockMultiple == 0 && rows >= stream_min_rows()) {
+    if (g_rows_path.load() == 2 && stream_valu_fits(kblocks, batch)) {
+      TimedLaunch t(tm, s);
+      return launch_rows_stream_valu(a, s);
+    }
     uint32_t seq = ++calls;
     if (seq == 0) seq = ++calls;
     int r = launch_digits_raw(d_x, batch, cols, planes, kp, bp, 0, flag, seq, s);

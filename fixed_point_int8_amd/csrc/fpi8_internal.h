@@ -255,6 +255,10 @@ int launch_rows_raw(int mt, const RowsArgs &a, void *stream);
 // Worth it from stream_min_rows() rows on (every wave gets a 64-row tile).
 constexpr uint32_t kStreamBlockMultiple = 8;
 uint32_t stream_min_rows();
+// The vector-ALU streaming kernel (1 to 4 inputs, their digits in LDS).
+constexpr uint32_t kStreamValuLds = 147456;
+bool stream_valu_fits(uint32_t kblocks, uint32_t n_runs);
+int launch_rows_stream_valu(const RowsArgs &a, void *stream);
 int launch_rows_stream(const RowsArgs &a, void *stream);
 // The standalone row (fpi8_matrix_rows / fpi8_matrix_rows_packed) over a
 // caller's workspace; `timed` lets fpi8_matrix_rows_set_timing bracket its

@@ -24,6 +24,14 @@
 //    one LDS-only barrier per stage.  For 17 to 128 runs, where the digits
 //    are several times the weight bytes a wave reads.
 //
+//  * k_rows_stream_valu (1 to 4 inputs, on request): the same digits on the
+//    vector ALU instead of the matrix cores, v_dot4_i32_i8 adding four
+//    byte products per instruction, with the inputs' digits resident in LDS
+//    for the whole launch.  It computes the same words; measured over
+//    stacked 4096-column matrices it streams a little slower than the
+//    matrix-core kernel at 1 and 2 inputs and much slower from 4 on, so the
+//    library takes it only when asked to (fpi8_matrix_rows_set_path).
+//
 // A launch whose inputs hold a word beyond three digits takes an exact
 // 64-bit loop instead, so the result is the page's for every input.
 #include <hip/hip_runtime.h>
@@ -354,6 +362,135 @@ __global__ __launch_bounds__(64 * W) void k_rows_stream_shared(RowsArgs a) {
   wait_vm<0>();  // no staging load may still be landing in LDS when the workgroup ends
 }
 
+// The vector-ALU kernel.  Lane l = 16g + i holds row i of each 16-row tile
+// and columns 16g .. 16g+15 of each 64-column block (the packed operand
+// layout), so the 16 lanes of a group read the same 16 digit bytes from LDS
+// (a broadcast).  Every workgroup first splits the NB inputs into their
+// three signed byte digits, [input][digit][column] in LDS (zero past the
+// last column), and notes a word beyond three digits, which sends every
+// wave down the exact loop.  Each wave then walks its tiles as in
+// k_rows_stream, a ring of P weight blocks ahead; per block it adds, for
+// every tile, input and digit, four v_dot4_i32_i8 products into an i32 sum
+// (exact: |sum| <= 2^14 * cols < 2^31).  At the end of a tile the four lane
+// groups' sums of a row are added across lanes and recombined in i64.
+template <int MT, int NB, int P>
+__global__ __launch_bounds__(256) void k_rows_stream_valu(RowsArgs a) {
+  extern __shared__ __align__(16) int8_t dig[];  // [NB][3][kblocks * 64]
+  __shared__ uint32_t over;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const Seg &sg = a.seg[0];
+  const uint32_t nkb = a.kblocks, K = nkb * 64, cols = a.cols;
+  if (tid == 0) over = 0;
+  __syncthreads();
+  bool bad = false;
+  for (uint32_t c = tid; c < NB * (K / 4); c += 256) {
+    const uint32_t r = c / (K / 4), k4 = (c % (K / 4)) * 4;
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (k4 + j >= cols) break;
+      int8_t d0, d1, d2;
+      bad |= !digits3(a.x_raw[(uint64_t)r * cols + k4 + j], d0, d1, d2);
+      w0 |= (uint32_t)(uint8_t)d0 << (8 * j);
+      w1 |= (uint32_t)(uint8_t)d1 << (8 * j);
+      w2 |= (uint32_t)(uint8_t)d2 << (8 * j);
+    }
+    *reinterpret_cast<uint32_t *>(dig + ((uint64_t)r * 3 + 0) * K + k4) = w0;
+    *reinterpret_cast<uint32_t *>(dig + ((uint64_t)r * 3 + 1) * K + k4) = w1;
+    *reinterpret_cast<uint32_t *>(dig + ((uint64_t)r * 3 + 2) * K + k4) = w2;
+  }
+  if (bad) atomicOr(&over, 1u);
+  __syncthreads();
+
+  const uint32_t G = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  if (gw >= a.ntiles) return;
+  const uint32_t my = (a.ntiles - gw + G - 1) / G;  // tiles of this wave
+  const uint32_t last_ptile = (sg.rows - 1) / 16;
+  if (over) {
+    for (uint32_t t = 0; t < my; t++) stream_exact(a, (gw + t * G) * MT, MT, 1, li, lg);
+    return;
+  }
+
+  int acc[MT][NB][3];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int r = 0; r < NB; r++) acc[mt][r][0] = acc[mt][r][1] = acc[mt][r][2] = 0;
+  v4i Wr[P][MT];
+  uint32_t it = 0, ikb = 0;
+  auto issue = [&](int s) {
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t t = it < my ? it : my - 1;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      uint32_t pt = (gw + t * G) * MT + mt;
+      pt = pt < last_ptile ? pt : last_ptile;
+      Wr[s][mt] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i *>(sg.P + ((uint64_t)pt * nkb + ikb) * 1024 + lane * 16));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (++ikb == nkb) {
+      ikb = 0;
+      ++it;
+    }
+  };
+  auto compute = [&](int s, uint32_t kb) {
+    v4i w[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) w[mt] = flip_weights(Wr[s][mt]);
+#pragma unroll
+    for (int r = 0; r < NB; r++)
+#pragma unroll
+      for (int d = 0; d < 3; d++) {
+        const v4i dv = *reinterpret_cast<const v4i *>(dig + ((uint64_t)r * 3 + d) * K + kb * 64 + lg * 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          int c = acc[mt][r][d];
+          c = __builtin_amdgcn_sdot4(w[mt].x, dv.x, c, false);
+          c = __builtin_amdgcn_sdot4(w[mt].y, dv.y, c, false);
+          c = __builtin_amdgcn_sdot4(w[mt].z, dv.z, c, false);
+          c = __builtin_amdgcn_sdot4(w[mt].w, dv.w, c, false);
+          acc[mt][r][d] = c;
+        }
+      }
+  };
+
+#pragma unroll
+  for (int s = 0; s < P; s++) issue(s);
+  for (uint32_t t = 0; t < my; t++) {
+    const uint32_t ptile0 = (gw + t * G) * MT;
+    for (uint32_t kb = 0; kb < nkb; kb += P) {
+#pragma unroll
+      for (int s = 0; s < P; s++) {
+        compute(s, kb + s);
+        issue(s);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const uint32_t row = (ptile0 + mt) * 16 + li;
+      const uint32_t sc = sg.S[row < sg.rows ? row : sg.rows - 1];
+#pragma unroll
+      for (int r = 0; r < NB; r++) {
+        int s3[3];
+#pragma unroll
+        for (int d = 0; d < 3; d++) {
+          int v = acc[mt][r][d];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          s3[d] = v;
+          acc[mt][r][d] = 0;
+        }
+        const int64_t v = (int64_t)s3[0] + ((int64_t)s3[1] << 8) + ((int64_t)s3[2] << 16);
+        if (lg == 0 && row < sg.rows) a.y_raw[(uint64_t)r * sg.rows + row] = wmul(v, (int64_t)sc) >> 24;
+      }
+    }
+  }
+  wait_vm<0>();  // the ring's last (unused) loads land before the wave ends
+}
+
 // ---------------------------------------------------------------------------
 
 namespace {
@@ -390,6 +527,40 @@ int launch_shr(RowsArgs a, hipStream_t s) {
 }  // namespace
 
 uint32_t stream_min_rows() { return (uint32_t)cu_count() * 256u; }
+
+namespace {
+
+template <int NB>
+int launch_valu(RowsArgs a, hipStream_t s) {
+  constexpr int MT = 4, P = 4;
+  const size_t lds = (size_t)NB * 3 * a.kblocks * 64;
+  if (hipFuncSetAttribute((const void *)k_rows_stream_valu<MT, NB, P>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamValuLds) != hipSuccess)
+    return FPI8_ERR_HIP;
+  a.ntiles = (a.seg[0].rows + 16 * MT - 1) / (16 * MT);
+  const uint32_t wgs = std::min<uint32_t>((a.ntiles + 3) / 4, (uint32_t)cu_count());
+  hipLaunchKernelGGL((k_rows_stream_valu<MT, NB, P>), dim3(wgs), dim3(256), lds, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : FPI8_ERR_HIP;
+}
+
+}  // namespace
+
+bool stream_valu_fits(uint32_t kblocks, uint32_t n_runs) {
+  return n_runs >= 1 && n_runs <= 4 && kblocks % 4 == 0 &&
+         (uint64_t)n_runs * 3 * kblocks * 64 <= kStreamValuLds;
+}
+
+int launch_rows_stream_valu(const RowsArgs &a, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.nseg != 1 || !a.seg[0].P || !a.x_raw || !a.y_raw || !stream_valu_fits(a.kblocks, a.n_runs))
+    return FPI8_ERR_ARGUMENT;
+  switch (a.n_runs) {
+    case 1: return launch_valu<1>(a, s);
+    case 2: return launch_valu<2>(a, s);
+    case 3: return launch_valu<3>(a, s);
+    default: return launch_valu<4>(a, s);
+  }
+}
 
 // The launch shapes by batch (measured on MI355X over a pool of 48
 // 4096-column matrices): up to 16 runs, waves of 64 rows with an 8-block

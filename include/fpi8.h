@@ -407,6 +407,20 @@ int32_t fpi8_quote_turns(const uint8_t *h_section_zero, uint64_t section_zero_le
 int32_t fpi8_matrix_rows_set_timing(int32_t enable);
 int32_t fpi8_matrix_rows_timing(double *total_ms, uint64_t *launches);
 
+/* Which arithmetic the standalone row uses over a packed matrix of many rows
+ * ("A matrix row"; the same words either way): 0 (the default) and 1 the
+ * int8 matrix cores, three signed byte digits of each input word; 2 the
+ * vector ALU (v_dot4_i32_i8 over the same digits) for calls it applies to:
+ * a packed matrix that takes the streaming kernel (at least 256 rows per
+ * compute unit, columns filling a multiple of 8 blocks of 64), 1 to 4
+ * inputs, and digits that fit 144 KB of LDS (3 bytes per input and column
+ * rounded up to 512: 49,152 columns for one input, 12,288 for four).
+ * Other calls run as under
+ * 0.  For measuring one arithmetic against the other: on MI355X the matrix
+ * cores stream closer to the HBM roof at every batch.  Process-wide, like
+ * the timing switch.  Error 102 for another value. */
+int32_t fpi8_matrix_rows_set_path(int32_t path);
+
 /* The same matrix prepared once for many calls: its bytes packed into tiles
  * of 16 rows x 64 columns (bytes past the last row or column are 128, the
  * weight 0), the operand layout the matrix cores read, so that every load of

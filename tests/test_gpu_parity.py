@@ -100,6 +100,37 @@ def test_matrix_rows_packed_stream_exact_path(batch):
         O.set_threads(1)
 
 
+# The vector-ALU streaming kernel (fpi8_matrix_rows_set_path(2)): 1 to 4
+# inputs whose digits sit in LDS, v_dot4 over the packed tiles.  Rows past
+# the last full tile, columns inside the last block, the largest column
+# count its LDS holds for four inputs, a word beyond three digits (the exact
+# loop), and five inputs (not taken: the matrix-core kernel runs).
+@pytest.mark.parametrize("rows,cols,batch,big", [
+    (65573, 4066, 1, False), (65536, 1000, 2, False), (65600, 4096, 3, False),
+    (65536, 4096, 4, False), (65536, 12288, 4, False), (65536, 512, 2, True), (65536, 512, 5, False)])
+def test_matrix_rows_packed_stream_valu(rows, cols, batch, big):
+    say(f"matrix_rows_packed stream, vector ALU, {rows}x{cols} batch {batch} big {big}")
+    O.set_threads(16)
+    assert B.fpi8_matrix_rows_set_path(B.PATH_VALU) == 0
+    try:
+        Wm, s, x = W.row_operands(rows, cols, batch, rows + cols * 11 + batch)
+        if big:
+            x[batch - 1, 7] = 2**40 + 5
+            x[0, :64] = W.adversarial_row_inputs(1, 64, batch)[0]
+            Wm[0, :] = 255
+            s[1] = 2**32 - 1
+        assert np.array_equal(gpu_rows_packed(Wm, s, x), O.rows(Wm, s, x))
+    finally:
+        B.fpi8_matrix_rows_set_path(B.PATH_AUTO)
+        O.set_threads(1)
+
+
+def test_matrix_rows_set_path_rejects_unknown():
+    assert B.fpi8_matrix_rows_set_path(3) == 102
+    assert B.fpi8_matrix_rows_set_path(-1) == 102
+    assert B.fpi8_matrix_rows_set_path(B.PATH_AUTO) == 0
+
+
 def gpu_rows(Wm, s, x, work=None):
     torch = require_gpu()
     rows, cols = Wm.shape
