@@ -7,8 +7,9 @@ SiLU, down rows), the final normalization, the classifier rows and sampling.
 The workload is the 7B-shaped model (dim 4096, 32 layers, 32 heads of 128,
 FFN 11008, vocab 32000) with 64 runs of 512 prompt ids each; the prompts
 are prefilled first (untimed), then W warm-up steps and K timed decode
-steps run.  Inputs are seeded and synthetic and already in HBM when the
-timed region starts.
+steps run (by default K covers the rest of the 255-step decode window but
+for 8 kernel-timed steps at its end).  Inputs are seeded and synthetic and
+already in HBM when the timed region starts.
 
 Also measured: the standalone matrix row at 4096 x 4096 for batches of 1,
 8, 32 and 128 input vectors over a pool of distinct matrices larger than the
@@ -305,7 +306,9 @@ def cpu_baseline(blob, shape, name, seconds=12.0, max_positions=64):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="decode steps timed (default: every decode position after the warm-up "
+                         "and before the kernel-timed steps)")
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--kernel-steps", type=int, default=8,
                     help="extra steps after the timed ones, with per-launch kernel timing")
@@ -338,7 +341,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = Wl.by_name(args.workload)
     shape = w.shape
-    if args.warmup + args.steps + args.kernel_steps > w.max_tokens - 1:
+    if args.steps is None:
+        args.steps = w.max_tokens - 1 - args.warmup - args.kernel_steps
+    if args.steps < 1 or args.warmup + args.steps + args.kernel_steps > w.max_tokens - 1:
         raise SystemExit("warmup + steps + kernel steps exceed the decode positions of the workload")
 
     t = time.perf_counter()
@@ -364,9 +369,11 @@ def main():
     log(f"prefill {w.prompt} positions x {w.runs} runs in {prefill_s:.2f} s")
 
     gen_prefill = sum(batch.info(i)["generated"] for i in range(w.runs))
-    # The timed steps sit around the middle of the decode window (positions
-    # prompt .. prompt + max_tokens - 2), where a step reads the window's mean
-    # cache length; the steps before them are untimed (warm-up included).
+    # By default the timed steps are the whole decode window (positions
+    # prompt .. prompt + max_tokens - 2) less the warm-up steps before them
+    # and the kernel-timed steps after them.  A shorter run of steps sits
+    # around the window's middle, where a step reads its mean cache length;
+    # the steps before them are untimed (warm-up included).
     first_dec, last_dec = w.prompt, w.prompt + w.max_tokens - 2
     mid = (first_dec + last_dec) // 2
     start = max(first_dec + args.warmup, mid - args.steps // 2)
@@ -450,7 +457,7 @@ def main():
     if sweep:
         bsel = min(("1", "8", "32"), key=lambda b: sweep[b]["pool"]["frac"])
         pl = sweep[bsel]["pool"]
-        roofline = {"kernel": "k_rows_stream" if int(bsel) <= 16 else "k_rows_stream_shared",
+        roofline = {"kernel": "k_rows_stream_shared",
                     "bound": "hbm", "achieved": pl["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": pl["frac"], "traffic": pl["traffic"],
                     "workload": f"4096-column rows, 48 stacked 4096x4096 matrices, batch {bsel}",

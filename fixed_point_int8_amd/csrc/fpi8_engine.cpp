@@ -99,9 +99,12 @@ struct TimedLaunch {
     on = t.on;
     if (!on) return;
     if (t.used == t.starts.size()) {
+      // Timing only: no system-scope fence when an event is recorded, so
+      // the event pair neither writes back and invalidates the caches around
+      // the timed launch nor adds that cost to its interval.
       hipEvent_t a, b;
-      (void)hipEventCreate(&a);
-      (void)hipEventCreate(&b);
+      (void)hipEventCreateWithFlags(&a, hipEventDisableSystemFence);
+      (void)hipEventCreateWithFlags(&b, hipEventDisableSystemFence);
       t.starts.push_back(a);
       t.stops.push_back(b);
     }

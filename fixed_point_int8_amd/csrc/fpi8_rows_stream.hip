@@ -15,15 +15,10 @@
 //    straight across tile boundaries, so the weight stream never drains
 //    between tiles; the epilogue of a tile overlaps the next tile's loads.
 //  * Weight tiles are read with nontemporal loads (each byte is used once).
-//  * k_rows_stream: every wave owns its own tiles and reads the digit
-//    fragments of its runs itself (they stay in L2); no wave waits for
-//    another.  For up to 16 runs.
 //  * k_rows_stream_shared: the waves of a workgroup walk the same blocks in
 //    lockstep, each owning different rows, and stage the digit fragments
 //    once per workgroup into an LDS ring with direct global-to-LDS loads;
-//    one LDS-only barrier per stage.  For 17 to 128 runs, where the digits
-//    are several times the weight bytes a wave reads.
-//
+//    one LDS-only barrier per stage.  Three to twelve waves by batch.
 //  * k_rows_stream_valu (1 to 4 inputs, on request): the same digits on the
 //    vector ALU instead of the matrix cores, v_dot4_i32_i8 adding four
 //    byte products per instruction, with the inputs' digits resident in LDS
@@ -119,120 +114,12 @@ __device__ __forceinline__ v4i flip_weights(v4i w) {
 
 }  // namespace
 
-// Every wave owns tiles of 16 * MT rows (the wave tiles t = gw, gw + G, ...
-// where gw numbers the waves of the grid and G counts them) over the whole
-// contraction and 16 * BT runs.  Its ring holds P blocks of weight tiles and
-// digit fragments; block i of the flattened (tile, block) sequence sits in
-// slot i % P, and kblocks is a multiple of P, so every tile starts at slot 0.
-template <int MT, int BT, int P>
-__global__ __launch_bounds__(256) void k_rows_stream(RowsArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, lg = lane >> 4;
-  const Seg &sg = a.seg[0];
-  const uint32_t nkb = a.kblocks, kbp = a.kp / 64, nbt = a.bp / 16;
-  const uint32_t G = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
-  if (gw >= a.ntiles) return;
-  const uint32_t my = (a.ntiles - gw + G - 1) / G;  // tiles of this wave
-  const uint32_t last_ptile = (sg.rows - 1) / 16;
-
-  if (input_needs_exact(a)) {
-    for (uint32_t t = 0; t < my; t++) stream_exact(a, (gw + t * G) * MT, MT, BT, li, lg);
-    return;
-  }
-
-  // Lanes of runs past the batch read run 0's fragment bytes (the planes
-  // hold zeros there anyway); their product columns are never stored.
-  const int8_t *dsrc[3][BT];
-#pragma unroll
-  for (int l = 0; l < 3; l++)
-#pragma unroll
-    for (int bt = 0; bt < BT; bt++)
-      dsrc[l][bt] = a.planes + ((((uint64_t)l * nbt + bt) * kbp) * 64 + lane) * 16;
-
-  v4i acc[MT][3][BT];
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
-  v4i Wr[P][MT], Dr[P][3][BT];
-
-  // The block issued next: (it-th tile of this wave, block ikb).  Past the
-  // last tile the ring re-reads the last one (valid addresses, never used).
-  uint32_t it = 0, ikb = 0;
-  auto issue = [&](int s) {
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t t = it < my ? it : my - 1;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      uint32_t pt = (gw + t * G) * MT + mt;
-      pt = pt < last_ptile ? pt : last_ptile;
-      Wr[s][mt] = __builtin_nontemporal_load(
-          reinterpret_cast<const v4i *>(sg.P + ((uint64_t)pt * nkb + ikb) * 1024 + lane * 16));
-    }
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-        Dr[s][l][bt] = *reinterpret_cast<const v4i *>(dsrc[l][bt] + (uint64_t)ikb * 1024);
-    __builtin_amdgcn_sched_barrier(0);
-    if (++ikb == nkb) {
-      ikb = 0;
-      ++it;
-    }
-  };
-  auto compute = [&](int s) {
-    v4i w[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) w[mt] = flip_weights(Wr[s][mt]);
-#pragma unroll
-    for (int l = 0; l < 3; l++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-          acc[mt][l][bt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[mt], Dr[s][l][bt], acc[mt][l][bt], 0, 0, 0);
-  };
-
-#pragma unroll
-  for (int s = 0; s < P; s++) issue(s);
-  for (uint32_t t = 0; t < my; t++) {
-    const uint32_t ptile0 = (gw + t * G) * MT;
-    uint32_t sc[MT][4];
-    stream_scales<MT>(a, ptile0, lg, sc);
-    for (uint32_t kb = 0; kb < nkb; kb += P) {
-#pragma unroll
-      for (int s = 0; s < P; s++) {
-        compute(s);
-        issue(s);
-      }
-    }
-    int64_t v[MT][BT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int bt = 0; bt < BT; bt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          v[mt][bt][j] = (int64_t)acc[mt][0][bt][j] + ((int64_t)acc[mt][1][bt][j] << 8) +
-                         ((int64_t)acc[mt][2][bt][j] << 16);
-          acc[mt][0][bt][j] = 0;
-          acc[mt][1][bt][j] = 0;
-          acc[mt][2][bt][j] = 0;
-        }
-    stream_store<MT, BT>(a, ptile0, li, lg, v, sc);
-  }
-  wait_vm<0>();  // the ring's last (unused) loads land before the wave ends
-}
-
 // Stages of CD blocks; the digits of a stage are 3 * BT * CD fragments, W
 // waves issue FR / W of them each into LDS buffer s; the weights of the
-// stage go to register slot s.  NB = P + 1 buffers: after the barrier of
-// stage k every wave has finished stage k - 1, so stage k + P may refill
-// its buffer.  kblocks / CD is a multiple of NB, so every tile starts at
-// buffer 0.
+// stage go to register slot s.  NB = P + 1 buffers (2 or 4): after the
+// barrier of stage k every wave has finished stage k - 1, so stage k + P
+// may refill its buffer.  kblocks / CD is a multiple of NB, so every tile
+// starts at buffer 0.
 template <int BT, int CD, int W>
 struct StreamShared {
   static constexpr int FR = 3 * BT * CD;
@@ -251,7 +138,7 @@ __global__ __launch_bounds__(64 * W) void k_rows_stream_shared(RowsArgs a) {
   using G_ = StreamShared<BT, CD, W>;
   constexpr int FR = G_::FR, FW = G_::FW, NB = P + 1;
   constexpr int NL = MT * CD + FW;  // loads per stage and wave
-  static_assert(NB == 4, "four ring buffers");
+  static_assert(NB == 2 || NB == 4, "two or four ring buffers");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -267,8 +154,13 @@ __global__ __launch_bounds__(64 * W) void k_rows_stream_shared(RowsArgs a) {
     return;
   }
 
-  v4i *ring[NB] = {stream_ring<0, FR * 64>(), stream_ring<1, FR * 64>(), stream_ring<2, FR * 64>(),
-                   stream_ring<3, FR * 64>()};
+  v4i *ring[NB];
+  ring[0] = stream_ring<0, FR * 64>();
+  ring[1] = stream_ring<1, FR * 64>();
+  if constexpr (NB == 4) {
+    ring[2] = stream_ring<2, FR * 64>();
+    ring[3] = stream_ring<3, FR * 64>();
+  }
   // This wave stages fragments f = wave + W q of every stage: (limb l, run
   // tile bt, block c of the stage).
   const int8_t *dsrc[FW];
@@ -508,14 +400,6 @@ int cu_count() {
   return n;
 }
 
-template <int MT, int BT, int P>
-int launch_dir(RowsArgs a, hipStream_t s) {
-  a.ntiles = (a.seg[0].rows + 16 * MT - 1) / (16 * MT);
-  const uint32_t wgs = std::min<uint32_t>((a.ntiles + 3) / 4, (uint32_t)cu_count());
-  hipLaunchKernelGGL((k_rows_stream<MT, BT, P>), dim3(wgs), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? 0 : FPI8_ERR_HIP;
-}
-
 template <int MT, int BT, int P, int CD, int W>
 int launch_shr(RowsArgs a, hipStream_t s) {
   a.ntiles = (a.seg[0].rows + W * 16 * MT - 1) / (W * 16 * MT);
@@ -562,27 +446,29 @@ int launch_rows_stream_valu(const RowsArgs &a, void *stream) {
   }
 }
 
-// The launch shapes by batch (measured on MI355X over a pool of 48
-// 4096-column matrices): up to 16 runs, waves of 64 rows with an 8-block
-// ring reading their own digits; 17-32 runs, workgroups of 4 waves x 64
-// rows sharing digits through LDS; 33-64 and 65-128 runs, 8 waves sharing.
-// Every shape walks 8 blocks (one ring turn) at a time.
+// The launch shapes by batch, measured on MI355X over a pool of 48
+// 4096-column matrices, all staging one block of digit fragments per stage:
+// up to 16 runs, 3 waves x 64 rows (each wave stages one digit plane);
+// 17-32 runs, 6 waves x 64 rows; 33-64 runs, 12 waves x 32 rows; 65-128
+// runs, 12 waves x 16 rows with two ring buffers.  More waves than the four
+// SIMDs keep more weight loads in flight; one block per stage keeps the
+// waves closest together.
 int launch_rows_stream(const RowsArgs &a, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.nseg != 1 || !a.seg[0].P || a.compact || a.n_runs == 0 || a.n_runs > 128 ||
       a.kblocks % kStreamBlockMultiple != 0 || a.bp < (a.n_runs + 15) / 16 * 16)
     return FPI8_ERR_ARGUMENT;
-  if (a.n_runs <= 16) return launch_dir<4, 1, 8>(a, s);
+  if (a.n_runs <= 16) return launch_shr<4, 1, 3, 1, 3>(a, s);
   if (a.n_runs <= 32) {
     if (a.bp < 32) return FPI8_ERR_ARGUMENT;
-    return launch_shr<4, 2, 3, 2, 4>(a, s);
+    return launch_shr<4, 2, 3, 1, 6>(a, s);
   }
   if (a.n_runs <= 64) {
     if (a.bp < 64) return FPI8_ERR_ARGUMENT;
-    return launch_shr<2, 4, 3, 2, 8>(a, s);
+    return launch_shr<2, 4, 1, 1, 12>(a, s);
   }
   if (a.bp < 128) return FPI8_ERR_ARGUMENT;
-  return launch_shr<1, 8, 3, 1, 8>(a, s);
+  return launch_shr<1, 8, 1, 1, 12>(a, s);
 }
 
 }  // namespace fpi8
