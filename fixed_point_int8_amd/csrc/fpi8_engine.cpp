@@ -67,7 +67,7 @@ struct fpi8_engine {
   uint32_t graph_runs = 0;
   uint32_t graph_cap = 0;
   uint32_t score_cap = 0;  // attention's LDS score slots for the current turn
-  int row_kind = 0;  // 0 planner's choice, 1 to 3 restrict it (fpi8_engine_set_row_kernel)
+  int row_kind = 0;  // 0 planner's choice, 1 to 6 restrict it (fpi8_engine_set_row_kernel)
   // Runs split into two groups advanced on two streams, so one group's
   // row kernels overlap the other's attention (2); one stream (0, 1).
   // Measured on the 7B-shaped decode at 64 runs, two groups are slower:
@@ -162,25 +162,37 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
                   int force) {
   // rate: GB/s one compute unit draws for the shape; occ: workgroups of the
   // shape that fit on one compute unit (registers, LDS).
+  // Kind 2 (3 * bt waves, all owning rows, one block per stage): rates from
+  // sweeps of the 7B-shaped matrices at 64 runs, taken a little below the
+  // slowest matrix's so that the kind wins only where it clearly does.
   struct Cand { int kind, mt, bt, wr; double gbs; int occ; };
   static const Cand plain[] = {{0, 1, 1, 1, 26, 1}, {0, 1, 2, 1, 44, 2}, {0, 1, 4, 1, 46, 1},
                                {0, 2, 2, 1, 37, 1}, {0, 2, 4, 1, 42, 1}, {0, 4, 1, 1, 34, 1},
                                {0, 4, 2, 1, 28, 1},
                                {1, 1, 2, 4, 36, 2}, {1, 1, 4, 4, 30, 1}, {1, 2, 2, 4, 34, 2},
-                               {1, 2, 4, 4, 26, 1}, {1, 2, 2, 3, 33, 2}, {1, 2, 4, 3, 24, 1}};
+                               {1, 2, 4, 4, 26, 1}, {1, 2, 2, 3, 33, 2}, {1, 2, 4, 3, 24, 1},
+                               {2, 1, 1, 3, 42, 1}, {2, 2, 1, 3, 38, 1}, {2, 4, 1, 3, 40, 1},
+                               {2, 1, 2, 6, 36, 1}, {2, 2, 2, 6, 40, 1}, {2, 1, 4, 12, 38, 1}};
   static const Cand pairs[] = {{0, 2, 2, 1, 37, 1}, {0, 2, 4, 1, 42, 1}, {0, 4, 2, 1, 28, 1},
                                {1, 2, 2, 4, 34, 2}, {1, 2, 4, 4, 26, 1}, {1, 2, 2, 3, 33, 2},
-                               {1, 2, 4, 3, 24, 1}};
+                               {1, 2, 4, 3, 24, 1},
+                               {2, 2, 1, 3, 38, 1}, {2, 4, 1, 3, 40, 1}, {2, 2, 2, 6, 40, 1}};
   const Cand *cand = gateup ? pairs : plain;
-  const int n = gateup ? 7 : 13;
+  const int n = gateup ? 10 : 19;
   const double cus = 256, hbm_cu = 20e9;
   RowPlan best{0, 1, 1, 1, 1, 1};
   double best_t = 1e30;
   for (int i = 0; i < n; i++) {
     const int kind = cand[i].kind;
-    if (kind == 1 && !shared_ok) continue;
-    if ((force == 1 && kind != 0) || (force >= 2 && shared_ok && kind != 1) ||
-        (force == 3 && shared_ok && cand[i].wr != 3))
+    if (kind >= 1 && !shared_ok) continue;
+    // Kind 2 was measured to pay on the 4096-column matrices at 64 runs
+    // (query/key/value, gate/up, classifier); at 16 and 32 runs over 2048
+    // to 5632 columns the planner's other choices were faster, so it is
+    // offered from 48 runs and 64 blocks of contraction on.
+    if (kind == 2 && (cols < 4096 || n_runs < 48) && force < 4) continue;
+    if ((force == 1 && kind != 0) || ((force == 2 || force == 3) && shared_ok && kind != 1) ||
+        (force == 3 && shared_ok && cand[i].wr != 3) ||
+        (force >= 4 && shared_ok && (kind != 2 || cand[i].bt != 1 << (force - 4))))
       continue;
     RowPlan p{kind, cand[i].mt, cand[i].bt, cand[i].wr, 0, 0};
     const uint32_t bc = 16 * p.bt;
@@ -204,6 +216,9 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
     const double t = std::max(t_hbm, t_l2);
     if (t < best_t * 0.999) { best_t = t; best = p; }
   }
+  // A restriction no candidate meets (the gate/up pair has no 12-wave
+  // shape): the planner's own choice.
+  if (best_t == 1e30 && force) return plan_rows(rows, cols, n_runs, gateup, shared_ok, 0);
   return best;
 }
 
@@ -792,7 +807,7 @@ int32_t fpi8_turn_units(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint
 }
 
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
-  if (!e || kind < 0 || kind > 3) return FPI8_ERR_ARGUMENT;
+  if (!e || kind < 0 || kind > 6) return FPI8_ERR_ARGUMENT;
   if (e->row_kind != kind) {
     e->row_kind = kind;
     e->graph_states = nullptr;  // record the position again with the new shapes

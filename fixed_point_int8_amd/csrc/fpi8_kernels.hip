@@ -1071,24 +1071,25 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
   rows_epilogue<EPI, MT, BT, PART>(a, t, b0, v, li, lg, in, silu_lds);
 }
 
-// The matrix row with the digits shared through LDS.  A workgroup of four
-// waves owns wave_rows * 16 * MT rows (wave_rows = 3 or 4 waves each own
-// 16 * MT of them) and 16 * BT runs, over the whole contraction.  All four
-// waves stage each run of CD 64-column blocks of digit fragments into an
-// LDS ring with direct global-to-LDS loads (a quarter of the fragments
-// each), P stages ahead, and every row-owning wave streams its own weight
-// rows into a register ring of the same depth; one barrier per stage.  The
-// digits then cross L2 once per wave_rows * 16 * MT rows rather than once
-// per 16 * MT.  For packed matrices (kblocks even), or rows that are
+// The matrix row with the digits shared through LDS.  A workgroup of W
+// waves owns wave_rows * 16 * MT rows (wave_rows of its waves each own
+// 16 * MT of them: 3 or 4 of four, or all W of 3, 6 or 12) and 16 * BT runs,
+// over the whole contraction.  All W waves stage each run of CD 64-column
+// blocks of digit fragments into an LDS ring with direct global-to-LDS
+// loads (an equal share each), P stages ahead, and every row-owning wave
+// streams its own weight rows into a register ring of the same depth; one
+// barrier per stage.  The digits then cross L2 once per wave_rows * 16 * MT
+// rows rather than once per 16 * MT.  More waves than the four SIMDs keep
+// more weight loads in flight and let one wave's matrix-core work overlap
+// another's waits.  For packed matrices (kblocks even), or rows that are
 // 16-byte aligned with a column count that is a multiple of 64 * CD.
-template <int BT>
+template <int BT, int CD, int W>
 struct SharedGeom {
-  static constexpr int CD = 2;                 // 64-column blocks per stage
   static constexpr int FR = 3 * BT * CD;       // digit fragments per stage
-  static constexpr int FW = FR / 4;            // fragments each wave stages
-  static constexpr int P = BT >= 4 ? 3 : 4;    // stages in flight
+  static constexpr int FW = FR / W;            // fragments each wave stages
+  static constexpr int P = CD == 1 ? 3 : BT >= 4 ? 3 : 4;  // stages in flight
   static constexpr int NB = P + 1;             // stage buffers (LDS and registers)
-  static_assert(FR % 4 == 0, "every wave stages the same number of fragments");
+  static_assert(FR % W == 0, "every wave stages the same number of fragments");
 };
 
 
@@ -1100,10 +1101,10 @@ __device__ __forceinline__ v4i *ring_buf() {
   return buf;
 }
 
-template <int EPI, int MT, int BT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2 : 1))) void k_rows_shared(RowsArgs a) {
-  using G = SharedGeom<BT>;
-  constexpr int CD = G::CD, FR = G::FR, FW = G::FW, P = G::P, NB = G::NB;
+template <int EPI, int MT, int BT, int W = 4, int CD = 2>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 && BT <= 2 ? 2 : 1))) void k_rows_shared(RowsArgs a) {
+  using G = SharedGeom<BT, CD, W>;
+  constexpr int FR = G::FR, FW = G::FW, P = G::P, NB = G::NB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int li = lane & 15, lg = lane >> 4;
@@ -1126,7 +1127,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
   row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, own, t);
   EpiIn<EPI, MT, BT> in;
   if (own) epi_begin<EPI, MT, BT>(a, b0, li, in);  // waves that own rows run an epilogue
-  if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, 4, lane);
+  if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, W, lane);
   const bool exact = input_needs_exact(a);
   if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
     wait_vm<0>();  // no table load may still be landing in LDS
@@ -1158,13 +1159,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
       wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)t.ptile[mt] * a.kblocks * 1024 + lane * 16
                           : t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
     }
-    // This wave stages fragments f = wave + 4q of every stage; fragment f
+    // This wave stages fragments f = wave + Wq of every stage; fragment f
     // is (limb l, run tile bt, block c).  Runs past the batch bring
     // whatever their plane rows hold; those product columns are never stored.
     const int8_t *dsrc[FW];
 #pragma unroll
     for (int q = 0; q < FW; q++) {
-      const int f = wave + 4 * q;
+      const int f = wave + W * q;
       const int l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
       dsrc[q] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + c) * 64 + lane) * 16;
     }
@@ -1195,7 +1196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT <= 2 ? 2
 #pragma unroll
         for (int q = 0; q < FW; q++)
           __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
-                                           (lds_void *)(ring[s] + (wave + 4 * q) * 64), 16, 0, 0);
+                                           (lds_void *)(ring[s] + (wave + W * q) * 64), 16, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       };
       auto compute = [&](int s) {
@@ -1724,11 +1725,28 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     const uint32_t c0 = tid * chunk, c1 = min(V, c0 + chunk);
     // a stop inside the maximum pass: the entries before its row
     const uint32_t lim0 = (ustop && rd.stop_pass == 0) ? rd.stop_row : V;
-    // Maximum pass: the largest logit, the lowest index on a tie.
+    // Maximum pass: the largest logit, the lowest index on a tie.  Each
+    // thread strides over the entries (a wave reads 64 consecutive words),
+    // U loads in flight; a thread meets its entries in increasing order, so
+    // its first maximum is its lowest-index one, and the reduction below
+    // keeps the lowest index among equal maxima.
+    constexpr int U = 8;
+    const uint32_t lim = min(V, lim0);
     int64_t bv = INT64_MIN;
     uint32_t bi = 0xFFFFFFFFu;
-    for (uint32_t i = c0; i < min(c1, lim0); i++)
-      if (bi == 0xFFFFFFFFu || lgt[i] > bv) { bv = lgt[i]; bi = i; }
+    for (uint32_t i0 = tid; i0 < lim; i0 += U * 256) {
+      int64_t x[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t i = i0 + u * 256;
+        x[u] = i < lim ? lgt[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t i = i0 + u * 256;
+        if (i < lim && (bi == 0xFFFFFFFFu || x[u] > bv)) { bv = x[u]; bi = i; }
+      }
+    }
     best_v[tid] = bv;
     best_i[tid] = bi;
     __syncthreads();
@@ -1761,8 +1779,18 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
     if (T != 0) {
       // Sum pass over each thread's slice, then the draw and the walk.
       const uint32_t lim1 = ustop ? rd.stop_row : V;  // a stop inside the sum pass
+      // Each thread sums its own contiguous slice (the walk below needs the
+      // slices' sums in index order), U loads in flight.
+      const uint32_t e1 = min(c1, lim1);
       uint64_t s = 0;
-      for (uint32_t i = c0; i < min(c1, lim1); i++) s += a.exp_tab[temp_index((uint64_t)m - (uint64_t)lgt[i], T)];
+      for (uint32_t i0 = c0; i0 < e1; i0 += U) {
+        int64_t x[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) x[u] = i0 + u < e1 ? lgt[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+          if (i0 + u < e1) s += a.exp_tab[temp_index((uint64_t)m - (uint64_t)x[u], T)];
+      }
       part[tid] = s;
       __syncthreads();
       if (ustop) {
@@ -1907,12 +1935,22 @@ static int rows_launch(const RowsArgs &a, hipStream_t s) {
   return ok(hipGetLastError());
 }
 
-template <int EPI, int MT, int BT>
+template <int EPI, int MT, int BT, int W = 4, int CD = 2>
 static int rows_launch_shared(const RowsArgs &a, hipStream_t s) {
   const uint32_t groups = (a.ntiles + 7) / 8;
-  const dim3 grid(groups * 8 * a.chunks), block(256);
-  hipLaunchKernelGGL((k_rows_shared<EPI, MT, BT>), grid, block, 0, s, a);
+  const dim3 grid(groups * 8 * a.chunks), block(64 * W);
+  hipLaunchKernelGGL((k_rows_shared<EPI, MT, BT, W, CD>), grid, block, 0, s, a);
   return ok(hipGetLastError());
+}
+
+// Kind 2: every wave owns rows, one block of digits per stage, and the waves
+// per workgroup follow the runs: 3 for 16 runs, 6 for 32, 12 for 64 (one
+// digit fragment per wave and stage).
+template <int EPI, int MT, int BT>
+static int rows_launch_waves(const RowsArgs &a, hipStream_t s) {
+  constexpr int W = 3 * BT;
+  if (a.wave_rows != (uint32_t)W) return FPI8_ERR_ARGUMENT;
+  return rows_launch_shared<EPI, MT, BT, W, 1>(a, s);
 }
 
 template <int EPI>
@@ -1931,6 +1969,12 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 114: return rows_launch_shared<EPI, 1, 4>(a, s);
       case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
       case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
+      case 211: return rows_launch_waves<EPI, 1, 1>(a, s);
+      case 221: return rows_launch_waves<EPI, 2, 1>(a, s);
+      case 241: return rows_launch_waves<EPI, 4, 1>(a, s);
+      case 212: return rows_launch_waves<EPI, 1, 2>(a, s);
+      case 222: return rows_launch_waves<EPI, 2, 2>(a, s);
+      case 214: return rows_launch_waves<EPI, 1, 4>(a, s);
     }
   } else {
     switch (key) {
@@ -1939,6 +1983,9 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 42: return rows_launch<EPI, 4, 2>(a, s);
       case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
       case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
+      case 221: return rows_launch_waves<EPI, 2, 1>(a, s);
+      case 241: return rows_launch_waves<EPI, 4, 1>(a, s);
+      case 222: return rows_launch_waves<EPI, 2, 2>(a, s);
     }
   }
   return FPI8_ERR_ARGUMENT;

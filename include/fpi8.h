@@ -313,8 +313,11 @@ int32_t fpi8_turn_units(fpi8_engine *engine, uint8_t *d_states, uint64_t state_s
  * 2 the kernel whose waves share their runs' digits through LDS wherever it
  * can run (columns a multiple of 128, 16-byte aligned rows), 3 that kernel
  * with three of its four waves owning rows and the fourth only staging
- * digits.  Results are identical under every setting; it exists for tests
- * and tuning.  Error 102 for another value. */
+ * digits, 4, 5 and 6 that kernel with 3, 6 or 12 waves (16, 32 or 64 runs
+ * per workgroup), every one owning rows, one block of digits per stage
+ * (where a launch has no such shape, the gate/up pair under 6, the
+ * planner's choice).  Results are identical under every setting; it exists
+ * for tests and tuning.  Error 102 for another value. */
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
 
 /* Whether a turn replays one position recorded as a HIP graph (nonzero, the
