@@ -67,7 +67,7 @@ struct fpi8_engine {
   uint32_t graph_runs = 0;
   uint32_t graph_cap = 0;
   uint32_t score_cap = 0;  // attention's LDS score slots for the current turn
-  int row_kind = 0;  // 0 planner's choice, 1 to 6 restrict it (fpi8_engine_set_row_kernel)
+  int row_kind = 0;  // 0 planner's choice, 1 to 7 restrict it (fpi8_engine_set_row_kernel)
   // Runs split into two groups advanced on two streams, so one group's
   // row kernels overlap the other's attention (2); one stream (0, 1).
   // Measured on the 7B-shaped decode at 64 runs, two groups are slower:
@@ -185,11 +185,8 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
   for (int i = 0; i < n; i++) {
     const int kind = cand[i].kind;
     if (kind >= 1 && !shared_ok) continue;
-    // Kind 2 was measured to pay on the 4096-column matrices at 64 runs
-    // (query/key/value, gate/up, classifier); at 16 and 32 runs over 2048
-    // to 5632 columns the planner's other choices were faster, so it is
-    // offered from 48 runs and 64 blocks of contraction on.
-    if (kind == 2 && (cols < 4096 || n_runs < 48) && force < 4) continue;
+    // Kind 2 is chosen by launch (multi_wave_plan) unless forced.
+    if (kind == 2 && force < 4) continue;
     if ((force == 1 && kind != 0) || ((force == 2 || force == 3) && shared_ok && kind != 1) ||
         (force == 3 && shared_ok && cand[i].wr != 3) ||
         (force >= 4 && shared_ok && (kind != 2 || cand[i].bt != 1 << (force - 4))))
@@ -220,6 +217,33 @@ RowPlan plan_rows(uint32_t rows, uint32_t cols, uint32_t n_runs, bool gateup, bo
   // shape): the planner's own choice.
   if (best_t == 1e30 && force) return plan_rows(rows, cols, n_runs, gateup, shared_ok, 0);
   return best;
+}
+
+// The shape of the multi-wave shared-digit kernel (kinds 2 and 3: 3, 6 or
+// 12 waves, every one owning rows, one block of digits per stage) for the
+// launches it was measured to win, else kind -1.  Measured on MI355X over
+// the decode matrices of the 7B-shaped (64 runs, 4096 columns), 1.1B-shaped
+// (32 runs, 2048) and long-context (16 runs, 2048) models against the
+// planner's shapes: query/key/value and gate/up at every one of them (3
+// waves and seven stages in flight from 2048 columns, 6 waves from 4096),
+// the classifier at 64 runs over 4096 columns (12 waves); the output and
+// down matrices stay with the kernel whose waves split the contraction.
+RowPlan multi_wave_plan(int epi, uint32_t rows, uint32_t cols, uint32_t n_runs, bool any_width) {
+  RowPlan p{-1, 1, 1, 1, 0, 0};
+  const bool wide = cols >= 4096;
+  if ((cols < 2048 && !any_width) || cols % 128 != 0) return p;
+  if (epi == EPI_QKV)
+    p = wide ? RowPlan{3, 1, 2, 6, 0, 0} : RowPlan{3, 1, 1, 3, 0, 0};
+  else if (epi == EPI_GATEUP)
+    p = wide ? RowPlan{2, 2, 2, 6, 0, 0} : RowPlan{3, 2, 1, 3, 0, 0};
+  else if (epi == EPI_CLS && ((wide && n_runs >= 48) || any_width))
+    p = RowPlan{2, 1, 4, 12, 0, 0};
+  else
+    return p;
+  p.chunks = (n_runs + 16 * p.bt - 1) / (16 * p.bt);
+  const uint32_t per_tile = 16 * (epi == EPI_GATEUP ? p.mt / 2 : p.mt) * p.wr;
+  p.tiles = (rows + per_tile - 1) / per_tile;
+  return p;
 }
 
 // The runs [r0, r0 + n) of a batch with their own digit planes and flags:
@@ -288,9 +312,13 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   shared_ok = shared_ok || a.packed != 0;
   // A position where some run starts or stops between two phases uses the
   // one shape built for it (32 rows, 32 runs, kind 0).
-  const RowPlan p = a.partial ? RowPlan{0, 2, 2, 1, (n_runs + 31) / 32, 0}
-                              : plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup,
-                                          shared_ok, e->row_kind);
+  RowPlan p = a.partial ? RowPlan{0, 2, 2, 1, (n_runs + 31) / 32, 0}
+                        : plan_rows(gateup ? a.seg[0].rows : rows, a.cols, n_runs, gateup,
+                                    shared_ok, e->row_kind);
+  if (!a.partial && (e->row_kind == 0 || e->row_kind == 7) && shared_ok) {
+    const RowPlan m = multi_wave_plan(epi, gateup ? a.seg[0].rows : rows, a.cols, n_runs, e->row_kind == 7);
+    if (m.kind >= 0) p = m;
+  }
   // Units of 16 * mt rows (of each matrix of the gate/up pair: 16 * mt / 2)
   // over the segments in order; a workgroup finishes one (kind 0) or wr.
   const uint32_t unit_rows = 16 * (gateup ? p.mt / 2 : p.mt);
@@ -299,7 +327,7 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
     a.seg[i].unit0 = gateup ? 0 : units;
     if (!gateup || i == 0) units += (a.seg[i].rows + unit_rows - 1) / unit_rows;
   }
-  const uint32_t per = p.kind ? (uint32_t)p.wr : 1u;
+  const uint32_t per = p.kind ? (uint32_t)p.wr : 1u;  // kinds 1-3: wr row-owning waves
   a.ntiles = (units + per - 1) / per;
   a.wave_rows = per;
   a.chunks = p.chunks;
@@ -807,7 +835,7 @@ int32_t fpi8_turn_units(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint
 }
 
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *e, int32_t kind) {
-  if (!e || kind < 0 || kind > 6) return FPI8_ERR_ARGUMENT;
+  if (!e || kind < 0 || kind > 7) return FPI8_ERR_ARGUMENT;
   if (e->row_kind != kind) {
     e->row_kind = kind;
     e->graph_states = nullptr;  // record the position again with the new shapes

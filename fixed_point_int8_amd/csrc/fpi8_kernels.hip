@@ -1083,13 +1083,16 @@ __global__ __launch_bounds__(256) void k_rows(RowsArgs a) {
 // more weight loads in flight and let one wave's matrix-core work overlap
 // another's waits.  For packed matrices (kblocks even), or rows that are
 // 16-byte aligned with a column count that is a multiple of 64 * CD.
-template <int BT, int CD, int W>
+template <int BT, int CD, int W, int PP = 0>
 struct SharedGeom {
   static constexpr int FR = 3 * BT * CD;       // digit fragments per stage
   static constexpr int FW = FR / W;            // fragments each wave stages
-  static constexpr int P = CD == 1 ? 3 : BT >= 4 ? 3 : 4;  // stages in flight
+  // stages in flight: PP when given, else 3 (4 for two-block stages of up
+  // to 32 runs)
+  static constexpr int P = PP > 0 ? PP : CD == 1 ? 3 : BT >= 4 ? 3 : 4;
   static constexpr int NB = P + 1;             // stage buffers (LDS and registers)
   static_assert(FR % W == 0, "every wave stages the same number of fragments");
+  static_assert(NB <= 8, "at most eight stage buffers");
 };
 
 
@@ -1101,9 +1104,9 @@ __device__ __forceinline__ v4i *ring_buf() {
   return buf;
 }
 
-template <int EPI, int MT, int BT, int W = 4, int CD = 2>
+template <int EPI, int MT, int BT, int W = 4, int CD = 2, int PP = 0>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 && BT <= 2 ? 2 : 1))) void k_rows_shared(RowsArgs a) {
-  using G = SharedGeom<BT, CD, W>;
+  using G = SharedGeom<BT, CD, W, PP>;
   constexpr int FR = G::FR, FW = G::FW, P = G::P, NB = G::NB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
@@ -1175,6 +1178,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
     ring[2] = ring_buf<2, FR * 64>();
     ring[3] = ring_buf<3, FR * 64>();
     if constexpr (NB > 4) ring[4] = ring_buf<4, FR * 64>();
+    if constexpr (NB > 5) ring[5] = ring_buf<5, FR * 64>();
+    if constexpr (NB > 6) ring[6] = ring_buf<6, FR * 64>();
+    if constexpr (NB > 7) ring[7] = ring_buf<7, FR * 64>();
 
     v4i Wr[NB][MT][CD];
     // The stage loop of a wave that owns rows (OWN) or only stages digits.
@@ -1935,22 +1941,23 @@ static int rows_launch(const RowsArgs &a, hipStream_t s) {
   return ok(hipGetLastError());
 }
 
-template <int EPI, int MT, int BT, int W = 4, int CD = 2>
+template <int EPI, int MT, int BT, int W = 4, int CD = 2, int PP = 0>
 static int rows_launch_shared(const RowsArgs &a, hipStream_t s) {
   const uint32_t groups = (a.ntiles + 7) / 8;
   const dim3 grid(groups * 8 * a.chunks), block(64 * W);
-  hipLaunchKernelGGL((k_rows_shared<EPI, MT, BT, W, CD>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((k_rows_shared<EPI, MT, BT, W, CD, PP>), grid, block, 0, s, a);
   return ok(hipGetLastError());
 }
 
-// Kind 2: every wave owns rows, one block of digits per stage, and the waves
-// per workgroup follow the runs: 3 for 16 runs, 6 for 32, 12 for 64 (one
-// digit fragment per wave and stage).
-template <int EPI, int MT, int BT>
+// Kinds 2 and 3: every wave owns rows, one block of digits per stage, and
+// the waves per workgroup follow the runs: 3 for 16 runs, 6 for 32, 12 for
+// 64 (one digit fragment per wave and stage); P = 3 stages in flight (kind
+// 2) or 7 (kind 3).
+template <int EPI, int MT, int BT, int P>
 static int rows_launch_waves(const RowsArgs &a, hipStream_t s) {
   constexpr int W = 3 * BT;
   if (a.wave_rows != (uint32_t)W) return FPI8_ERR_ARGUMENT;
-  return rows_launch_shared<EPI, MT, BT, W, 1>(a, s);
+  return rows_launch_shared<EPI, MT, BT, W, 1, P>(a, s);
 }
 
 template <int EPI>
@@ -1969,12 +1976,14 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 114: return rows_launch_shared<EPI, 1, 4>(a, s);
       case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
       case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
-      case 211: return rows_launch_waves<EPI, 1, 1>(a, s);
-      case 221: return rows_launch_waves<EPI, 2, 1>(a, s);
-      case 241: return rows_launch_waves<EPI, 4, 1>(a, s);
-      case 212: return rows_launch_waves<EPI, 1, 2>(a, s);
-      case 222: return rows_launch_waves<EPI, 2, 2>(a, s);
-      case 214: return rows_launch_waves<EPI, 1, 4>(a, s);
+      case 211: return rows_launch_waves<EPI, 1, 1, 3>(a, s);
+      case 221: return rows_launch_waves<EPI, 2, 1, 3>(a, s);
+      case 241: return rows_launch_waves<EPI, 4, 1, 3>(a, s);
+      case 212: return rows_launch_waves<EPI, 1, 2, 3>(a, s);
+      case 222: return rows_launch_waves<EPI, 2, 2, 3>(a, s);
+      case 214: return rows_launch_waves<EPI, 1, 4, 3>(a, s);
+      case 311: return rows_launch_waves<EPI, 1, 1, 7>(a, s);
+      case 312: return rows_launch_waves<EPI, 1, 2, 7>(a, s);
     }
   } else {
     switch (key) {
@@ -1983,9 +1992,10 @@ static int rows_shape(int kind, int mt, int bt, const RowsArgs &a, hipStream_t s
       case 42: return rows_launch<EPI, 4, 2>(a, s);
       case 122: return rows_launch_shared<EPI, 2, 2>(a, s);
       case 124: return rows_launch_shared<EPI, 2, 4>(a, s);
-      case 221: return rows_launch_waves<EPI, 2, 1>(a, s);
-      case 241: return rows_launch_waves<EPI, 4, 1>(a, s);
-      case 222: return rows_launch_waves<EPI, 2, 2>(a, s);
+      case 221: return rows_launch_waves<EPI, 2, 1, 3>(a, s);
+      case 241: return rows_launch_waves<EPI, 4, 1, 3>(a, s);
+      case 222: return rows_launch_waves<EPI, 2, 2, 3>(a, s);
+      case 321: return rows_launch_waves<EPI, 2, 1, 7>(a, s);
     }
   }
   return FPI8_ERR_ARGUMENT;

@@ -316,8 +316,10 @@ int32_t fpi8_turn_units(fpi8_engine *engine, uint8_t *d_states, uint64_t state_s
  * digits, 4, 5 and 6 that kernel with 3, 6 or 12 waves (16, 32 or 64 runs
  * per workgroup), every one owning rows, one block of digits per stage
  * (where a launch has no such shape, the gate/up pair under 6, the
- * planner's choice).  Results are identical under every setting; it exists
- * for tests and tuning.  Error 102 for another value. */
+ * planner's choice), 7 the default choice with the multi-wave shapes the
+ * default gives query/key/value, gate/up and classifier launches from 2048
+ * columns on taken at every width.  Results are identical under every
+ * setting; it exists for tests and tuning.  Error 102 for another value. */
 int32_t fpi8_engine_set_row_kernel(fpi8_engine *engine, int32_t kind);
 
 /* Whether a turn replays one position recorded as a HIP graph (nonzero, the

@@ -301,7 +301,7 @@ def test_split_contraction_whole_pass(n_runs):
     run_pair(shape, blob, runs, [2, 3])
 
 
-@pytest.mark.parametrize("row_kernel", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("row_kernel", [1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("n_runs", [3, 20, 70])
 def test_row_kernels_whole_pass(n_runs, row_kernel):
     # Every matrix of the split shape has a column count that is a multiple
@@ -309,7 +309,8 @@ def test_row_kernels_whole_pass(n_runs, row_kernel):
     # whose waves split the contraction, 2 the one that shares digits in LDS,
     # 3 that one with three row-owning waves, so that workgroups end inside
     # a matrix and span the Q/K and K/V boundaries, 4 to 6 that one with 3,
-    # 6 or 12 waves all owning rows (16, 32 or 64 runs per workgroup).
+    # 6 or 12 waves all owning rows (16, 32 or 64 runs per workgroup), 7 the
+    # default's multi-wave shapes (seven stages in flight) at this width.
     shape = W.SMALL_SHAPES["split"]
     say(f"split shape, {n_runs} runs, row kernel {row_kernel}")
     blob = Bl.build_blob(shape, 22)
@@ -329,7 +330,7 @@ def test_run_groups_on_two_streams(streams, n_runs, graph):
     run_pair(shape, blob, runs, [1, 2, 4], streams=streams, graph=graph)
 
 
-@pytest.mark.parametrize("row_kernel", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("row_kernel", [2, 3, 4, 5, 6, 7])
 def test_shared_kernel_exact_path(row_kernel):
     shape = W.SMALL_SHAPES["split"]
     say(f"exact path, shared-digit row kernel {row_kernel}")
@@ -978,7 +979,7 @@ def test_units_one_at_a_time():
         pair.model.close()
 
 
-@pytest.mark.parametrize("row_kernel,streams", [(0, 0), (2, 0), (0, 2), (4, 0)])
+@pytest.mark.parametrize("row_kernel,streams", [(0, 0), (2, 0), (0, 2), (4, 0), (7, 0)])
 def test_units_random_budgets(row_kernel, streams):
     # Random budgets over a batch of runs that start at every cursor of a
     # position (between phases and inside them), grouped heads, temperature
