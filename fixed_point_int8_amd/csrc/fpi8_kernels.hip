@@ -62,7 +62,7 @@ __device__ __forceinline__ uint64_t isqrt64(uint64_t n) {
 // double quotient (rem * 2^32 is exact in a double; the rounded quotient is
 // at most one above the true floor), checked with one exact product.  Two
 // 64-bit integer divisions cost about 1.4 us of a normalization's chain.
-__host__ __device__ __forceinline__ uint64_t recip64_32(uint32_t r) {
+__device__ __forceinline__ uint64_t recip64_32(uint32_t r) {
   uint32_t q1 = 0xFFFFFFFFu / r;
   if (0xFFFFFFFFu - q1 * r == r - 1) q1++;           // floor(2^32 / r)
   const uint32_t rem = 0u - q1 * r;                   // 2^32 - q1 * r, in [0, r)
@@ -70,6 +70,17 @@ __host__ __device__ __forceinline__ uint64_t recip64_32(uint32_t r) {
   uint64_t q0 = (uint64_t)((double)n / (double)r);
   if (q0 * r > n) q0--;                               // floor(rem * 2^32 / r)
   return ((uint64_t)q1 << 32) | q0;
+}
+
+// floor(2^64 / d) for any d >= 2: recip64_32 below 2^32; from 2^32 on the
+// quotient is below 2^32, so a correctly rounded double quotient is the
+// floor or one above it, settled by the exact 128-bit product.
+__device__ __forceinline__ uint64_t recip64(uint64_t d) {
+  if (d < (1ull << 32)) return recip64_32((uint32_t)d);
+  uint64_t q = (uint64_t)(18446744073709551616.0 / (double)d);
+  const uint64_t hi = __umul64hi(q, d);
+  if (hi > 1 || (hi == 1 && q * d != 0)) q--;  // q * d > 2^64
+  return q;
 }
 
 __device__ __forceinline__ uint8_t *run_base(uint8_t *states, const RunDesc &rd) {
@@ -1525,8 +1536,18 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     *reinterpret_cast<int64_t *>(st + ST_MAXSCORE) = m;
     *reinterpret_cast<uint64_t *>(st + ST_SUM) = S;
   }
+  // The division by S through its reciprocal floor(2^64 / S): the high half
+  // of n times it is the quotient or one less, and one remainder test fixes
+  // it (Granlund and Montgomery, 1994).
+  const uint64_t Sm = S > 1 ? recip64(S) : 0;
   for (uint32_t j = tid; j < npos; j += blockDim.x) {
-    const int64_t p = (int64_t)(((uint64_t)sc[j] << 24) / S);
+    const uint64_t n = (uint64_t)sc[j] << 24;
+    uint64_t q = n;
+    if (S > 1) {
+      q = __umul64hi(n, Sm);
+      if (n - q * S >= S) q++;
+    }
+    const int64_t p = (int64_t)q;
     sc[j] = p;
     if (scores_out) scores_out[j] = p;
   }
