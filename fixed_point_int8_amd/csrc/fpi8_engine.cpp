@@ -530,7 +530,8 @@ int32_t fpi8_engine_create(const uint8_t *h_section0, uint64_t section0_len, con
   e->blob_len = blob_len;
   e->max_runs = max_runs;
   e->max_npos = c.context;
-  if (attention_lds_bytes(e->max_npos, c.head) > 160 * 1024) { delete e; return FPI8_ERR_UNSUPPORTED; }
+  // scores and partial sums, plus the kernel's own 4 KB, within 160 KB of LDS
+  if (attention_lds_bytes(e->max_npos, c.head) + 4096 > 160 * 1024) { delete e; return FPI8_ERR_UNSUPPORTED; }
   e->exp_tab = reinterpret_cast<const uint32_t *>(d_blob + e->model.off_exp);
   e->silu = reinterpret_cast<const int32_t *>(d_blob + e->model.off_silu);
   e->cos_t = reinterpret_cast<const int32_t *>(d_blob + e->model.off_cos);
