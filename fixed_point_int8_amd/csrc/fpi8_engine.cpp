@@ -82,6 +82,12 @@ struct fpi8_engine {
   // run still has; `resume`: some run stood inside a position at the bind.
   uint8_t *bound_states = nullptr;
   uint32_t bound_runs = 0, bound_left = 0, bound_resume = 0;
+  // The current turn's arena stride and, when every run of the batch is a
+  // valid state with x at the same offset, that offset (~0 otherwise): the
+  // normalization then reads x before the run descriptors.  Part of what a
+  // recorded graph is valid for.
+  uint64_t x_stride = 0, x_off = ~0ull;
+  uint64_t graph_x_stride = 0, graph_x_off = 0;
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -335,6 +341,14 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
   return launch_rows(epi, p.kind, p.mt, p.bt, a, s);
 }
 
+// Where the group's runs keep x, when every run of the turn keeps it at
+// the same offset.
+void uniform_x(const fpi8_engine *e, const Group &G, uint8_t *states, NormArgs &na) {
+  if (e->x_off == ~0ull) return;
+  na.x_first = states + (uint64_t)(G.runs - e->d_runs) * e->x_stride + e->x_off;
+  na.x_stride = e->x_stride;
+}
+
 // One position of every active run of a group.  `partial`: some run starts
 // this position between two phases or stops before its end, so each launch
 // checks the steps each run runs (run_flags, RunDesc::end); every launch
@@ -358,6 +372,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
     const uint32_t s0 = 1 + 7 * l;
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * l) * c.dim,
                 G.planes0, e->kp, e->bp, fl + 0, 0, s0, partial};
+    uniform_x(e, G, states, na);
     {
       TimedLaunch t(e, T_NORM, s);
       if ((r = launch_norm(na, s))) return r;
@@ -413,6 +428,7 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
   {
     NormArgs na{states, G.runs, n_runs, c.dim, e->norm + (uint64_t)(2 * c.layers) * c.dim,
                 G.planes0, e->kp, e->bp, ff, 1, 1 + 7 * c.layers, partial};
+    uniform_x(e, G, states, na);
     TimedLaunch t(e, T_NORM, s);
     if ((r = launch_norm(na, s))) return r;
   }
@@ -458,7 +474,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s, uint32
 // descriptors on the device, so the same graph serves every position.
 int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   if (e->graph && e->graph_states == states && e->graph_runs == n_runs && e->graph_cap == e->score_cap &&
-      e->graph_groups == n_groups(e, n_runs))
+      e->graph_groups == n_groups(e, n_runs) && e->graph_x_stride == e->x_stride && e->graph_x_off == e->x_off)
     return 0;
   if (e->graph) {
     (void)hipGraphExecDestroy(e->graph);
@@ -486,6 +502,8 @@ int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   e->graph_runs = n_runs;
   e->graph_cap = e->score_cap;
   e->graph_groups = n_groups(e, n_runs);
+  e->graph_x_stride = e->x_stride;
+  e->graph_x_off = e->x_off;
   return 0;
 }
 
@@ -728,6 +746,12 @@ int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs
   uint32_t cap = 256;
   for (uint32_t b = 0; b < n_runs; b++)
     if (e->h_runs[b].valid) cap = std::max(cap, (e->h_runs[b].cachepos + 255) / 256 * 256);
+  // One offset of x for the whole batch, all of whose states are valid (so
+  // that every run's state holds the bytes read there).
+  e->x_stride = stride;
+  e->x_off = e->h_runs[0].valid ? e->h_runs[0].off_x : ~0ull;
+  for (uint32_t b = 1; b < n_runs && e->x_off != ~0ull; b++)
+    if (!e->h_runs[b].valid || e->h_runs[b].off_x != e->x_off) e->x_off = ~0ull;
   e->score_cap = std::min(cap, e->max_npos);
   if ((r = hip_ok(hipMemcpyAsync(e->d_runs, e->h_runs, sizeof(RunDesc) * n_runs,
                                  hipMemcpyHostToDevice, s))) ||

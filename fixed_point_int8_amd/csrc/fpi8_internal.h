@@ -180,6 +180,10 @@ struct NormArgs {
   uint32_t *oflag;
   uint32_t final_norm;      // 1: only generating runs (phase 17)
   uint32_t step, partial;   // as in RowsArgs
+  // Every run of the batch keeps x at the same offset of its state: run b's
+  // x is at x_first + b * x_stride (nullptr: read each run's descriptor first)
+  const uint8_t *x_first;
+  uint64_t x_stride;
 };
 
 struct EmbedArgs {

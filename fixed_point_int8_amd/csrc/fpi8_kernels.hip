@@ -321,8 +321,25 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
   __shared__ uint64_t scratch[8];
   constexpr int U = 8;  // loads in flight per thread
   const uint32_t b = blockIdx.x, nt = blockDim.x;
+  const bool whole = a.dim <= nt * U;
+  // When every run keeps x at the same offset (a.x_first), the whole-vector
+  // path reads x before the run's descriptor arrives, so the two round trips
+  // overlap; a run that takes no part leaves after its sum.
+  const int64_t *xu = whole && a.x_first ? reinterpret_cast<const int64_t *>(a.x_first + (uint64_t)b * a.x_stride)
+                                         : nullptr;
+  int64_t xv[U];
+  int32_t wv[U];
+  if (xu) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t i = threadIdx.x + u * nt;
+      xv[u] = i < a.dim ? xu[i] : 0;
+      wv[u] = i < a.dim ? a.w[i] : 0;
+    }
+  }
   const RunDesc &rd = a.runs[b];
-  if (!live_at(rd, rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.partial)) return;
+  const bool live = live_at(rd, rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.partial);
+  if (!xu && !live) return;
   uint8_t *st = run_base(a.states, rd);
   const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
   int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
@@ -349,23 +366,24 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     m = r > 1 ? recip64_32((uint32_t)r) : 0;
     return r;
   };
-  if (a.dim <= nt * U) {
+  if (whole) {
     // The whole vector fits in registers: x and the weights are read once,
     // together.  gridDim.y workgroups share a run: each sums all of x (a
     // few L2 reads) and finishes its own share of the registers, so the
     // stores spread over more compute units.
-    int64_t xv[U];
-    int32_t wv[U];
     uint64_t ss = 0;
+    if (!xu) {
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const uint32_t i = threadIdx.x + u * nt;
-      xv[u] = i < a.dim ? x[i] : 0;
-      wv[u] = i < a.dim ? a.w[i] : 0;
+      for (int u = 0; u < U; u++) {
+        const uint32_t i = threadIdx.x + u * nt;
+        xv[u] = i < a.dim ? x[i] : 0;
+        wv[u] = i < a.dim ? a.w[i] : 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) ss += (uint64_t)wmul(xv[u], xv[u]);
     ss = block_sum_u64(ss, scratch);
+    if (!live) return;
     uint64_t m;
     const uint64_t r = rms_of(ss, m);
     const uint32_t part = blockIdx.y, parts = gridDim.y;
