@@ -82,12 +82,19 @@ struct fpi8_engine {
   // run still has; `resume`: some run stood inside a position at the bind.
   uint8_t *bound_states = nullptr;
   uint32_t bound_runs = 0, bound_left = 0, bound_resume = 0;
-  // The current turn's arena stride and, when every run of the batch is a
-  // valid state with x at the same offset, that offset (~0 otherwise): the
-  // normalization then reads x before the run descriptors.  Part of what a
-  // recorded graph is valid for.
-  uint64_t x_stride = 0, x_off = ~0ull;
-  uint64_t graph_x_stride = 0, graph_x_off = 0;
+  // The current turn's layout when every run of the batch is a valid state
+  // with the same buffer offsets and cache length (uni.on): the
+  // normalization and attention then read their inputs before the run
+  // descriptors arrive.  Part of what a recorded graph is valid for.
+  struct Uniform {
+    bool on = false;
+    uint64_t stride = 0, off_x = 0, off_w2 = 0, off_keys = 0, off_values = 0;
+    uint32_t cachepos = 0;
+    bool operator==(const Uniform &o) const {
+      return on == o.on && stride == o.stride && off_x == o.off_x && off_w2 == o.off_w2 &&
+             off_keys == o.off_keys && off_values == o.off_values && cachepos == o.cachepos;
+    }
+  } uni, graph_uni;
 
   const Mat &layer_mat(uint32_t l, uint32_t kind) const { return mats[1 + 7 * l + (kind - M_Q)]; }
 };
@@ -344,9 +351,9 @@ int run_rows(fpi8_engine *e, int epi, RowsArgs &a, uint32_t n_runs, hipStream_t 
 // Where the group's runs keep x, when every run of the turn keeps it at
 // the same offset.
 void uniform_x(const fpi8_engine *e, const Group &G, uint8_t *states, NormArgs &na) {
-  if (e->x_off == ~0ull) return;
-  na.x_first = states + (uint64_t)(G.runs - e->d_runs) * e->x_stride + e->x_off;
-  na.x_stride = e->x_stride;
+  if (!e->uni.on) return;
+  na.x_first = states + (uint64_t)(G.runs - e->d_runs) * e->uni.stride + e->uni.off_x;
+  na.x_stride = e->uni.stride;
 }
 
 // One position of every active run of a group.  `partial`: some run starts
@@ -388,6 +395,13 @@ int step_group(fpi8_engine *e, const Group &G, uint8_t *states, hipStream_t s, u
       AttnArgs a{states, G.runs, n_runs, l, c.heads, c.kv_heads, c.head,
                  c.heads / c.kv_heads, e->model.inv, e->exp_tab, G.planes0, e->kp, e->bp,
                  fl + 1, e->score_cap, s0 + 2, partial};
+      if (e->uni.on) {
+        a.u_first = states + (uint64_t)(G.runs - e->d_runs) * e->uni.stride;
+        a.u_stride = e->uni.stride;
+        a.u_off_q = e->uni.off_w2;
+        a.u_off_keys = e->uni.off_keys;
+        a.u_cachepos = e->uni.cachepos;
+      }
       TimedLaunch t(e, T_ATTN, s);
       if ((r = launch_attention(a, s))) return r;
     }
@@ -474,7 +488,7 @@ int step(fpi8_engine *e, uint8_t *states, uint32_t n_runs, hipStream_t s, uint32
 // descriptors on the device, so the same graph serves every position.
 int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   if (e->graph && e->graph_states == states && e->graph_runs == n_runs && e->graph_cap == e->score_cap &&
-      e->graph_groups == n_groups(e, n_runs) && e->graph_x_stride == e->x_stride && e->graph_x_off == e->x_off)
+      e->graph_groups == n_groups(e, n_runs) && e->graph_uni == e->uni)
     return 0;
   if (e->graph) {
     (void)hipGraphExecDestroy(e->graph);
@@ -502,8 +516,7 @@ int step_graph(fpi8_engine *e, uint8_t *states, uint32_t n_runs) {
   e->graph_runs = n_runs;
   e->graph_cap = e->score_cap;
   e->graph_groups = n_groups(e, n_runs);
-  e->graph_x_stride = e->x_stride;
-  e->graph_x_off = e->x_off;
+  e->graph_uni = e->uni;
   return 0;
 }
 
@@ -746,12 +759,23 @@ int32_t turn(fpi8_engine *e, uint8_t *d_states, uint64_t stride, uint32_t n_runs
   uint32_t cap = 256;
   for (uint32_t b = 0; b < n_runs; b++)
     if (e->h_runs[b].valid) cap = std::max(cap, (e->h_runs[b].cachepos + 255) / 256 * 256);
-  // One offset of x for the whole batch, all of whose states are valid (so
-  // that every run's state holds the bytes read there).
-  e->x_stride = stride;
-  e->x_off = e->h_runs[0].valid ? e->h_runs[0].off_x : ~0ull;
-  for (uint32_t b = 1; b < n_runs && e->x_off != ~0ull; b++)
-    if (!e->h_runs[b].valid || e->h_runs[b].off_x != e->x_off) e->x_off = ~0ull;
+  // One layout for the whole batch, all of whose states are valid (so that
+  // every run's state holds the bytes read at those offsets).
+  {
+    const RunDesc &r0 = e->h_runs[0];
+    fpi8_engine::Uniform u;
+    u.on = r0.valid != 0;
+    u.stride = stride;
+    u.off_x = r0.off_x; u.off_w2 = r0.off_w2; u.off_keys = r0.off_keys; u.off_values = r0.off_values;
+    u.cachepos = r0.cachepos;
+    for (uint32_t b = 1; b < n_runs && u.on; b++) {
+      const RunDesc &rd = e->h_runs[b];
+      u.on = rd.valid && rd.off_x == u.off_x && rd.off_w2 == u.off_w2 && rd.off_keys == u.off_keys &&
+             rd.off_values == u.off_values && rd.cachepos == u.cachepos;
+    }
+    if (!u.on) u = fpi8_engine::Uniform{};
+    e->uni = u;
+  }
   e->score_cap = std::min(cap, e->max_npos);
   if ((r = hip_ok(hipMemcpyAsync(e->d_runs, e->h_runs, sizeof(RunDesc) * n_runs,
                                  hipMemcpyHostToDevice, s))) ||

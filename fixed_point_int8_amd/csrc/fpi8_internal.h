@@ -206,6 +206,13 @@ struct AttnArgs {
   uint32_t *oflag;
   uint32_t max_npos;        // LDS score slots: at least every run's cache positions
   uint32_t step, partial;   // as in RowsArgs
+  // Every run of the batch has the same layout: run b's state is at
+  // u_first + b * u_stride, its queries at u_off_q, its keys at u_off_keys
+  // and u_cachepos cache positions (u_first nullptr: read each run's
+  // descriptor first)
+  const uint8_t *u_first;
+  uint64_t u_stride, u_off_q, u_off_keys;
+  uint32_t u_cachepos;
 };
 
 // The head of attention a turn of units stops inside: its stages up to the

@@ -337,12 +337,17 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
       wv[u] = i < a.dim ? a.w[i] : 0;
     }
   }
+  // The descriptor fields this kernel reads, requested together.
   const RunDesc &rd = a.runs[b];
-  const bool live = live_at(rd, rd.flags, a.final_norm ? RUN_GEN : RUN_ACTIVE, a.step, a.partial);
+  const uint32_t flags = rd.flags, rend = rd.end, partial = a.partial, step = a.step;
+  const uint64_t base = rd.base, off_x = rd.off_x, off_w1 = rd.off_w1;
+  asm volatile("" ::"s"(flags), "s"(rend), "s"(partial), "s"(step), "s"(base), "s"(off_x), "s"(off_w1));
+  const bool live = (flags & (a.final_norm ? RUN_GEN : RUN_ACTIVE)) != 0 &&
+                    (partial == 0 || ((flags >> 8) <= step && step < rend));
   if (!xu && !live) return;
-  uint8_t *st = run_base(a.states, rd);
-  const int64_t *x = reinterpret_cast<const int64_t *>(st + rd.off_x);
-  int64_t *y = reinterpret_cast<int64_t *>(st + rd.off_w1);
+  uint8_t *st = a.states + base;
+  const int64_t *x = reinterpret_cast<const int64_t *>(st + off_x);
+  int64_t *y = reinterpret_cast<int64_t *>(st + off_w1);
   // y = ((x * w) / rms) >> 8 with a truncating division by rms, through
   // its 64-bit reciprocal m = floor(2^64 / rms): q = mulhi(|p|, m) is the
   // quotient or one less, and one remainder test fixes it (Granlund and
@@ -1386,27 +1391,9 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   int64_t *red = sc + a.max_npos;
 
   const uint32_t h = blockIdx.x, b = blockIdx.y;
-  const RunDesc &rd = a.runs[b];
-  if (!live_at(rd, rd.flags, RUN_ACTIVE, a.step, a.partial)) return;
-  // A turn of units that stops the run inside this phase: the heads before
-  // the stop's head are whole, the rest is the tail's (k_attention_tail).
-  uint32_t last = a.heads - 1;
-  if (a.partial && rd.stop_ph == 9 && a.step == rd.stop_in) {
-    if (h >= rd.stop_row) return;
-    last = rd.stop_row - 1;
-  }
   const uint32_t hs = HS ? HS : a.head;
   const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
-  const uint32_t npos = rd.pos + 1, cachepos = rd.cachepos;
-  uint8_t *st = a.states + rd.base;
-  const int64_t *q = reinterpret_cast<const int64_t *>(st + rd.off_w2) + (uint64_t)h * hs;
   const uint32_t kvh = h / a.group;
-  const uint64_t head_base = ((uint64_t)a.layer * a.kv_heads + kvh) * cachepos * hs;
-  const int32_t *K = reinterpret_cast<const int32_t *>(st + rd.off_keys) + head_base;
-  const int32_t *V = reinterpret_cast<const int32_t *>(st + rd.off_values) + head_base;
-
-  for (uint32_t i = tid; i < hs; i += blockDim.x) qs[i] = q[i];
-  __syncthreads();
 
   // Heads of a power-of-two size of at least 4 take the vector path: LPP
   // lanes hold one position's row, 16 bytes each, so one load instruction of
@@ -1416,6 +1403,59 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   constexpr int GP = 256 / LPP;          // positions per workgroup step
   constexpr int U = 4;                   // positions per lane in one batch; two batches in flight
   const int lp = tid % LPP, pg = tid / LPP;
+
+  // When every run has the same layout (a.u_first), the head's queries and
+  // its first batch of keys are requested before the run's descriptor
+  // arrives, so the two round trips overlap.  That batch's rows past the
+  // cache read its last row (in bounds); like every row at or past the
+  // position, they count for nothing.
+  const bool pre = VEC && a.u_first != nullptr;
+  int64_t qpre = 0;
+  v4i A[U];
+  if (pre) {
+    const uint8_t *su = a.u_first + (uint64_t)b * a.u_stride;
+    if (tid < (int)hs) qpre = reinterpret_cast<const int64_t *>(su + a.u_off_q)[(uint64_t)h * hs + tid];
+    const int32_t *Ku = reinterpret_cast<const int32_t *>(su + a.u_off_keys) +
+                        ((uint64_t)a.layer * a.kv_heads + kvh) * a.u_cachepos * hs;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t j = pg + GP * u;
+      A[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i *>(Ku + (uint64_t)(j < a.u_cachepos ? j : a.u_cachepos - 1) * hs + 4 * lp));
+    }
+  }
+
+  // The descriptor fields this kernel reads, requested together (one round
+  // trip rather than one per test below).
+  const RunDesc &rd = a.runs[b];
+  const uint32_t flags = rd.flags, pos = rd.pos, rend = rd.end, cachepos = rd.cachepos;
+  const uint32_t stop_ph = rd.stop_ph, stop_in = rd.stop_in, stop_row = rd.stop_row;
+  const uint64_t base = rd.base, off_w2 = rd.off_w2, off_keys = rd.off_keys, off_values = rd.off_values;
+  const uint32_t partial = a.partial, step = a.step;
+  asm volatile("" ::"s"(flags), "s"(pos), "s"(rend), "s"(cachepos), "s"(stop_ph), "s"(stop_in), "s"(stop_row),
+               "s"(base), "s"(off_w2), "s"(off_keys), "s"(off_values), "s"(partial), "s"(step));
+  if ((flags & RUN_ACTIVE) == 0 || (partial != 0 && ((flags >> 8) > step || step >= rend))) return;
+  // A turn of units that stops the run inside this phase: the heads before
+  // the stop's head are whole, the rest is the tail's (k_attention_tail).
+  uint32_t last = a.heads - 1;
+  if (partial && stop_ph == 9 && step == stop_in) {
+    if (h >= stop_row) return;
+    last = stop_row - 1;
+  }
+  const uint32_t npos = pos + 1;
+  uint8_t *st = a.states + base;
+  const int64_t *q = reinterpret_cast<const int64_t *>(st + off_w2) + (uint64_t)h * hs;
+  const uint64_t head_base = ((uint64_t)a.layer * a.kv_heads + kvh) * cachepos * hs;
+  const int32_t *K = reinterpret_cast<const int32_t *>(st + off_keys) + head_base;
+  const int32_t *V = reinterpret_cast<const int32_t *>(st + off_values) + head_base;
+
+  if (pre) {
+    if (tid < (int)hs) qs[tid] = qpre;
+  } else {
+    for (uint32_t i = tid; i < hs; i += blockDim.x) qs[i] = q[i];
+  }
+  __syncthreads();
+
   // Batch jb holds positions jb + pg + GP u.  Positions past the end load
   // the last row (a valid address whose line is already near) and count
   // for nothing, so every load is unconditional and the next batch is
@@ -1506,8 +1546,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       };
       // The scheduling fences keep each batch's loads in program order, so
       // summing one batch waits only for that batch.
-      v4i A[U], B[U];
-      fetch(A, 0);
+      v4i B[U];
+      if (!pre) fetch(A, 0);
       for (uint32_t jb = 0; jb < npos; jb += 2 * GP * U) {
         __builtin_amdgcn_sched_barrier(0);
         fetch(B, jb + GP * U);
