@@ -1173,22 +1173,87 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
   const uint32_t b0 = chunk * BT * 16;
   const uint32_t wr = a.wave_rows;
   const bool own = (uint32_t)wave < wr;
+  // Whether this batch chunk has a run in this phase; read first, tested
+  // after the first stages are on their way.
   const bool busy = EPI == EPI_RAW || row_run_ok<EPI, false>(a, b0 + (tid & (16 * BT - 1)));
 
   __shared__ int32_t silu_lds[EPI == EPI_GATEUP ? 4096 : 1];
   RowTile<MT> t;
   row_tile<EPI, MT>(a, tile * wr + (own ? wave : 0), lg, own, t);
+
+  const uint32_t nch = a.kblocks / CD;
+  const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
+  const uint8_t *wsrc[MT];
+  const uint32_t wstride = a.packed ? 1024 : 64;  // bytes from one 64-column block to the next
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
+    wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)t.ptile[mt] * a.kblocks * 1024 + lane * 16
+                        : t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
+  }
+  // This wave stages fragments f = wave + Wq of every stage; fragment f
+  // is (limb l, run tile bt, block c).  Runs past the batch bring
+  // whatever their plane rows hold; those product columns are never stored.
+  const int8_t *dsrc[FW];
+#pragma unroll
+  for (int q = 0; q < FW; q++) {
+    const int f = wave + W * q;
+    const int l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
+    dsrc[q] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + c) * 64 + lane) * 16;
+  }
+  v4i *ring[NB];
+  ring[0] = ring_buf<0, FR * 64>();
+  ring[1] = ring_buf<1, FR * 64>();
+  ring[2] = ring_buf<2, FR * 64>();
+  ring[3] = ring_buf<3, FR * 64>();
+  if constexpr (NB > 4) ring[4] = ring_buf<4, FR * 64>();
+  if constexpr (NB > 5) ring[5] = ring_buf<5, FR * 64>();
+  if constexpr (NB > 6) ring[6] = ring_buf<6, FR * 64>();
+  if constexpr (NB > 7) ring[7] = ring_buf<7, FR * 64>();
+
+  v4i Wr[NB][MT][CD];
+  // Stage st into buffer s (weights into register slot s, digits into LDS
+  // buffer s), by a wave that owns rows (OWN) or only stages digits.
+  auto issue = [&](auto own_tag, int s, uint32_t st) {
+    constexpr bool OWN = decltype(own_tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (OWN) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int c = 0; c < CD; c++)
+          Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * wstride);
+    }
+#pragma unroll
+    for (int q = 0; q < FW; q++)
+      __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
+                                       (lds_void *)(ring[s] + (wave + W * q) * 64), 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The ring's first P stages go out before anything waits (the run flags,
+  // the descriptors, the inputs' digit check); the exact path and a chunk
+  // with no run in this phase only drain them.
+  const uint32_t last = nch - 1;
+  if (own) {
+#pragma unroll
+    for (int s = 0; s < P; s++) issue(std::true_type{}, s, (uint32_t)s < nch ? (uint32_t)s : last);
+  } else {
+#pragma unroll
+    for (int s = 0; s < P; s++) issue(std::false_type{}, s, (uint32_t)s < nch ? (uint32_t)s : last);
+  }
+
   EpiIn<EPI, MT, BT> in;
   if (own) epi_begin<EPI, MT, BT>(a, b0, li, in);  // waves that own rows run an epilogue
   if constexpr (EPI == EPI_GATEUP) silu_to_lds(a.silu, silu_lds, wave, W, lane);
   const bool exact = input_needs_exact(a);
   if (EPI != EPI_RAW && !__any(busy ? 1 : 0)) {  // every wave sees all runs of the chunk
-    wait_vm<0>();  // no table load may still be landing in LDS
+    wait_vm<0>();  // no staging or table load may still be landing in LDS
     return;
   }
 
   int64_t v[MT][BT][4];
   if (exact) {
+    wait_vm<0>();  // the staged stages are not used; none may still be landing in LDS
     if (own) {
       epi_fetch<EPI, MT, BT>(a, t, lg, in);
       rows_exact<EPI, MT, BT, false>(a, t, b0, 0, a.cols, li, lg, v);
@@ -1202,59 +1267,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
 #pragma unroll
         for (int bt = 0; bt < BT; bt++) acc[mt][l][bt] = v4i{0, 0, 0, 0};
 
-    const uint32_t nch = a.kblocks / CD;
-    const uint32_t kbp = a.kp / 64, nbt = a.bp / 16;
-    const uint8_t *wsrc[MT];
-    const uint32_t wstride = a.packed ? 1024 : 64;  // bytes from one 64-column block to the next
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      const uint32_t row = t.rbase[mt] + li < t.rcount[mt] ? t.rbase[mt] + li : t.rcount[mt] - 1;
-      wsrc[mt] = a.packed ? t.Pp[mt] + (uint64_t)t.ptile[mt] * a.kblocks * 1024 + lane * 16
-                          : t.Wp[mt] + (uint64_t)row * a.cols + lg * 16;
-    }
-    // This wave stages fragments f = wave + Wq of every stage; fragment f
-    // is (limb l, run tile bt, block c).  Runs past the batch bring
-    // whatever their plane rows hold; those product columns are never stored.
-    const int8_t *dsrc[FW];
-#pragma unroll
-    for (int q = 0; q < FW; q++) {
-      const int f = wave + W * q;
-      const int l = f / (BT * CD), bt = (f / CD) % BT, c = f % CD;
-      dsrc[q] = a.planes + ((((uint64_t)l * nbt + (b0 >> 4) + bt) * kbp + c) * 64 + lane) * 16;
-    }
-    v4i *ring[NB];
-    ring[0] = ring_buf<0, FR * 64>();
-    ring[1] = ring_buf<1, FR * 64>();
-    ring[2] = ring_buf<2, FR * 64>();
-    ring[3] = ring_buf<3, FR * 64>();
-    if constexpr (NB > 4) ring[4] = ring_buf<4, FR * 64>();
-    if constexpr (NB > 5) ring[5] = ring_buf<5, FR * 64>();
-    if constexpr (NB > 6) ring[6] = ring_buf<6, FR * 64>();
-    if constexpr (NB > 7) ring[7] = ring_buf<7, FR * 64>();
-
-    v4i Wr[NB][MT][CD];
-    // The stage loop of a wave that owns rows (OWN) or only stages digits.
-    // Both take the same stages and barriers.
+    // The stage loop, after the first P stages.
     auto stream = [&](auto own_tag) {
       constexpr bool OWN = decltype(own_tag)::value;
       constexpr int NL = (OWN ? MT * CD : 0) + FW;  // loads per stage
-      // Stage st into buffer s (weights into register slot s, digits into
-      // LDS buffer s).
-      auto issue = [&](int s, uint32_t st) {
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (OWN) {
-#pragma unroll
-          for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-            for (int c = 0; c < CD; c++)
-              Wr[s][mt][c] = *reinterpret_cast<const v4i *>(wsrc[mt] + ((uint64_t)st * CD + c) * wstride);
-        }
-#pragma unroll
-        for (int q = 0; q < FW; q++)
-          __builtin_amdgcn_global_load_lds((const void *)(dsrc[q] + (uint64_t)st * CD * 1024),
-                                           (lds_void *)(ring[s] + (wave + W * q) * 64), 16, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      };
       auto compute = [&](int s) {
         if constexpr (OWN) {
           const int flip = (int)0x80808080u;
@@ -1284,10 +1300,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
       // wave issues stage k + P (the last stage again when there is no
       // further one) into buffer (k + P) % NB, the one stage k - 1 used,
       // then computes stage k.  P - 1 younger stages are in flight at every
-      // wait.
-      const uint32_t last = nch - 1;
-#pragma unroll
-      for (int s = 0; s < P; s++) issue(s, (uint32_t)s < nch ? (uint32_t)s : last);
+      // wait (and the loads issued after the first P stages, which only
+      // make the first waits longer).
       if constexpr (OWN) epi_fetch<EPI, MT, BT>(a, t, lg, in);
       uint32_t ch = 0;
       for (; ch + NB <= nch; ch += NB) {
@@ -1296,7 +1310,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
           wait_vm<(P - 1) * NL>();
           lds_barrier();
           const uint32_t nx = ch + s + P;
-          issue((s + P) % NB, nx < nch ? nx : last);
+          issue(own_tag, (s + P) % NB, nx < nch ? nx : last);
           compute(s);
         }
       }
@@ -1306,7 +1320,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 &
           wait_vm<(P - 1) * NL>();
           lds_barrier();
           const uint32_t nx = ch + s + P;
-          issue((s + P) % NB, nx < nch ? nx : last);
+          issue(own_tag, (s + P) % NB, nx < nch ? nx : last);
           compute(s);
         }
       }
