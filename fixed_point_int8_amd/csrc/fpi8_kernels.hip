@@ -2033,10 +2033,13 @@ int launch_embed(const EmbedArgs &a, void *stream) {
 }
 
 int launch_norm(const NormArgs &a, void *stream) {
-  // Four workgroups per run share the stores when the vector fits one
-  // workgroup's registers (8 of them per thread); otherwise one workgroup.
-  const uint32_t parts = a.dim <= 512 * 8 ? 4 : 1;
-  hipLaunchKernelGGL(k_norm, dim3(a.n_runs, parts), dim3(512), 0, (hipStream_t)stream, a);
+  // Several workgroups per run share the stores when the vector fits one
+  // workgroup's registers (8 of them per thread): eight of 256 threads up
+  // to 2048 elements, four of 512 up to 4096 (measured: eight of 512 were
+  // slower there); otherwise one workgroup.
+  const uint32_t threads = a.dim <= 256 * 8 ? 256 : 512;
+  const uint32_t parts = a.dim <= 256 * 8 ? 8 : a.dim <= 512 * 8 ? 4 : 1;
+  hipLaunchKernelGGL(k_norm, dim3(a.n_runs, parts), dim3(threads), 0, (hipStream_t)stream, a);
   return ok(hipGetLastError());
 }
 
