@@ -290,6 +290,45 @@ def test_small_shapes_greedy(name):
     run_pair(shape, blob, runs, [1, 2, 3, 1, 5])
 
 
+def test_one_arena_across_layouts():
+    # The engine records a position as a graph per (arena, run count, score
+    # slots, layout).  When every run of a batch has the same buffer offsets,
+    # the normalization and attention read through those offsets before the
+    # run descriptors arrive; the same arena then holds batches whose runs
+    # differ (the descriptors' path) and another common layout: each must
+    # record its own graph, or the step reads the previous batch's offsets.
+    torch = require_gpu()
+    shape = W.SMALL_SHAPES["wide"]
+    cfg = shape.as_tuple()
+    say("one arena across layouts")
+    blob = Bl.build_blob(shape, 31)
+    batches = [spec(shape, 4, 5, 6, seed=1),                  # one layout
+               spec(shape, 4, [3, 4, 5, 7], [6, 5, 4, 3], seed=2),  # four layouts
+               spec(shape, 4, 9, 4, seed=3),                  # one layout, other offsets
+               spec(shape, 4, 5, 6, seed=4)]                  # the first layout again
+    stride = max(B.fpi8_state_size(cfg, len(ids), mx) for b in batches for ids, mx, _, _ in b)
+    stride = (stride + 255) // 256 * 256
+    model = DeviceModel(blob, 4)
+    try:
+        arena = None
+        for k, runs in enumerate(batches):
+            pair = Pair(shape, blob, runs, model=model)
+            if arena is None:
+                arena = torch.zeros(4 * stride, dtype=torch.uint8, device="cuda")
+            # the batch's fresh states, moved into the one arena at the one stride
+            arena.zero_()
+            b = pair.batch
+            for i in range(4):
+                arena[i * stride: i * stride + b.sizes[i]].copy_(b.d_states[i * b.stride: i * b.stride + b.sizes[i]])
+            b.d_states, b.stride = arena, stride
+            for cut in (2, 3):
+                pair.turn(cut)
+                pair.compare()
+            say(f"batch {k} matches")
+    finally:
+        model.close()
+
+
 @pytest.mark.parametrize("n_runs", [3, 20, 40, 70])
 def test_split_contraction_whole_pass(n_runs):
     # dim 1024 and hidden 2816: every matrix's columns are shared by several
