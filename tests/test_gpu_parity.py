@@ -63,14 +63,14 @@ def test_matrix_rows_packed_exact_path():
 
 # Matrices of 65,536 rows or more (the stream launch's threshold on 256
 # compute units: every wave gets a tile of 64 rows) with a multiple of 8
-# blocks of 64 columns take the persistent streaming kernel: its wave-owned
-# shape up to 16 inputs, the shared-digit shapes from 17 to 128.  Rows past
-# the last full tile, columns inside the last block, inputs that end inside
-# a run tile, and every launch-shape boundary.
+# blocks of 64 columns take the persistent streaming kernels: the
+# digit-sharing shapes up to 64 inputs, the weight-sharing one from 65 to
+# 128.  Rows past the last full tile, columns inside the last block, inputs
+# that end inside a run tile, and every launch-shape boundary.
 @pytest.mark.parametrize("rows,cols,batch", [
     (65573, 4066, 1), (65536, 4096, 8), (65552, 512, 16), (65536, 4096, 17), (65600, 4096, 32),
     (65536, 2048, 33), (65541, 4096, 64), (65536, 512, 65), (65536, 512, 100), (65536, 4096, 128),
-    (131072, 512, 3)])
+    (65573, 4066, 97), (66000, 1024, 128), (131072, 512, 3)])
 def test_matrix_rows_packed_stream(rows, cols, batch):
     say(f"matrix_rows_packed stream {rows}x{cols} batch {batch}")
     O.set_threads(16)
@@ -81,7 +81,7 @@ def test_matrix_rows_packed_stream(rows, cols, batch):
         O.set_threads(1)
 
 
-@pytest.mark.parametrize("batch", [5, 40])
+@pytest.mark.parametrize("batch", [5, 40, 100])
 def test_matrix_rows_packed_stream_exact_path(batch):
     # A word beyond three digits sends the whole streaming launch down the
     # exact 64-bit loop; extreme weights and scales in the first rows.
