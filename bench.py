@@ -278,7 +278,7 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
 def cpu_baseline(blob, shape, name, seconds=12.0, max_positions=64):
     """The oracle on the host: one run of the same model from a one-id prompt,
     generating (classifier included) in turns of 4 positions until about
-    `seconds` of wall time have passed, on as many threads as the box gives
+    `seconds` of wall time have passed, on as many threads as the host gives
     this job (at most 16)."""
     import oracle as O
     import workloads as Wl
