@@ -575,6 +575,48 @@ def test_queued_turns():
         pair.model.close()
 
 
+def test_queued_turns_across_layouts():
+    # Queued turns over one arena whose batches change layout between binds:
+    # one common layout, another common layout, then runs of several
+    # layouts.  Each bind decides whether the normalization and attention
+    # may read through common offsets, and the recorded graph follows it.
+    torch = require_gpu()
+    shape = W.SMALL_SHAPES["wide"]
+    cfg = shape.as_tuple()
+    say("queued turns across layouts")
+    blob = Bl.build_blob(shape, 41)
+    batches = [spec(shape, 4, 5, 6, seed=5), spec(shape, 4, 7, 5, seed=6),
+               spec(shape, 4, [3, 4, 5, 6], [7, 6, 5, 4], seed=7)]
+    stride = max(B.fpi8_state_size(cfg, len(ids), mx) for b in batches for ids, mx, _, _ in b)
+    stride = (stride + 255) // 256 * 256
+    model = DeviceModel(blob, 4)
+    arena = torch.zeros(4 * stride, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    derr = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    try:
+        for k, runs in enumerate(batches):
+            pair = Pair(shape, blob, runs, model=model)
+            arena.zero_()
+            b = pair.batch
+            for i in range(4):
+                arena[i * stride: i * stride + b.sizes[i]].copy_(b.d_states[i * b.stride: i * b.stride + b.sizes[i]])
+            b.d_states, b.stride = arena, stride
+            torch.cuda.synchronize()
+            e, herrs = B.fpi8_turn_bind(model.engine, arena, stride, 4, stream)
+            assert e == 0 and list(herrs) == [0, 0, 0, 0]
+            for cut in (2, 1, 3):
+                assert B.fpi8_turn_async(model.engine, cut, stream, derr) == 0
+            stream.synchronize()
+            assert derr.cpu().tolist() == [0, 0, 0, 0]
+            for i in range(4):
+                for cut in (2, 1, 3):
+                    assert O.turn(blob, pair.ref[i], cut) == 0
+            pair.compare()
+            say(f"batch {k} matches")
+    finally:
+        model.close()
+
+
 def test_full_size_units():
     # Turns of unit budgets at the 1.1B shape and its batch width: the
     # budgets stop runs inside matrices, attention stages and sampling
