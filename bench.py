@@ -343,7 +343,17 @@ def main():
     shape = w.shape
     if args.steps is None:
         args.steps = w.max_tokens - 1 - args.warmup - args.kernel_steps
-    if args.steps < 1 or args.warmup + args.steps + args.kernel_steps > w.max_tokens - 1:
+    window = w.max_tokens - 1  # decode positions of the workload
+    if args.warmup + args.steps + args.kernel_steps > window:
+        # more than the window holds: keep the order (warm-up, timed, kernel-timed)
+        # and time what is left, saying so
+        args.warmup = min(args.warmup, window - 2)
+        args.kernel_steps = max(1, min(args.kernel_steps, window - args.warmup - 1))
+        asked = args.steps
+        args.steps = window - args.warmup - args.kernel_steps
+        log(f"{asked} timed steps do not fit the {window} decode positions with the warm-up and "
+            f"kernel-timed steps; timing {args.steps}")
+    if args.steps < 1 or args.warmup < 0:
         raise SystemExit("warmup + steps + kernel steps exceed the decode positions of the workload")
 
     t = time.perf_counter()
