@@ -281,13 +281,26 @@ def test_tiny_context_fills_exactly():
     run_pair(w.shape, blob, [(ids, 17, 0, 0)], [40])
 
 
-@pytest.mark.parametrize("name", ["gqa", "ragged", "wide", "h8"])
+@pytest.mark.parametrize("name", ["gqa", "ragged", "wide", "h8", "h256", "h4"])
 def test_small_shapes_greedy(name):
     shape = W.SMALL_SHAPES[name]
     say(f"small shape {name}")
     blob = Bl.build_blob(shape, 11)
     runs = spec(shape, 5, [1, 4, 7, 2, 9], [9, 5, 3, 12, 1])
     run_pair(shape, blob, runs, [1, 2, 3, 1, 5])
+
+
+@pytest.mark.parametrize("name", ["h256", "h4", "gqa", "split"])
+def test_small_shapes_one_layout(name):
+    # Every run of the batch with the same layout: the normalization and
+    # attention read through the common offsets (queries and first keys
+    # requested before the run descriptors), at head sizes 256, 4, 16
+    # (grouped) and 128.
+    shape = W.SMALL_SHAPES[name]
+    say(f"small shape {name}, one layout")
+    blob = Bl.build_blob(shape, 13)
+    runs = spec(shape, 6, 5, 8, seed=9)
+    run_pair(shape, blob, runs, [1, 3, 2, 6])
 
 
 def test_one_arena_across_layouts():

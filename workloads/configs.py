@@ -97,6 +97,9 @@ SMALL_SHAPES = {
     "h8": Shape(64, 128, 1, 8, 4, 64, 24),
     # wide enough that the row kernel splits the columns of every matrix
     "split": Shape(1024, 2816, 2, 8, 4, 700, 24),
+    # the longest and the shortest heads of the vector attention path, grouped
+    "h256": Shape(512, 1024, 2, 2, 1, 500, 40),
+    "h4": Shape(32, 96, 1, 8, 2, 200, 24),
 }
 
 
