@@ -370,15 +370,21 @@ def test_row_kernels_whole_pass(n_runs, row_kernel):
     run_pair(shape, blob, runs, [1, 3], row_kernel=row_kernel)
 
 
-@pytest.mark.parametrize("streams,n_runs,graph", [(2, 5, True), (2, 20, True), (1, 70, True),
-                                                  (1, 20, False), (2, 20, False)])
-def test_run_groups_on_two_streams(streams, n_runs, graph):
+@pytest.mark.parametrize("streams,n_runs,graph,one_layout", [
+    (2, 5, True, False), (2, 20, True, False), (1, 70, True, False), (1, 20, False, False),
+    (2, 20, False, False), (2, 20, True, True), (2, 7, False, True)])
+def test_run_groups_on_two_streams(streams, n_runs, graph, one_layout):
     # The batch split in two groups, each advanced on its own stream, and a
-    # wide batch on one stream.
+    # wide batch on one stream; runs of several layouts, or of one (the
+    # second group then reads through the common offsets from its own first
+    # run on).
     shape = W.SMALL_SHAPES["gqa"]
-    say(f"{n_runs} runs on {streams} stream(s), graph {graph}")
+    say(f"{n_runs} runs on {streams} stream(s), graph {graph}, one layout {one_layout}")
     blob = Bl.build_blob(shape, 25)
-    runs = spec(shape, n_runs, [1 + (r % 6) for r in range(n_runs)], [1 + (r % 5) for r in range(n_runs)])
+    if one_layout:
+        runs = spec(shape, n_runs, 4, 5)
+    else:
+        runs = spec(shape, n_runs, [1 + (r % 6) for r in range(n_runs)], [1 + (r % 5) for r in range(n_runs)])
     run_pair(shape, blob, runs, [1, 2, 4], streams=streams, graph=graph)
 
 
